@@ -1,0 +1,104 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of an oracle module (a textual edit
+of its source, executed as a fresh module on the CPU), points one pin test at
+the copy and expects that pin to fail. The real oracle is never modified."""
+
+import inspect
+import types
+
+import pytest
+
+import oracle.bf16
+import oracle.loss
+import oracle.philox
+import oracle.verify
+
+from . import test_oracle_bf16 as t_bf16
+from . import test_oracle_loss as t_loss
+from . import test_oracle_philox as t_philox
+from . import test_oracle_verify as t_verify
+
+
+def _mutant(module, old, new):
+    src = inspect.getsource(module)
+    assert src.count(old) == 1, f"mutation anchor not unique in {module.__name__}: {old!r}"
+    mod = types.ModuleType(module.__name__)
+    mod.__package__ = "oracle"
+    mod.__file__ = module.__file__
+    exec(compile(src.replace(old, new), module.__file__, "exec"), mod.__dict__)
+    return mod
+
+
+# (oracle module, anchor, replacement, test module, its alias for the oracle
+#  module, pin test, args)
+CASES = [
+    ("accept compares with <=", oracle.verify,
+     "return bool(u < r), abs(u - r)", "return bool(u <= r), abs(u - r)",
+     t_verify, "ov", "test_accept_rule_threshold_on_the_24_bit_lattice", ()),
+    ("accept when q(y) = 0 and p(y) = 0", oracle.verify,
+     "return bool(p_y > 0.0), np.inf", "return True, np.inf",
+     t_verify, "ov", "test_accept_rule_threshold_on_the_24_bit_lattice", ()),
+    ("residual drawn from p instead of max(0, p - q)", oracle.verify,
+     "w = np.maximum(0.0, p[j] - q[j])", "w = p[j]",
+     t_verify, "ov", "test_residual_support_invariant", ()),
+    ("residual drawn from max(0, q - p)", oracle.verify,
+     "w = np.maximum(0.0, p[j] - q[j])", "w = np.maximum(0.0, q[j] - p[j])",
+     t_verify, "ov", "test_single_position_law_rebuilds_target", ()),
+    ("bonus drawn from the last draft position", oracle.verify,
+     "        w = p[k_b]\n", "        w = p[k_b - 1]\n",
+     t_verify, "ov", "test_chi_square_emitted_law_two_positions", ()),
+    ("inverse CDF takes the first C[v] >= target", oracle.verify,
+     'side="right"', 'side="left"',
+     t_verify, "ov", "test_draw_counts_on_the_24_bit_lattice", ()),
+    ("overlap sums max instead of min", oracle.verify,
+     "np.sum(np.minimum(p, q))", "np.sum(np.maximum(p, q))",
+     t_verify, "ov", "test_alpha_is_one_minus_tv", (1.0,)),
+    ("temperature multiplies instead of divides", oracle.verify,
+     "inv_t = np.float32(1.0) / np.float32(temperature)",
+     "inv_t = np.float32(temperature)",
+     t_verify, "ov", "test_alpha_is_one_minus_tv", (0.6,)),
+    ("greedy correction takes the draft argmax", oracle.verify,
+     'out["tokens"][j] = g[j]', 'out["tokens"][j] = h[j] if j < k_b else g[j]',
+     t_verify, "ov", "test_greedy_literal_rule_with_arbitrary_tokens", ()),
+    ("scan continues past a rejection", oracle.verify,
+     "            j = k\n            break\n\n    _, u_draw",
+     "            j = k\n\n    _, u_draw",
+     t_verify, "ov", "test_chi_square_emitted_law_two_positions", ()),
+    ("gradient weight uses P_k instead of P_{k-1}", oracle.loss,
+     "g = -prev * suffix", "g = -prefix * suffix",
+     t_loss, "ol", "test_gradient_matches_torch_autograd", ()),
+    ("gradient sign flipped on the q >= p side", oracle.loss,
+     "-coef * q * s_below[:, None]", "coef * q * s_below[:, None]",
+     t_loss, "ol", "test_gradient_central_differences", ()),
+    ("suffix recursion drops alpha", oracle.loss,
+     "suffix[k] = 1.0 + alpha[k + 1] * suffix[k + 1]",
+     "suffix[k] = 1.0 + suffix[k + 1]",
+     t_loss, "ol", "test_gradient_matches_torch_autograd", ()),
+    ("branches summed instead of averaged", oracle.loss,
+     '"loss": total / n_br,', '"loss": total,',
+     t_loss, "ol", "test_worked_examples",
+     ({"alphas": [0.8, 0.8, 0.8, 0.8], "expected_emitted": 3.3616},)),
+    ("Philox key not bumped between rounds", oracle.philox,
+     "k0 = (k0 + _WEYL_A) & _MASK64", "k0 = k0",
+     t_philox, "philox", "test_block_matches_numpy_random_counters", ()),
+    ("Philox words permuted wrongly", oracle.philox,
+     "c0, c1, c2, c3 = hi_b ^ c1 ^ k0, lo_b, hi_a ^ c3 ^ k1, lo_a",
+     "c0, c1, c2, c3 = hi_a ^ c1 ^ k0, lo_b, hi_b ^ c3 ^ k1, lo_a",
+     t_philox, "philox", "test_block_matches_numpy_random_counters", ()),
+    ("uniform from the low bits", oracle.philox,
+     "float(int(word) >> 40)", "float(int(word) & 0xFFFFFF)",
+     t_philox, "philox", "test_uniforms_are_top_24_bits", ()),
+    ("bf16 ties rounded away from zero", oracle.bf16,
+     "np.rint(scaled)", "np.floor(scaled + 0.5)",
+     t_bf16, "bf16", "test_ties_round_to_even", ()),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pin_catches_planted_mistake(case, monkeypatch):
+    _, module, old, new, test_mod, alias, test_name, args = case
+    mutant = _mutant(module, old, new)
+    monkeypatch.setattr(test_mod, alias, mutant)
+    with pytest.raises(AssertionError):
+        getattr(test_mod, test_name)(*args)
