@@ -1,0 +1,170 @@
+/*
+ * lvtv -- speculative-sampling verify and E2E-TV loss on AMD MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only. Every pointer argument except the
+ * workspace-size queries is a DEVICE pointer on the current HIP device;
+ * `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *
+ * Ownership: the caller owns every buffer, the workspace included. The
+ * library never allocates, frees or keeps device memory between calls and
+ * never synchronises the stream. All work is enqueued on `stream` in order;
+ * outputs are valid once the caller's later work on that stream (or an
+ * event recorded after the call) has completed. One workspace serves one
+ * call at a time: calls that share a workspace must be ordered on one
+ * stream.
+ *
+ * Errors: a call returns LVTV_OK (0) or a negative code. A negative code
+ * means nothing was enqueued and no output was written (host-checkable
+ * errors: null pointers, bad sizes, unknown dtype, too small a workspace),
+ * except LVTV_ERR_LAUNCH, returned when the HIP runtime rejects a launch.
+ * Faults that live in device memory (per-request K, token ids,
+ * temperatures, non-finite logits) cannot be checked on the host without a
+ * sync; spec_verify reports them per request in `status` instead.
+ *
+ * Sources, cited by page title and section:
+ *   "Reading Qwen Bebop and DeepSeek DSpark" (lilfry09.github.io), section
+ *     "Formulas: what makes a guess worth it" (eqs. alpha(y), alpha_RS,
+ *     d_TV, P(tau >= j), E[tau]) and section "Bebop's solution" (TV loss,
+ *     end-to-end TV loss).
+ *   "SpecOPD: Branch-Parallel On-Policy Distillation for Speculative
+ *     Decoding" (paper.rainbus.top summary), prerequisite "Acceptance length
+ *     and the E2E-TV objective" and method step (6).
+ *   "Speculative Decoding and MTP" survey (papers-3lj.pages.dev), sections 2
+ *     (draft/target loop), 3 (probabilistic correctness), 4 (greedy versus
+ *     sampling), 21 (fuse acceptance and residual sampling on the GPU to
+ *     avoid a CPU sync per cycle).
+ */
+#ifndef LVTV_H
+#define LVTV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Logit storage types. */
+#define LVTV_F32 0  /* IEEE binary32                                  */
+#define LVTV_BF16 1 /* bfloat16 bit patterns in uint16 (top half of binary32) */
+
+/* Return codes. */
+#define LVTV_OK 0
+#define LVTV_ERR_NULL (-1)      /* a required pointer is NULL            */
+#define LVTV_ERR_SHAPE (-2)     /* a size is out of the supported range  */
+#define LVTV_ERR_DTYPE (-3)     /* unknown dtype                         */
+#define LVTV_ERR_WORKSPACE (-4) /* workspace NULL or smaller than queried */
+#define LVTV_ERR_LAUNCH (-5)    /* the HIP runtime rejected a launch     */
+
+/* Supported ranges. */
+#define LVTV_MAX_K 16         /* draft positions per request (Kmax)      */
+#define LVTV_MAX_W 16         /* positions per branch (W)                */
+#define LVTV_MAX_V (1 << 27)  /* vocabulary size                         */
+
+/* Per-request status bits written by spec_verify. */
+#define LVTV_STATUS_BAD_K 1           /* K_b outside [0, Kmax]                 */
+#define LVTV_STATUS_BAD_TOKEN 2       /* a draft token (k < K_b) outside [0,V) */
+#define LVTV_STATUS_BAD_TEMPERATURE 4 /* T_b negative, NaN or infinite         */
+#define LVTV_STATUS_NONFINITE 8       /* a used row holds NaN or +inf, or is
+                                         entirely -inf (after scaling)         */
+
+int lvtv_version(void);
+const char* lvtv_strerror(int code);
+
+/*
+ * Workspace bytes spec_verify needs for these sizes (0 if the sizes are out
+ * of range). Host function; no HIP call.
+ */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype);
+
+/*
+ * spec_verify -- one verify step for B requests.
+ *
+ * What it computes, per request b with K_b draft positions:
+ *   * scaled logits s = fl32(x * fl32(1/T_b)), the same transform for target
+ *     and draft (survey, section 4); p_k = softmax(s_target[b,k]) for
+ *     k <= K_b, q_k = softmax(s_draft[b,k]) for k < K_b;
+ *   * overlap alpha_k = sum_v min(p_k, q_k) = 1 - d_TV(p_k, q_k) for every
+ *     k < K_b ("Formulas", eq. alpha_RS);
+ *   * the accept scan: draft token y_k is accepted iff u_k < p_k(y_k)/q_k(y_k)
+ *     (acceptance probability min(1, p/q), "Formulas", eq. alpha(y)), in
+ *     order, up to the first rejection j (survey, section 2);
+ *   * the correction token drawn from max(0, p_j - q_j)/Z_j if j < K_b
+ *     (survey, section 3), or the bonus token drawn from p_{K_b} if every
+ *     draft was accepted (survey, section 2); draws are inverse-CDF in
+ *     ascending token id;
+ *   * at T_b = 0 the greedy rule (survey, section 4): accept while y_k is
+ *     the target argmax (lowest index among ties), emit the target argmax at
+ *     the first mismatch or as the bonus; alpha_k = [argmax t == argmax d].
+ * Randomness: Philox4x64-10 (Salmon et al., SC'11) with key (seed_b, 0) and
+ * counter (b, k, 0, 0); u_k = (word0 >> 40) * 2^-24 for the accept test at
+ * position k, u'_k = (word1 >> 40) * 2^-24 for a draw at position k. No
+ * per-call state: a call is a pure function of its inputs.
+ *
+ * Arguments (device pointers; row-major, V contiguous):
+ *   target_logits  [B, Kmax+1, V] of `dtype`; rows k > K_b are not read.
+ *   draft_logits   [B, Kmax,   V] of `dtype`; rows k >= K_b are not read.
+ *   dtype          LVTV_F32 or LVTV_BF16.
+ *   draft_tokens   int32 [B, Kmax]; entries k >= K_b are not read.
+ *   k_per_req      int32 [B], K_b in 0..Kmax (0 = one token sampled from p_0).
+ *   temperature    float [B]; 0 = greedy, > 0 stochastic.
+ *   seed           uint64 [B], Philox key word 0 for request b.
+ *   B, Kmax, V     1 <= B, 0 <= Kmax <= LVTV_MAX_K, 1 <= V <= LVTV_MAX_V.
+ *   accepted_len   int32 [B] out: j (number of accepted drafts), -1 if faulted.
+ *   out_tokens     int32 [B, Kmax+1] out: y_0..y_{j-1}, the drawn token, then -1.
+ *   alpha          float [B, Kmax] out: alpha_k for k < K_b, 0 otherwise.
+ *   status         int32 [B] out: LVTV_STATUS_* bits, 0 if fine. A faulted
+ *                  request gets accepted_len = -1, all tokens -1, alpha 0.
+ *   workspace      device scratch of >= spec_verify_workspace_bytes(...)
+ *                  bytes, 256-byte aligned; contents need no initialisation
+ *                  and are garbage after the call.
+ *   stream         hipStream_t.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                const int32_t* draft_tokens, const int32_t* k_per_req,
+                const float* temperature, const uint64_t* seed, int32_t B,
+                int32_t Kmax, int32_t V, int32_t* accepted_len,
+                int32_t* out_tokens, float* alpha, int32_t* status,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes e2e_tv_loss_fwd_bwd needs (0 if out of range). Host only.
+ */
+size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V);
+
+/*
+ * e2e_tv_loss_fwd_bwd -- E2E-TV prefix-product loss and its gradient.
+ *
+ * What it computes (SpecOPD, method step (6); Bebop section, E[tau]):
+ *   q_{n,k} = softmax(z[n,k,:]) of the draft logits (no temperature);
+ *   alpha_{n,k} = sum_v min(q_{n,k}(v), p[n,k,v]) with p used as given;
+ *   L_n = -sum_{j<W} prod_{k<=j} alpha_{n,k};   loss = (1/N) sum_n L_n;
+ *   dlogits[n,k,u] = dloss/dz[n,k,u] with p held constant:
+ *     (G_{n,k}/N) * q(u) * ([q(u) < p(u)] - S_{n,k}),
+ *     G_{n,k} = -P_{k-1} R_k, P_j = prod_{i<=j} alpha_i, P_{-1} = 1,
+ *     R_{W-1} = 1, R_k = 1 + alpha_{k+1} R_{k+1}, S = sum_{q<p} q;
+ *   the subgradient of min at q = p is 0; dlogits is rounded to bfloat16,
+ *   round-to-nearest-even, from its fp32 value.
+ *
+ * Arguments (device pointers; row-major, V contiguous):
+ *   draft_logits   bfloat16 (uint16) [N, W, V].
+ *   target_probs   float [N, W, V], constants.
+ *   N, W, V        1 <= N, 1 <= W <= LVTV_MAX_W, 1 <= V <= LVTV_MAX_V.
+ *   loss           float [1] out.
+ *   alpha          float [N, W] out.
+ *   dlogits        bfloat16 (uint16) [N, W, V] out.
+ *   workspace      device scratch of >= e2e_tv_loss_workspace_bytes(...)
+ *                  bytes, 256-byte aligned, no initialisation needed.
+ *   stream         hipStream_t.
+ * NaN or infinite inputs propagate into the outputs; there is no status.
+ */
+int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
+                        int32_t N, int32_t W, int32_t V, float* loss,
+                        float* alpha, uint16_t* dlogits, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LVTV_H */

@@ -1,0 +1,29 @@
+"""lossless_verify_tv_amd -- speculative-sampling verify and E2E-TV loss on
+AMD MI355X (gfx950).
+
+The work runs in hand-written HIP kernels behind a C ABI (``include/lvtv.h``,
+``liblvtv.so``). This package holds the kernels and the ABI
+(``csrc/``), the build script (``build``), a thin ctypes binding
+(``spec_verify``, ``e2e_tv_loss_fwd_bwd``) and the seeded synthetic input
+generators (``synth``).
+
+The binding loads the library lazily, on first call, and raises if it is
+missing; there is no CPU fallback.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LVTV_BF16,
+    LVTV_F32,
+    STATUS_BAD_K,
+    STATUS_BAD_TEMPERATURE,
+    STATUS_BAD_TOKEN,
+    STATUS_NONFINITE,
+    LvtvError,
+    e2e_tv_loss_fwd_bwd,
+    e2e_tv_loss_workspace_bytes,
+    load_library,
+    spec_verify,
+    spec_verify_workspace_bytes,
+    strerror,
+)

@@ -1,0 +1,203 @@
+"""ctypes binding of liblvtv.so: argument marshalling only.
+
+Every step of the verify and the loss runs in the library's HIP kernels;
+this module checks tensor dtypes, devices and layouts, allocates outputs and
+the workspace with torch on the tensors' device, and passes raw pointers and
+torch's current HIP stream. There is no CPU fallback: if the library is not
+built, or the tensors are not on a GPU, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblvtv.so")
+
+LVTV_F32 = 0
+LVTV_BF16 = 1
+
+STATUS_BAD_K = 1
+STATUS_BAD_TOKEN = 2
+STATUS_BAD_TEMPERATURE = 4
+STATUS_NONFINITE = 8
+
+EXPORTS = (
+    "lvtv_version",
+    "lvtv_strerror",
+    "spec_verify_workspace_bytes",
+    "spec_verify",
+    "e2e_tv_loss_workspace_bytes",
+    "e2e_tv_loss_fwd_bwd",
+)
+
+_lib = None
+_lock = threading.Lock()
+
+
+class LvtvError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load liblvtv.so and declare its signatures (no HIP call is made)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise LvtvError(
+                f"{path} is missing: build it with `python -m lossless_verify_tv_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        lib.lvtv_version.restype = ctypes.c_int
+        lib.lvtv_version.argtypes = []
+        lib.lvtv_strerror.restype = ctypes.c_char_p
+        lib.lvtv_strerror.argtypes = [ctypes.c_int]
+        lib.spec_verify_workspace_bytes.restype = sz
+        lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
+        lib.spec_verify.restype = ctypes.c_int
+        lib.spec_verify.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32,
+                                    vp, vp, vp, vp, vp, sz, vp]
+        lib.e2e_tv_loss_workspace_bytes.restype = sz
+        lib.e2e_tv_loss_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.e2e_tv_loss_fwd_bwd.restype = ctypes.c_int
+        lib.e2e_tv_loss_fwd_bwd.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        _lib = lib
+        return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().lvtv_strerror(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise LvtvError(f"{what} failed: {strerror(code)} (code {code})")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+# Workspaces are cached per device and grown on demand. Calls on one device
+# that share the cached workspace must run on one stream (torch's current
+# stream); pass an explicit `workspace` otherwise.
+_workspaces: dict = {}
+
+
+def _workspace(device, nbytes):
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def spec_verify_workspace_bytes(B, Kmax, V, dtype=LVTV_BF16) -> int:
+    return int(load_library().spec_verify_workspace_bytes(B, Kmax, V, dtype))
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperature, seed,
+                workspace=None, out=None):
+    """Verify step for B requests (see include/lvtv.h for the contract).
+
+    target_logits [B, Kmax+1, V] and draft_logits [B, Kmax, V]: float32 or
+    bfloat16, contiguous, on one GPU. draft_tokens int32 [B, Kmax];
+    k_per_req int32 [B]; temperature float32 [B]; seed int64/uint64 [B]
+    (bit pattern used as the 64-bit Philox key). Returns (accepted_len
+    int32 [B], out_tokens int32 [B, Kmax+1], alpha float32 [B, Kmax],
+    status int32 [B]) on the device; no synchronisation.
+    """
+    lib = load_library()
+    dev = target_logits.device
+    _require(dev.type == "cuda", "spec_verify needs GPU tensors")
+    _require(target_logits.dim() == 3 and draft_logits.dim() == 3, "logits must be 3-D")
+    B, K1, V = target_logits.shape
+    Kmax = K1 - 1
+    _require(tuple(draft_logits.shape) == (B, Kmax, V), "draft_logits must be [B, Kmax, V]")
+    _require(target_logits.dtype == draft_logits.dtype, "target and draft dtypes differ")
+    if target_logits.dtype == torch.bfloat16:
+        dtype = LVTV_BF16
+    elif target_logits.dtype == torch.float32:
+        dtype = LVTV_F32
+    else:
+        raise ValueError("logits must be float32 or bfloat16")
+    for name, t, dt, shape in (("draft_tokens", draft_tokens, (torch.int32,), (B, Kmax)),
+                               ("k_per_req", k_per_req, (torch.int32,), (B,)),
+                               ("temperature", temperature, (torch.float32,), (B,)),
+                               ("seed", seed, (torch.int64, torch.uint64), (B,))):
+        _require(t.dtype in dt, f"{name} must be {dt}")
+        _require(tuple(t.shape) == shape, f"{name} must have shape {shape}")
+        _require(t.device == dev and t.is_contiguous(), f"{name} must be contiguous on {dev}")
+    for t in (target_logits, draft_logits):
+        _require(t.device == dev and t.is_contiguous(), "logits must be contiguous on one GPU")
+    need = lib.spec_verify_workspace_bytes(B, Kmax, V, dtype)
+    _require(need > 0, f"sizes out of range: B={B} Kmax={Kmax} V={V}")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(B, Kmax + 1, dtype=torch.int32, device=dev)
+        alpha = torch.empty(B, max(Kmax, 0), dtype=torch.float32, device=dev)
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        acc, toks, alpha, status = out
+    with torch.cuda.device(dev):
+        code = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype,
+                               _ptr(draft_tokens), _ptr(k_per_req), _ptr(temperature),
+                               _ptr(seed), B, Kmax, V, _ptr(acc), _ptr(toks), _ptr(alpha),
+                               _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    _check(code, "spec_verify")
+    return acc, toks, alpha, status
+
+
+def e2e_tv_loss_workspace_bytes(N, W, V) -> int:
+    return int(load_library().e2e_tv_loss_workspace_bytes(N, W, V))
+
+
+def e2e_tv_loss_fwd_bwd(draft_logits, target_probs, workspace=None, out=None):
+    """E2E-TV loss and gradient (see include/lvtv.h).
+
+    draft_logits bfloat16 [N, W, V], target_probs float32 [N, W, V], both
+    contiguous on one GPU. Returns (loss float32 [1], alpha float32 [N, W],
+    dlogits bfloat16 [N, W, V]) on the device; no synchronisation.
+    """
+    lib = load_library()
+    dev = draft_logits.device
+    _require(dev.type == "cuda", "e2e_tv_loss_fwd_bwd needs GPU tensors")
+    _require(draft_logits.dtype == torch.bfloat16, "draft_logits must be bfloat16")
+    _require(target_probs.dtype == torch.float32, "target_probs must be float32")
+    _require(draft_logits.dim() == 3 and tuple(target_probs.shape) == tuple(draft_logits.shape),
+             "draft_logits and target_probs must both be [N, W, V]")
+    for t in (draft_logits, target_probs):
+        _require(t.device == dev and t.is_contiguous(), "inputs must be contiguous on one GPU")
+    N, W, V = draft_logits.shape
+    need = lib.e2e_tv_loss_workspace_bytes(N, W, V)
+    _require(need > 0, f"sizes out of range: N={N} W={W} V={V}")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    if out is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        alpha = torch.empty(N, W, dtype=torch.float32, device=dev)
+        dlogits = torch.empty(N, W, V, dtype=torch.bfloat16, device=dev)
+    else:
+        loss, alpha, dlogits = out
+    with torch.cuda.device(dev):
+        code = lib.e2e_tv_loss_fwd_bwd(_ptr(draft_logits), _ptr(target_probs), N, W, V,
+                                       _ptr(loss), _ptr(alpha), _ptr(dlogits), _ptr(ws),
+                                       ws.numel(), _stream(dev))
+    _check(code, "e2e_tv_loss_fwd_bwd")
+    return loss, alpha, dlogits

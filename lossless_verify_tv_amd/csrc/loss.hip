@@ -1,0 +1,325 @@
+// e2e_tv_loss_fwd_bwd: E2E-TV prefix-product loss and its gradient on gfx950.
+//
+// Definition (page title, section): "SpecOPD: Branch-Parallel On-Policy
+// Distillation for Speculative Decoding", prerequisite "Acceptance length and
+// the E2E-TV objective" (alpha = sum min(q, p) = 1 - TV; prefix products of
+// alpha aggregate it) and method step (6) (the prefix product of the
+// per-position overlaps gives the loss; only the draft probabilities are
+// differentiated, samples and target are constants); "Reading Qwen Bebop and
+// DeepSeek DSpark", section "Bebop's solution" (E[tau] = sum_j prod_{k<=j}
+// (1 - d_TV)).
+//
+// Pipeline (launches on the caller's stream, no host sync):
+//   1. row_stats  grid (slice, position, branch): per slice (m, sum exp(z - m)).
+//   2. overlap    grid (slice, position, branch): q = softmax(z) from the
+//                 combined statistics; per slice alpha = sum min(q, p),
+//                 S = sum_{q<p} q and S' = sum_{q>=p} q, in fp64.
+//   3. branch     grid (branch): alpha_k, S_k, S'_k; prefix products P_j,
+//                 suffix sums R_k = 1 + alpha_{k+1} R_{k+1}, the branch loss
+//                 L_n = -sum_j P_j and dL_n/dalpha_k = -P_{k-1} R_k; the
+//                 per-row gradient coefficients.
+//   4. reduce     one workgroup: loss = (1/N) sum_n L_n in fixed order.
+//   5. grad       grid (slice, position, branch): dz = q (G/N) S' where q < p,
+//                 -q (G/N) S elsewhere; bfloat16 round-to-nearest-even.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/lvtv.h"
+#include "device_common.hpp"
+
+namespace lvtv {
+namespace {
+
+constexpr int kSlice = kBlock * kVec * 4;  // 8192 elements per slice
+constexpr int kSteps = kSlice / (kBlock * kVec);
+
+struct RowFinal {
+  float neg_m_log2e;  // -M log2(e)
+  float inv_l;        // 1 / L
+  float c_below;      // (G/N) S'   applied where q < p
+  float c_above;      // -(G/N) S   applied where q >= p
+};
+
+struct Part {
+  double alpha, s_below, s_above;
+};
+
+struct Layout {
+  int S;
+  size_t off_stat, off_part, off_fin, off_branch, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(int N, int W, int V) {
+  Layout L;
+  L.S = (V + kSlice - 1) / kSlice;
+  const size_t rows = size_t(N) * W;
+  size_t off = 0;
+  L.off_stat = off;
+  off = align256(off + sizeof(SliceStat) * rows * L.S);
+  L.off_part = off;
+  off = align256(off + sizeof(Part) * rows * L.S);
+  L.off_fin = off;
+  off = align256(off + sizeof(RowFinal) * rows);
+  L.off_branch = off;
+  off = align256(off + sizeof(double) * size_t(N));
+  L.total = off;
+  return L;
+}
+
+struct Args {
+  const uint16_t* z;
+  const float* p;
+  int N, W, V;
+  bool vec_ok;
+  float* loss;
+  float* alpha;
+  uint16_t* dz;
+  Layout L;
+  SliceStat* stat;
+  Part* part;
+  RowFinal* fin;
+  double* branch_loss;
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x0040u);  // quiet NaN
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ void load8_p(const float* row, int64_t e, int64_t V, bool vec_ok,
+                                        float (&x)[kVec]) {
+  if (vec_ok && e + kVec <= V) {
+    const float4 a = *reinterpret_cast<const float4*>(row + e);
+    const float4 b = *reinterpret_cast<const float4*>(row + e + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) x[i] = (e + i < V) ? row[e + i] : 0.f;
+  }
+}
+
+__device__ __forceinline__ int64_t elem_index(int s, int it) {
+  return int64_t(s) * kSlice + it * (kBlock * kVec) + threadIdx.x * kVec;
+}
+
+__global__ __launch_bounds__(kBlock) void row_stats_kernel(Args a) {
+  const int s = blockIdx.x;
+  const size_t row = size_t(blockIdx.z) * a.W + blockIdx.y;
+  const uint16_t* z = a.z + row * a.V;
+  __shared__ double sd[kWavesPerBlock];
+  __shared__ float sf[kWavesPerBlock];
+  float x[kSteps][kVec];
+  float m = -INFINITY;
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    load8<1>(z, elem_index(s, it), a.V, a.vec_ok, x[it]);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) m = fmaxf(m, x[it][i]);
+  }
+  m = block_max(m, sf);
+  const float ref = (m == -INFINITY) ? 0.f : m;
+  const float neg = -ref * kLog2e;
+  double l = 0.0;
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) acc += exp_shifted(x[it][i], neg);
+    l += acc;
+  }
+  l = block_sum(l, sd);
+  if (threadIdx.x == 0) a.stat[row * a.L.S + s] = SliceStat{(double)m, l};
+}
+
+__global__ __launch_bounds__(kBlock) void overlap_kernel(Args a) {
+  const int s = blockIdx.x;
+  const size_t row = size_t(blockIdx.z) * a.W + blockIdx.y;
+  __shared__ double sd[kWavesPerBlock];
+  __shared__ float sf[kWavesPerBlock];
+  double M, L;
+  combine_row_stats(a.stat + row * a.L.S, a.L.S, sd, sf, M, L);
+  const float neg = -float(M) * kLog2e;
+  const float inv_l = float(1.0 / L);
+  const uint16_t* z = a.z + row * a.V;
+  const float* p = a.p + row * a.V;
+  double al = 0.0, sb = 0.0, sa = 0.0;
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    const int64_t e = elem_index(s, it);
+    float xz[kVec], xp[kVec];
+    load8<1>(z, e, a.V, a.vec_ok, xz);
+    load8_p(p, e, a.V, a.vec_ok, xp);
+    float a_min = 0.f, a_below = 0.f, a_above = 0.f;
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const float q = exp_shifted(xz[i], neg) * inv_l;
+      a_min += fminf(q, xp[i]);
+      const bool below = q < xp[i];
+      a_below += below ? q : 0.f;
+      a_above += below ? 0.f : q;
+    }
+    al += a_min;
+    sb += a_below;
+    sa += a_above;
+  }
+  al = block_sum(al, sd);
+  sb = block_sum(sb, sd);
+  sa = block_sum(sa, sd);
+  if (threadIdx.x == 0) a.part[row * a.L.S + s] = Part{al, sb, sa};
+}
+
+__global__ __launch_bounds__(kBlock) void branch_kernel(Args a) {
+  const int n = blockIdx.x;
+  const int W = a.W;
+  __shared__ double sd[kWavesPerBlock];
+  __shared__ float sf[kWavesPerBlock];
+  __shared__ double al[LVTV_MAX_W], sb[LVTV_MAX_W], sa[LVTV_MAX_W];
+  __shared__ double Ms[LVTV_MAX_W], Ls[LVTV_MAX_W];
+  for (int k = 0; k < W; ++k) {
+    const size_t row = size_t(n) * W + k;
+    double M, L;
+    combine_row_stats(a.stat + row * a.L.S, a.L.S, sd, sf, M, L);
+    double x = 0.0, y = 0.0, w = 0.0;
+    for (int s = threadIdx.x; s < a.L.S; s += kBlock) {
+      const Part pt = a.part[row * a.L.S + s];
+      x += pt.alpha;
+      y += pt.s_below;
+      w += pt.s_above;
+    }
+    x = block_sum(x, sd);
+    y = block_sum(y, sd);
+    w = block_sum(w, sd);
+    if (threadIdx.x == 0) {
+      al[k] = x;
+      sb[k] = y;
+      sa[k] = w;
+      Ms[k] = M;
+      Ls[k] = L;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double prefix[LVTV_MAX_W], suffix[LVTV_MAX_W];
+    double run = 1.0, loss_n = 0.0;
+    for (int k = 0; k < W; ++k) {
+      run *= al[k];
+      prefix[k] = run;
+      loss_n -= run;
+    }
+    suffix[W - 1] = 1.0;
+    for (int k = W - 2; k >= 0; --k) suffix[k] = 1.0 + al[k + 1] * suffix[k + 1];
+    const double inv_n = 1.0 / double(a.N);
+    for (int k = 0; k < W; ++k) {
+      const double g = -(k > 0 ? prefix[k - 1] : 1.0) * suffix[k] * inv_n;
+      const size_t row = size_t(n) * W + k;
+      a.fin[row] = RowFinal{-float(Ms[k]) * kLog2e, float(1.0 / Ls[k]), float(g * sa[k]),
+                            float(-g * sb[k])};
+      a.alpha[row] = float(al[k]);
+    }
+    a.branch_loss[n] = loss_n;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void reduce_kernel(Args a) {
+  __shared__ double sd[kWavesPerBlock];
+  // fixed order: contiguous blocks per thread, then the block tree
+  const int per = (a.N + kBlock - 1) / kBlock;
+  double x = 0.0;
+  for (int n = threadIdx.x * per; n < min(a.N, (int(threadIdx.x) + 1) * per); ++n)
+    x += a.branch_loss[n];
+  x = block_sum(x, sd);
+  if (threadIdx.x == 0) a.loss[0] = float(x / double(a.N));
+}
+
+__global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
+  const int s = blockIdx.x;
+  const size_t row = size_t(blockIdx.z) * a.W + blockIdx.y;
+  const RowFinal f = a.fin[row];
+  const uint16_t* z = a.z + row * a.V;
+  const float* p = a.p + row * a.V;
+  uint16_t* dz = a.dz + row * a.V;
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    const int64_t e = elem_index(s, it);
+    if (e >= a.V) break;
+    float xz[kVec], xp[kVec];
+    load8<1>(z, e, a.V, a.vec_ok, xz);
+    load8_p(p, e, a.V, a.vec_ok, xp);
+    uint16_t out[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const float q = exp_shifted(xz[i], f.neg_m_log2e) * f.inv_l;
+      const float g = q * (q < xp[i] ? f.c_below : f.c_above);
+      out[i] = f32_to_bf16_rne(g);
+    }
+    if (a.vec_ok && e + kVec <= a.V) {
+      uint4 w;
+      w.x = uint32_t(out[0]) | (uint32_t(out[1]) << 16);
+      w.y = uint32_t(out[2]) | (uint32_t(out[3]) << 16);
+      w.z = uint32_t(out[4]) | (uint32_t(out[5]) << 16);
+      w.w = uint32_t(out[6]) | (uint32_t(out[7]) << 16);
+      *reinterpret_cast<uint4*>(dz + e) = w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i)
+        if (e + i < a.V) dz[e + i] = out[i];
+    }
+  }
+}
+
+bool sizes_ok(int32_t N, int32_t W, int32_t V) {
+  return N >= 1 && N <= 65535 && W >= 1 && W <= LVTV_MAX_W && V >= 1 && V <= LVTV_MAX_V;
+}
+
+}  // namespace
+}  // namespace lvtv
+
+extern "C" size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V) {
+  if (!lvtv::sizes_ok(N, W, V)) return 0;
+  return lvtv::make_layout(N, W, V).total;
+}
+
+extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
+                                   int32_t N, int32_t W, int32_t V, float* loss, float* alpha,
+                                   uint16_t* dlogits, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  using namespace lvtv;
+  if (!sizes_ok(N, W, V)) return LVTV_ERR_SHAPE;
+  if (!draft_logits || !target_probs || !loss || !alpha || !dlogits) return LVTV_ERR_NULL;
+  const Layout L = make_layout(N, W, V);
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return LVTV_ERR_WORKSPACE;
+  Args a;
+  a.z = draft_logits;
+  a.p = target_probs;
+  a.N = N;
+  a.W = W;
+  a.V = V;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(draft_logits) |
+                        reinterpret_cast<uintptr_t>(target_probs) |
+                        reinterpret_cast<uintptr_t>(dlogits);
+  a.vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
+  a.loss = loss;
+  a.alpha = alpha;
+  a.dz = dlogits;
+  a.L = L;
+  char* ws = static_cast<char*>(workspace);
+  a.stat = reinterpret_cast<SliceStat*>(ws + L.off_stat);
+  a.part = reinterpret_cast<Part*>(ws + L.off_part);
+  a.fin = reinterpret_cast<RowFinal*>(ws + L.off_fin);
+  a.branch_loss = reinterpret_cast<double*>(ws + L.off_branch);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(L.S, W, N);
+  hipLaunchKernelGGL(row_stats_kernel, grid, dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(overlap_kernel, grid, dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(branch_kernel, dim3(N), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(grad_kernel, grid, dim3(kBlock), 0, s, a);
+  return hipGetLastError() == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+}

@@ -184,6 +184,20 @@ def verify_case(case, temperature=None, batch=None, kmax=None, vocab=None,
                       meta={"B": B, "Kmax": K, "V": V})
 
 
+def redraw_tokens(case: VerifyCase, temperature: float) -> VerifyCase:
+    """Same logits, draft tokens drawn at another temperature, and that
+    temperature for every request (workload 3 sweeps T over one set of
+    logits)."""
+    tokens = np.full_like(case.tokens, -1)
+    for b in range(case.tokens.shape[0]):
+        for k in range(int(case.k[b])):
+            tokens[b, k] = _draw_token(case.case, b, k, case.draft[b, k], case.dtype,
+                                       temperature)
+    temps = np.full_like(case.temperature, temperature)
+    return VerifyCase(case.case, case.dtype, case.target, case.draft, tokens, case.k, temps,
+                      case.seed, meta=dict(case.meta))
+
+
 @dataclass
 class LossCase:
     draft_logits: np.ndarray   # uint16 bf16 [N, W, V]

@@ -1,0 +1,139 @@
+"""Parity rules between the HIP path and the oracle.
+
+Verify (per request):
+  * status must be equal; a faulted request must have accepted_len -1, all
+    tokens -1 and alpha 0;
+  * greedy requests (T = 0): accepted_len, tokens and alpha bit-exact;
+  * stochastic requests: find the first decision where the two differ: an
+    accept bit at k = min(j_gpu, j_oracle) if the accepted lengths differ,
+    otherwise the drawn token. The request is excused if the oracle's margin
+    at that decision is below 1e-6 (|u - p/q| for an accept bit, the
+    normalised CDF margin for a draw); otherwise it fails. Excused requests
+    are counted and reported;
+  * alpha_k within 1e-5 relative for every k < K_b (also for excused
+    requests), exactly 0 for K_b <= k < Kmax.
+
+Loss:
+  * loss and alpha within 1e-5 relative;
+  * bfloat16 dlogits equal to the oracle's round-to-nearest-even of its fp64
+    gradient, except (i) +-1 bf16 ulp where the fp64 value lies within 1e-5
+    relative of a rounding midpoint, (ii) elements whose q and p are within
+    1e-6 relative of each other (the [q < p] indicator is then a coin flip
+    of rounding). Values below the fp32 minimum normal compare as 0. Both
+    exemptions are counted.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+MARGIN = 1e-6
+ALPHA_RTOL = 1e-5
+LOSS_RTOL = 1e-5
+MIDPOINT_RTOL = 1e-5
+TIE_RTOL = 1e-6
+FP32_MIN_NORMAL = 1.1754943508222875e-38
+
+
+def compare_verify(gpu, orc, k_per_req, kmax):
+    """gpu: dict of numpy arrays accepted_len, tokens, alpha, status.
+    orc: the oracle's batched dict. Returns a report dict; report["failures"]
+    lists (request, reason)."""
+    rep = {"requests": 0, "greedy": 0, "stochastic": 0, "faulted": 0,
+           "excused_accept": 0, "excused_draw": 0, "failures": []}
+    B = len(k_per_req)
+    for b in range(B):
+        rep["requests"] += 1
+        kb = int(k_per_req[b])
+        st_g, st_o = int(gpu["status"][b]), int(orc["status"][b])
+        if st_g != st_o:
+            rep["failures"].append((b, f"status {st_g} != {st_o}"))
+            continue
+        if st_o:
+            rep["faulted"] += 1
+            if gpu["accepted_len"][b] != -1 or np.any(gpu["tokens"][b] != -1) \
+                    or np.any(gpu["alpha"][b] != 0):
+                rep["failures"].append((b, "faulted request outputs not cleared"))
+            continue
+        a_g = np.asarray(gpu["alpha"][b], dtype=np.float64)
+        a_o = np.asarray(orc["alpha"][b], dtype=np.float64)
+        if kb < kmax and np.any(a_g[kb:] != 0):
+            rep["failures"].append((b, "alpha beyond K_b not zero"))
+        if kb > 0:
+            err = np.abs(a_g[:kb] - a_o[:kb])
+            bad = err > ALPHA_RTOL * np.abs(a_o[:kb])
+            if orc["greedy"][b]:
+                bad = err != 0
+            if np.any(bad):
+                k = int(np.flatnonzero(bad)[0])
+                rep["failures"].append((b, f"alpha[{k}] {a_g[k]!r} vs {a_o[k]!r}"))
+        j_g, j_o = int(gpu["accepted_len"][b]), int(orc["accepted_len"][b])
+        t_g, t_o = np.asarray(gpu["tokens"][b]), np.asarray(orc["tokens"][b])
+        if orc["greedy"][b]:
+            rep["greedy"] += 1
+            if j_g != j_o or not np.array_equal(t_g, t_o):
+                rep["failures"].append((b, f"greedy mismatch j {j_g} vs {j_o}"))
+            continue
+        rep["stochastic"] += 1
+        if j_g != j_o:
+            k = min(j_g, j_o)
+            margin = orc["accept_margin"][b][k] if 0 <= k < kb else np.inf
+            if margin < MARGIN:
+                rep["excused_accept"] += 1
+            else:
+                rep["failures"].append((b, f"accepted_len {j_g} vs {j_o}, margin {margin:.3g}"))
+            continue
+        if not np.array_equal(t_g, t_o):
+            if np.array_equal(t_g[:j_o], t_o[:j_o]) and np.all(t_g[j_o + 1:] == -1) \
+                    and orc["draw_margin"][b] < MARGIN:
+                rep["excused_draw"] += 1
+            else:
+                rep["failures"].append(
+                    (b, f"token at {j_o}: {t_g[j_o]} vs {t_o[j_o]}, "
+                        f"margin {orc['draw_margin'][b]:.3g}"))
+    return rep
+
+
+def bf16_bits_to_f64(u16):
+    return (np.asarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)) \
+        .view(np.float32).astype(np.float64)
+
+
+def near_bf16_midpoint(d64, rtol=MIDPOINT_RTOL):
+    """True where the fp64 value lies within rtol (relative) of the midpoint
+    between two adjacent bf16 values."""
+    d = np.abs(np.asarray(d64, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(d > 0, d, 1.0)))
+    e = np.maximum(e, -126)
+    quantum = np.ldexp(1.0, (e - 7).astype(np.int64))
+    frac = d / quantum - np.floor(d / quantum)
+    return (np.abs(frac - 0.5) * quantum <= rtol * d) & (d > 0)
+
+
+def compare_dlogits(gpu_u16, orc_u16, orc_dz64, q64, p64):
+    """Element-wise bf16 gradient comparison. Returns (n_bad, n_midpoint,
+    n_tie, first_bad_index or None)."""
+    g = np.asarray(gpu_u16, dtype=np.uint16)
+    o = np.asarray(orc_u16, dtype=np.uint16)
+    gv = bf16_bits_to_f64(g)
+    ov = bf16_bits_to_f64(o)
+    tiny = (np.abs(orc_dz64) < FP32_MIN_NORMAL) & (np.abs(gv) < FP32_MIN_NORMAL)
+    equal = (g == o) | tiny | (gv == ov)
+    mismatch = ~equal
+    tie = mismatch & (np.abs(q64 - p64) <= TIE_RTOL * np.maximum(q64, p64))
+    rest = mismatch & ~tie
+    gi = g.astype(np.int64) & 0x7FFF
+    oi = o.astype(np.int64) & 0x7FFF
+    same_sign = (g >> 15) == (o >> 15)
+    one_ulp = same_sign & (np.abs(gi - oi) == 1)
+    mid = rest & one_ulp & near_bf16_midpoint(orc_dz64)
+    bad = rest & ~mid
+    first = int(np.flatnonzero(bad.ravel())[0]) if bad.any() else None
+    return int(bad.sum()), int(mid.sum()), int(tie.sum()), first
+
+
+def rel_close(a, b, rtol):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.abs(a - b) <= rtol * np.abs(b)

@@ -1,0 +1,85 @@
+"""GPU parity of e2e_tv_loss_fwd_bwd against the oracle, through the C ABI.
+
+Small and ragged shapes are compared element by element; the full workload
+(N=512, W=7, V=151936) is compared on sampled branches, and on properties
+that hold at any size (the loss equals -mean_n sum_j prod alpha of the
+returned alphas; gradient rows sum to ~0)."""
+
+import numpy as np
+import pytest
+
+from lossless_verify_tv_amd import synth
+from oracle import bf16 as obf16
+from oracle import loss as ol
+
+from .gpu_util import announce, run_loss
+from .parity import ALPHA_RTOL, LOSS_RTOL, compare_dlogits, rel_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _q64(z_u16):
+    z = obf16.decode(z_u16)
+    e = np.exp(z - z.max(-1, keepdims=True))
+    return e / e.sum(-1, keepdims=True)
+
+
+def _check_small(z, p, tag):
+    announce(f"loss {tag} shape={z.shape}")
+    gpu = run_loss(z, p)
+    orc = ol.e2e_tv_loss(z, p)
+    assert rel_close(gpu["loss"], orc["loss"], LOSS_RTOL), (gpu["loss"], orc["loss"])
+    assert np.all(rel_close(gpu["alpha"], orc["alpha"], ALPHA_RTOL))
+    bad, mid, tie, first = compare_dlogits(gpu["dlogits"], orc["dlogits"], orc["dz"],
+                                           _q64(z), p.astype(np.float64))
+    announce(f"loss {tag}: midpoint-exempt {mid}, tie-exempt {tie}, bad {bad}")
+    assert bad == 0, (first, gpu["dlogits"].ravel()[first], orc["dlogits"].ravel()[first],
+                      orc["dz"].ravel()[first])
+    return gpu, orc
+
+
+@pytest.mark.parametrize("vocab", [20000, 20001, 8192, 1001, 3])
+def test_loss_shrunk(vocab):
+    c = synth.loss_case(n_branches=5, width=7, vocab=vocab)
+    _check_small(c.draft_logits, c.target_probs, f"N=5 W=7 V={vocab}")
+
+
+def test_loss_single_position_and_branch():
+    c = synth.loss_case(n_branches=1, width=1, vocab=5000)
+    gpu, orc = _check_small(c.draft_logits, c.target_probs, "N=1 W=1")
+    assert gpu["loss"] == pytest.approx(-float(gpu["alpha"][0, 0]), rel=1e-6)
+
+
+def test_loss_width_16():
+    c = synth.loss_case(n_branches=3, width=16, vocab=4096)
+    _check_small(c.draft_logits, c.target_probs, "W=16")
+
+
+def test_loss_full_workload_sampled():
+    announce("loss full workload N=512 W=7 V=151936 (generating)")
+    c = synth.loss_case(workers=16)
+    gpu = run_loss(c.draft_logits, c.target_probs)
+    N, W, _ = c.draft_logits.shape
+    # the loss is the mean prefix-product sum of the returned alphas
+    a = gpu["alpha"].astype(np.float64)
+    assert rel_close(gpu["loss"], -np.cumprod(a, axis=1).sum(1).mean(), 1e-6)
+    for n in [0, 1, 2, 255, 511]:
+        l_n, alpha, _, _, dz = ol.branch(obf16.decode(c.draft_logits[n]), c.target_probs[n], N)
+        assert np.all(rel_close(gpu["alpha"][n], alpha, ALPHA_RTOL)), n
+        bad, mid, tie, first = compare_dlogits(
+            gpu["dlogits"][n], obf16.encode_rne(dz), dz, _q64(c.draft_logits[n]),
+            c.target_probs[n].astype(np.float64))
+        announce(f"branch {n}: midpoint-exempt {mid}, tie-exempt {tie}, bad {bad}")
+        assert bad == 0, (n, first)
+    g = obf16.decode(gpu["dlogits"][:8])
+    assert np.all(np.abs(g.sum(-1)) <= 4e-3 * np.abs(g).sum(-1) + 1e-30)
+
+
+def test_loss_bit_identical_reruns():
+    c = synth.loss_case(n_branches=4, width=7, vocab=30000)
+    first = run_loss(c.draft_logits, c.target_probs)
+    for _ in range(2):
+        again = run_loss(c.draft_logits, c.target_probs)
+        assert first["loss"] == again["loss"]
+        assert np.array_equal(first["alpha"], again["alpha"])
+        assert np.array_equal(first["dlogits"], again["dlogits"])

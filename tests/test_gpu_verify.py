@@ -1,0 +1,195 @@
+"""GPU parity of spec_verify against the oracle, through the C ABI.
+
+Sizes: the five workloads at full size (4 and 2 exactly; 3 and 5 at full
+size), shrunk versions that span several slices with ragged tails, and the
+edge cases (K_b = 0, Kmax = 0, V = 1, V not a multiple of 8, faulted
+requests, greedy ties). Plus oracle-independent checks on GPU outputs:
+chi-square of the emitted-token law and bit-identical reruns.
+"""
+
+import numpy as np
+import pytest
+import torch
+from scipy.stats import chisquare
+
+import lossless_verify_tv_amd as lv
+from lossless_verify_tv_amd import synth
+
+from .gpu_util import announce, device, run_oracle_verify, run_verify, verify_inputs
+from .parity import compare_verify
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, tag):
+    announce(f"verify {tag} shape={case.shape} dtype={case.dtype}")
+    gpu = run_verify(case)
+    orc = run_oracle_verify(case)
+    rep = compare_verify(gpu, orc, case.k, case.shape[1])
+    announce(f"verify {tag}: {rep['requests']} requests, {rep['stochastic']} stochastic, "
+             f"{rep['greedy']} greedy, {rep['faulted']} faulted, excused accept "
+             f"{rep['excused_accept']}, excused draw {rep['excused_draw']}")
+    assert not rep["failures"], rep["failures"][:5]
+    return rep
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.0])
+def test_workload1_full(temperature):
+    case = synth.verify_case(1, temperature=temperature)
+    _check(case, f"w1 T={temperature}")
+
+
+def test_workload2_full():
+    _check(synth.verify_case(2), "w2")
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.6, 1.0])
+@pytest.mark.parametrize("vocab", [20000, 20001, 8192, 513])
+def test_workload3_shrunk(temperature, vocab):
+    case = synth.verify_case(3, temperature=temperature, batch=6, vocab=vocab)
+    _check(case, f"w3-shrunk V={vocab} T={temperature}")
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.6, 1.0])
+def test_workload3_full(temperature):
+    _check(synth.verify_case(3, temperature=temperature), f"w3 T={temperature}")
+
+
+def test_workload5_full():
+    rep = _check(synth.verify_case(5), "w5")
+    assert rep["greedy"] == 128 and rep["stochastic"] == 128
+
+
+def test_workload5_shrunk_ragged_fp32():
+    case = synth.verify_case(5, batch=24, vocab=3001)
+    case.dtype = "f32"
+    case.target = synth.from_bf16(case.target)
+    case.draft = synth.from_bf16(case.draft)
+    _check(case, "w5-shrunk fp32 V=3001")
+
+
+def test_k_zero_and_kmax_zero():
+    case = synth.verify_case(2, batch=8, vocab=4000, k_values=[0, 1, 0, 4, 2, 0, 3, 4])
+    _check(case, "K_b=0 mix")
+    case0 = synth.verify_case(2, batch=5, kmax=0, vocab=777)
+    _check(case0, "Kmax=0")
+
+
+def test_tiny_vocab():
+    for V in (1, 2, 7):
+        case = synth.verify_case(1, batch=4, kmax=3, vocab=V)
+        _check(case, f"V={V} T=1")
+        case.temperature[:] = 0.0
+        _check(case, f"V={V} T=0")
+
+
+def test_faulted_requests():
+    case = synth.verify_case(2, batch=10, vocab=3000)
+    V = case.shape[2]
+    case.k[0] = 9                                   # K_b > Kmax
+    case.k[1] = -1
+    case.tokens[2, 1] = V                           # token out of range
+    case.tokens[3, 0] = -7
+    case.temperature[4] = -1.0
+    case.temperature[5] = np.nan
+    case.target[6, 2, 17] = 0x7FC0                  # NaN in a used row
+    case.draft[7, 0, :] = 0xFF80                    # a draft row entirely -inf
+    case.target[8, 1, 5] = 0x7F80                   # +inf in a used row
+    case.target[9, 4, 3] = 0x7FC0                   # NaN in the bonus row
+    rep = _check(case, "faults")
+    assert rep["faulted"] == 10
+
+
+def test_unused_rows_are_not_read():
+    # padding rows hold NaN; requests with K_b < Kmax must still be clean
+    case = synth.verify_case(3, temperature=1.0, batch=6, vocab=5000,
+                             k_values=[1, 7, 3, 0, 5, 2])
+    rep = _check(case, "padding NaN")
+    assert rep["faulted"] == 0
+
+
+def test_greedy_ties_lowest_index():
+    case = synth.verify_case(2, batch=4, vocab=20000)
+    case.temperature[:] = 0.0
+    # plant equal maxima in target and draft rows across slices
+    for b in range(4):
+        for k in range(case.shape[1] + 1):
+            case.target[b, k, [100 + k, 9000 + k, 19999 - k]] = synth.to_bf16(np.float32([60.0] * 3))
+        for k in range(case.shape[1]):
+            case.draft[b, k, [9000 + k, 150]] = synth.to_bf16(np.float32([60.0, 60.0]))
+    case.tokens[:, :] = [[100, 101, 102, 103], [150, 101, 102, 103],
+                         [100, 101, 9002, 103], [100, 101, 102, 103]]
+    rep = _check(case, "greedy ties")
+    assert rep["greedy"] == 4
+
+
+def test_bit_identical_reruns():
+    case = synth.verify_case(3, temperature=1.0, batch=8, vocab=40000)
+    dev = device()
+    inputs = verify_inputs(case, dev)
+    first = run_verify(case, dev, inputs)
+    for _ in range(3):
+        again = run_verify(case, dev, inputs)
+        for key in first:
+            assert np.array_equal(first[key], again[key]), key
+
+
+def test_alpha_matches_torch_fp32_reference():
+    """Plain PyTorch fp32 reference of the overlap: sum min(softmax(t/T),
+    softmax(d/T))."""
+    case = synth.verify_case(3, temperature=0.6, batch=4, vocab=30000)
+    dev = device()
+    gpu = run_verify(case, dev)
+    t = torch.from_numpy(synth.from_bf16(case.target)).to(dev)
+    d = torch.from_numpy(synth.from_bf16(case.draft)).to(dev)
+    inv = np.float32(1) / np.float32(0.6)
+    p = torch.softmax(t[:, :-1] * float(inv), dim=-1)
+    q = torch.softmax(d * float(inv), dim=-1)
+    ref = torch.minimum(p, q).sum(-1).cpu().numpy()
+    assert np.allclose(gpu["alpha"], ref, rtol=2e-5)
+
+
+def test_emitted_law_chi_square_on_gpu():
+    """Oracle-free: many requests share the same rows (V = 12, K = 2) with
+    fresh draft tokens y ~ q and distinct seeds. The first emitted token must
+    follow p_0; after an accepted first draft the next emitted token must
+    follow p_1; when both drafts are accepted the bonus follows p_2."""
+    rng = np.random.default_rng(5)
+    B, K, V = 30000, 2, 12
+    t = (1.5 * rng.standard_normal((K + 1, V))).astype(np.float32)
+    d = (t[:K] + rng.standard_normal((K, V))).astype(np.float32)
+    p = np.exp(t.astype(np.float64))
+    p /= p.sum(-1, keepdims=True)
+    q = np.exp(d.astype(np.float64))
+    q /= q.sum(-1, keepdims=True)
+    case = synth.VerifyCase(
+        case=0, dtype="f32",
+        target=np.broadcast_to(t, (B, K + 1, V)).copy(),
+        draft=np.broadcast_to(d, (B, K, V)).copy(),
+        tokens=np.stack([rng.choice(V, size=B, p=q[0]), rng.choice(V, size=B, p=q[1])],
+                        axis=1).astype(np.int32),
+        k=np.full(B, K, np.int32), temperature=np.ones(B, np.float32),
+        seed=rng.integers(0, 2**63, size=B, dtype=np.int64).astype(np.uint64))
+    announce("chi-square B=30000 V=12")
+    gpu = run_verify(case)
+    assert np.all(gpu["status"] == 0)
+    j, tok = gpu["accepted_len"], gpu["tokens"]
+    first = np.bincount(tok[:, 0], minlength=V)
+    assert chisquare(first, p[0] * B).pvalue > 1e-3
+    sec = np.bincount(tok[j >= 1, 1], minlength=V)
+    assert chisquare(sec, p[1] * sec.sum()).pvalue > 1e-3
+    bon = np.bincount(tok[j == 2, 2], minlength=V)
+    assert chisquare(bon, p[2] * bon.sum()).pvalue > 1e-3
+    alpha = gpu["alpha"][0]
+    for count, prob in [((j >= 1).sum(), alpha[0]), ((j >= 2).sum(), alpha[0] * alpha[1])]:
+        sd = np.sqrt(B * prob * (1 - prob))
+        assert abs(count - B * prob) < 5 * sd
+
+
+def test_host_errors_do_not_launch():
+    dev = device()
+    case = synth.verify_case(2, batch=2, vocab=1000)
+    inputs = verify_inputs(case, dev)
+    tiny_ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    with pytest.raises(lv.LvtvError):
+        lv.spec_verify(**inputs, workspace=tiny_ws)
