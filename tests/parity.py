@@ -21,6 +21,13 @@ Loss:
     1e-6 relative of each other (the [q < p] indicator is then a coin flip
     of rounding). Values below the fp32 minimum normal compare as 0. Both
     exemptions are counted.
+  * a near-tie also moves q(u) between S and S' for its whole row, so the
+    row's other gradients shift by about q(u)/S. The pages leave the
+    subgradient of min at q = p open (either side is a valid one), so for a
+    row holding near-ties the GPU row must match the oracle's row for one of
+    the tie choices: the oracle is rerun with p nudged across q at the tie
+    elements (by 1e-12 relative, which moves alpha by less than 1e-11), so
+    that its own indicator takes the other side.
 """
 
 from __future__ import annotations
@@ -137,3 +144,45 @@ def rel_close(a, b, rtol):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return np.abs(a - b) <= rtol * np.abs(b)
+
+
+def compare_branch(gpu_u16, z_u16, p32, n_branches):
+    """Compare the GPU gradient rows of one branch ([W, V] bf16) with the
+    oracle, with the tie alternatives described in the module docstring.
+    Returns (n_bad, n_midpoint, n_tie, n_rows_on_alternative, first_bad)."""
+    from oracle import bf16 as obf16
+    from oracle import loss as ol
+
+    z64 = obf16.decode(z_u16)
+    p64 = np.asarray(p32, dtype=np.float64)
+    _, _, _, _, dz = ol.branch(z64, p64, n_branches)
+    q = np.exp(z64 - z64.max(-1, keepdims=True))
+    q /= q.sum(-1, keepdims=True)
+    tie = np.abs(q - p64) <= TIE_RTOL * np.maximum(q, p64)
+    tot_bad = tot_mid = tot_tie = alt_rows = 0
+    first = None
+    for k in range(z64.shape[0]):
+        cands = [dz[k]]
+        idx = np.flatnonzero(tie[k])
+        if idx.size:
+            subsets = [idx] if idx.size > 4 else [
+                idx[[bool(m >> i & 1) for i in range(idx.size)]]
+                for m in range(1, 1 << idx.size)]
+            for sub in subsets:
+                p_alt = p64.copy()
+                below = q[k, sub] < p64[k, sub]
+                p_alt[k, sub] = np.where(below, q[k, sub] * (1 - 1e-12), q[k, sub] * (1 + 1e-12))
+                cands.append(ol.branch(z64, p_alt, n_branches)[4][k])
+        best = None
+        for ci, cand in enumerate(cands):
+            res = compare_dlogits(gpu_u16[k], obf16.encode_rne(cand), cand, q[k], p64[k])
+            if best is None or res[0] < best[0][0]:
+                best = (res, ci)
+        (bad, mid, nt, fb), ci = best
+        tot_bad += bad
+        tot_mid += mid
+        tot_tie += nt
+        alt_rows += ci > 0
+        if first is None and fb is not None:
+            first = (k, fb)
+    return tot_bad, tot_mid, tot_tie, alt_rows, first

@@ -13,15 +13,20 @@ from oracle import bf16 as obf16
 from oracle import loss as ol
 
 from .gpu_util import announce, run_loss
-from .parity import ALPHA_RTOL, LOSS_RTOL, compare_dlogits, rel_close
+from .parity import ALPHA_RTOL, LOSS_RTOL, compare_branch, rel_close
 
 pytestmark = pytest.mark.gpu
 
 
-def _q64(z_u16):
-    z = obf16.decode(z_u16)
-    e = np.exp(z - z.max(-1, keepdims=True))
-    return e / e.sum(-1, keepdims=True)
+def _check_branches(gpu, z, p, branches, tag):
+    N = z.shape[0]
+    totals = np.zeros(4, dtype=np.int64)
+    for n in branches:
+        bad, mid, tie, alt, first = compare_branch(gpu["dlogits"][n], z[n], p[n], N)
+        totals += (bad, mid, tie, alt)
+        assert bad == 0, (tag, n, first)
+    announce(f"loss {tag}: midpoint-exempt {totals[1]}, tie-exempt {totals[2]}, "
+             f"rows on the other tie side {totals[3]}, bad {totals[0]}")
 
 
 def _check_small(z, p, tag):
@@ -30,11 +35,7 @@ def _check_small(z, p, tag):
     orc = ol.e2e_tv_loss(z, p)
     assert rel_close(gpu["loss"], orc["loss"], LOSS_RTOL), (gpu["loss"], orc["loss"])
     assert np.all(rel_close(gpu["alpha"], orc["alpha"], ALPHA_RTOL))
-    bad, mid, tie, first = compare_dlogits(gpu["dlogits"], orc["dlogits"], orc["dz"],
-                                           _q64(z), p.astype(np.float64))
-    announce(f"loss {tag}: midpoint-exempt {mid}, tie-exempt {tie}, bad {bad}")
-    assert bad == 0, (first, gpu["dlogits"].ravel()[first], orc["dlogits"].ravel()[first],
-                      orc["dz"].ravel()[first])
+    _check_branches(gpu, z, p, range(z.shape[0]), tag)
     return gpu, orc
 
 
@@ -63,14 +64,11 @@ def test_loss_full_workload_sampled():
     # the loss is the mean prefix-product sum of the returned alphas
     a = gpu["alpha"].astype(np.float64)
     assert rel_close(gpu["loss"], -np.cumprod(a, axis=1).sum(1).mean(), 1e-6)
-    for n in [0, 1, 2, 255, 511]:
-        l_n, alpha, _, _, dz = ol.branch(obf16.decode(c.draft_logits[n]), c.target_probs[n], N)
+    sample = [0, 1, 2, 255, 511]
+    for n in sample:
+        _, alpha, _, _, _ = ol.branch(obf16.decode(c.draft_logits[n]), c.target_probs[n], N)
         assert np.all(rel_close(gpu["alpha"][n], alpha, ALPHA_RTOL)), n
-        bad, mid, tie, first = compare_dlogits(
-            gpu["dlogits"][n], obf16.encode_rne(dz), dz, _q64(c.draft_logits[n]),
-            c.target_probs[n].astype(np.float64))
-        announce(f"branch {n}: midpoint-exempt {mid}, tie-exempt {tie}, bad {bad}")
-        assert bad == 0, (n, first)
+    _check_branches(gpu, c.draft_logits, c.target_probs, sample, "full workload (sampled)")
     g = obf16.decode(gpu["dlogits"][:8])
     assert np.all(np.abs(g.sum(-1)) <= 4e-3 * np.abs(g).sum(-1) + 1e-30)
 
