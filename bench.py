@@ -161,10 +161,8 @@ def main():
     lout = (torch.empty(1, dtype=torch.float32, device=dev),
             torch.empty(LOSS_N, LOSS_W, dtype=torch.float32, device=dev),
             torch.empty(LOSS_N, LOSS_W, VOCAB, dtype=torch.bfloat16, device=dev))
-    vws = torch.empty(lv.spec_verify_workspace_bytes(VERIFY_B, VERIFY_K, VOCAB), dtype=torch.uint8,
-                      device=dev)
-    lws = torch.empty(lv.e2e_tv_loss_workspace_bytes(LOSS_N, LOSS_W, VOCAB), dtype=torch.uint8,
-                      device=dev)
+    vws = lv.new_workspace(lv.spec_verify_workspace_bytes(VERIFY_B, VERIFY_K, VOCAB), dev)
+    lws = lv.new_workspace(lv.e2e_tv_loss_workspace_bytes(LOSS_N, LOSS_W, VOCAB), dev)
     torch.cuda.synchronize()
     log("inputs resident")
 

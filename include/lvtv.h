@@ -72,6 +72,16 @@ int lvtv_version(void);
 const char* lvtv_strerror(int code);
 
 /*
+ * Zero-fill a workspace on `stream` (a plain fill kernel, so it may sit in a
+ * captured graph). A workspace must be zero-filled once before its first
+ * use: the single-read kernels keep a call counter and per-request counters
+ * there and leave them ready for the next call, so later calls need no
+ * reset. Returns LVTV_ERR_NULL / LVTV_ERR_WORKSPACE (misaligned) before
+ * enqueueing anything.
+ */
+int lvtv_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Workspace bytes spec_verify needs for these sizes (0 if the sizes are out
  * of range). Host function; no HIP call.
  */
@@ -116,8 +126,10 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype
  *   status         int32 [B] out: LVTV_STATUS_* bits, 0 if fine. A faulted
  *                  request gets accepted_len = -1, all tokens -1, alpha 0.
  *   workspace      device scratch of >= spec_verify_workspace_bytes(...)
- *                  bytes, 256-byte aligned; contents need no initialisation
- *                  and are garbage after the call.
+ *                  bytes, 256-byte aligned, zero-filled before its first
+ *                  use (lvtv_workspace_reset); each call leaves it ready for
+ *                  the next. Calls sharing a workspace must be ordered on
+ *                  one stream.
  *   stream         hipStream_t.
  */
 int spec_verify(const void* target_logits, const void* draft_logits, int dtype,

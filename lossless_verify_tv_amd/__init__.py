@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     e2e_tv_loss_fwd_bwd,
     e2e_tv_loss_workspace_bytes,
     load_library,
+    new_workspace,
     spec_verify,
     spec_verify_workspace_bytes,
     strerror,

@@ -29,6 +29,7 @@ STATUS_NONFINITE = 8
 EXPORTS = (
     "lvtv_version",
     "lvtv_strerror",
+    "lvtv_workspace_reset",
     "spec_verify_workspace_bytes",
     "spec_verify",
     "e2e_tv_loss_workspace_bytes",
@@ -58,6 +59,8 @@ def load_library(path: str = LIB_PATH):
         lib.lvtv_version.argtypes = []
         lib.lvtv_strerror.restype = ctypes.c_char_p
         lib.lvtv_strerror.argtypes = [ctypes.c_int]
+        lib.lvtv_workspace_reset.restype = ctypes.c_int
+        lib.lvtv_workspace_reset.argtypes = [vp, sz, vp]
         lib.spec_verify_workspace_bytes.restype = sz
         lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
         lib.spec_verify.restype = ctypes.c_int
@@ -99,11 +102,21 @@ def _require(cond, msg):
 _workspaces: dict = {}
 
 
-def _workspace(device, nbytes):
-    key = (device.type, device.index)
+def new_workspace(nbytes, device):
+    """A zero-filled workspace of at least `nbytes` bytes on `device`, as the
+    library requires before a workspace's first use."""
+    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    with torch.cuda.device(device):
+        _check(load_library().lvtv_workspace_reset(_ptr(ws), ws.numel(), _stream(device)),
+               "lvtv_workspace_reset")
+    return ws
+
+
+def _workspace(op, device, nbytes):
+    key = (op, device.type, device.index)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = new_workspace(nbytes, device)
         _workspaces[key] = ws
     return ws
 
@@ -148,7 +161,7 @@ def spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperatur
         _require(t.device == dev and t.is_contiguous(), "logits must be contiguous on one GPU")
     need = lib.spec_verify_workspace_bytes(B, Kmax, V, dtype)
     _require(need > 0, f"sizes out of range: B={B} Kmax={Kmax} V={V}")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = workspace if workspace is not None else _workspace("verify", dev, need)
     if out is None:
         acc = torch.empty(B, dtype=torch.int32, device=dev)
         toks = torch.empty(B, Kmax + 1, dtype=torch.int32, device=dev)
@@ -188,7 +201,7 @@ def e2e_tv_loss_fwd_bwd(draft_logits, target_probs, workspace=None, out=None):
     N, W, V = draft_logits.shape
     need = lib.e2e_tv_loss_workspace_bytes(N, W, V)
     _require(need > 0, f"sizes out of range: N={N} W={W} V={V}")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = workspace if workspace is not None else _workspace("loss", dev, need)
     if out is None:
         loss = torch.empty(1, dtype=torch.float32, device=dev)
         alpha = torch.empty(N, W, dtype=torch.float32, device=dev)

@@ -1,5 +1,38 @@
-// Library-level entry points of the C ABI (version, error strings).
+// Library-level entry points of the C ABI (version, error strings,
+// workspace reset).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
 #include "../../include/lvtv.h"
+
+namespace {
+
+// Zero fill with vector stores (a plain kernel, so the reset can sit inside
+// a captured graph).
+__global__ void zero_fill(uint4* p, size_t n16, unsigned char* tail, size_t ntail) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+}  // namespace
+
+extern "C" int lvtv_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return LVTV_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return LVTV_ERR_WORKSPACE;
+  const size_t n16 = workspace_bytes / 16;
+  const size_t ntail = workspace_bytes - n16 * 16;
+  if (workspace_bytes == 0) return LVTV_OK;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_fill, dim3(unsigned(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<uint4*>(workspace), n16,
+                     static_cast<unsigned char*>(workspace) + n16 * 16, ntail);
+  return hipGetLastError() == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+}
 
 extern "C" int lvtv_version(void) { return 1; }
 

@@ -1,0 +1,149 @@
+// Cross-workgroup exchange for the single-read kernels (gfx950).
+//
+// A row of V = 1.5e5 bf16 logits is spread over several workgroups, each
+// holding its slice in registers. They swap a few numbers (slice softmax
+// statistics, partial sums) through a workspace of 64-bit tagged words: the
+// high half is a tag naming the call, the low half the payload, written and
+// read with single relaxed agent-scope atomic accesses. A reader knows a
+// word is fresh when its tag is the current one, so no fences, no resets and
+// no ordering between different words are needed.
+//
+// Calls are told apart by an epoch counter in the workspace control block;
+// the tag is derived from it and is never 0, so a zero-filled workspace
+// holds no fresh word. The last unit of work to complete in a call (a
+// request of the verify step, a branch of the loss) bumps the epoch and
+// clears the completion counter; everything else a call leaves behind is
+// either tagged or reset by its own last user. The workspace must therefore
+// be zero-filled once before its first use (lvtv_workspace_reset).
+//
+// Every wait is bounded: a workgroup that polls a word for `spin_limit`
+// rounds without seeing it gives up and recomputes the missing value from
+// the inputs with the same function (same element order, same reduction
+// tree) its producer uses, so the result is bit-identical either way and no
+// schedule of workgroups can deadlock.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace lvtv {
+
+struct FusedCtl {
+  uint32_t epoch;  // bumped once per completed call
+  uint32_t done;   // completed units in the running call
+  uint32_t pad[62];
+};
+static_assert(sizeof(FusedCtl) == 256, "control block is one 256-byte line");
+
+// Every workspace starts with a region of fixed layout, whatever the call's
+// shapes: the control block, then one arrival counter per unit of work (a
+// request or a branch; at most 65535 of them). Counters return to zero by the
+// end of each call, so the region stays valid across calls of any shape;
+// the shape-dependent arrays (tagged words, or the two-read pipeline's
+// partial sums) come after it.
+constexpr int kMaxUnits = 65536;
+constexpr size_t kReservedBytes = sizeof(FusedCtl) + sizeof(uint32_t) * size_t(kMaxUnits);
+static_assert(kReservedBytes % 256 == 0, "reserved region keeps 256-byte alignment");
+
+__host__ __device__ inline FusedCtl* workspace_ctl(void* ws) { return static_cast<FusedCtl*>(ws); }
+__host__ __device__ inline uint32_t* workspace_counters(void* ws) {
+  return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + sizeof(FusedCtl));
+}
+
+__device__ __forceinline__ uint32_t tag_from_epoch(uint32_t epoch) {
+  return ((epoch & 0x7fffffffu) << 1) | 1u;
+}
+
+__device__ __forceinline__ uint32_t read_epoch(FusedCtl* ctl) {
+  return __hip_atomic_load(&ctl->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void tag_store(uint64_t* p, uint32_t tag, uint32_t bits) {
+  __hip_atomic_store(p, (uint64_t(tag) << 32) | uint64_t(bits), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t tag_load(uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block-wide poll of n consecutive tagged words. Payloads land in `dst`,
+// `have[i]` says whether word i was seen fresh. Returns true when all were.
+// Every thread of the block must call it.
+__device__ __forceinline__ bool poll_tagged(uint64_t* src, int n, uint32_t tag, uint32_t* dst,
+                                            uint8_t* have, int spin_limit) {
+  for (int i = threadIdx.x; i < n; i += kBlock) have[i] = 0;
+  __syncthreads();
+  int round = 0;
+  while (true) {
+    int missing = 0;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+      if (!have[i]) {
+        const uint64_t w = tag_load(src + i);
+        if (uint32_t(w >> 32) == tag) {
+          dst[i] = uint32_t(w);
+          have[i] = 1;
+        } else {
+          missing = 1;
+        }
+      }
+    }
+    const int any = __syncthreads_or(missing);
+    if (!any) return true;
+    if (++round > spin_limit) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Nontemporal 16-byte vector loads/stores: streamed data is read once.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_nt16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void st_nt16(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+// Eight consecutive elements [e, e+8) of a row as fp32 (streaming loads);
+// elements at or beyond V read as -inf. kVecOk: the row base is 16-byte
+// aligned and V % 8 == 0, so an in-range group is one or two 16-byte loads.
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void load8_nt(const void* row, int64_t e, int64_t V, float (&x)[kVec]) {
+  if (kVecOk && e + kVec <= V) {
+    if constexpr (kDtype == 1) {
+      const u32x4 w = ld_nt16(static_cast<const uint16_t*>(row) + e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    } else {
+      const u32x4 a = ld_nt16(static_cast<const float*>(row) + e);
+      const u32x4 b = ld_nt16(static_cast<const float*>(row) + e + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = __uint_as_float(a[i]);
+        x[4 + i] = __uint_as_float(b[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) {
+      const int64_t idx = e + i;
+      if (idx < V) {
+        if constexpr (kDtype == 1)
+          x[i] = bf16_bits_to_f32(static_cast<const uint16_t*>(row)[idx]);
+        else
+          x[i] = static_cast<const float*>(row)[idx];
+      } else {
+        x[i] = -INFINITY;
+      }
+    }
+  }
+}
+
+}  // namespace lvtv

@@ -28,6 +28,7 @@
 
 #include "../../include/lvtv.h"
 #include "device_common.hpp"
+#include "fused_common.hpp"
 
 namespace lvtv {
 namespace {
@@ -57,7 +58,7 @@ Layout make_layout(int N, int W, int V) {
   Layout L;
   L.S = (V + kSlice - 1) / kSlice;
   const size_t rows = size_t(N) * W;
-  size_t off = 0;
+  size_t off = kReservedBytes;
   L.off_stat = off;
   off = align256(off + sizeof(SliceStat) * rows * L.S);
   L.off_part = off;

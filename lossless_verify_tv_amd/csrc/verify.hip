@@ -28,9 +28,14 @@
 #include <cstddef>
 #include <cstdint>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "../../include/lvtv.h"
 #include "device_common.hpp"
+#include "fused_common.hpp"
 #include "philox.hpp"
+#include "verify_fused.hpp"
 
 namespace lvtv {
 namespace {
@@ -54,7 +59,7 @@ Layout make_layout(int B, int Kmax, int V) {
   L.S = (V + kSlice - 1) / kSlice;
   L.NC = (V + kChunk - 1) / kChunk;
   L.R = 2 * Kmax + 1;
-  size_t off = 0;
+  size_t off = kReservedBytes;  // the fixed region stays untouched by this path
   L.off_stat = off;
   off = align256(off + sizeof(SliceStat) * size_t(B) * L.R * L.S);
   L.off_arg = off;
@@ -583,9 +588,39 @@ bool sizes_ok(int32_t B, int32_t Kmax, int32_t V) {
 }  // namespace
 }  // namespace lvtv
 
+namespace lvtv {
+namespace {
+
+// The single-read kernel serves every size it can hold; the two-read
+// pipeline above serves the rest, and can be forced with
+// LVTV_VERIFY_PATH=two-read (used to cross-check the two).
+bool use_fused(int32_t B, int32_t Kmax, int32_t V) {
+  const char* path = std::getenv("LVTV_VERIFY_PATH");
+  if (path && std::strcmp(path, "two-read") == 0) return false;
+  return vf::applicable(B, Kmax, V);
+}
+
+// Rounds a workgroup polls for a word before recomputing it itself
+// (LVTV_SPIN_LIMIT; 0 makes every wait take the recompute path, which the
+// tests use to exercise it).
+int spin_limit() {
+  const char* v = std::getenv("LVTV_SPIN_LIMIT");
+  if (!v || !*v) return 1 << 16;
+  const long n = std::strtol(v, nullptr, 10);
+  return n < 0 ? 0 : (n > (1 << 30) ? (1 << 30) : int(n));
+}
+
+}  // namespace
+}  // namespace lvtv
+
 extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype) {
   if (!lvtv::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
-  return lvtv::make_layout(B, Kmax, V).total;
+  size_t n = lvtv::make_layout(B, Kmax, V).total;
+  if (lvtv::vf::applicable(B, Kmax, V)) {
+    const size_t f = lvtv::vf::workspace_bytes(B, Kmax, V);
+    if (f > n) n = f;
+  }
+  return n;
 }
 
 extern "C" int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
@@ -602,8 +637,32 @@ extern "C" int spec_verify(const void* target_logits, const void* draft_logits, 
     return LVTV_ERR_NULL;
   if (Kmax > 0 && (!draft_logits || !draft_tokens || !alpha)) return LVTV_ERR_NULL;
   const Layout L = make_layout(B, Kmax, V);
-  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+  if (!workspace || workspace_bytes < spec_verify_workspace_bytes(B, Kmax, V, dtype) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
+  const uintptr_t mis0 = reinterpret_cast<uintptr_t>(target_logits) |
+                         reinterpret_cast<uintptr_t>(draft_logits);
+  if (use_fused(B, Kmax, V)) {
+    vf::VerifyCall c;
+    c.target = target_logits;
+    c.draft = draft_logits;
+    c.dtype = dtype;
+    c.vec_ok = (V % kVec == 0) && ((mis0 & 15) == 0);
+    c.tokens = draft_tokens;
+    c.kreq = k_per_req;
+    c.temp = temperature;
+    c.seed = seed;
+    c.B = B;
+    c.Kmax = Kmax;
+    c.V = V;
+    c.spin_limit = spin_limit();
+    c.acc_len = accepted_len;
+    c.out_tokens = out_tokens;
+    c.alpha = alpha;
+    c.status = status;
+    const hipError_t e = vf::run(c, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+  }
   Args a;
   a.target = target_logits;
   a.draft = draft_logits;
