@@ -1,16 +1,17 @@
 // spec_verify, single-read kernel (one launch) for gfx950.
 //
-// Each workgroup owns one slice of 8192 tokens of one (request b, position
-// k) pair of rows: target row k and, for k < K_b, draft row k (k = K_b is
-// the bonus row, target only). It streams the slice from HBM once into
-// registers, then:
+// Each 512-thread workgroup owns one slice of 16384 tokens of one (request b,
+// position k) pair of rows: target row k and, for k < K_b, draft row k
+// (k = K_b is the bonus row, target only). It streams its slice from HBM
+// once, keeping the raw logits in registers (bf16 stays packed, two tokens
+// per register), then:
 //   1. computes the slice's softmax statistics for both rows (max, sum of
 //      exp), publishes them as tagged words and collects those of the other
 //      slices of the same rows (bounded wait, see fused_common.hpp);
-//   2. with the row statistics, turns its register-held exponentials into
-//      p and q and accumulates alpha = sum min(p, q) over the slice and, per
-//      2048-token chunk (one wave's contiguous span), the residual mass
-//      sum max(0, p - q), or for the bonus row the mass of p;
+//   2. with the row statistics, recomputes the exponentials from the
+//      registers into p and q and accumulates alpha = sum min(p, q) over the
+//      slice and, per 2048-token chunk (one wave's contiguous span), the
+//      residual mass sum max(0, p - q); for the bonus row, the mass of p;
 //   3. counts itself in at its request; the last of the request's
 //      workgroups finalises it: status checks, alpha_k, the accept scan with
 //      Philox uniforms, and the inverse-CDF draw (chunk from the chunk
@@ -48,12 +49,15 @@ namespace lvtv {
 namespace vf {
 namespace {
 
-constexpr int kSteps = 4;                          // 16-byte groups per thread per row
-constexpr int kSlice = kBlock * kVec * kSteps;     // 8192 tokens per workgroup
-constexpr int kSpan = kWave * kVec * kSteps;       // 2048 tokens per wave = one chunk
-constexpr int kStepStride = kWave * kVec;          // 512
+constexpr int kThreads = 512;                       // threads per workgroup
+constexpr int kWaves = kThreads / kWave;            // 8
+constexpr int kSteps = 4;                           // 8-token groups per thread per row
+constexpr int kSlice = kThreads * kVec * kSteps;    // 16384 tokens per workgroup
+constexpr int kSpan = kWave * kVec * kSteps;        // 2048 tokens per wave = one chunk
+constexpr int kStepStride = kWave * kVec;           // 512
 constexpr int kRowsMax = 2 * LVTV_MAX_K + 1;
 constexpr float kL2E = 1.44269504088896340736f;
+static_assert(kSlice * kMaxSlices >= 524288, "slice count limit covers V <= 524288");
 
 struct Args {
   const void* target;
@@ -95,28 +99,14 @@ __device__ __forceinline__ size_t chunk_idx(const Args& a, int b, int k, int c) 
   return (size_t(b) * (a.Kmax + 1) + k) * a.NC + c;
 }
 
-// ------------------------------------------------------------------ slices
+// ------------------------------------------------------------------ reductions (8 waves)
 
-// Token index of thread-element (step i, element j) in slice s.
-__device__ __forceinline__ int64_t elem_base(int s) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
-  return int64_t(s) * kSlice + wave * kSpan + lane * kVec;
-}
-
-template <int kDtype, bool kVecOk>
-__device__ __forceinline__ void load_slice(const void* row, int64_t V, int s,
-                                           float (&x)[kSteps][kVec]) {
-  const int64_t base = elem_base(s);
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i) load8_nt<kDtype, kVecOk>(row, base + i * kStepStride, V, x[i]);
-}
-
-// Block reduction of two floats at once (max or sum), fixed order.
-struct Red2 {
-  float v[kWavesPerBlock][2];
+template <int N>
+struct Red {
+  float v[kWaves][N];
 };
 
-__device__ __forceinline__ void block_max2(float& a, float& b, Red2& sh) {
+__device__ __forceinline__ void bmax2(float& a, float& b, Red<2>& sh) {
   a = wave_max(a);
   b = wave_max(b);
   __syncthreads();
@@ -128,13 +118,13 @@ __device__ __forceinline__ void block_max2(float& a, float& b, Red2& sh) {
   a = sh.v[0][0];
   b = sh.v[0][1];
 #pragma unroll
-  for (int w = 1; w < kWavesPerBlock; ++w) {
+  for (int w = 1; w < kWaves; ++w) {
     a = fmaxf(a, sh.v[w][0]);
     b = fmaxf(b, sh.v[w][1]);
   }
 }
 
-__device__ __forceinline__ void block_sum2(float& a, float& b, Red2& sh) {
+__device__ __forceinline__ void bsum2(float& a, float& b, Red<2>& sh) {
   a = wave_sum(a);
   b = wave_sum(b);
   __syncthreads();
@@ -146,10 +136,181 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, Red2& sh) {
   a = sh.v[0][0];
   b = sh.v[0][1];
 #pragma unroll
-  for (int w = 1; w < kWavesPerBlock; ++w) {
+  for (int w = 1; w < kWaves; ++w) {
     a += sh.v[w][0];
     b += sh.v[w][1];
   }
+}
+
+__device__ __forceinline__ ArgMax bargmax(ArgMax x, ArgMax* sh) {
+  x = wave_argmax(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = x;
+  __syncthreads();
+  ArgMax r = sh[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = argmax_combine(r, sh[w]);
+  return r;
+}
+
+__device__ __forceinline__ double bexscan(double v, double* sh, double& total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) sh[wave] = inc;
+  __syncthreads();
+  double pre = 0.0;
+  for (int w = 0; w < wave; ++w) pre += sh[w];
+  total = 0.0;
+  for (int w = 0; w < kWaves; ++w) total += sh[w];
+  return pre + inc - v;
+}
+
+__device__ __forceinline__ int bmin_i(int v, int* sh) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = sh[0];
+  for (int w = 1; w < kWaves; ++w) r = min(r, sh[w]);
+  return r;
+}
+
+// Block-wide poll of up to two ranges of tagged words into dst / have
+// (concatenated). Returns true when every word was seen fresh.
+struct Ranges {
+  uint64_t* src0;
+  uint64_t* src1;
+  int n0, n1;
+};
+
+__device__ __forceinline__ bool poll(const Ranges& r, uint32_t tag, uint32_t* dst, uint8_t* have,
+                                     int spin_limit) {
+  const int n0 = r.n0;
+  const int n = n0 + r.n1;
+  for (int i = threadIdx.x; i < n; i += kThreads) have[i] = 0;
+  __syncthreads();
+  int round = 0;
+  while (true) {
+    int missing = 0;
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      if (!have[i]) {
+        uint64_t* p = i < n0 ? r.src0 + i : r.src1 + (i - n0);
+        const uint64_t w = tag_load(p);
+        if (uint32_t(w >> 32) == tag) {
+          dst[i] = uint32_t(w);
+          have[i] = 1;
+        } else {
+          missing = 1;
+        }
+      }
+    }
+    if (!__syncthreads_or(missing)) return true;
+    if (++round > spin_limit) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+__device__ __forceinline__ bool have4(const uint8_t* have, int e) {
+  return have[4 * e] && have[4 * e + 1] && have[4 * e + 2] && have[4 * e + 3];
+}
+
+// ------------------------------------------------------------------ raw slices in registers
+
+// A thread's share of one row slice: kSteps groups of 8 tokens, bf16 kept
+// packed (one 16-byte register quad per group), fp32 as two quads.
+template <int kDtype>
+struct Raw {
+  u32x4 q[kSteps][kDtype == 1 ? 1 : 2];
+};
+
+template <int kDtype>
+__device__ __forceinline__ float elem(const Raw<kDtype>& r, int i, int j) {
+  if constexpr (kDtype == 1) {
+    const uint32_t w = r.q[i][0][j >> 1];
+    return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return __uint_as_float(r.q[i][j >> 2][j & 3]);
+  }
+}
+
+// Makes the compiler treat the raw registers as rewritten, so pass 2
+// recomputes the exponentials from them instead of keeping pass 1's
+// unpacked values and exponentials alive across the exchange (that would
+// need four times the registers).
+template <int kDtype>
+__device__ __forceinline__ void launder(Raw<kDtype>& r) {
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+    for (int q = 0; q < (kDtype == 1 ? 1 : 2); ++q) asm volatile("" : "+v"(r.q[i][q]));
+}
+
+__device__ __forceinline__ int64_t elem_base(int s) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  return int64_t(s) * kSlice + wave * kSpan + lane * kVec;
+}
+
+// Streaming loads of a slice; tokens at or beyond V read as -inf. With
+// kVecOk (16-byte aligned rows, V % 8 == 0) a group of 8 is either wholly
+// inside the row or wholly past its end.
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void load_raw(const void* row, int64_t V, int s, Raw<kDtype>& r) {
+  const int64_t base = elem_base(s);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int64_t e = base + i * kStepStride;
+    if constexpr (kVecOk) {
+      if (e < V) {
+        if constexpr (kDtype == 1) {
+          r.q[i][0] = ld_nt16(static_cast<const uint16_t*>(row) + e);
+        } else {
+          r.q[i][0] = ld_nt16(static_cast<const float*>(row) + e);
+          r.q[i][1] = ld_nt16(static_cast<const float*>(row) + e + 4);
+        }
+      } else if constexpr (kDtype == 1) {
+        r.q[i][0] = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+      } else {
+        r.q[i][0] = u32x4{0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
+        r.q[i][1] = r.q[i][0];
+      }
+    } else {
+      if constexpr (kDtype == 1) {
+        const uint16_t* p = static_cast<const uint16_t*>(row);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t lo = (e + 2 * h < V) ? p[e + 2 * h] : 0xff80u;
+          const uint32_t hi = (e + 2 * h + 1 < V) ? p[e + 2 * h + 1] : 0xff80u;
+          r.q[i][0][h] = lo | (hi << 16);
+        }
+      } else {
+        const uint32_t* p = static_cast<const uint32_t*>(row);
+#pragma unroll
+        for (int h = 0; h < 8; ++h) r.q[i][h >> 2][h & 3] = (e + h < V) ? p[e + h] : 0xff800000u;
+      }
+    }
+  }
+}
+
+// Maximum of the raw logits a thread holds. Each token is unpacked exactly:
+// a packed bf16 word read as one float can be a signalling-NaN pattern (two
+// -inf padding tokens are), which the hardware maximum propagates. A NaN
+// token may or may not surface here; it always surfaces through its
+// exponential (the slice sum turns NaN).
+template <int kDtype>
+__device__ __forceinline__ float raw_max(const Raw<kDtype>& r) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) m = fmaxf(m, elem(r, i, j));
+  return m;
 }
 
 struct SliceStats {
@@ -158,55 +319,202 @@ struct SliceStats {
   float wsum;  // this wave's part of l (its chunk)
 };
 
-// In place: x <- scaled logits -> exponentials; returns the slice statistics
-// of the target row and, with kTwo, of the draft row. Every thread of the
-// block must call it.
-template <bool kTwo>
-__device__ __forceinline__ void slice_stats(float (&xt)[kSteps][kVec], float (&xd)[kSteps][kVec],
-                                            float inv_t, bool unit, Red2& sh, SliceStats& st,
+// Exponent offset for a slice reference R (0 for an all -inf slice, so its
+// -inf tokens still give 0 and a NaN still gives NaN).
+__device__ __forceinline__ float neg_ref(float R) { return R == -INFINITY ? 0.f : -R; }
+
+__device__ __forceinline__ float ex(float x, float inv_t, bool unit, float nr) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(scale_logit(x, inv_t, unit), kL2E, nr));
+}
+
+// Softmax statistics of the target slice and, with kTwo, of the draft slice.
+// Every thread of the block must call it.
+template <int kDtype, bool kTwo>
+__device__ __forceinline__ void slice_stats(Raw<kDtype>& rt, Raw<kDtype>& rd, float inv_t,
+                                            bool unit, Red<2>& sh, SliceStats& st,
                                             SliceStats& sd) {
-  float mt = -INFINITY, md = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i)
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      xt[i][j] = scale_logit(xt[i][j], inv_t, unit);
-      mt = fmaxf(mt, xt[i][j]);
-      if constexpr (kTwo) {
-        xd[i][j] = scale_logit(xd[i][j], inv_t, unit);
-        md = fmaxf(md, xd[i][j]);
-      }
-    }
-  block_max2(mt, md, sh);
-  const float rt = (mt == -INFINITY) ? -INFINITY : mt * kL2E;
-  const float rd = (md == -INFINITY) ? -INFINITY : md * kL2E;
-  const float nt = (mt == -INFINITY) ? 0.f : -rt;
-  const float nd = (md == -INFINITY) ? 0.f : -rd;
+  float mt = raw_max(rt), md = kTwo ? raw_max(rd) : -INFINITY;
+  launder(rt);
+  if constexpr (kTwo) launder(rd);
+  bmax2(mt, md, sh);
+  mt = scale_logit(mt, inv_t, unit);
+  md = scale_logit(md, inv_t, unit);
+  const float rtf = (mt == -INFINITY) ? -INFINITY : mt * kL2E;
+  const float rdf = (md == -INFINITY) ? -INFINITY : md * kL2E;
+  const float nt = neg_ref(rtf), nd = neg_ref(rdf);
   float lt = 0.f, ld = 0.f;
 #pragma unroll
   for (int i = 0; i < kSteps; ++i)
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
-      xt[i][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(xt[i][j], kL2E, nt));
-      lt += xt[i][j];
-      if constexpr (kTwo) {
-        xd[i][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(xd[i][j], kL2E, nd));
-        ld += xd[i][j];
-      }
+      lt += ex(elem(rt, i, j), inv_t, unit, nt);
+      if constexpr (kTwo) ld += ex(elem(rd, i, j), inv_t, unit, nd);
     }
   const float wt = wave_sum(lt), wd = wave_sum(ld);
   float bt = lt, bd = ld;
-  block_sum2(bt, bd, sh);
-  st = SliceStats{rt, bt, wt};
-  sd = SliceStats{rd, bd, wd};
+  bsum2(bt, bd, sh);
+  st = SliceStats{rtf, bt, wt};
+  sd = SliceStats{rdf, bd, wd};
 }
 
-// Row statistics from the per-slice (R, l) words (4 words per slice, R at
-// offset offR, l at offL), computed by one wave with one slice per lane:
-// R_max = max R_s and L = sum_s l_s 2^(R_s - R_max) in fp64 (fixed
-// butterfly order). Slices that are entirely -inf weigh 0 (their l is 0, or
-// NaN when a NaN was present, which must propagate). All lanes of the
-// calling wave get the result.
+// Pass 2 of a pair slice: the exponentials are recomputed from the
+// registers exactly as in slice_stats, scaled into p and q; alpha over the
+// slice and the residual mass of this wave's chunk.
+template <int kDtype>
+__device__ __forceinline__ void pair_overlap(const Raw<kDtype>& rt, const Raw<kDtype>& rd,
+                                             float inv_t, bool unit, float nt, float nd, float at,
+                                             float ad, Red<2>& sh, float& alpha_slice,
+                                             float& chunk_mass) {
+  float sa = 0.f, sr = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const float p = ex(elem(rt, i, j), inv_t, unit, nt) * at;
+      const float q = ex(elem(rd, i, j), inv_t, unit, nd) * ad;
+      const float mn = fminf(p, q);
+      sa += mn;
+      sr += p - mn;
+    }
+  chunk_mass = wave_sum(sr);
+  float unused = 0.f;
+  bsum2(sa, unused, sh);
+  alpha_slice = sa;
+}
+
+// Argmax of one slice of raw logits (lowest index among equal values; NaN
+// flagged).
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ ArgMax slice_argmax(const void* row, int64_t V, int s, ArgMax* sh) {
+  Raw<kDtype> r;
+  load_raw<kDtype, kVecOk>(row, V, s, r);
+  const int64_t base = elem_base(s);
+  ArgMax best{-INFINITY, INT_MAX, 0};
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i)
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const int64_t idx = base + i * kStepStride + j;
+      const float v = elem(r, i, j);
+      if (idx < V) {
+        if (isnan(v)) best.nan = 1;
+        else if (v > best.v || (v == best.v && idx < best.i)) {
+          best.v = v;
+          best.i = int32_t(idx);
+        }
+      }
+    }
+  return bargmax(best, sh);
+}
+
+// ------------------------------------------------------------------ shared memory
+
+constexpr int kFinWords = 4 * kMaxSlices * (LVTV_MAX_K + 1) + kMaxSlices * LVTV_MAX_K;
+
+struct Shared {
+  Red<2> red;
+  ArgMax am[kWaves];
+  double redd[kWaves];
+  int redi[kWaves];
+  float cm8[kWaves];
+  // item exchange
+  uint32_t words[4 * kMaxSlices];
+  uint8_t have[4 * kMaxSlices];
+  float at, ad;
+  float Rt, Rd;
+  double Lt, Ld;
+  int last;
+  // finalize
+  uint32_t fwords[kFinWords];
+  uint8_t fhave[kFinWords];
+  float R[kRowsMax];
+  double L[kRowsMax];
+  int32_t arg[kRowsMax];
+  double alpha[LVTV_MAX_K];
+  double ratio[LVTV_MAX_K];
+  double uacc[LVTV_MAX_K];
+  float cm[kWaves * kMaxSlices];
+  int j;
+  int pick;
+  double before;
+  double scale;
+};
+
+// ------------------------------------------------------------------ recomputation
+
+// The four statistics words a (b, k, s) workgroup publishes, recomputed from
+// the inputs (bit-identical to what it publishes).
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void recompute_stat_words(const Args& a, int b, int k, int s, int kb,
+                                                     float T, uint32_t (&w)[4], Shared& sh) {
+  const int64_t V = a.V;
+  const bool pair = k < kb;
+  if (T == 0.f) {
+    const ArgMax at = slice_argmax<kDtype, kVecOk>(row_ptr<kDtype>(a, b, true, k), V, s, sh.am);
+    ArgMax ad{-INFINITY, INT_MAX, 0};
+    if (pair) ad = slice_argmax<kDtype, kVecOk>(row_ptr<kDtype>(a, b, false, k), V, s, sh.am);
+    w[0] = __float_as_uint(at.nan ? NAN : at.v);
+    w[1] = uint32_t(at.i);
+    w[2] = __float_as_uint(ad.nan ? NAN : ad.v);
+    w[3] = uint32_t(ad.i);
+    return;
+  }
+  const float inv_t = __fdiv_rn(1.f, T);
+  const bool unit = T == 1.f;
+  Raw<kDtype> rt, rd;
+  SliceStats st, sd;
+  load_raw<kDtype, kVecOk>(row_ptr<kDtype>(a, b, true, k), V, s, rt);
+  if (pair) {
+    load_raw<kDtype, kVecOk>(row_ptr<kDtype>(a, b, false, k), V, s, rd);
+    slice_stats<kDtype, true>(rt, rd, inv_t, unit, sh.red, st, sd);
+  } else {
+    slice_stats<kDtype, false>(rt, rd, inv_t, unit, sh.red, st, sd);
+  }
+  w[0] = __float_as_uint(st.R);
+  w[1] = __float_as_uint(st.l);
+  w[2] = __float_as_uint(pair ? sd.R : 0.f);
+  w[3] = __float_as_uint(pair ? sd.l : 1.f);
+}
+
+// Slice alpha and the slice's chunk masses (cm8[wave]) of (b, k, s),
+// recomputed from the inputs given the row statistics.
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void recompute_overlap(const Args& a, int b, int k, int s, int kb,
+                                                  float T, float Rt, double Lt, float Rd,
+                                                  double Ld, float& alpha_slice, Shared& sh) {
+  const int64_t V = a.V;
+  const bool pair = k < kb;
+  const float inv_t = __fdiv_rn(1.f, T);
+  const bool unit = T == 1.f;
+  Raw<kDtype> rt, rd;
+  SliceStats st, sd;
+  float cmass;
+  load_raw<kDtype, kVecOk>(row_ptr<kDtype>(a, b, true, k), V, s, rt);
+  if (pair) {
+    load_raw<kDtype, kVecOk>(row_ptr<kDtype>(a, b, false, k), V, s, rd);
+    slice_stats<kDtype, true>(rt, rd, inv_t, unit, sh.red, st, sd);
+    launder(rt);
+    launder(rd);
+    const float at = float(exp2((double)st.R - (double)Rt) / Lt);
+    const float ad = float(exp2((double)sd.R - (double)Rd) / Ld);
+    pair_overlap<kDtype>(rt, rd, inv_t, unit, neg_ref(st.R), neg_ref(sd.R), at, ad, sh.red,
+                         alpha_slice, cmass);
+  } else {
+    slice_stats<kDtype, false>(rt, rd, inv_t, unit, sh.red, st, sd);
+    const float at = float(exp2((double)st.R - (double)Rt) / Lt);
+    alpha_slice = 0.f;
+    cmass = st.wsum * at;
+  }
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh.cm8[threadIdx.x / kWave] = cmass;
+  __syncthreads();
+}
+
+// Row statistics from per-slice (R, l) words (4 words per slice, R at offset
+// offR, l at offL), combined by one wave, one slice per lane: R_max = max R_s
+// and L = sum_s l_s 2^(R_s - R_max) in fp64 (fixed butterfly order). Slices
+// that are entirely -inf weigh 0 (their l is 0, or NaN when a NaN was
+// present, which must propagate). All lanes of the wave get the result.
 __device__ __forceinline__ void combine_row_wave(const uint32_t* words, int S, int offR, int offL,
                                                  float& Rmax, double& L) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -216,235 +524,6 @@ __device__ __forceinline__ void combine_row_wave(const uint32_t* words, int S, i
   const double w = (R == -INFINITY) ? (double)l * 0.0 : (double)l * exp2((double)R - (double)m);
   L = wave_sum(w);
   Rmax = m;
-}
-
-// Pass 2 of a pair slice: alpha over the slice and the residual mass per
-// wave chunk, from exponentials held in registers.
-__device__ __forceinline__ void pair_overlap(const float (&et)[kSteps][kVec],
-                                             const float (&ed)[kSteps][kVec], float at, float ad,
-                                             float* red4, float& alpha_slice, float& chunk_mass) {
-  float sa = 0.f, sr = 0.f;
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i)
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const float p = et[i][j] * at;
-      const float q = ed[i][j] * ad;
-      const float mn = fminf(p, q);
-      sa += mn;
-      sr += p - mn;
-    }
-  chunk_mass = wave_sum(sr);
-  alpha_slice = block_sum(sa, red4);
-}
-
-// Argmax of one slice of raw logits (lowest index among equal values; NaN
-// flagged), one 8-token group at a time.
-template <int kDtype, bool kVecOk>
-__device__ __forceinline__ ArgMax slice_argmax(const void* row, int64_t V, int s, ArgMax* sh) {
-  const int64_t base = elem_base(s);
-  ArgMax best{-INFINITY, INT_MAX, 0};
-#pragma unroll 1
-  for (int i = 0; i < kSteps; ++i) {
-    float x[kVec];
-    load8_nt<kDtype, kVecOk>(row, base + i * kStepStride, V, x);
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const int64_t idx = base + i * kStepStride + j;
-      if (idx < V) {
-        const float v = x[j];
-        if (isnan(v)) best.nan = 1;
-        else if (v > best.v || (v == best.v && idx < best.i)) {
-          best.v = v;
-          best.i = int32_t(idx);
-        }
-      }
-    }
-  }
-  return block_argmax(best, sh);
-}
-
-// Streaming forms of slice_stats / pair_overlap for the recompute path: the
-// slice is re-read from HBM one 8-token group at a time (few registers),
-// with the same per-thread accumulation order and the same reductions, so
-// the results are bit-identical to the register-held path.
-template <int kDtype, bool kVecOk, bool kTwo>
-__device__ __forceinline__ void stream_stats(const void* trow, const void* drow, int64_t V, int s,
-                                             float inv_t, bool unit, Red2& sh, SliceStats& st,
-                                             SliceStats& sd) {
-  const int64_t base = elem_base(s);
-  float mt = -INFINITY, md = -INFINITY;
-#pragma unroll 1
-  for (int i = 0; i < kSteps; ++i) {
-    float xt[kVec], xd[kVec];
-    load8_nt<kDtype, kVecOk>(trow, base + i * kStepStride, V, xt);
-    if constexpr (kTwo) load8_nt<kDtype, kVecOk>(drow, base + i * kStepStride, V, xd);
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      mt = fmaxf(mt, scale_logit(xt[j], inv_t, unit));
-      if constexpr (kTwo) md = fmaxf(md, scale_logit(xd[j], inv_t, unit));
-    }
-  }
-  block_max2(mt, md, sh);
-  const float rt = (mt == -INFINITY) ? -INFINITY : mt * kL2E;
-  const float rd = (md == -INFINITY) ? -INFINITY : md * kL2E;
-  const float nt = (mt == -INFINITY) ? 0.f : -rt;
-  const float nd = (md == -INFINITY) ? 0.f : -rd;
-  float lt = 0.f, ld = 0.f;
-#pragma unroll 1
-  for (int i = 0; i < kSteps; ++i) {
-    float xt[kVec], xd[kVec];
-    load8_nt<kDtype, kVecOk>(trow, base + i * kStepStride, V, xt);
-    if constexpr (kTwo) load8_nt<kDtype, kVecOk>(drow, base + i * kStepStride, V, xd);
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      lt += __builtin_amdgcn_exp2f(__builtin_fmaf(scale_logit(xt[j], inv_t, unit), kL2E, nt));
-      if constexpr (kTwo)
-        ld += __builtin_amdgcn_exp2f(__builtin_fmaf(scale_logit(xd[j], inv_t, unit), kL2E, nd));
-    }
-  }
-  const float wt = wave_sum(lt), wd = wave_sum(ld);
-  float bt = lt, bd = ld;
-  block_sum2(bt, bd, sh);
-  st = SliceStats{rt, bt, wt};
-  sd = SliceStats{rd, bd, wd};
-}
-
-template <int kDtype, bool kVecOk>
-__device__ __forceinline__ void stream_overlap(const void* trow, const void* drow, int64_t V, int s,
-                                               float inv_t, bool unit, const SliceStats& st,
-                                               const SliceStats& sd, float at, float ad,
-                                               float* red4, float& alpha_slice,
-                                               float& chunk_mass) {
-  const int64_t base = elem_base(s);
-  const float nt = (st.R == -INFINITY) ? 0.f : -st.R;
-  const float nd = (sd.R == -INFINITY) ? 0.f : -sd.R;
-  float sa = 0.f, sr = 0.f;
-#pragma unroll 1
-  for (int i = 0; i < kSteps; ++i) {
-    float xt[kVec], xd[kVec];
-    load8_nt<kDtype, kVecOk>(trow, base + i * kStepStride, V, xt);
-    load8_nt<kDtype, kVecOk>(drow, base + i * kStepStride, V, xd);
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(scale_logit(xt[j], inv_t, unit), kL2E, nt));
-      const float ed = __builtin_amdgcn_exp2f(__builtin_fmaf(scale_logit(xd[j], inv_t, unit), kL2E, nd));
-      const float p = et * at;
-      const float q = ed * ad;
-      const float mn = fminf(p, q);
-      sa += mn;
-      sr += p - mn;
-    }
-  }
-  chunk_mass = wave_sum(sr);
-  alpha_slice = block_sum(sa, red4);
-}
-
-// ------------------------------------------------------------------ shared memory
-
-struct ItemShared {
-  Red2 red;
-  float red4[kWavesPerBlock];
-  float cm4[kWavesPerBlock];
-  ArgMax am[kWavesPerBlock];
-  uint32_t words[4 * kMaxSlices];
-  uint8_t have[4 * kMaxSlices];
-  float at, ad;
-  float Rt, Rd;
-  double Lt, Ld;
-  int last;
-};
-
-struct FinShared {
-  Red2 red;
-  double redd[kWavesPerBlock];
-  float red4[kWavesPerBlock];
-  int redi[kWavesPerBlock];
-  ArgMax am[kWavesPerBlock];
-  uint32_t words[4 * kMaxSlices * (LVTV_MAX_K + 1)];
-  uint8_t have[4 * kMaxSlices * (LVTV_MAX_K + 1)];
-  float R[kRowsMax];
-  double L[kRowsMax];
-  int32_t arg[kRowsMax];
-  double alpha[LVTV_MAX_K];
-  float cm[4 * kMaxSlices];
-  float cm4[kWavesPerBlock];
-  int status;
-  int j;
-  int pick;
-  double before;
-};
-
-struct Shared {
-  ItemShared it;
-  FinShared fin;
-};
-
-// ------------------------------------------------------------------ recomputation
-
-// The statistics words a (b, k, s) workgroup publishes, recomputed from the
-// inputs (bit-identical to what it publishes).
-template <int kDtype, bool kVecOk>
-__device__ __forceinline__ void recompute_stat_words(const Args& a, int b, int k, int s, int kb,
-                                                     float T, uint32_t (&w)[4], Shared& sh) {
-  const int64_t V = a.V;
-  const bool pair = k < kb;
-  if (T == 0.f) {
-    const ArgMax at = slice_argmax<kDtype, kVecOk>(row_ptr<kDtype>(a, b, true, k), V, s, sh.it.am);
-    ArgMax ad{-INFINITY, INT_MAX, 0};
-    if (pair) ad = slice_argmax<kDtype, kVecOk>(row_ptr<kDtype>(a, b, false, k), V, s, sh.it.am);
-    w[0] = __float_as_uint(at.nan ? NAN : at.v);
-    w[1] = uint32_t(at.i);
-    w[2] = __float_as_uint(ad.nan ? NAN : ad.v);
-    w[3] = uint32_t(ad.i);
-    return;
-  }
-  const float inv_t = __fdiv_rn(1.f, T);
-  const bool unit = T == 1.f;
-  SliceStats st, sd;
-  if (pair)
-    stream_stats<kDtype, kVecOk, true>(row_ptr<kDtype>(a, b, true, k),
-                                       row_ptr<kDtype>(a, b, false, k), V, s, inv_t, unit,
-                                       sh.it.red, st, sd);
-  else
-    stream_stats<kDtype, kVecOk, false>(row_ptr<kDtype>(a, b, true, k), nullptr, V, s, inv_t,
-                                        unit, sh.it.red, st, sd);
-  w[0] = __float_as_uint(st.R);
-  w[1] = __float_as_uint(st.l);
-  w[2] = __float_as_uint(pair ? sd.R : 0.f);
-  w[3] = __float_as_uint(pair ? sd.l : 1.f);
-}
-
-// Slice alpha and the slice's four chunk masses of (b, k, s), recomputed
-// from the inputs given the row statistics (cm4 in shared memory).
-template <int kDtype, bool kVecOk>
-__device__ __forceinline__ void recompute_overlap(const Args& a, int b, int k, int s, int kb,
-                                                  float T, float Rt, double Lt, float Rd,
-                                                  double Ld, float& alpha_slice, float* cm4,
-                                                  Shared& sh) {
-  const int64_t V = a.V;
-  const bool pair = k < kb;
-  const float inv_t = __fdiv_rn(1.f, T);
-  const bool unit = T == 1.f;
-  const void* trow = row_ptr<kDtype>(a, b, true, k);
-  SliceStats st, sd;
-  float cmass;
-  if (pair) {
-    const void* drow = row_ptr<kDtype>(a, b, false, k);
-    stream_stats<kDtype, kVecOk, true>(trow, drow, V, s, inv_t, unit, sh.it.red, st, sd);
-    const float at = float(exp2((double)st.R - (double)Rt) / Lt);
-    const float ad = float(exp2((double)sd.R - (double)Rd) / Ld);
-    stream_overlap<kDtype, kVecOk>(trow, drow, V, s, inv_t, unit, st, sd, at, ad, sh.it.red4,
-                                   alpha_slice, cmass);
-  } else {
-    stream_stats<kDtype, kVecOk, false>(trow, nullptr, V, s, inv_t, unit, sh.it.red, st, sd);
-    const float at = float(exp2((double)st.R - (double)Rt) / Lt);
-    alpha_slice = 0.f;
-    cmass = st.wsum * at;
-  }
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) cm4[threadIdx.x / kWave] = cmass;
-  __syncthreads();
 }
 
 // ------------------------------------------------------------------ completion
@@ -461,8 +540,8 @@ __device__ __forceinline__ void complete_unit(const Args& a, uint32_t epoch) {
 __device__ __forceinline__ void write_fault(const Args& a, int b, int status) {
   int32_t* out_tok = a.out_tokens + size_t(b) * (a.Kmax + 1);
   float* out_alpha = a.alpha + size_t(b) * a.Kmax;
-  for (int k = threadIdx.x; k <= a.Kmax; k += kBlock) out_tok[k] = -1;
-  for (int k = threadIdx.x; k < a.Kmax; k += kBlock) out_alpha[k] = 0.f;
+  for (int k = threadIdx.x; k <= a.Kmax; k += kThreads) out_tok[k] = -1;
+  for (int k = threadIdx.x; k < a.Kmax; k += kThreads) out_alpha[k] = 0.f;
   if (threadIdx.x == 0) {
     a.status[b] = status;
     a.acc_len[b] = -1;
@@ -479,44 +558,17 @@ __device__ __forceinline__ double prob64(const void* row, int64_t v, float inv_t
   return exp2((double)s * (double)kL2E - (double)R) / L;
 }
 
-__device__ __forceinline__ double block_exclusive_scan(double v, double* sh, double& total) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  double inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double n = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += n;
-  }
-  __syncthreads();
-  if (lane == kWave - 1) sh[wave] = inc;
-  __syncthreads();
-  double pre = 0.0;
-  for (int w = 0; w < wave; ++w) pre += sh[w];
-  total = 0.0;
-  for (int w = 0; w < kWavesPerBlock; ++w) total += sh[w];
-  return pre + inc - v;
-}
+constexpr int kPerThread = kSpan / kThreads;  // 4 tokens of a chunk per thread
 
-__device__ __forceinline__ int block_min_i(int v, int* sh) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = v;
-  __syncthreads();
-  int r = sh[0];
-  for (int w = 1; w < kWavesPerBlock; ++w) r = min(r, sh[w]);
-  return r;
-}
-
-// Weights of the draw inside chunk c: 8 consecutive tokens per thread.
+// Weights of the draw inside chunk c (fp64, from the inputs).
 template <int kDtype>
 __device__ __forceinline__ void chunk_weights(const void* trow, const void* drow, int64_t V,
                                               int c, float inv_t, bool unit, float Rt, double Lt,
                                               float Rd, double Ld, bool residual,
-                                              double (&w)[kVec], int64_t& v0) {
-  v0 = int64_t(c) * kSpan + threadIdx.x * kVec;
+                                              double (&w)[kPerThread], int64_t& v0) {
+  v0 = int64_t(c) * kSpan + threadIdx.x * kPerThread;
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
+  for (int i = 0; i < kPerThread; ++i) {
     const int64_t v = v0 + i;
     double x = 0.0;
     if (v < V) {
@@ -527,146 +579,154 @@ __device__ __forceinline__ void chunk_weights(const void* trow, const void* drow
   }
 }
 
-// Smallest token of chunk c whose cumulative weight exceeds `rem` (weights
-// recomputed in fp64); falls back to the last positive-weight token of the
-// chunk when rounding leaves `rem` at or above the chunk's fp64 total.
+// Smallest token of chunk c whose cumulative weight passes `rem`. The fp64
+// weights are rescaled to sum to the chunk's mass `cmass` (the unit the
+// chunk was chosen in); when rounding leaves `rem` at or above that, the
+// last positive-weight token of the chunk is taken.
 template <int kDtype>
-__device__ __forceinline__ int search_chunk(const void* trow, const void* drow, int64_t V, int c, double rem,
-                            float inv_t, bool unit, float Rt, double Lt, float Rd, double Ld,
-                            bool residual, FinShared& sh) {
-  double w[kVec];
+__device__ __forceinline__ int search_chunk(const void* trow, const void* drow, int64_t V, int c,
+                                            double rem, double cmass, float inv_t, bool unit,
+                                            float Rt, double Lt, float Rd, double Ld,
+                                            bool residual, Shared& sh) {
+  double w[kPerThread];
   int64_t v0;
   chunk_weights<kDtype>(trow, drow, V, c, inv_t, unit, Rt, Lt, Rd, Ld, residual, w, v0);
   double mine = 0.0;
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) mine += w[i];
+  for (int i = 0; i < kPerThread; ++i) mine += w[i];
   double total;
-  const double exc = block_exclusive_scan(mine, sh.redd, total);
+  const double exc = bexscan(mine, sh.redd, total);
+  const double f = (total > 0.0 && cmass > 0.0) ? cmass / total : 1.0;
   int pick = INT_MAX, last = -1;
   double run = exc;
 #pragma unroll
-  for (int i = 0; i < kVec; ++i) {
+  for (int i = 0; i < kPerThread; ++i) {
     run += w[i];
     if (w[i] > 0.0) {
       last = int(v0 + i);
-      if (pick == INT_MAX && run > rem) pick = int(v0 + i);
+      if (pick == INT_MAX && run * f > rem) pick = int(v0 + i);
     }
   }
-  int v = block_min_i(pick, sh.redi);
+  int v = bmin_i(pick, sh.redi);
   if (v == INT_MAX) {
-    v = -block_min_i(last >= 0 ? -last : INT_MAX, sh.redi);
+    v = -bmin_i(last >= 0 ? -last : INT_MAX, sh.redi);
     if (v == -INT_MAX) v = int(int64_t(c) * kSpan);
   }
   return v;
 }
 
-// Inverse-CDF draw from the per-chunk masses `cm` (NC values in LDS).
+// Inverse-CDF draw from the per-chunk masses sh.cm[0..NC).
 template <int kDtype>
-__device__ __forceinline__ int draw_from_masses(const float* cm, int NC, double u, const void* trow,
-                                const void* drow, int64_t V, float inv_t, bool unit, float Rt,
-                                double Lt, float Rd, double Ld, bool residual, FinShared& sh) {
-  // thread 0 scans the chunk masses in fp64 (NC <= 4 * kMaxSlices)
+__device__ __forceinline__ int draw_from_masses(int NC, double u, const void* trow,
+                                                const void* drow, int64_t V, float inv_t,
+                                                bool unit, float Rt, double Lt, float Rd,
+                                                double Ld, bool residual, Shared& sh) {
   if (threadIdx.x == 0) {
     double total = 0.0;
-    for (int c = 0; c < NC; ++c) total += (double)cm[c];
+    for (int c = 0; c < NC; ++c) total += (double)sh.cm[c];
     const double target = u * total;
     double run = 0.0;
     int pick = -1;
     for (int c = 0; c < NC; ++c) {
-      const double nxt = run + (double)cm[c];
-      if (nxt > target && cm[c] > 0.f) {
+      const double nxt = run + (double)sh.cm[c];
+      if (nxt > target && sh.cm[c] > 0.f) {
         pick = c;
         break;
       }
       run = nxt;
     }
-    if (pick < 0) {            // rounding: target at or past the last sum
+    if (pick < 0) {  // rounding put the target at or past the last sum
       for (int c = NC - 1; c >= 0; --c)
-        if (cm[c] > 0.f) {
+        if (sh.cm[c] > 0.f) {
           pick = c;
           break;
         }
-      if (pick < 0) pick = NC - 1;
-      run = INFINITY;           // makes the in-chunk search take its last token
+      if (pick < 0) pick = 0;
       sh.before = INFINITY;
     } else {
       sh.before = target - run;
     }
     sh.pick = pick;
+    sh.scale = (double)sh.cm[pick];
   }
   __syncthreads();
   const int c = sh.pick;
   const double rem = sh.before;
-  return search_chunk<kDtype>(trow, drow, V, c, rem, inv_t, unit, Rt, Lt, Rd, Ld, residual, sh);
+  const double cmass = sh.scale;
+  __syncthreads();
+  return search_chunk<kDtype>(trow, drow, V, c, rem, cmass, inv_t, unit, Rt, Lt, Rd, Ld,
+                              residual, sh);
 }
 
 // Draw from p over the whole row when there are no chunk masses for it (a
 // rejection where the residual is zero everywhere, p_j == q_j): masses of p
-// per chunk in fp64, then the same search.
+// per chunk in fp64 first, then the same search.
 template <int kDtype>
-__device__ __forceinline__ int draw_full_row(int NC, double u, const void* trow, int64_t V, float inv_t,
-                             bool unit, float Rt, double Lt, FinShared& sh) {
+__device__ __forceinline__ int draw_full_row(int NC, double u, const void* trow, int64_t V,
+                                             float inv_t, bool unit, float Rt, double Lt,
+                                             Shared& sh) {
   for (int c = 0; c < NC; ++c) {
-    double w[kVec];
+    double w[kPerThread];
     int64_t v0;
     chunk_weights<kDtype>(trow, nullptr, V, c, inv_t, unit, Rt, Lt, 0.f, 1.0, false, w, v0);
     double mine = 0.0;
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) mine += w[i];
-    const double m = block_sum(mine, sh.redd);
-    if (threadIdx.x == 0) sh.cm[c] = float(m);
+    for (int i = 0; i < kPerThread; ++i) mine += w[i];
+    double total;
+    (void)bexscan(mine, sh.redd, total);
+    if (threadIdx.x == 0) sh.cm[c] = float(total);
     __syncthreads();
   }
-  return draw_from_masses<kDtype>(sh.cm, NC, u, trow, nullptr, V, inv_t, unit, Rt, Lt, 0.f, 1.0,
-                                  false, sh);
+  return draw_from_masses<kDtype>(NC, u, trow, nullptr, V, inv_t, unit, Rt, Lt, 0.f, 1.0, false,
+                                  sh);
 }
 
 // ------------------------------------------------------------------ finalize
 
-// True when the four words of slice entry e were all seen fresh.
-__device__ __forceinline__ bool have4(const uint8_t* have, int e) {
-  return have[4 * e] && have[4 * e + 1] && have[4 * e + 2] && have[4 * e + 3];
-}
-
 template <int kDtype, bool kVecOk>
-__device__ __forceinline__ void finalize(const Args& a, int b, int kb, float T, uint32_t epoch, Shared& shu) {
-  FinShared& sh = shu.fin;
+__device__ __forceinline__ void finalize(const Args& a, int b, int kb, float T, uint32_t epoch,
+                                         Shared& sh) {
   const uint32_t tag = tag_from_epoch(epoch);
   const int S = a.S;
   const int Kmax = a.Kmax;
   const bool greedy = (T == 0.f);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int32_t* y = a.tokens + size_t(b) * Kmax;
 
   // draft tokens of this request
   int bad = 0;
-  const int32_t* y = a.tokens + size_t(b) * Kmax;
-  for (int k = threadIdx.x; k < kb; k += kBlock) bad |= (y[k] < 0 || y[k] >= a.V);
+  for (int k = threadIdx.x; k < kb; k += kThreads) bad |= (y[k] < 0 || y[k] >= a.V);
   const int status_tok = __syncthreads_or(bad) ? LVTV_STATUS_BAD_TOKEN : 0;
 
-  // statistics words of every row: [k][s][4] for k = 0..kb
-  const int nwords = (kb + 1) * S * 4;
-  if (!poll_tagged(a.stat + stat_idx(a, b, 0, 0), nwords, tag, sh.words, sh.have,
-                   a.spin_limit)) {
-    for (int e = 0; e < (kb + 1) * S; ++e) {
-      if (!have4(sh.have, e)) {
+  // statistics words of every row ([k][s][4], k = 0..kb) and, for sampling
+  // requests, the slice alphas ([k][s], k < kb), in one poll
+  const int nstat = (kb + 1) * S * 4;
+  Ranges rg;
+  rg.src0 = a.stat + stat_idx(a, b, 0, 0);
+  rg.n0 = nstat;
+  rg.src1 = a.apart + apart_idx(a, b, 0, 0);
+  rg.n1 = greedy ? 0 : kb * S;
+  const bool all = poll(rg, tag, sh.fwords, sh.fhave, a.spin_limit);
+  if (!all) {
+    for (int e = 0; e < (kb + 1) * S; ++e)
+      if (!have4(sh.fhave, e)) {
         uint32_t w[4];
-        recompute_stat_words<kDtype, kVecOk>(a, b, e / S, e % S, kb, T, w, shu);
+        recompute_stat_words<kDtype, kVecOk>(a, b, e / S, e % S, kb, T, w, sh);
         __syncthreads();
         if (threadIdx.x == 0)
-          for (int i = 0; i < 4; ++i) sh.words[4 * e + i] = w[i];
+          for (int i = 0; i < 4; ++i) sh.fwords[4 * e + i] = w[i];
         __syncthreads();
       }
-    }
   }
 
   // per-row statistics; rows r = k (target, k <= kb) and r = kb + 1 + k
-  // (draft, k < kb); wave w takes rows r = w, w + 4, ...
+  // (draft, k < kb); wave w takes rows w, w + 8, ...
   int fault = 0;
-  for (int r = wave; r < 2 * kb + 1; r += kWavesPerBlock) {
+  for (int r = wave; r < 2 * kb + 1; r += kWaves) {
     const bool tgt = r <= kb;
     const int k = tgt ? r : r - kb - 1;
     const int off = tgt ? 0 : 2;
-    const uint32_t* words = sh.words + size_t(k) * S * 4;
+    const uint32_t* words = sh.fwords + size_t(k) * S * 4;
     if (greedy) {
       ArgMax cand{-INFINITY, INT_MAX, 0};
       if (lane < S) {
@@ -722,48 +782,46 @@ __device__ __forceinline__ void finalize(const Args& a, int b, int kb, float T, 
   const float inv_t = __fdiv_rn(1.f, T);
   const int64_t V = a.V;
 
-  // slice alphas: [k][s] for k < kb
-  if (kb > 0) {
-    const int n = kb * S;
-    if (!poll_tagged(a.apart + apart_idx(a, b, 0, 0), n, tag, sh.words, sh.have,
-                     a.spin_limit)) {
-      for (int e = 0; e < n; ++e)
-        if (!sh.have[e]) {
-          const int k = e / S;
-          float al;
-          recompute_overlap<kDtype, kVecOk>(a, b, k, e % S, kb, T, sh.R[k], sh.L[k],
-                                            sh.R[kb + 1 + k], sh.L[kb + 1 + k], al, sh.cm4, shu);
-          if (threadIdx.x == 0) sh.words[e] = __float_as_uint(al);
-          __syncthreads();
-        }
-    }
-    if (threadIdx.x == 0)
-      for (int k = 0; k < kb; ++k) {
-        double al = 0.0;
-        for (int s = 0; s < S; ++s) al += (double)__uint_as_float(sh.words[k * S + s]);
-        sh.alpha[k] = al;
+  // slice alphas that did not arrive, then alpha_k
+  const uint8_t* ahave = sh.fhave + nstat;
+  uint32_t* awords = sh.fwords + nstat;
+  if (!all) {
+    for (int e = 0; e < kb * S; ++e)
+      if (!ahave[e]) {
+        const int k = e / S;
+        float al;
+        recompute_overlap<kDtype, kVecOk>(a, b, k, e % S, kb, T, sh.R[k], sh.L[k],
+                                          sh.R[kb + 1 + k], sh.L[kb + 1 + k], al, sh);
+        if (threadIdx.x == 0) awords[e] = __float_as_uint(al);
+        __syncthreads();
       }
-    __syncthreads();
   }
-
-  // accept scan (thread 0, at most LVTV_MAX_K steps)
+  // accept inputs for every position in parallel: u_k and p(y_k)/q(y_k)
+  if (threadIdx.x < kb) {
+    const int k = threadIdx.x;
+    double al = 0.0;
+    for (int s = 0; s < S; ++s) al += (double)__uint_as_float(awords[k * S + s]);
+    sh.alpha[k] = al;
+    double u, u2;
+    verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
+    sh.uacc[k] = u;
+    const int yk = y[k];
+    const double p = prob64<kDtype>(row_ptr<kDtype>(a, b, true, k), yk, inv_t, unit, sh.R[k],
+                                    sh.L[k]);
+    const double q = prob64<kDtype>(row_ptr<kDtype>(a, b, false, k), yk, inv_t, unit,
+                                    sh.R[kb + 1 + k], sh.L[kb + 1 + k]);
+    // q == 0: accept iff p > 0, encoded as an infinite or zero ratio
+    sh.ratio[k] = (q == 0.0) ? (p > 0.0 ? INFINITY : 0.0) : p / q;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     for (int k = 0; k < Kmax; ++k) out_alpha[k] = k < kb ? float(sh.alpha[k]) : 0.f;
     int j = kb;
-    for (int k = 0; k < kb; ++k) {
-      double u, u2;
-      verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
-      const int yk = y[k];
-      const double p = prob64<kDtype>(row_ptr<kDtype>(a, b, true, k), yk, inv_t, unit, sh.R[k],
-                                      sh.L[k]);
-      const double q = prob64<kDtype>(row_ptr<kDtype>(a, b, false, k), yk, inv_t, unit,
-                                      sh.R[kb + 1 + k], sh.L[kb + 1 + k]);
-      const bool ok = (q == 0.0) ? (p > 0.0) : (u < p / q);
-      if (!ok) {
+    for (int k = 0; k < kb; ++k)
+      if (!(sh.uacc[k] < sh.ratio[k])) {
         j = k;
         break;
       }
-    }
     sh.j = j;
   }
   __syncthreads();
@@ -780,31 +838,35 @@ __device__ __forceinline__ void finalize(const Args& a, int b, int kb, float T, 
   const float Rd = residual ? sh.R[kb + 1 + j] : 0.f;
   const double Ld = residual ? sh.L[kb + 1 + j] : 1.0;
   const int NC = a.NC;
-  if (!poll_tagged(a.chunk + chunk_idx(a, b, j, 0), NC, tag, sh.words, sh.have, a.spin_limit)) {
-    for (int s = 0; s < S; ++s)
-      if (!have4(sh.have, s)) {
+  Ranges rc;
+  rc.src0 = a.chunk + chunk_idx(a, b, j, 0);
+  rc.n0 = NC;
+  rc.src1 = a.chunk;
+  rc.n1 = 0;
+  if (!poll(rc, tag, sh.fwords, sh.fhave, a.spin_limit)) {
+    for (int s = 0; s < S; ++s) {
+      bool miss = false;
+      for (int w = 0; w < kWaves; ++w) miss |= !sh.fhave[kWaves * s + w];
+      if (miss) {
         float al;
-        recompute_overlap<kDtype, kVecOk>(a, b, j, s, kb, T, Rt, Lt, Rd, Ld, al, sh.cm4, shu);
-        if (threadIdx.x < kWavesPerBlock)
-          sh.words[4 * s + threadIdx.x] = __float_as_uint(sh.cm4[threadIdx.x]);
+        recompute_overlap<kDtype, kVecOk>(a, b, j, s, kb, T, Rt, Lt, Rd, Ld, al, sh);
+        if (threadIdx.x < kWaves)
+          sh.fwords[kWaves * s + threadIdx.x] = __float_as_uint(sh.cm8[threadIdx.x]);
         __syncthreads();
       }
+    }
   }
-  for (int c = threadIdx.x; c < NC; c += kBlock) sh.cm[c] = __uint_as_float(sh.words[c]);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double z = 0.0;
-    for (int c = 0; c < NC; ++c) z += (double)sh.cm[c];
-    sh.before = z;
+  int has_mass = 0;
+  for (int c = threadIdx.x; c < NC; c += kThreads) {
+    sh.cm[c] = __uint_as_float(sh.fwords[c]);
+    has_mass |= sh.cm[c] > 0.f;
   }
-  __syncthreads();
+  const bool any_mass = __syncthreads_or(has_mass);
   int v;
-  if (residual && !(sh.before > 0.0)) {
-    __syncthreads();
+  if (residual && !any_mass) {
     v = draw_full_row<kDtype>(NC, u_draw, trow, V, inv_t, unit, Rt, Lt, sh);
   } else {
-    __syncthreads();
-    v = draw_from_masses<kDtype>(sh.cm, NC, u_draw, trow, drow, V, inv_t, unit, Rt, Lt, Rd, Ld,
+    v = draw_from_masses<kDtype>(NC, u_draw, trow, drow, V, inv_t, unit, Rt, Lt, Rd, Ld,
                                  residual, sh);
   }
   if (v < 0 || v >= a.V) v = a.V - 1;  // unreachable: the chosen chunk has positive mass
@@ -818,20 +880,21 @@ __device__ __forceinline__ void finalize(const Args& a, int b, int kb, float T, 
 // ------------------------------------------------------------------ the kernel
 
 template <int kDtype, bool kVecOk, bool kPair>
-__device__ __forceinline__ void stochastic_item(const Args& a, int b, int k, int s, int kb, float T,
-                                                uint32_t& epoch, Shared& shu) {
-  ItemShared& sh = shu.it;
+__device__ __forceinline__ void stochastic_item(const Args& a, int b, int k, int s, int kb,
+                                                float T, uint32_t& epoch, Shared& sh) {
   const int S = a.S;
   const int64_t V = a.V;
   const bool unit = (T == 1.f);
   const float inv_t = __fdiv_rn(1.f, T);
-  float xt[kSteps][kVec], xd[kSteps][kVec];
-  load_slice<kDtype, kVecOk>(row_ptr<kDtype>(a, b, true, k), V, s, xt);
-  if constexpr (kPair) load_slice<kDtype, kVecOk>(row_ptr<kDtype>(a, b, false, k), V, s, xd);
+  Raw<kDtype> rt, rd;
+  load_raw<kDtype, kVecOk>(row_ptr<kDtype>(a, b, true, k), V, s, rt);
+  if constexpr (kPair) load_raw<kDtype, kVecOk>(row_ptr<kDtype>(a, b, false, k), V, s, rd);
   epoch = read_epoch(a.ctl);
   const uint32_t tag = tag_from_epoch(epoch);
   SliceStats st, sd;
-  slice_stats<kPair>(xt, xd, inv_t, unit, sh.red, st, sd);
+  slice_stats<kDtype, kPair>(rt, rd, inv_t, unit, sh.red, st, sd);
+  launder(rt);
+  if constexpr (kPair) launder(rd);
   if (threadIdx.x == 0) {
     uint64_t* w = a.stat + stat_idx(a, b, k, s);
     tag_store(w + 0, tag, __float_as_uint(st.R));
@@ -840,8 +903,12 @@ __device__ __forceinline__ void stochastic_item(const Args& a, int b, int k, int
     tag_store(w + 3, tag, __float_as_uint(kPair ? sd.l : 1.f));
   }
   // collect the statistics of every slice of these rows
-  const bool fresh = poll_tagged(a.stat + stat_idx(a, b, k, 0), 4 * S, tag, sh.words, sh.have,
-                                 a.spin_limit);
+  Ranges rg;
+  rg.src0 = a.stat + stat_idx(a, b, k, 0);
+  rg.n0 = 4 * S;
+  rg.src1 = a.stat;
+  rg.n1 = 0;
+  const bool fresh = poll(rg, tag, sh.words, sh.have, a.spin_limit);
   float alpha_slice = 0.f, cmass;
   if (fresh) {
     if (threadIdx.x < kWave) {
@@ -856,7 +923,8 @@ __device__ __forceinline__ void stochastic_item(const Args& a, int b, int k, int
     }
     __syncthreads();
     if constexpr (kPair) {
-      pair_overlap(xt, xd, sh.at, sh.ad, sh.red4, alpha_slice, cmass);
+      pair_overlap<kDtype>(rt, rd, inv_t, unit, neg_ref(st.R), neg_ref(sd.R), sh.at, sh.ad,
+                           sh.red, alpha_slice, cmass);
     } else {
       cmass = st.wsum * sh.at;
     }
@@ -867,7 +935,7 @@ __device__ __forceinline__ void stochastic_item(const Args& a, int b, int k, int
     for (int s2 = 0; s2 < S; ++s2)
       if (!have4(sh.have, s2)) {
         uint32_t w[4];
-        recompute_stat_words<kDtype, kVecOk>(a, b, k, s2, kb, T, w, shu);
+        recompute_stat_words<kDtype, kVecOk>(a, b, k, s2, kb, T, w, sh);
         __syncthreads();
         if (threadIdx.x == 0)
           for (int i = 0; i < 4; ++i) sh.words[4 * s2 + i] = w[i];
@@ -887,21 +955,20 @@ __device__ __forceinline__ void stochastic_item(const Args& a, int b, int k, int
     }
     __syncthreads();
     recompute_overlap<kDtype, kVecOk>(a, b, k, s, kb, T, sh.Rt, sh.Lt, sh.Rd, sh.Ld, alpha_slice,
-                                      sh.cm4, shu);
-    cmass = sh.cm4[threadIdx.x / kWave];
+                                      sh);
+    cmass = sh.cm8[threadIdx.x / kWave];
     __syncthreads();
   }
   if ((threadIdx.x & (kWave - 1)) == 0)
-    tag_store(a.chunk + chunk_idx(a, b, k, kWavesPerBlock * s + threadIdx.x / kWave), tag,
+    tag_store(a.chunk + chunk_idx(a, b, k, kWaves * s + threadIdx.x / kWave), tag,
               __float_as_uint(cmass));
   if (kPair && threadIdx.x == 0)
     tag_store(a.apart + apart_idx(a, b, k, s), tag, __float_as_uint(alpha_slice));
 }
 
 template <int kDtype, bool kVecOk>
-__global__ __launch_bounds__(kBlock) void verify_fused_kernel(Args a) {
-  __shared__ Shared shu;
-  ItemShared& sh = shu.it;
+__device__ __forceinline__ void verify_body(const Args& a) {
+  __shared__ Shared sh;
   const int S = a.S;
   const int per_req = (a.Kmax + 1) * S;
   const int item = blockIdx.x;
@@ -930,7 +997,7 @@ __global__ __launch_bounds__(kBlock) void verify_fused_kernel(Args a) {
   uint32_t epoch;
   if (T == 0.f) {
     uint32_t w[4];
-    recompute_stat_words<kDtype, kVecOk>(a, b, k, s, kb, T, w, shu);
+    recompute_stat_words<kDtype, kVecOk>(a, b, k, s, kb, T, w, sh);
     epoch = read_epoch(a.ctl);
     if (threadIdx.x == 0) {
       const uint32_t tag = tag_from_epoch(epoch);
@@ -941,9 +1008,9 @@ __global__ __launch_bounds__(kBlock) void verify_fused_kernel(Args a) {
       tag_store(dst + 3, tag, w[3]);
     }
   } else if (k < kb) {
-    stochastic_item<kDtype, kVecOk, true>(a, b, k, s, kb, T, epoch, shu);
+    stochastic_item<kDtype, kVecOk, true>(a, b, k, s, kb, T, epoch, sh);
   } else {
-    stochastic_item<kDtype, kVecOk, false>(a, b, k, s, kb, T, epoch, shu);
+    stochastic_item<kDtype, kVecOk, false>(a, b, k, s, kb, T, epoch, sh);
   }
 
   // count this workgroup in; the request's last one finalises it
@@ -955,12 +1022,25 @@ __global__ __launch_bounds__(kBlock) void verify_fused_kernel(Args a) {
   }
   __syncthreads();
   if (!sh.last) return;
-  finalize<kDtype, kVecOk>(a, b, kb, T, epoch, shu);
+  finalize<kDtype, kVecOk>(a, b, kb, T, epoch, sh);
   __syncthreads();
   if (threadIdx.x == 0) {
     __hip_atomic_store(a.req + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     complete_unit(a, epoch);
   }
+}
+
+// bf16 rows fit the item path in 128 registers: four waves per SIMD, two
+// workgroups per compute unit.
+template <bool kVecOk>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+verify_fused_bf16(Args a) {
+  verify_body<1, kVecOk>(a);
+}
+
+template <bool kVecOk>
+__global__ __launch_bounds__(kThreads) void verify_fused_f32(Args a) {
+  verify_body<0, kVecOk>(a);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -973,7 +1053,7 @@ struct Layout {
 Layout make_layout(int B, int Kmax, int V) {
   Layout L;
   L.S = (V + kSlice - 1) / kSlice;
-  L.NC = L.S * kWavesPerBlock;
+  L.NC = L.S * kWaves;
   size_t off = kReservedBytes;
   L.off_stat = off;
   off = align256(off + sizeof(uint64_t) * size_t(B) * (Kmax + 1) * L.S * 4);
@@ -988,8 +1068,12 @@ Layout make_layout(int B, int Kmax, int V) {
 template <int kDtype, bool kVecOk>
 hipError_t launch(const Args& a, hipStream_t stream) {
   const size_t grid = size_t(a.B) * (a.Kmax + 1) * a.S;
-  hipLaunchKernelGGL((verify_fused_kernel<kDtype, kVecOk>), dim3(unsigned(grid)), dim3(kBlock), 0,
-                     stream, a);
+  if constexpr (kDtype == 1)
+    hipLaunchKernelGGL((verify_fused_bf16<kVecOk>), dim3(unsigned(grid)), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((verify_fused_f32<kVecOk>), dim3(unsigned(grid)), dim3(kThreads), 0,
+                       stream, a);
   return hipGetLastError();
 }
 

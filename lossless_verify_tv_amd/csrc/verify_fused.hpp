@@ -8,10 +8,10 @@
 namespace lvtv {
 namespace vf {
 
-// Rows are cut into slices of 8192 tokens; the single-read kernel handles up
+// Rows are cut into slices of 16384 tokens; the single-read kernel handles up
 // to this many slices per row (V <= 524288). Larger V take the two-read
 // pipeline.
-constexpr int kMaxSlices = 64;
+constexpr int kMaxSlices = 32;
 
 struct VerifyCall {
   const void* target;
