@@ -54,11 +54,11 @@ def loss_bytes(n, w, vocab):
     return 8 * n * w * vocab
 
 
-def cpu_baseline(verify_cases, loss_case, n_verify_req=4, n_branches=6):
+def cpu_baseline(verify_cases, loss_case, n_verify_req=64, n_branches=96):
     """Time the fp64 oracle, as it stands, on a bounded sample of the same
-    workload: the first requests of each temperature's verify inputs and the
-    first branches of the loss inputs. Single process (numpy elementwise
-    work is single-threaded)."""
+    workload (about 15 s of CPU work): every request of each temperature's
+    verify inputs and the first branches of the loss inputs. Single process,
+    one thread (numpy elementwise work is single-threaded)."""
     sys.path.insert(0, ROOT)
     from oracle import bf16 as obf16
     from oracle import loss as ol
