@@ -126,11 +126,12 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype
  *   status         int32 [B] out: LVTV_STATUS_* bits, 0 if fine. A faulted
  *                  request gets accepted_len = -1, all tokens -1, alpha 0.
  *   workspace      device scratch of >= spec_verify_workspace_bytes(...)
- *                  bytes, 256-byte aligned, zero-filled before its first
- *                  use (lvtv_workspace_reset); each call leaves it ready for
- *                  the next. Calls sharing a workspace must be ordered on
- *                  one stream.
- *   stream         hipStream_t.
+ *                  bytes, 256-byte aligned. Its contents on entry do not
+ *                  matter (every value a call reads from it, the call wrote
+ *                  first). Calls sharing a workspace must be ordered on one
+ *                  stream.
+ *   stream         hipStream_t. Two kernels are enqueued: one workgroup per
+ *                  used (request, position) row pair, then one per request.
  */
 int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
                 const int32_t* draft_tokens, const int32_t* k_per_req,

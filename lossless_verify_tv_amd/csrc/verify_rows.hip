@@ -1,0 +1,895 @@
+// spec_verify for gfx950: two launches per call on the caller's stream.
+//
+//   1. verify_rows      one workgroup per (request b, position k <= K_b):
+//                       the pair of target row k and draft row k (k < K_b),
+//                       or the target row alone (the bonus row k = K_b).
+//                       Sampling (T_b > 0): pass 1 streams both rows once
+//                       and keeps an online maximum and sum of exponentials
+//                       per thread; the last tiles of the rows stay in
+//                       registers. The block combines these into the row
+//                       statistics. Pass 2 walks the rows back to front (the
+//                       held tiles first, the rest from the cache hierarchy,
+//                       where pass 1 just left them) and forms p and q, the
+//                       overlap alpha_k = sum min(p, q) and, per 512-token
+//                       chunk, the residual mass sum max(0, p - q) (for the
+//                       bonus row the mass of p). Greedy (T_b = 0): one pass
+//                       taking the argmax of both rows.
+//   2. verify_finalize  one workgroup per request: status checks, alpha, the
+//                       accept scan with Philox uniforms and the inverse-CDF
+//                       draw (chunk from the chunk masses, token from an fp64
+//                       evaluation inside the chunk), emitted tokens.
+//
+// Cites (page title, section): "Reading Qwen Bebop and DeepSeek DSpark",
+// "Formulas" (acceptance min(1, p/q); overlap sum min(p, q) = 1 - d_TV);
+// "Speculative Decoding and MTP" survey, section 2 (ordered acceptance, the
+// bonus token from p_{K+1}), section 3 (residual max(0, p - q)/Z), section 4
+// (one temperature for p and q; greedy compares with the target argmax),
+// section 21 (acceptance and residual sampling on the GPU, no per-cycle
+// host sync).
+//
+// Arithmetic. Scaled logits s = fl32(x * fl32(1/T)) (x itself at T = 1).
+// Exponentials are base 2: a row's statistics are R = fl32(M * log2 e), M the
+// row maximum of s, and L = sum_v 2^(s_v log2 e - R), both fp32, so that
+// p(v) = 2^(s_v log2 e - R) / L. The finalize step evaluates that formula in
+// fp64 for the accept ratios and inside the chosen chunk.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/lvtv.h"
+#include "device_common.hpp"
+#include "fused_common.hpp"
+#include "philox.hpp"
+#include "wave_dpp.hpp"
+
+namespace lvtv {
+namespace vr {
+namespace {
+
+constexpr int kThreads = 512;                 // threads per workgroup
+constexpr int kWaves = kThreads / kWave;      // 8
+constexpr int kTile = kThreads * kVec;        // 4096 tokens: 8 per thread
+constexpr int kChunk = kWave * kVec;          // 512 tokens: one wave's part of a tile
+constexpr int kBatch = 4;                     // tiles whose loads are in flight together
+constexpr float kL2E = 1.44269504088896340736f;
+
+// Tiles kept in registers between the passes (the last ones of the row).
+template <int kDtype>
+constexpr int hold_tiles() {
+  return kDtype == 1 ? 3 : 2;
+}
+
+// Per (request, position) results of the row kernel.
+struct RowOut {
+  float Rt, Lt;   // target row: R and L (greedy: max value, unused)
+  float Rd, Ld;   // draft row
+  float alpha;    // sum min(p, q) (greedy: unused)
+  int32_t arg_t;  // greedy argmax of the target row
+  int32_t arg_d;  // greedy argmax of the draft row
+  int32_t nan;    // greedy: bit 0 target row, bit 1 draft row held a NaN
+};
+static_assert(sizeof(RowOut) == 32, "row record is 32 bytes");
+
+struct Args {
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* kreq;
+  const float* temp;
+  const uint64_t* seed;
+  int B, Kmax, V;
+  int n_tiles;  // tiles per row
+  int NC;       // chunks per row (n_tiles * kWaves)
+  int32_t* acc_len;
+  int32_t* out_tokens;
+  float* alpha;
+  int32_t* status;
+  RowOut* rows;  // [B][Kmax+1]
+  float* chunk;  // [B][Kmax+1][NC]
+};
+
+__device__ __forceinline__ bool temperature_ok(float t) { return (t >= 0.f) && !isinf(t); }
+
+template <int kDtype>
+__device__ __forceinline__ const void* row_ptr(const Args& a, int b, bool target, int k) {
+  constexpr int kSize = kDtype == 1 ? 2 : 4;
+  const int64_t row = target ? (int64_t(b) * (a.Kmax + 1) + k) : (int64_t(b) * a.Kmax + k);
+  return static_cast<const char*>(target ? a.target : a.draft) + row * int64_t(a.V) * kSize;
+}
+
+// ------------------------------------------------------------------ groups of 8 tokens
+
+// One thread's 8 tokens of one row in a tile, as raw bits: bf16 packed two
+// per register, fp32 one per register.
+template <int kDtype>
+struct Grp {
+  u32x4 q[kDtype == 1 ? 1 : 2];
+};
+
+template <int kDtype>
+__device__ __forceinline__ float gelem(const Grp<kDtype>& g, int j) {
+  if constexpr (kDtype == 1) {
+    const uint32_t w = g.q[0][j >> 1];
+    return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+  } else {
+    return __uint_as_float(g.q[j >> 2][j & 3]);
+  }
+}
+
+template <int kDtype>
+__device__ __forceinline__ void fill_grp(Grp<kDtype>& g) {
+  const uint32_t fill = kDtype == 1 ? 0xff80ff80u : 0xff800000u;
+#pragma unroll
+  for (int q = 0; q < (kDtype == 1 ? 1 : 2); ++q) g.q[q] = u32x4{fill, fill, fill, fill};
+}
+
+// First token of this thread's group in tile t.
+__device__ __forceinline__ int tile_elem(int t) { return t * kTile + threadIdx.x * kVec; }
+
+// Load of the group starting at token e of a row; tokens at or beyond V read
+// as -inf. With kVecOk (16-byte aligned rows, V % 8 == 0) a group is wholly
+// inside the row or wholly past its end: past-the-end groups are loaded from
+// the row's first group (so the load needs no branch) and then overwritten.
+// kNt: streaming (nontemporal) load, for data that is not read again.
+template <int kDtype, bool kVecOk, bool kNt>
+__device__ __forceinline__ void load_grp(const void* row, int V, int e, Grp<kDtype>& g) {
+  if constexpr (kVecOk) {
+    const uint32_t off = uint32_t(e < V ? e : 0) * (kDtype == 1 ? 2u : 4u);
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + off);
+    if constexpr (kNt) {
+      g.q[0] = __builtin_nontemporal_load(p);
+      if constexpr (kDtype == 0) g.q[1] = __builtin_nontemporal_load(p + 1);
+    } else {
+      g.q[0] = p[0];
+      if constexpr (kDtype == 0) g.q[1] = p[1];
+    }
+  } else if constexpr (kDtype == 1) {
+    const uint16_t* p = static_cast<const uint16_t*>(row);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t lo = (e + 2 * h < V) ? p[e + 2 * h] : 0xff80u;
+      const uint32_t hi = (e + 2 * h + 1 < V) ? p[e + 2 * h + 1] : 0xff80u;
+      g.q[0][h] = lo | (hi << 16);
+    }
+  } else {
+    const uint32_t* p = static_cast<const uint32_t*>(row);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) g.q[h >> 2][h & 3] = (e + h < V) ? p[e + h] : 0xff800000u;
+  }
+}
+
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void mask_grp(Grp<kDtype>& g, int e, int V) {
+  if constexpr (kVecOk) {
+    if (e >= V) fill_grp(g);
+  }
+}
+
+// Keeps the compiler from carrying values derived from a group (unpacked or
+// exponentiated tokens) from one pass to the next instead of recomputing
+// them from the raw bits: that would need several times the registers.
+template <int kDtype>
+__device__ __forceinline__ void launder(Grp<kDtype>& g) {
+#pragma unroll
+  for (int q = 0; q < (kDtype == 1 ? 1 : 2); ++q) asm volatile("" : "+v"(g.q[q]));
+}
+
+// ------------------------------------------------------------------ block reductions
+
+struct Shared {
+  float f[kWaves][4];
+  int i[kWaves][4];
+  double d[kWaves];
+};
+
+// Block-wide combination of per-thread online statistics of two rows. A
+// thread holds its maximum raw logit m and l = sum 2^(x c - fl32(m c)) over
+// its tokens, c = fl32(log2(e) / T) > 0; the block gets the row maximum M,
+// R = fl32(M c) and L = sum_threads l 2^(fl32(m c) - R). A thread that saw
+// only -inf (m = -inf) contributes l * 0.
+__device__ __forceinline__ void block_online(float c, float& m0, float& l0, float& m1, float& l1,
+                                             Shared& sh) {
+  const float M0w = wmax(m0), M1w = wmax(m1);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sh.f[threadIdx.x / kWave][0] = M0w;
+    sh.f[threadIdx.x / kWave][1] = M1w;
+  }
+  __syncthreads();
+  float M0 = sh.f[0][0], M1 = sh.f[0][1];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    M0 = fmaxf(M0, sh.f[w][0]);
+    M1 = fmaxf(M1, sh.f[w][1]);
+  }
+  const float w0 = (m0 == -INFINITY) ? l0 * 0.f : l0 * __builtin_amdgcn_exp2f(m0 * c - M0 * c);
+  const float w1 = (m1 == -INFINITY) ? l1 * 0.f : l1 * __builtin_amdgcn_exp2f(m1 * c - M1 * c);
+  const float S0w = wsum(w0), S1w = wsum(w1);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sh.f[threadIdx.x / kWave][2] = S0w;
+    sh.f[threadIdx.x / kWave][3] = S1w;
+  }
+  __syncthreads();
+  float S0 = sh.f[0][2], S1 = sh.f[0][3];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    S0 += sh.f[w][2];
+    S1 += sh.f[w][3];
+  }
+  m0 = M0;
+  l0 = S0;
+  m1 = M1;
+  l1 = S1;
+}
+
+__device__ __forceinline__ float block_sum1(float v, Shared& sh) {
+  v = wsum(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh.f[threadIdx.x / kWave][0] = v;
+  __syncthreads();
+  float r = sh.f[0][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r += sh.f[w][0];
+  return r;
+}
+
+// ------------------------------------------------------------------ sampling rows
+//
+// Exponents are formed as fma(x, c, -r) with x the raw logit and
+// c = fl32(log2(e) * fl32(1/T)) (log2(e) itself at T = 1): the temperature
+// and the base change in one rounding. Within the kernel this differs from
+// the canonical 2^(fl32(x / T) log2 e) by about one ulp of the exponent; the
+// accept ratios and the in-chunk draw use the canonical form in fp64.
+
+// Online statistics of a batch of groups of one row: the batch maximum of
+// the raw logits first, one rescale of the running sum, then the
+// exponentials against the new maximum.
+template <int kDtype, int kN>
+__device__ __forceinline__ void online_batch(const Grp<kDtype> (&g)[kN], float c, float& m,
+                                             float& l) {
+  float bm = m;
+#pragma unroll
+  for (int n = 0; n < kN; ++n)
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) bm = fmaxf(bm, gelem(g[n], j));
+  if (bm > m) {
+    l = (m == -INFINITY) ? 0.f : l * __builtin_amdgcn_exp2f(m * c - bm * c);
+    m = bm;
+  }
+  // a -inf maximum: every token so far is -inf and contributes 0
+  const float nr = (m == -INFINITY) ? 0.f : -(m * c);
+#pragma unroll
+  for (int n = 0; n < kN; ++n)
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) l += __builtin_amdgcn_exp2f(__builtin_fmaf(gelem(g[n], j), c, nr));
+}
+
+// Pass 2 over one tile: p = 2^(x c - Rt'), q = 2^(x c - Rd') with the row
+// sums folded into the references (R' = R + log2 L), alpha and this wave's
+// chunk mass (lane 0 writes it).
+template <int kDtype, bool kPair>
+__device__ __forceinline__ void overlap_tile(const Grp<kDtype>& gt, const Grp<kDtype>& gd,
+                                             float c, float nrt, float nrd, float& sa,
+                                             float* chunk_row, int t) {
+  float r = 0.f;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(gelem(gt, j), c, nrt));
+    if constexpr (kPair) {
+      const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(gelem(gd, j), c, nrd));
+      const float mn = fminf(p, q);
+      sa += mn;
+      r += p - mn;
+    } else {
+      r += p;
+    }
+  }
+  const float cm = wsum(r);
+  if ((threadIdx.x & (kWave - 1)) == 0) chunk_row[t * kWaves + threadIdx.x / kWave] = cm;
+}
+
+// The group of the last, partial tile: loaded where it lies inside the row,
+// -inf elsewhere.
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void load_tail(const void* row, int V, int t, Grp<kDtype>& g) {
+  const int e = tile_elem(t);
+  if constexpr (kVecOk) {
+    if (e < V)
+      load_grp<kDtype, kVecOk, true>(row, V, e, g);
+    else
+      fill_grp(g);
+  } else {
+    load_grp<kDtype, kVecOk, true>(row, V, e, g);
+  }
+}
+
+template <int kDtype, bool kVecOk, bool kPair>
+__device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float T, Shared& sh) {
+  constexpr int kHold = hold_tiles<kDtype>();
+  const int V = a.V;
+  const int nfull = V / kTile;                  // tiles wholly inside the row
+  const bool tail = nfull * kTile < V;          // a last, partial tile
+  const int held = nfull < kHold ? nfull : kHold;
+  const int nstream = nfull - held;             // tiles [0, nstream) are streamed twice
+  const float c = (T == 1.f) ? kL2E : __fmul_rn(kL2E, __fdiv_rn(1.f, T));
+  const void* trow = row_ptr<kDtype>(a, b, true, k);
+  const void* drow = kPair ? row_ptr<kDtype>(a, b, false, k) : nullptr;
+
+  // ---- pass 1: streamed full tiles, held full tiles, the partial tile
+  float mt = -INFINITY, lt = 0.f, md = -INFINITY, ld = 0.f;
+  int t = 0;
+  for (; t + kBatch <= nstream; t += kBatch) {
+    Grp<kDtype> gt[kBatch], gd[kBatch];
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n) {
+      load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t + n), gt[n]);
+      if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t + n), gd[n]);
+    }
+    online_batch<kDtype, kBatch>(gt, c, mt, lt);
+    if constexpr (kPair) online_batch<kDtype, kBatch>(gd, c, md, ld);
+  }
+  for (; t < nstream; ++t) {
+    Grp<kDtype> gt[1], gd[1];
+    load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t), gt[0]);
+    if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t), gd[0]);
+    online_batch<kDtype, 1>(gt, c, mt, lt);
+    if constexpr (kPair) online_batch<kDtype, 1>(gd, c, md, ld);
+  }
+  Grp<kDtype> ht[kHold], hd[kHold], tt[1], td[1];
+  if (held == kHold) {
+#pragma unroll
+    for (int h = 0; h < kHold; ++h) {
+      load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(nstream + h), ht[h]);
+      if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(nstream + h), hd[h]);
+    }
+    online_batch<kDtype, kHold>(ht, c, mt, lt);
+    if constexpr (kPair) online_batch<kDtype, kHold>(hd, c, md, ld);
+  } else {
+#pragma unroll
+    for (int h = 0; h < kHold; ++h)
+      if (h < held) {
+        Grp<kDtype> g1[1], g2[1];
+        load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(nstream + h), g1[0]);
+        if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(nstream + h), g2[0]);
+        online_batch<kDtype, 1>(g1, c, mt, lt);
+        if constexpr (kPair) online_batch<kDtype, 1>(g2, c, md, ld);
+        ht[h] = g1[0];
+        hd[h] = g2[0];
+      }
+  }
+  if (tail) {
+    load_tail<kDtype, kVecOk>(trow, V, nfull, tt[0]);
+    if constexpr (kPair) load_tail<kDtype, kVecOk>(drow, V, nfull, td[0]);
+    online_batch<kDtype, 1>(tt, c, mt, lt);
+    if constexpr (kPair) online_batch<kDtype, 1>(td, c, md, ld);
+  }
+#pragma unroll
+  for (int h = 0; h < kHold; ++h) {
+    launder(ht[h]);
+    if constexpr (kPair) launder(hd[h]);
+  }
+  launder(tt[0]);
+  if constexpr (kPair) launder(td[0]);
+  block_online(c, mt, lt, md, ld, sh);
+  const float Rt = (mt == -INFINITY) ? -INFINITY : mt * c;
+  const float Rd = (md == -INFINITY) ? -INFINITY : md * c;
+  // references with the row sums folded in: p = 2^(x c - (R + log2 L))
+  const float nrt = float(-((double)Rt + log2((double)lt)));
+  const float nrd = kPair ? float(-((double)Rd + log2((double)ld))) : 0.f;
+
+  // ---- pass 2: the partial tile, the held tiles, the rest back to front
+  float* chunk_row = a.chunk + (size_t(b) * (a.Kmax + 1) + k) * a.NC;
+  float sa = 0.f;
+  if (tail) overlap_tile<kDtype, kPair>(tt[0], td[0], c, nrt, nrd, sa, chunk_row, nfull);
+#pragma unroll
+  for (int h = kHold - 1; h >= 0; --h)
+    if (h < held) overlap_tile<kDtype, kPair>(ht[h], hd[h], c, nrt, nrd, sa, chunk_row, nstream + h);
+  t = nstream;
+  for (; t >= kBatch; t -= kBatch) {
+    Grp<kDtype> gt[kBatch], gd[kBatch];
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n) {
+      load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t - 1 - n), gt[n]);
+      if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t - 1 - n), gd[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n)
+      overlap_tile<kDtype, kPair>(gt[n], gd[n], c, nrt, nrd, sa, chunk_row, t - 1 - n);
+  }
+  for (; t > 0; --t) {
+    Grp<kDtype> gt, gd;
+    load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t - 1), gt);
+    if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t - 1), gd);
+    overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, t - 1);
+  }
+  const float alpha = kPair ? block_sum1(sa, sh) : 0.f;
+  if (threadIdx.x == 0) {
+    RowOut o;
+    o.Rt = Rt;
+    o.Lt = lt;
+    o.Rd = kPair ? Rd : 0.f;
+    o.Ld = kPair ? ld : 1.f;
+    o.alpha = alpha;
+    o.arg_t = -1;
+    o.arg_d = -1;
+    o.nan = 0;
+    a.rows[size_t(b) * (a.Kmax + 1) + k] = o;
+  }
+}
+
+// ------------------------------------------------------------------ greedy rows
+
+// Largest value, lowest index holding it (the group's tokens are visited in
+// increasing index, so a later equal value never replaces an earlier one),
+// NaN flagged and left out.
+template <int kDtype>
+__device__ __forceinline__ void argmax_grp(const Grp<kDtype>& g, int e, int V, float& bv, int& bi,
+                                           int& nan) {
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const float v = gelem(g, j);
+    nan |= (v != v);
+    if (e + j < V && v > bv) {
+      bv = v;
+      bi = e + j;
+    }
+  }
+}
+
+__device__ __forceinline__ ArgMax block_argmax2(ArgMax x, Shared& sh, int slot) {
+  x = wargmax(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sh.f[threadIdx.x / kWave][slot] = x.v;
+    sh.i[threadIdx.x / kWave][slot] = x.i;
+    sh.i[threadIdx.x / kWave][slot + 2] = x.nan;
+  }
+  __syncthreads();
+  ArgMax r{sh.f[0][slot], sh.i[0][slot], sh.i[0][slot + 2]};
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w)
+    r = argmax_combine(r, ArgMax{sh.f[w][slot], sh.i[w][slot], sh.i[w][slot + 2]});
+  return r;
+}
+
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void greedy_row(const Args& a, int b, int k, bool pair, Shared& sh) {
+  const int V = a.V;
+  const void* trow = row_ptr<kDtype>(a, b, true, k);
+  const void* drow = pair ? row_ptr<kDtype>(a, b, false, k) : nullptr;
+  // a first maximum of -inf is still a valid argmax (lowest index of the
+  // row); INT_MAX marks "none yet"
+  float vt = -INFINITY, vd = -INFINITY;
+  int it = INT_MAX, id = INT_MAX, nt = 0, nd = 0;
+  for (int t0 = 0; t0 < a.n_tiles; t0 += kBatch) {
+    Grp<kDtype> gt[kBatch], gd[kBatch];
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n) {
+      const int t = t0 + n < a.n_tiles ? t0 + n : t0;
+      load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t), gt[n]);
+      if (pair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t), gd[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n) {
+      const int e = tile_elem(t0 + n);
+      if (t0 + n < a.n_tiles) {
+        mask_grp<kDtype, kVecOk>(gt[n], e, V);
+        argmax_grp(gt[n], e, V, vt, it, nt);
+        if (pair) {
+          mask_grp<kDtype, kVecOk>(gd[n], e, V);
+          argmax_grp(gd[n], e, V, vd, id, nd);
+        }
+      }
+    }
+  }
+  // a thread whose tokens are all -inf reports its first in-range index
+  if (it == INT_MAX && tile_elem(0) < V) it = tile_elem(0);
+  if (id == INT_MAX && tile_elem(0) < V) id = tile_elem(0);
+  const ArgMax bt = block_argmax2(ArgMax{vt, it, nt}, sh, 0);
+  const ArgMax bd = block_argmax2(ArgMax{vd, id, nd}, sh, 1);
+  if (threadIdx.x == 0) {
+    RowOut o;
+    o.Rt = bt.v;
+    o.Lt = 0.f;
+    o.Rd = pair ? bd.v : 0.f;
+    o.Ld = 0.f;
+    o.alpha = 0.f;
+    o.arg_t = bt.i;
+    o.arg_d = pair ? bd.i : -1;
+    o.nan = (bt.nan ? 1 : 0) | (pair && bd.nan ? 2 : 0);
+    a.rows[size_t(b) * (a.Kmax + 1) + k] = o;
+  }
+}
+
+// ------------------------------------------------------------------ row kernel
+
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void rows_body(const Args& a) {
+  __shared__ Shared sh;
+  const int b = blockIdx.x / (a.Kmax + 1);
+  const int k = blockIdx.x - b * (a.Kmax + 1);
+  const int kb = a.kreq[b];
+  const float T = a.temp[b];
+  if (!(kb >= 0 && kb <= a.Kmax && temperature_ok(T)) || k > kb) return;
+  if (T == 0.f) {
+    greedy_row<kDtype, kVecOk>(a, b, k, k < kb, sh);
+  } else if (k < kb) {
+    sampling_row<kDtype, kVecOk, true>(a, b, k, T, sh);
+  } else {
+    sampling_row<kDtype, kVecOk, false>(a, b, k, T, sh);
+  }
+}
+
+template <bool kVecOk>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+verify_rows_bf16(Args a) {
+  rows_body<1, kVecOk>(a);
+}
+
+template <bool kVecOk>
+__global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
+  rows_body<0, kVecOk>(a);
+}
+
+// ------------------------------------------------------------------ finalize
+
+// Block-wide exclusive scan in fp64 (fixed order); `total` gets the sum.
+__device__ __forceinline__ double block_exscan(double v, Shared& sh, double& total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) sh.d[wave] = inc;
+  __syncthreads();
+  double pre = 0.0;
+  total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) pre += sh.d[w];
+    total += sh.d[w];
+  }
+  return pre + inc - v;
+}
+
+__device__ __forceinline__ int block_min(int v, Shared& sh) {
+  v = wmin(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh.i[threadIdx.x / kWave][0] = v;
+  __syncthreads();
+  int r = sh.i[0][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = min(r, sh.i[w][0]);
+  return r;
+}
+
+// fp64 probability of token v under a row's (R, L), base-2 convention.
+template <int kDtype>
+__device__ __forceinline__ double prob64(const void* row, int v, float inv_t, bool unit, float R,
+                                         float L) {
+  const float s = scale_logit(load1<kDtype>(row, v), inv_t, unit);
+  return exp2((double)s * (double)kL2E - (double)R) / (double)L;
+}
+
+// Inverse-CDF choice of a chunk from the masses m[0..NC) at u * total: the
+// first chunk of positive mass whose running sum passes the target (if
+// rounding leaves none, the last chunk of positive mass). Returns the chunk
+// and, in `rem`, the target minus the mass before it.
+__device__ __forceinline__ int pick_chunk(const float* m, int NC, double u, Shared& sh,
+                                          double& rem) {
+  double total = 0.0;
+  for (int c0 = 0; c0 < NC; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    double part;
+    (void)block_exscan(c < NC ? (double)m[c] : 0.0, sh, part);
+    total += part;
+  }
+  const double target = u * total;
+  double base = 0.0;
+  for (int c0 = 0; c0 < NC; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    const double mc = c < NC ? (double)m[c] : 0.0;
+    double part;
+    const double exc = base + block_exscan(mc, sh, part);
+    const int hit = block_min((mc > 0.0 && exc + mc > target) ? c : INT_MAX, sh);
+    if (hit != INT_MAX) {
+      if (c == hit) sh.d[0] = target - exc;
+      __syncthreads();
+      rem = sh.d[0];
+      __syncthreads();
+      return hit;
+    }
+    base += part;
+  }
+  int last = -1;
+  for (int c0 = 0; c0 < NC; c0 += kThreads) {
+    const int c = c0 + threadIdx.x;
+    const int mine = (c < NC && m[c] > 0.f) ? c : -1;
+    last = max(last, -block_min(mine >= 0 ? -mine : INT_MAX, sh));
+  }
+  rem = INFINITY;
+  return last >= 0 ? last : 0;
+}
+
+// Token of chunk c at remaining mass `rem`: fp64 weights of the chunk's 512
+// tokens (one per thread), rescaled so they sum to the chunk's mass `cmass`
+// (the unit the chunk was chosen in); the first token whose running weight
+// passes `rem`, else the last token of positive weight.
+template <int kDtype>
+__device__ __forceinline__ int search_chunk(const void* trow, const void* drow, int V, int c,
+                                            double rem, double cmass, float inv_t, bool unit,
+                                            float Rt, float Lt, float Rd, float Ld, Shared& sh) {
+  const int v = c * kChunk + (int)threadIdx.x;
+  double w = 0.0;
+  if (threadIdx.x < kChunk && v < V) {
+    const double p = prob64<kDtype>(trow, v, inv_t, unit, Rt, Lt);
+    w = drow ? fmax(0.0, p - prob64<kDtype>(drow, v, inv_t, unit, Rd, Ld)) : p;
+  }
+  double total;
+  const double exc = block_exscan(w, sh, total);
+  const double f = (total > 0.0 && cmass > 0.0) ? cmass / total : 1.0;
+  int pick = block_min((w > 0.0 && (exc + w) * f > rem) ? v : INT_MAX, sh);
+  if (pick == INT_MAX) {
+    const int last = -block_min(w > 0.0 ? -v : INT_MAX, sh);
+    pick = (last == -INT_MAX) ? c * kChunk : last;
+  }
+  return pick;
+}
+
+// Masses of p per chunk over a whole row, written over `m` (used when a
+// rejection meets an all-zero residual, p_j == q_j).
+template <int kDtype>
+__device__ __forceinline__ void p_chunk_masses(const void* trow, int V, int NC, float inv_t,
+                                               bool unit, float Rt, float Lt, float* m) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  for (int c = wave; c < NC; c += kWaves) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const int v = c * kChunk + lane * kVec + j;
+      if (v < V)
+        s += (float)prob64<kDtype>(trow, v, inv_t, unit, Rt, Lt);
+    }
+    s = wsum(s);
+    if (lane == 0) m[c] = s;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void write_fault(const Args& a, int b, int status) {
+  int32_t* out_tok = a.out_tokens + size_t(b) * (a.Kmax + 1);
+  float* out_alpha = a.alpha + size_t(b) * a.Kmax;
+  for (int k = threadIdx.x; k <= a.Kmax; k += kThreads) out_tok[k] = -1;
+  for (int k = threadIdx.x; k < a.Kmax; k += kThreads) out_alpha[k] = 0.f;
+  if (threadIdx.x == 0) {
+    a.status[b] = status;
+    a.acc_len[b] = -1;
+  }
+}
+
+struct FinShared {
+  Shared red;
+  double ratio[LVTV_MAX_K];
+  double uacc[LVTV_MAX_K];
+  int j;
+};
+
+template <int kDtype>
+__device__ __forceinline__ void finalize_body(const Args& a) {
+  __shared__ FinShared fs;
+  Shared& sh = fs.red;
+  const int b = blockIdx.x;
+  const int kb = a.kreq[b];
+  const float T = a.temp[b];
+  const int Kmax = a.Kmax;
+  if (!(kb >= 0 && kb <= Kmax && temperature_ok(T))) {
+    int st = 0;
+    if (!temperature_ok(T)) st |= LVTV_STATUS_BAD_TEMPERATURE;
+    if (kb < 0 || kb > Kmax) st |= LVTV_STATUS_BAD_K;
+    write_fault(a, b, st);
+    return;
+  }
+  const int32_t* y = a.tokens + size_t(b) * Kmax;
+  const RowOut* rows = a.rows + size_t(b) * (Kmax + 1);
+  const bool greedy = (T == 0.f);
+  int bad = 0, fault = 0;
+  for (int k = threadIdx.x; k <= kb; k += kThreads) {
+    const RowOut r = rows[k];
+    if (k < kb) bad |= (y[k] < 0 || y[k] >= a.V);
+    if (greedy) {
+      fault |= (r.nan & 1) || !isfinite(r.Rt);
+      if (k < kb) fault |= (r.nan & 2) || !isfinite(r.Rd);
+    } else {
+      fault |= !isfinite(r.Rt) || !isfinite(r.Lt) || !(r.Lt > 0.f);
+      if (k < kb) fault |= !isfinite(r.Rd) || !isfinite(r.Ld) || !(r.Ld > 0.f);
+    }
+  }
+  const int status = (__syncthreads_or(bad) ? LVTV_STATUS_BAD_TOKEN : 0) |
+                     (__syncthreads_or(fault) ? LVTV_STATUS_NONFINITE : 0);
+  if (status) {
+    write_fault(a, b, status);
+    return;
+  }
+  int32_t* out_tok = a.out_tokens + size_t(b) * (Kmax + 1);
+  float* out_alpha = a.alpha + size_t(b) * Kmax;
+
+  if (greedy) {
+    if (threadIdx.x == 0) {
+      int j = kb;
+      for (int k = 0; k < kb; ++k)
+        if (y[k] != rows[k].arg_t) {
+          j = k;
+          break;
+        }
+      for (int k = 0; k < Kmax; ++k)
+        out_alpha[k] = (k < kb) ? (rows[k].arg_t == rows[k].arg_d ? 1.f : 0.f) : 0.f;
+      for (int k = 0; k <= Kmax; ++k) out_tok[k] = k < j ? y[k] : (k == j ? rows[j].arg_t : -1);
+      a.acc_len[b] = j;
+      a.status[b] = 0;
+    }
+    return;
+  }
+
+  const bool unit = (T == 1.f);
+  const float inv_t = __fdiv_rn(1.f, T);
+  // accept inputs for every position in parallel: u_k and p(y_k)/q(y_k)
+  if (threadIdx.x < kb) {
+    const int k = threadIdx.x;
+    double u, u2;
+    verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
+    fs.uacc[k] = u;
+    const RowOut r = rows[k];
+    const double p = prob64<kDtype>(row_ptr<kDtype>(a, b, true, k), y[k], inv_t, unit, r.Rt, r.Lt);
+    const double q = prob64<kDtype>(row_ptr<kDtype>(a, b, false, k), y[k], inv_t, unit, r.Rd, r.Ld);
+    // q == 0: accept iff p > 0, encoded as an infinite or zero ratio
+    fs.ratio[k] = (q == 0.0) ? (p > 0.0 ? INFINITY : 0.0) : p / q;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 0; k < Kmax; ++k) out_alpha[k] = k < kb ? rows[k].alpha : 0.f;
+    int j = kb;
+    for (int k = 0; k < kb; ++k)
+      if (!(fs.uacc[k] < fs.ratio[k])) {
+        j = k;
+        break;
+      }
+    fs.j = j;
+  }
+  __syncthreads();
+  const int j = fs.j;
+
+  // the draw at position j
+  double u_acc, u_draw;
+  verify_uniforms(a.seed[b], uint64_t(b), uint64_t(j), u_acc, u_draw);
+  const bool residual = j < kb;
+  const RowOut r = rows[j];
+  const void* trow = row_ptr<kDtype>(a, b, true, j);
+  const void* drow = residual ? row_ptr<kDtype>(a, b, false, j) : nullptr;
+  float* m = a.chunk + (size_t(b) * (Kmax + 1) + j) * a.NC;
+  const int NC = a.NC;
+  int any = 0;
+  for (int c = threadIdx.x; c < NC; c += kThreads) any |= m[c] > 0.f;
+  if (residual && !__syncthreads_or(any)) {
+    // residual zero everywhere: draw from p_j
+    p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, m);
+    drow = nullptr;
+  }
+  double rem;
+  const int c = pick_chunk(m, NC, u_draw, sh, rem);
+  const double cmass = (double)m[c];
+  int v = search_chunk<kDtype>(trow, drow, a.V, c, rem, cmass, inv_t, unit, r.Rt, r.Lt, r.Rd,
+                               r.Ld, sh);
+  if (v < 0 || v >= a.V) v = a.V - 1;  // unreachable: the chosen chunk has positive mass
+  if (threadIdx.x == 0) {
+    for (int k = 0; k <= Kmax; ++k) out_tok[k] = k < j ? y[k] : (k == j ? v : -1);
+    a.acc_len[b] = j;
+    a.status[b] = 0;
+  }
+}
+
+template <int kDtype>
+__global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
+  finalize_body<kDtype>(a);
+}
+
+// ------------------------------------------------------------------ host side
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Layout {
+  int n_tiles, NC;
+  size_t off_rows, off_chunk, total;
+};
+
+Layout make_layout(int B, int Kmax, int V) {
+  Layout L;
+  L.n_tiles = (V + kTile - 1) / kTile;
+  L.NC = L.n_tiles * kWaves;
+  size_t off = kReservedBytes;
+  L.off_rows = off;
+  off = align256(off + sizeof(RowOut) * size_t(B) * (Kmax + 1));
+  L.off_chunk = off;
+  off = align256(off + sizeof(float) * size_t(B) * (Kmax + 1) * L.NC);
+  L.total = off;
+  return L;
+}
+
+bool sizes_ok(int32_t B, int32_t Kmax, int32_t V) {
+  return B >= 1 && B <= 65535 && Kmax >= 0 && Kmax <= LVTV_MAX_K && V >= 1 && V <= LVTV_MAX_V;
+}
+
+template <int kDtype, bool kVecOk>
+hipError_t launch(const Args& a, hipStream_t stream) {
+  const unsigned grid = unsigned(a.B) * unsigned(a.Kmax + 1);
+  if constexpr (kDtype == 1)
+    hipLaunchKernelGGL(verify_rows_bf16<kVecOk>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(verify_rows_f32<kVecOk>, dim3(grid), dim3(kThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_finalize<kDtype>, dim3(unsigned(a.B)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace vr
+}  // namespace lvtv
+
+extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype) {
+  if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
+  return lvtv::vr::make_layout(B, Kmax, V).total;
+}
+
+extern "C" int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                           const int32_t* draft_tokens, const int32_t* k_per_req,
+                           const float* temperature, const uint64_t* seed, int32_t B,
+                           int32_t Kmax, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                           float* alpha, int32_t* status, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  using namespace lvtv;
+  using namespace lvtv::vr;
+  if (dtype != LVTV_F32 && dtype != LVTV_BF16) return LVTV_ERR_DTYPE;
+  if (!sizes_ok(B, Kmax, V)) return LVTV_ERR_SHAPE;
+  if (!target_logits || !k_per_req || !temperature || !seed || !accepted_len || !out_tokens ||
+      !status)
+    return LVTV_ERR_NULL;
+  if (Kmax > 0 && (!draft_logits || !draft_tokens || !alpha)) return LVTV_ERR_NULL;
+  const Layout L = make_layout(B, Kmax, V);
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return LVTV_ERR_WORKSPACE;
+  Args a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.kreq = k_per_req;
+  a.temp = temperature;
+  a.seed = seed;
+  a.B = B;
+  a.Kmax = Kmax;
+  a.V = V;
+  a.n_tiles = L.n_tiles;
+  a.NC = L.NC;
+  a.acc_len = accepted_len;
+  a.out_tokens = out_tokens;
+  a.alpha = alpha;
+  a.status = status;
+  char* ws = static_cast<char*>(workspace);
+  a.rows = reinterpret_cast<RowOut*>(ws + L.off_rows);
+  a.chunk = reinterpret_cast<float*>(ws + L.off_chunk);
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
+                        reinterpret_cast<uintptr_t>(draft_logits);
+  const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == LVTV_BF16)
+    e = vec_ok ? launch<1, true>(a, s) : launch<1, false>(a, s);
+  else
+    e = vec_ok ? launch<0, true>(a, s) : launch<0, false>(a, s);
+  return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+}
