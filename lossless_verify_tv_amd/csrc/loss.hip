@@ -29,6 +29,9 @@
 #include "../../include/lvtv.h"
 #include "device_common.hpp"
 #include "fused_common.hpp"
+#include "loss_fused.hpp"
+
+#include <cstdlib>
 
 namespace lvtv {
 namespace {
@@ -281,9 +284,39 @@ bool sizes_ok(int32_t N, int32_t W, int32_t V) {
 }  // namespace
 }  // namespace lvtv
 
+namespace lvtv {
+namespace {
+
+// Rounds a row workgroup of the single-read kernel polls for the rest of its
+// branch before recomputing the missing rows itself (LVTV_SPIN_LIMIT; 0
+// makes every wait take the recompute path, which the tests use).
+int spin_limit() {
+  const char* v = std::getenv("LVTV_SPIN_LIMIT");
+  if (!v || !*v) return 1 << 16;
+  const long n = std::strtol(v, nullptr, 10);
+  return n < 0 ? 0 : (n > (1 << 30) ? (1 << 30) : int(n));
+}
+
+// The single-read kernel serves every V it can hold; the multi-pass
+// pipeline above serves the rest and can be forced with
+// LVTV_LOSS_PATH=multi-pass (used to cross-check the two).
+bool use_fused(int32_t N, int32_t W, int32_t V) {
+  const char* path = std::getenv("LVTV_LOSS_PATH");
+  if (path && path[0] == 'm') return false;
+  return lf::applicable(N, W, V);
+}
+
+}  // namespace
+}  // namespace lvtv
+
 extern "C" size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V) {
   if (!lvtv::sizes_ok(N, W, V)) return 0;
-  return lvtv::make_layout(N, W, V).total;
+  size_t n = lvtv::make_layout(N, W, V).total;
+  if (lvtv::lf::applicable(N, W, V)) {
+    const size_t f = lvtv::lf::workspace_bytes(N, W, V);
+    if (f > n) n = f;
+  }
+  return n;
 }
 
 extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
@@ -294,8 +327,27 @@ extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* ta
   if (!sizes_ok(N, W, V)) return LVTV_ERR_SHAPE;
   if (!draft_logits || !target_probs || !loss || !alpha || !dlogits) return LVTV_ERR_NULL;
   const Layout L = make_layout(N, W, V);
-  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+  if (!workspace || workspace_bytes < e2e_tv_loss_workspace_bytes(N, W, V) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
+  const uintptr_t mis0 = reinterpret_cast<uintptr_t>(draft_logits) |
+                         reinterpret_cast<uintptr_t>(target_probs) |
+                         reinterpret_cast<uintptr_t>(dlogits);
+  if (use_fused(N, W, V)) {
+    lf::LossCall c;
+    c.z = draft_logits;
+    c.p = target_probs;
+    c.N = N;
+    c.W = W;
+    c.V = V;
+    c.vec_ok = (V % kVec == 0) && ((mis0 & 15) == 0);
+    c.spin_limit = spin_limit();
+    c.loss = loss;
+    c.alpha = alpha;
+    c.dz = dlogits;
+    const hipError_t e = lf::run(c, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+  }
   Args a;
   a.z = draft_logits;
   a.p = target_probs;

@@ -1,0 +1,33 @@
+// Host-side interface of the single-read loss kernel (loss_fused.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lvtv {
+namespace lf {
+
+// A row is held in registers as kMaxGroups groups of 8 tokens per thread of
+// a 1024-thread workgroup: V up to 155648 (larger V take the multi-pass
+// pipeline).
+constexpr int kMaxGroups = 19;
+constexpr int kMaxV = kMaxGroups * 1024 * 8;
+
+struct LossCall {
+  const uint16_t* z;
+  const float* p;
+  int N, W, V;
+  bool vec_ok;
+  int spin_limit;
+  float* loss;
+  float* alpha;
+  uint16_t* dz;
+};
+
+bool applicable(int N, int W, int V);
+size_t workspace_bytes(int N, int W, int V);
+hipError_t run(const LossCall& c, void* workspace, hipStream_t stream);
+
+}  // namespace lf
+}  // namespace lvtv

@@ -81,3 +81,45 @@ def test_loss_bit_identical_reruns():
         assert first["loss"] == again["loss"]
         assert np.array_equal(first["alpha"], again["alpha"])
         assert np.array_equal(first["dlogits"], again["dlogits"])
+
+
+@pytest.mark.parametrize("path", ["fused", "multi-pass"])
+def test_loss_both_paths_against_oracle(path, monkeypatch):
+    """The single-read kernel and the multi-pass pipeline (the one large V
+    uses) both match the oracle."""
+    monkeypatch.setenv("LVTV_LOSS_PATH", path)
+    c = synth.loss_case(n_branches=4, width=7, vocab=24000)
+    _check_small(c.draft_logits, c.target_probs, f"{path} N=4 W=7 V=24000")
+
+
+def test_loss_vocab_beyond_register_capacity():
+    """V above what one workgroup holds in registers takes the multi-pass
+    pipeline."""
+    c = synth.loss_case(n_branches=2, width=3, vocab=160000)
+    _check_small(c.draft_logits, c.target_probs, "N=2 W=3 V=160000")
+
+
+def test_loss_forced_recompute_is_bit_identical(monkeypatch):
+    """With a spin limit of 0 every row gives up waiting for its branch at
+    once and recomputes the other rows' overlaps from the inputs; the
+    outputs must be bit-identical to the normal path."""
+    for shape in ((3, 7, 30000), (2, 16, 4096), (4, 1, 5000)):
+        c = synth.loss_case(n_branches=shape[0], width=shape[1], vocab=shape[2])
+        normal = run_loss(c.draft_logits, c.target_probs)
+        monkeypatch.setenv("LVTV_SPIN_LIMIT", "0")
+        announce(f"loss forced recompute shape={shape}")
+        forced = run_loss(c.draft_logits, c.target_probs)
+        monkeypatch.delenv("LVTV_SPIN_LIMIT")
+        assert normal["loss"] == forced["loss"]
+        assert np.array_equal(normal["alpha"], forced["alpha"])
+        assert np.array_equal(normal["dlogits"], forced["dlogits"])
+
+
+def test_loss_workspace_reuse_across_shapes():
+    """One cached workspace serves calls of different shapes in a row (the
+    exchange words of one call are never mistaken for the next call's)."""
+    shapes = [(4, 7, 30000), (2, 3, 9000), (4, 7, 30000), (6, 5, 12000)]
+    for rnd in range(2):
+        for shape in shapes:
+            c = synth.loss_case(n_branches=shape[0], width=shape[1], vocab=shape[2])
+            _check_small(c.draft_logits, c.target_probs, f"reuse round {rnd} {shape}")
