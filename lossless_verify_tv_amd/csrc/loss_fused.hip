@@ -9,17 +9,19 @@
 //      registers, alpha_j = sum min(q, p), S_j = sum_{q<p} q,
 //      S'_j = sum_{q>=p} q (fp64 across groups), and one bit [q < p] per
 //      token, kept in registers;
-//   4. publishes (alpha_j, S_j, S'_j) to the branch and collects those of the
-//      branch's other rows (tagged words, bounded wait with a bit-identical
-//      recompute fallback; see fused_common.hpp);
+//   4. publishes (alpha_j, S_j, S'_j) and its row statistics to the branch
+//      and collects those of the branch's other rows (tagged words; see
+//      fused_common.hpp). The wait is bounded: a row that gives up is marked
+//      unfinished and a repair launch, which runs once every row has
+//      published, completes it with the same per-group steps (bit-identical);
 //   5. the branch scalars in fp64: prefix products P_k, the loss
 //      L_n = -sum_k P_k, R_k = 1 + alpha_{k+1} R_{k+1} and
 //      dL_n/dalpha_j = -P_{j-1} R_j; the gradient
 //      dz(u) = (G_j / N) q(u) ([q(u) < p(u)] - S_j), evaluated as
 //      (G_j/N) S'_j q(u) where the bit is set and -(G_j/N) S_j q(u) elsewhere,
 //      rounded to bf16 (nearest even) and written once.
-// A second launch averages the branch losses in a fixed order and advances
-// the workspace's call epoch.
+// Then the repair launch (normally a no-op) and a last launch that averages
+// the branch losses in a fixed order and advances the workspace's call epoch.
 //
 // Definition (page title, section): "SpecOPD: Branch-Parallel On-Policy
 // Distillation for Speculative Decoding", prerequisite on acceptance length
@@ -53,7 +55,7 @@ constexpr int kZL = 8;                           // ... of which in LDS (128 KB 
 constexpr int kZR = kZG - kZL;                   // ... and in registers
 constexpr int kMaskWords = (kZG * kVec + 31) / 32;
 constexpr int kPBatch = 4;                       // groups of p in flight together
-constexpr int kWords = 6;                        // tagged words per row: alpha, S, S' (fp64)
+constexpr int kWords = 8;  // tagged words per row: alpha, S, S' (fp64 pairs), -M log2 e, 1/L
 constexpr float kL2E = 1.44269504088896340736f;
 static_assert(kZG * kTile >= kMaxV, "held groups cover the largest V");
 
@@ -67,6 +69,7 @@ struct Args {
   float* loss;
   FusedCtl* ctl;
   uint64_t* words;      // [N][W][kWords] tagged words
+  uint64_t* unfinished; // [N][W] tagged: this call left the row's dz to the repair launch
   double* branch_loss;  // [N]
 };
 
@@ -137,8 +140,14 @@ __device__ __forceinline__ float zelem(const u32x4& g, int j) {
 struct Held {
   u32x4 r[kZR];
   u32x4 (*lds)[kThreads];
+  // The LDS slot address goes through opaque() so each read stays where it
+  // is used (not hoisted, all at once, to the start of a phase).
   __device__ __forceinline__ u32x4 get(int g) const {
-    return g < kZL ? lds[g][threadIdx.x] : r[g - kZL];
+    if (g < kZL) {
+      const int slot = opaque(int(threadIdx.x));
+      return lds[g][slot];
+    }
+    return r[g - kZL];
   }
 };
 
@@ -261,35 +270,6 @@ __device__ __forceinline__ RowStats finish_stats(float m, double l, Shared& sh) 
   return r;
 }
 
-// ------------------------------------------------------------------ recomputation
-
-// (alpha, S, S') of row `row`, recomputed from the inputs by streaming them
-// with the same per-group steps and reductions the row's own workgroup uses.
-template <bool kVecOk>
-__device__ __forceinline__ void recompute_row(const Args& a, size_t row, double& al, double& sb,
-                                              double& sa, Shared& sh) {
-  const int V = a.V;
-  const uint16_t* z = a.z + row * V;
-  const float* p = a.p + row * V;
-  float m = -INFINITY;
-#pragma unroll 1
-  for (int g = 0; g < kZG; ++g) m = grp_max(load_z<kVecOk>(z, V, group_elem(g)), m);
-  m = block_max(m, sh);
-  const float nm0 = (m == -INFINITY) ? 0.f : -(m * kL2E);
-  double l = 0.0;
-#pragma unroll 1
-  for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(load_z<kVecOk>(z, V, group_elem(g)), nm0);
-  const RowStats rs = finish_stats(m, l, sh);
-  al = sb = sa = 0.0;
-#pragma unroll 1
-  for (int g = 0; g < kZG; ++g) {
-    u32x4 pa, pb;
-    load_p<kVecOk>(p, V, group_elem(g), pa, pb);
-    (void)grp_overlap(load_z<kVecOk>(z, V, group_elem(g)), pa, pb, rs.nm, rs.inv_l, al, sb, sa);
-  }
-  block_sum3(al, sb, sa, sh);
-}
-
 // ------------------------------------------------------------------ the kernel
 
 // fp64 value from two consecutive 32-bit exchange words (low half first).
@@ -297,13 +277,69 @@ __device__ __forceinline__ double word_f64(const uint32_t* w, int i) {
   return __longlong_as_double((long long)((uint64_t(w[i + 1]) << 32) | w[i]));
 }
 
+// Branch scalars from the W rows' words (thread 0, fp64): the branch loss
+// (written by row 0), alpha_j, and this row's two gradient coefficients in
+// sh.coef: (G_j/N) S'_j where q < p, -(G_j/N) S_j elsewhere.
+__device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size_t row,
+                                               Shared& sh) {
+  const int W = a.W;
+  if (threadIdx.x == 0) {
+    double run = 1.0, loss_n = 0.0, before = 1.0;
+    for (int k = 0; k < W; ++k) {
+      if (k == j) before = run;
+      run *= word_f64(sh.words, k * kWords);
+      loss_n -= run;
+    }
+    double suffix = 1.0;  // R_{W-1} = 1, R_k = 1 + alpha_{k+1} R_{k+1}
+    for (int k = W - 2; k >= j; --k) suffix = 1.0 + word_f64(sh.words, (k + 1) * kWords) * suffix;
+    const double g = -before * suffix / double(a.N);
+    sh.coef[0] = g * word_f64(sh.words, j * kWords + 4);   // S'_j
+    sh.coef[1] = -g * word_f64(sh.words, j * kWords + 2);  // S_j
+    a.alpha[row] = float(word_f64(sh.words, j * kWords));
+    if (j == 0) a.branch_loss[n] = loss_n;
+  }
+  __syncthreads();
+}
+
+// dz of one group of 8 tokens, bf16 (nearest even), from z, the group's
+// mask bits and the row's coefficients.
+template <bool kVecOk>
+__device__ __forceinline__ void dz_group(const u32x4& zv, const uint32_t (&mask)[kMaskWords],
+                                         int g, int e, int V, const RowStats& rs, float c_below,
+                                         float c_above, uint16_t* dz) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float v2[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int jj = 2 * h + t;
+      const bool below = (mask[(g * kVec + jj) / 32] >> ((g * kVec + jj) % 32)) & 1u;
+      v2[t] = qval(zelem(zv, jj), rs.nm, rs.inv_l) * (below ? c_below : c_above);
+    }
+    const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
+    out[h] = __builtin_bit_cast(uint32_t, b);
+  }
+  if (kVecOk) {
+    if (e < V) st_nt16(dz + e, out);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kVec; ++t)
+      if (e + t < V) dz[e + t] = uint16_t(out[t >> 1] >> (16 * (t & 1)));
+  }
+}
+
+
 template <bool kVecOk>
 __device__ __forceinline__ void row_body(const Args& a) {
   __shared__ Shared sh;
   const int W = a.W, V = a.V;
-  const int n = blockIdx.x / W;
-  const int j = blockIdx.x - n * W;
-  const size_t row = size_t(n) * W + j;
+  // uniform row coordinates, kept in scalar registers
+  const int n = __builtin_amdgcn_readfirstlane(int(blockIdx.x) / W);
+  const int j = __builtin_amdgcn_readfirstlane(int(blockIdx.x) - n * W);
+  const size_t row = size_t(blockIdx.x);
   const uint16_t* z = a.z + row * V;
   const float* p = a.p + row * V;
   const uint32_t tag = tag_from_epoch(read_epoch(a.ctl));
@@ -371,6 +407,8 @@ __device__ __forceinline__ void row_body(const Args& a) {
       tag_store(w + 2 * i, tag, uint32_t(bits));
       tag_store(w + 2 * i + 1, tag, uint32_t(bits >> 32));
     }
+    tag_store(w + 6, tag, __float_as_uint(rs.nm));
+    tag_store(w + 7, tag, __float_as_uint(rs.inv_l));
   }
   uint64_t* src = a.words + size_t(n) * W * kWords;
   const int nw = W * kWords;
@@ -398,85 +436,74 @@ __device__ __forceinline__ void row_body(const Args& a) {
     __builtin_amdgcn_s_sleep(2);
   }
   if (!fresh) {
-    // Rare: a row's words did not arrive within the spin limit; recompute
-    // them from the inputs (the same bits its own workgroup publishes).
-    for (int k = 0; k < W; ++k) {
-      bool miss = false;
-      for (int i = 0; i < kWords; ++i) miss |= !sh.have[k * kWords + i];
-      if (!miss) continue;
-      double x, y, zz;
-      recompute_row<kVecOk>(a, size_t(n) * W + k, x, y, zz, sh);
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        const double v[3] = {x, y, zz};
-        for (int i = 0; i < 3; ++i) {
-          const uint64_t bits = uint64_t(__double_as_longlong(v[i]));
-          sh.words[k * kWords + 2 * i] = uint32_t(bits);
-          sh.words[k * kWords + 2 * i + 1] = uint32_t(bits >> 32);
-        }
-      }
-      __syncthreads();
-    }
+    // Rare: the rest of the branch did not arrive within the spin limit
+    // (its rows may not be resident yet). Leave this row to the repair
+    // launch, which runs after every row has published its words.
+    if (threadIdx.x == 0) tag_store(a.unfinished + row, tag, 1u);
+    return;
   }
-
-  // 5. branch scalars (thread 0, fp64) and this row's coefficients
-  if (threadIdx.x == 0) {
-    double run = 1.0, loss_n = 0.0, before = 1.0;
-    for (int k = 0; k < W; ++k) {
-      if (k == j) before = run;
-      run *= word_f64(sh.words, k * kWords);
-      loss_n -= run;
-    }
-    double suffix = 1.0;  // R_{W-1} = 1, R_k = 1 + alpha_{k+1} R_{k+1}
-    for (int k = W - 2; k >= j; --k) suffix = 1.0 + word_f64(sh.words, (k + 1) * kWords) * suffix;
-    const double g = -before * suffix / double(a.N);
-    const double s_below = word_f64(sh.words, j * kWords + 2);
-    const double s_above = word_f64(sh.words, j * kWords + 4);
-    sh.coef[0] = g * s_above;   // where q < p
-    sh.coef[1] = -g * s_below;  // where q >= p
-    a.alpha[row] = float(word_f64(sh.words, j * kWords));
-    if (j == 0) a.branch_loss[n] = loss_n;
-  }
-  __syncthreads();
+  branch_scalars(a, n, j, row, sh);
   const float c_below = float(sh.coef[0]);
   const float c_above = float(sh.coef[1]);
-
-  // 6. dz from the registers and the mask
+  // 5. dz from the held row and the mask
   uint16_t* dz = a.dz + row * V;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
   const int tbd = opaque(int(threadIdx.x) * kVec);
 #pragma unroll
   for (int g = 0; g < kZG; ++g) {
-    const int e = opaque(tbd) + g * kTile;
-    const u32x4 zv = zg.get(g);
-    u32x4 out;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float v2[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int jj = 2 * h + t;
-        const bool below = (mask[(g * kVec + jj) / 32] >> ((g * kVec + jj) % 32)) & 1u;
-        v2[t] = qval(zelem(zv, jj), rs.nm, rs.inv_l) * (below ? c_below : c_above);
-      }
-      const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
-      out[h] = __builtin_bit_cast(uint32_t, b);
-    }
-    if (kVecOk) {
-      if (e < V) st_nt16(dz + e, out);
-    } else {
-#pragma unroll
-      for (int t = 0; t < kVec; ++t)
-        if (e + t < V) dz[e + t] = uint16_t(out[t >> 1] >> (16 * (t & 1)));
-    }
+    dz_group<kVecOk>(zg.get(g), mask, g, opaque(tbd) + g * kTile, V, rs, c_below, c_above, dz);
     __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Rows a workgroup left unfinished in this call (see above): every row has
+// published its words by now, so the branch scalars are at hand; z and p
+// are read again to form the mask and dz with the same per-group steps.
+template <bool kVecOk>
+__device__ __forceinline__ void repair_body(const Args& a) {
+  __shared__ Shared sh;
+  const int W = a.W, V = a.V;
+  const uint32_t tag = tag_from_epoch(read_epoch(a.ctl));
+  const size_t rows = size_t(a.N) * W;
+  for (size_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    if (uint32_t(tag_load(a.unfinished + row) >> 32) != tag) continue;
+    const int n = int(row / W), j = int(row - size_t(n) * W);
+    uint64_t* src = a.words + size_t(n) * W * kWords;
+    for (int i = threadIdx.x; i < W * kWords; i += kThreads) sh.words[i] = uint32_t(tag_load(src + i));
+    __syncthreads();
+    RowStats rs;
+    rs.nm = __uint_as_float(sh.words[j * kWords + 6]);
+    rs.inv_l = __uint_as_float(sh.words[j * kWords + 7]);
+    branch_scalars(a, n, j, row, sh);
+    const float c_below = float(sh.coef[0]);
+    const float c_above = float(sh.coef[1]);
+    const uint16_t* z = a.z + row * V;
+    const float* p = a.p + row * V;
+    uint16_t* dz = a.dz + row * V;
+#pragma unroll
+    for (int g = 0; g < kZG; ++g) {
+      const int e = group_elem(g);
+      const u32x4 zv = load_z<kVecOk>(z, V, e);
+      u32x4 pa, pb;
+      load_p<kVecOk>(p, V, e, pa, pb);
+      double x = 0.0, y = 0.0, w = 0.0;
+      uint32_t m1[kMaskWords];
+#pragma unroll
+      for (int i = 0; i < kMaskWords; ++i) m1[i] = 0u;
+      m1[(g * kVec) / 32] = grp_overlap(zv, pa, pb, rs.nm, rs.inv_l, x, y, w) << ((g * kVec) % 32);
+      dz_group<kVecOk>(zv, m1, g, e, V, rs, c_below, c_above, dz);
+    }
+    __syncthreads();
   }
 }
 
 template <bool kVecOk>
 __global__ __launch_bounds__(kThreads) void loss_rows(Args a) {
   row_body<kVecOk>(a);
+}
+
+template <bool kVecOk>
+__global__ __launch_bounds__(kThreads) void loss_repair(Args a) {
+  repair_body<kVecOk>(a);
 }
 
 // Mean of the branch losses in a fixed order; then the call epoch advances
@@ -503,7 +530,7 @@ __global__ __launch_bounds__(256) void loss_reduce(Args a) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t off_words, off_branch, total;
+  size_t off_words, off_unfinished, off_branch, total;
 };
 
 Layout make_layout(int N, int W) {
@@ -511,6 +538,8 @@ Layout make_layout(int N, int W) {
   size_t off = kReservedBytes;
   L.off_words = off;
   off = align256(off + sizeof(uint64_t) * size_t(N) * W * kWords);
+  L.off_unfinished = off;
+  off = align256(off + sizeof(uint64_t) * size_t(N) * W);
   L.off_branch = off;
   off = align256(off + sizeof(double) * size_t(N));
   L.total = off;
@@ -543,13 +572,21 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   a.ctl = workspace_ctl(workspace);
   a.words = reinterpret_cast<uint64_t*>(ws + L.off_words);
+  a.unfinished = reinterpret_cast<uint64_t*>(ws + L.off_unfinished);
   a.branch_loss = reinterpret_cast<double*>(ws + L.off_branch);
   const unsigned grid = unsigned(size_t(c.N) * c.W);
   if (c.vec_ok)
     hipLaunchKernelGGL(loss_rows<true>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(loss_rows<false>, dim3(grid), dim3(kThreads), 0, stream, a);
-  const hipError_t e = hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned rgrid = grid < 256u ? grid : 256u;
+  if (c.vec_ok)
+    hipLaunchKernelGGL(loss_repair<true>, dim3(rgrid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(loss_repair<false>, dim3(rgrid), dim3(kThreads), 0, stream, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(loss_reduce, dim3(1), dim3(256), 0, stream, a);
   return hipGetLastError();
