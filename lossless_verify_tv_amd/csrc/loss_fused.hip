@@ -1,27 +1,33 @@
-// e2e_tv_loss_fwd_bwd, single-read kernel for gfx950 (V <= 155648).
+// e2e_tv_loss_fwd_bwd, single-read kernels for gfx950 (V <= 155648).
 //
-// One 1024-thread workgroup per (branch n, position j) row:
-//   1. loads the row's bf16 draft logits z once and keeps them in registers
-//      (19 groups of 8 tokens per thread, packed two per register);
-//   2. the softmax statistics of z from the registers: the maximum M, then
-//      L = sum 2^((z - M) log2 e) (fp32 per group of 8, fp64 across groups);
-//   3. streams the fp32 target probabilities p once: q = softmax(z) from the
-//      registers, alpha_j = sum min(q, p), S_j = sum_{q<p} q,
-//      S'_j = sum_{q>=p} q (fp64 across groups), and one bit [q < p] per
-//      token, kept in registers;
-//   4. publishes (alpha_j, S_j, S'_j) and its row statistics to the branch
-//      and collects those of the branch's other rows (tagged words; see
-//      fused_common.hpp). The wait is bounded: a row that gives up is marked
-//      unfinished and a repair launch, which runs once every row has
-//      published, completes it with the same per-group steps (bit-identical);
+// Each (branch n, position j) row is split in two halves of up to 19 tiles
+// of 4096 tokens; one 512-thread workgroup per half, two per compute unit
+// (so one can compute while the other streams). A half-row workgroup:
+//   1. loads its half of the bf16 draft logits z once and keeps it: 19 groups
+//      of 8 tokens per thread, 8 groups in LDS (64 KB) and 11 in registers;
+//   2. computes the half's softmax statistics (maximum M_h, sum of
+//      2^((z - M_h) log2 e)), swaps them with the other half through tagged
+//      words and combines both into the row's M and L (the same arithmetic,
+//      in the same order, in both halves);
+//   3. streams its half of the fp32 target probabilities p once: q = softmax(z)
+//      from the held copy, and the half's parts of alpha_j = sum min(q, p),
+//      S_j = sum_{q<p} q and S'_j = sum_{q>=p} q (fp64 across groups), with one
+//      bit [q < p] per token kept in registers;
+//   4. publishes those parts and collects the parts of every half of the
+//      branch's rows (tagged words; see fused_common.hpp); alpha_k, S_k and
+//      S'_k are the two halves' sums, half 0 first;
 //   5. the branch scalars in fp64: prefix products P_k, the loss
 //      L_n = -sum_k P_k, R_k = 1 + alpha_{k+1} R_{k+1} and
 //      dL_n/dalpha_j = -P_{j-1} R_j; the gradient
 //      dz(u) = (G_j / N) q(u) ([q(u) < p(u)] - S_j), evaluated as
 //      (G_j/N) S'_j q(u) where the bit is set and -(G_j/N) S_j q(u) elsewhere,
 //      rounded to bf16 (nearest even) and written once.
-// Then the repair launch (normally a no-op) and a last launch that averages
-// the branch losses in a fixed order and advances the workspace's call epoch.
+// Every wait is bounded: a half that gives up marks its row unfinished and
+// stops. A repair launch, which runs once every workgroup has finished,
+// completes such rows from the published words, recomputing whatever is
+// missing with the same per-group steps and reductions (bit-identical). A
+// last launch averages the branch losses in a fixed order and advances the
+// workspace's call epoch.
 //
 // Definition (page title, section): "SpecOPD: Branch-Parallel On-Policy
 // Distillation for Speculative Decoding", prerequisite on acceptance length
@@ -47,17 +53,23 @@ namespace lvtv {
 namespace lf {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;         // 16
-constexpr int kTile = kThreads * kVec;           // 8192 tokens per group index
-constexpr int kZG = kMaxGroups;                  // groups of z held per thread
-constexpr int kZL = 8;                           // ... of which in LDS (128 KB per workgroup)
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;         // 8
+constexpr int kTile = kThreads * kVec;           // 4096 tokens per group index
+constexpr int kZG = kMaxGroups;                  // groups of z held per thread (one half)
+constexpr int kHalf = kZG * kTile;               // tokens per half row
+constexpr int kZL = 8;                           // ... of which in LDS (64 KB per workgroup)
 constexpr int kZR = kZG - kZL;                   // ... and in registers
 constexpr int kMaskWords = (kZG * kVec + 31) / 32;
 constexpr int kPBatch = 4;                       // groups of p in flight together
-constexpr int kWords = 8;  // tagged words per row: alpha, S, S' (fp64 pairs), -M log2 e, 1/L
 constexpr float kL2E = 1.44269504088896340736f;
-static_assert(kZG * kTile >= kMaxV, "held groups cover the largest V");
+static_assert(2 * kHalf >= kMaxV, "two halves cover the largest V");
+
+// Tagged words per half row: the half's statistics, then its parts of the
+// branch sums.
+constexpr int kStatWords = 3;    // M_h (fp32), L_h (fp64)
+constexpr int kPartWords = 6;    // alpha_h, S_h, S'_h (fp64)
+constexpr int kSlotWords = 16;   // per half: [0,3) statistics, [4,10) parts
 
 struct Args {
   const uint16_t* z;
@@ -68,29 +80,30 @@ struct Args {
   uint16_t* dz;
   float* loss;
   FusedCtl* ctl;
-  uint64_t* words;      // [N][W][kWords] tagged words
-  uint64_t* unfinished; // [N][W] tagged: this call left the row's dz to the repair launch
-  double* branch_loss;  // [N]
+  uint64_t* words;       // [N][W][2][kSlotWords] tagged words
+  uint64_t* unfinished;  // [N][W] tagged: the row's dz is left to the repair launch
+  double* branch_loss;   // [N]
 };
 
 // ------------------------------------------------------------------ loads
 
-// This thread's first token in group g is tb + g * kTile, tb = 8 * thread.
-// Each phase takes tb through opaque() so the compiler recomputes the
-// per-group offsets where they are used instead of keeping all 19 alive in
-// registers for the whole kernel.
+// Keeps a value opaque to the compiler: per-group offsets derived from it
+// are recomputed where used instead of being kept alive in registers for the
+// whole kernel.
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
 
-__device__ __forceinline__ int group_elem(int g) { return g * kTile + threadIdx.x * kVec; }
+// First token of this thread's group g in half h.
+__device__ __forceinline__ int group_elem(int h, int g) {
+  return h * kHalf + g * kTile + int(threadIdx.x) * kVec;
+}
 
-// z group g of a row: 8 bf16 tokens packed in 4 registers; tokens at or
-// beyond V read as -inf.
-// With kVecOk (16-byte aligned rows, V % 8 == 0) a group lies wholly inside
-// or wholly past the end of the row; the load is unconditional (a
-// past-the-end group reads the row's first group) and the select comes
+// z group of a row: 8 bf16 tokens packed in 4 registers; tokens at or beyond
+// V read as -inf. With kVecOk (16-byte aligned rows, V % 8 == 0) a group lies
+// wholly inside or wholly past the end of the row; the load is unconditional
+// (a past-the-end group reads the row's first group) and the select comes
 // after it, so no branch splits a batch of loads.
 template <bool kVecOk>
 __device__ __forceinline__ u32x4 load_z(const uint16_t* row, int V, int e) {
@@ -111,7 +124,7 @@ __device__ __forceinline__ u32x4 load_z(const uint16_t* row, int V, int e) {
   }
 }
 
-// p group g of a row: 8 fp32 values; values at or beyond V read as 0.
+// p group of a row: 8 fp32 values; values at or beyond V read as 0.
 template <bool kVecOk>
 __device__ __forceinline__ void load_p(const float* row, int V, int e, u32x4& a, u32x4& b) {
   if constexpr (kVecOk) {
@@ -134,8 +147,12 @@ __device__ __forceinline__ float zelem(const u32x4& g, int j) {
   return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-// The held row: groups [0, kZL) in LDS (each thread its own 16-byte slot
-// per group, so no barrier is needed between a thread's write and its
+__device__ __forceinline__ float pelem(const u32x4& a, const u32x4& b, int j) {
+  return __uint_as_float(j < 4 ? a[j] : b[j - 4]);
+}
+
+// The held half row: groups [0, kZL) in LDS (each thread its own 16-byte
+// slot per group, so no barrier is needed between a thread's write and its
 // reads), groups [kZL, kZG) in registers.
 struct Held {
   u32x4 r[kZR];
@@ -151,21 +168,15 @@ struct Held {
   }
 };
 
-// Makes the compiler treat the held z registers as rewritten, so each phase
+// Makes the compiler treat the held registers as rewritten, so each phase
 // recomputes its exponentials from them instead of carrying the previous
-// phase's (up to 152 values per thread) across a block reduction or the
-// exchange.
+// phase's across a block reduction or an exchange.
 __device__ __forceinline__ void launder(Held& h) {
 #pragma unroll
   for (int g = 0; g < kZR; ++g) asm volatile("" : "+v"(h.r[g]));
 }
 
-__device__ __forceinline__ float pelem(const u32x4& a, const u32x4& b, int j) {
-  return __uint_as_float(j < 4 ? a[j] : b[j - 4]);
-}
-
-// q of one token: 2^(z log2 e - M log2 e) / L, as in the oracle's softmax up
-// to fp32 rounding.
+// q of one token: 2^(z log2 e - M log2 e) / L.
 __device__ __forceinline__ float qval(float z, float nm, float inv_l) {
   return __builtin_amdgcn_exp2f(__builtin_fmaf(z, kL2E, nm)) * inv_l;
 }
@@ -175,8 +186,8 @@ __device__ __forceinline__ float qval(float z, float nm, float inv_l) {
 struct Shared {
   float f[kWaves];
   double d[kWaves][3];
-  uint32_t words[LVTV_MAX_W * kWords];
-  uint8_t have[LVTV_MAX_W * kWords];
+  uint32_t words[LVTV_MAX_W * 2 * kSlotWords];
+  uint8_t have[LVTV_MAX_W * 2 * kSlotWords];
   double coef[2];
 };
 
@@ -215,8 +226,8 @@ __device__ __forceinline__ void block_sum3(double& a, double& b, double& c, Shar
 
 // ------------------------------------------------------------------ per-group steps
 //
-// Shared by the register path and the streaming recomputation, so both give
-// the same bits (same element order, same reduction tree).
+// Shared by the workgroups and the repair launch, so both give the same bits
+// (same element order, same reduction tree).
 
 __device__ __forceinline__ float grp_max(const u32x4& g, float m) {
 #pragma unroll
@@ -253,60 +264,119 @@ __device__ __forceinline__ uint32_t grp_overlap(const u32x4& g, const u32x4& pa,
   return bits;
 }
 
-// Row statistics (M log2 e as the exponent offset, 1/L) from per-thread
-// partials.
+// Half statistics from per-thread partials: every thread's m is already the
+// block maximum; l is summed over the block.
+struct HalfStats {
+  float m;   // maximum of the half (-inf for a half past the end of the row)
+  double l;  // sum of 2^((z - m) log2 e) over the half
+};
+
+__device__ __forceinline__ double block_sum1(double v, Shared& sh) {
+  double u0 = 0.0, u1 = 0.0;
+  block_sum3(v, u0, u1, sh);
+  return v;
+}
+
+// Row statistics from the two halves' statistics, half 0 first: M = max,
+// L = sum_h l_h 2^((m_h - M) log2 e) in fp64 (a half of maximum -inf weighs
+// l_h * 0, which keeps a NaN). Both halves and the repair launch call this
+// with the same values, so they agree bit for bit.
 struct RowStats {
   float nm;     // -M log2 e (0 when M = -inf)
   float inv_l;  // fl32(1 / L)
 };
 
-__device__ __forceinline__ RowStats finish_stats(float m, double l, Shared& sh) {
-  // every thread's m is already the block maximum here
-  double x = l, unused0 = 0.0, unused1 = 0.0;
-  block_sum3(x, unused0, unused1, sh);
+__device__ __forceinline__ RowStats combine_halves(float m0, double l0, float m1, double l1) {
+  const float M = fmaxf(m0, m1);
+  const double w0 = (m0 == -INFINITY) ? l0 * 0.0
+                                      : l0 * (double)__builtin_amdgcn_exp2f((m0 - M) * kL2E);
+  const double w1 = (m1 == -INFINITY) ? l1 * 0.0
+                                      : l1 * (double)__builtin_amdgcn_exp2f((m1 - M) * kL2E);
   RowStats r;
-  r.nm = (m == -INFINITY) ? 0.f : -(m * kL2E);
-  r.inv_l = float(1.0 / x);
+  r.nm = (M == -INFINITY) ? 0.f : -(M * kL2E);
+  r.inv_l = float(1.0 / (w0 + w1));
   return r;
 }
 
-// ------------------------------------------------------------------ the kernel
-
-// fp64 value from two consecutive 32-bit exchange words (low half first).
+// fp64 value from two consecutive 32-bit words (low half first).
 __device__ __forceinline__ double word_f64(const uint32_t* w, int i) {
   return __longlong_as_double((long long)((uint64_t(w[i + 1]) << 32) | w[i]));
 }
 
-// Branch scalars from the W rows' words (thread 0, fp64): the branch loss
-// (written by row 0), alpha_j, and this row's two gradient coefficients in
-// sh.coef: (G_j/N) S'_j where q < p, -(G_j/N) S_j elsewhere.
+__device__ __forceinline__ void f64_words(double v, uint32_t& lo, uint32_t& hi) {
+  const uint64_t bits = uint64_t(__double_as_longlong(v));
+  lo = uint32_t(bits);
+  hi = uint32_t(bits >> 32);
+}
+
+// Block-wide poll of words [first, first + count) of nslots consecutive half
+// slots starting at `slots`; word k of slot s lands in
+// sh.words[s * kSlotWords + k]. Returns whether all were fresh within the
+// spin limit. Every thread calls it.
+__device__ __forceinline__ bool poll_slots(uint64_t* slots, int nslots, int first, int count,
+                                           uint32_t tag, int spin_limit, Shared& sh) {
+  const int n = nslots * count;
+  for (int i = threadIdx.x; i < n; i += kThreads) sh.have[i] = 0;
+  __syncthreads();
+  for (int round = 0;; ++round) {
+    int missing = 0;
+    for (int i = threadIdx.x; i < n; i += kThreads) {
+      if (!sh.have[i]) {
+        const int s = i / count, k = first + (i - s * count);
+        const uint64_t w = tag_load(slots + s * kSlotWords + k);
+        if (uint32_t(w >> 32) == tag) {
+          sh.words[s * kSlotWords + k] = uint32_t(w);
+          sh.have[i] = 1;
+        } else {
+          missing = 1;
+        }
+      }
+    }
+    if (!__syncthreads_or(missing)) return true;
+    if (round >= spin_limit) return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// ------------------------------------------------------------------ branch scalars
+
+// Branch scalars (thread 0, fp64) from the branch's parts in sh.words laid
+// out [k][h][kSlotWords] with the parts at offset 4: alpha_k, S_k, S'_k are
+// the sums of the two halves (half 0 first). Writes sh.coef for row j
+// ((G_j/N) S'_j where q < p, -(G_j/N) S_j elsewhere), alpha[row], and the
+// branch loss when j == 0.
 __device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size_t row,
                                                Shared& sh) {
   const int W = a.W;
   if (threadIdx.x == 0) {
+    auto part = [&](int k, int which) {
+      const int b0 = (k * 2) * kSlotWords + 4 + 2 * which;
+      const int b1 = (k * 2 + 1) * kSlotWords + 4 + 2 * which;
+      return word_f64(sh.words, b0) + word_f64(sh.words, b1);
+    };
     double run = 1.0, loss_n = 0.0, before = 1.0;
     for (int k = 0; k < W; ++k) {
       if (k == j) before = run;
-      run *= word_f64(sh.words, k * kWords);
+      run *= part(k, 0);
       loss_n -= run;
     }
     double suffix = 1.0;  // R_{W-1} = 1, R_k = 1 + alpha_{k+1} R_{k+1}
-    for (int k = W - 2; k >= j; --k) suffix = 1.0 + word_f64(sh.words, (k + 1) * kWords) * suffix;
+    for (int k = W - 2; k >= j; --k) suffix = 1.0 + part(k + 1, 0) * suffix;
     const double g = -before * suffix / double(a.N);
-    sh.coef[0] = g * word_f64(sh.words, j * kWords + 4);   // S'_j
-    sh.coef[1] = -g * word_f64(sh.words, j * kWords + 2);  // S_j
-    a.alpha[row] = float(word_f64(sh.words, j * kWords));
+    sh.coef[0] = g * part(j, 2);   // S'_j
+    sh.coef[1] = -g * part(j, 1);  // S_j
+    a.alpha[row] = float(part(j, 0));
     if (j == 0) a.branch_loss[n] = loss_n;
   }
   __syncthreads();
 }
 
-// dz of one group of 8 tokens, bf16 (nearest even), from z, the group's
-// mask bits and the row's coefficients.
+// dz of one group of 8 tokens, bf16 (nearest even), from z, the group's mask
+// bits and the row's coefficients.
 template <bool kVecOk>
-__device__ __forceinline__ void dz_group(const u32x4& zv, const uint32_t (&mask)[kMaskWords],
-                                         int g, int e, int V, const RowStats& rs, float c_below,
-                                         float c_above, uint16_t* dz) {
+__device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e, int V,
+                                         const RowStats& rs, float c_below, float c_above,
+                                         uint16_t* dz) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   u32x4 out;
@@ -316,7 +386,7 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, const uint32_t (&mask)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int jj = 2 * h + t;
-      const bool below = (mask[(g * kVec + jj) / 32] >> ((g * kVec + jj) % 32)) & 1u;
+      const bool below = (bits8 >> jj) & 1u;
       v2[t] = qval(zelem(zv, jj), rs.nm, rs.inv_l) * (below ? c_below : c_above);
     }
     const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
@@ -331,25 +401,33 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, const uint32_t (&mask)
   }
 }
 
+__device__ __forceinline__ uint32_t mask_bits(const uint32_t (&mask)[kMaskWords], int g) {
+  return (mask[(g * kVec) / 32] >> ((g * kVec) % 32)) & 0xffu;
+}
+
+// ------------------------------------------------------------------ half-row kernel
 
 template <bool kVecOk>
-__device__ __forceinline__ void row_body(const Args& a) {
+__device__ __forceinline__ void half_body(const Args& a) {
   __shared__ Shared sh;
+  __shared__ u32x4 zl[kZL][kThreads];
   const int W = a.W, V = a.V;
-  // uniform row coordinates, kept in scalar registers
-  const int n = __builtin_amdgcn_readfirstlane(int(blockIdx.x) / W);
-  const int j = __builtin_amdgcn_readfirstlane(int(blockIdx.x) - n * W);
-  const size_t row = size_t(blockIdx.x);
+  // uniform coordinates, kept in scalar registers
+  const int r = __builtin_amdgcn_readfirstlane(int(blockIdx.x) >> 1);
+  const int h = __builtin_amdgcn_readfirstlane(int(blockIdx.x) & 1);
+  const int n = __builtin_amdgcn_readfirstlane(r / W);
+  const int j = __builtin_amdgcn_readfirstlane(r - n * W);
+  const size_t row = size_t(r);
   const uint16_t* z = a.z + row * V;
   const float* p = a.p + row * V;
   const uint32_t tag = tag_from_epoch(read_epoch(a.ctl));
+  uint64_t* slot = a.words + (row * 2 + h) * kSlotWords;
 
-  // 1. z into registers
-  __shared__ u32x4 zl[kZL][kThreads];
+  // 1. this half of z into the held copy
   Held zg;
   zg.lds = zl;
   {
-    const int tb = opaque(int(threadIdx.x) * kVec);
+    const int tb = opaque(group_elem(h, 0));
     u32x4 tmp[kZL];
 #pragma unroll
     for (int g = 0; g < kZL; ++g) tmp[g] = load_z<kVecOk>(z, V, tb + g * kTile);
@@ -359,7 +437,7 @@ __device__ __forceinline__ void row_body(const Args& a) {
     for (int g = 0; g < kZL; ++g) zl[g][threadIdx.x] = tmp[g];
   }
 
-  // 2. statistics
+  // 2. half statistics, swapped with the other half
   float m = -INFINITY;
 #pragma unroll
   for (int g = 0; g < kZG; ++g) m = grp_max(zg.get(g), m);
@@ -370,14 +448,28 @@ __device__ __forceinline__ void row_body(const Args& a) {
 #pragma unroll
   for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(zg.get(g), nm0);
   launder(zg);
-  const RowStats rs = finish_stats(m, l, sh);
+  l = block_sum1(l, sh);
+  if (threadIdx.x == 0) {
+    uint32_t lo, hi;
+    f64_words(l, lo, hi);
+    tag_store(slot + 0, tag, __float_as_uint(m));
+    tag_store(slot + 1, tag, lo);
+    tag_store(slot + 2, tag, hi);
+  }
+  if (!poll_slots(a.words + row * 2 * kSlotWords, 2, 0, kStatWords, tag, a.spin_limit, sh)) {
+    if (threadIdx.x == 0) tag_store(a.unfinished + row, tag, 1u);
+    return;
+  }
+  const RowStats rs =
+      combine_halves(__uint_as_float(sh.words[0]), word_f64(sh.words, 1),
+                     __uint_as_float(sh.words[kSlotWords]), word_f64(sh.words, kSlotWords + 1));
 
-  // 3. one pass over p
+  // 3. one pass over this half of p
   double al = 0.0, sb = 0.0, sa = 0.0;
   uint32_t mask[kMaskWords];
 #pragma unroll
   for (int w = 0; w < kMaskWords; ++w) mask[w] = 0u;
-  const int tbp = opaque(int(threadIdx.x) * kVec);
+  const int tbp = opaque(group_elem(h, 0));
 #pragma unroll
   for (int g0 = 0; g0 < kZG; g0 += kPBatch) {
     u32x4 pa[kPBatch], pb[kPBatch];
@@ -397,108 +489,173 @@ __device__ __forceinline__ void row_body(const Args& a) {
   launder(zg);
   block_sum3(al, sb, sa, sh);
 
-  // 4. exchange within the branch
+  // 4. the branch's parts
   if (threadIdx.x == 0) {
-    uint64_t* w = a.words + row * kWords;
     const double v[3] = {al, sb, sa};
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
-      const uint64_t bits = uint64_t(__double_as_longlong(v[i]));
-      tag_store(w + 2 * i, tag, uint32_t(bits));
-      tag_store(w + 2 * i + 1, tag, uint32_t(bits >> 32));
+      uint32_t lo, hi;
+      f64_words(v[i], lo, hi);
+      tag_store(slot + 4 + 2 * i, tag, lo);
+      tag_store(slot + 5 + 2 * i, tag, hi);
     }
-    tag_store(w + 6, tag, __float_as_uint(rs.nm));
-    tag_store(w + 7, tag, __float_as_uint(rs.inv_l));
   }
-  uint64_t* src = a.words + size_t(n) * W * kWords;
-  const int nw = W * kWords;
-  for (int i = threadIdx.x; i < nw; i += kThreads) sh.have[i] = 0;
-  __syncthreads();
-  bool fresh = false;
-  for (int round = 0;; ++round) {
-    int missing = 0;
-    for (int i = threadIdx.x; i < nw; i += kThreads) {
-      if (!sh.have[i]) {
-        const uint64_t w = tag_load(src + i);
-        if (uint32_t(w >> 32) == tag) {
-          sh.words[i] = uint32_t(w);
-          sh.have[i] = 1;
-        } else {
-          missing = 1;
-        }
-      }
-    }
-    if (!__syncthreads_or(missing)) {
-      fresh = true;
-      break;
-    }
-    if (round >= a.spin_limit) break;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  if (!fresh) {
-    // Rare: the rest of the branch did not arrive within the spin limit
-    // (its rows may not be resident yet). Leave this row to the repair
-    // launch, which runs after every row has published its words.
+  if (!poll_slots(a.words + size_t(n) * W * 2 * kSlotWords, 2 * W, 4, kPartWords, tag,
+                  a.spin_limit, sh)) {
     if (threadIdx.x == 0) tag_store(a.unfinished + row, tag, 1u);
     return;
   }
   branch_scalars(a, n, j, row, sh);
   const float c_below = float(sh.coef[0]);
   const float c_above = float(sh.coef[1]);
-  // 5. dz from the held row and the mask
+
+  // 5. dz of this half from the held copy and the mask
   uint16_t* dz = a.dz + row * V;
-  const int tbd = opaque(int(threadIdx.x) * kVec);
+  const int tbd = opaque(group_elem(h, 0));
 #pragma unroll
   for (int g = 0; g < kZG; ++g) {
-    dz_group<kVecOk>(zg.get(g), mask, g, opaque(tbd) + g * kTile, V, rs, c_below, c_above, dz);
+    dz_group<kVecOk>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, rs, c_below,
+                     c_above, dz);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Rows a workgroup left unfinished in this call (see above): every row has
-// published its words by now, so the branch scalars are at hand; z and p
-// are read again to form the mask and dz with the same per-group steps.
+// ------------------------------------------------------------------ repair
+
+// Statistics of half h of a row, streamed from memory (same steps and
+// reductions as a half workgroup).
+template <bool kVecOk>
+__device__ __forceinline__ HalfStats stream_half_stats(const uint16_t* z, int V, int h,
+                                                       Shared& sh) {
+  float m = -INFINITY;
+#pragma unroll 1
+  for (int g = 0; g < kZG; ++g) m = grp_max(load_z<kVecOk>(z, V, group_elem(h, g)), m);
+  m = block_max(m, sh);
+  const float nm0 = (m == -INFINITY) ? 0.f : -(m * kL2E);
+  double l = 0.0;
+#pragma unroll 1
+  for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(load_z<kVecOk>(z, V, group_elem(h, g)), nm0);
+  l = block_sum1(l, sh);
+  return HalfStats{m, l};
+}
+
+// Parts of half h of a row, streamed from memory.
+template <bool kVecOk>
+__device__ __forceinline__ void stream_half_parts(const uint16_t* z, const float* p, int V, int h,
+                                                  const RowStats& rs, double& al, double& sb,
+                                                  double& sa, Shared& sh) {
+  al = sb = sa = 0.0;
+#pragma unroll 1
+  for (int g = 0; g < kZG; ++g) {
+    const int e = group_elem(h, g);
+    u32x4 pa, pb;
+    load_p<kVecOk>(p, V, e, pa, pb);
+    (void)grp_overlap(load_z<kVecOk>(z, V, e), pa, pb, rs.nm, rs.inv_l, al, sb, sa);
+  }
+  block_sum3(al, sb, sa, sh);
+}
+
+// Rows a half left unfinished in this call. Every workgroup has stopped, so
+// every word that will ever be published is there; what is missing is
+// recomputed from the inputs with the same steps and reductions. Then both
+// halves' dz are written (the mask recomputed from z and p).
 template <bool kVecOk>
 __device__ __forceinline__ void repair_body(const Args& a) {
   __shared__ Shared sh;
+  __shared__ uint32_t bw[LVTV_MAX_W * 2 * kSlotWords];  // the branch's words
   const int W = a.W, V = a.V;
   const uint32_t tag = tag_from_epoch(read_epoch(a.ctl));
-  const size_t rows = size_t(a.N) * W;
-  for (size_t row = blockIdx.x; row < rows; row += gridDim.x) {
+  const int rows = a.N * W;
+  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
     if (uint32_t(tag_load(a.unfinished + row) >> 32) != tag) continue;
-    const int n = int(row / W), j = int(row - size_t(n) * W);
-    uint64_t* src = a.words + size_t(n) * W * kWords;
-    for (int i = threadIdx.x; i < W * kWords; i += kThreads) sh.words[i] = uint32_t(tag_load(src + i));
+    const int n = row / W, j = row - n * W;
+    // the branch's published words (stale ones recomputed below)
+    uint64_t* base = a.words + size_t(n) * W * 2 * kSlotWords;
+    for (int i = threadIdx.x; i < W * 2 * kSlotWords; i += kThreads)
+      bw[i] = uint32_t(tag_load(base + i));
     __syncthreads();
-    RowStats rs;
-    rs.nm = __uint_as_float(sh.words[j * kWords + 6]);
-    rs.inv_l = __uint_as_float(sh.words[j * kWords + 7]);
-    branch_scalars(a, n, j, row, sh);
+    for (int s = threadIdx.x; s < 2 * W; s += kThreads) {
+      bool st = true, pt = true;
+      for (int k = 0; k < kStatWords; ++k)
+        st &= uint32_t(tag_load(base + s * kSlotWords + k) >> 32) == tag;
+      for (int k = 4; k < 4 + kPartWords; ++k)
+        pt &= uint32_t(tag_load(base + s * kSlotWords + k) >> 32) == tag;
+      sh.have[s] = uint8_t((st ? 1 : 0) | (pt ? 2 : 0));
+    }
+    __syncthreads();
+    for (int k = 0; k < W; ++k) {
+      const size_t rk = size_t(n) * W + k;
+      const uint16_t* zk = a.z + rk * V;
+      const float* pk = a.p + rk * V;
+      // statistics of both halves
+      for (int hh = 0; hh < 2; ++hh) {
+        const int s = 2 * k + hh;
+        if (!(sh.have[s] & 1)) {
+          const HalfStats hs = stream_half_stats<kVecOk>(zk, V, hh, sh);
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            uint32_t lo, hi;
+            f64_words(hs.l, lo, hi);
+            bw[s * kSlotWords + 0] = __float_as_uint(hs.m);
+            bw[s * kSlotWords + 1] = lo;
+            bw[s * kSlotWords + 2] = hi;
+          }
+          __syncthreads();
+        }
+      }
+      const RowStats rs = combine_halves(
+          __uint_as_float(bw[(2 * k) * kSlotWords]), word_f64(bw, (2 * k) * kSlotWords + 1),
+          __uint_as_float(bw[(2 * k + 1) * kSlotWords]), word_f64(bw, (2 * k + 1) * kSlotWords + 1));
+      for (int hh = 0; hh < 2; ++hh) {
+        const int s = 2 * k + hh;
+        if (!(sh.have[s] & 2)) {
+          double x, y, w;
+          stream_half_parts<kVecOk>(zk, pk, V, hh, rs, x, y, w, sh);
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            const double v[3] = {x, y, w};
+            for (int i = 0; i < 3; ++i) {
+              uint32_t lo, hi;
+              f64_words(v[i], lo, hi);
+              bw[s * kSlotWords + 4 + 2 * i] = lo;
+              bw[s * kSlotWords + 5 + 2 * i] = hi;
+            }
+          }
+          __syncthreads();
+        }
+      }
+    }
+    for (int i = threadIdx.x; i < W * 2 * kSlotWords; i += kThreads) sh.words[i] = bw[i];
+    __syncthreads();
+    branch_scalars(a, n, j, size_t(row), sh);
     const float c_below = float(sh.coef[0]);
     const float c_above = float(sh.coef[1]);
-    const uint16_t* z = a.z + row * V;
-    const float* p = a.p + row * V;
-    uint16_t* dz = a.dz + row * V;
-#pragma unroll
-    for (int g = 0; g < kZG; ++g) {
-      const int e = group_elem(g);
-      const u32x4 zv = load_z<kVecOk>(z, V, e);
-      u32x4 pa, pb;
-      load_p<kVecOk>(p, V, e, pa, pb);
-      double x = 0.0, y = 0.0, w = 0.0;
-      uint32_t m1[kMaskWords];
-#pragma unroll
-      for (int i = 0; i < kMaskWords; ++i) m1[i] = 0u;
-      m1[(g * kVec) / 32] = grp_overlap(zv, pa, pb, rs.nm, rs.inv_l, x, y, w) << ((g * kVec) % 32);
-      dz_group<kVecOk>(zv, m1, g, e, V, rs, c_below, c_above, dz);
+    const RowStats rs = combine_halves(
+        __uint_as_float(bw[(2 * j) * kSlotWords]), word_f64(bw, (2 * j) * kSlotWords + 1),
+        __uint_as_float(bw[(2 * j + 1) * kSlotWords]), word_f64(bw, (2 * j + 1) * kSlotWords + 1));
+    const uint16_t* z = a.z + size_t(row) * V;
+    const float* p = a.p + size_t(row) * V;
+    uint16_t* dz = a.dz + size_t(row) * V;
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll 1
+      for (int g = 0; g < kZG; ++g) {
+        const int e = group_elem(hh, g);
+        const u32x4 zv = load_z<kVecOk>(z, V, e);
+        u32x4 pa, pb;
+        load_p<kVecOk>(p, V, e, pa, pb);
+        double x = 0.0, y = 0.0, w = 0.0;
+        const uint32_t bits = grp_overlap(zv, pa, pb, rs.nm, rs.inv_l, x, y, w);
+        dz_group<kVecOk>(zv, bits, e, V, rs, c_below, c_above, dz);
+      }
     }
     __syncthreads();
   }
 }
 
 template <bool kVecOk>
-__global__ __launch_bounds__(kThreads) void loss_rows(Args a) {
-  row_body<kVecOk>(a);
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
+loss_halves(Args a) {
+  half_body<kVecOk>(a);
 }
 
 template <bool kVecOk>
@@ -507,8 +664,7 @@ __global__ __launch_bounds__(kThreads) void loss_repair(Args a) {
 }
 
 // Mean of the branch losses in a fixed order; then the call epoch advances
-// (every row workgroup of this call has finished: it ran before this
-// launch).
+// (every workgroup of this call has finished: they ran before this launch).
 __global__ __launch_bounds__(256) void loss_reduce(Args a) {
   __shared__ double sd[256 / kWave];
   const int per = (a.N + 255) / 256;
@@ -537,7 +693,7 @@ Layout make_layout(int N, int W) {
   Layout L;
   size_t off = kReservedBytes;
   L.off_words = off;
-  off = align256(off + sizeof(uint64_t) * size_t(N) * W * kWords);
+  off = align256(off + sizeof(uint64_t) * size_t(N) * W * 2 * kSlotWords);
   L.off_unfinished = off;
   off = align256(off + sizeof(uint64_t) * size_t(N) * W);
   L.off_branch = off;
@@ -549,7 +705,7 @@ Layout make_layout(int N, int W) {
 }  // namespace
 
 bool applicable(int N, int W, int V) {
-  return V <= kMaxV && size_t(N) * W < (size_t(1) << 31);
+  return V <= kMaxV && size_t(N) * W * 2 < (size_t(1) << 31);
 }
 
 size_t workspace_bytes(int N, int W, int V) {
@@ -574,14 +730,14 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   a.words = reinterpret_cast<uint64_t*>(ws + L.off_words);
   a.unfinished = reinterpret_cast<uint64_t*>(ws + L.off_unfinished);
   a.branch_loss = reinterpret_cast<double*>(ws + L.off_branch);
-  const unsigned grid = unsigned(size_t(c.N) * c.W);
+  const unsigned rows = unsigned(size_t(c.N) * c.W);
   if (c.vec_ok)
-    hipLaunchKernelGGL(loss_rows<true>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(loss_halves<true>, dim3(2 * rows), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(loss_rows<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(loss_halves<false>, dim3(2 * rows), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned rgrid = grid < 256u ? grid : 256u;
+  const unsigned rgrid = rows < 256u ? rows : 256u;
   if (c.vec_ok)
     hipLaunchKernelGGL(loss_repair<true>, dim3(rgrid), dim3(kThreads), 0, stream, a);
   else
