@@ -23,11 +23,11 @@
 //      (G_j/N) S'_j q(u) where the bit is set and -(G_j/N) S_j q(u) elsewhere,
 //      rounded to bf16 (nearest even) and written once.
 // Every wait is bounded: a half that gives up marks its row unfinished and
-// stops. A repair launch, which runs once every workgroup has finished,
-// completes such rows from the published words, recomputing whatever is
-// missing with the same per-group steps and reductions (bit-identical). A
-// last launch averages the branch losses in a fixed order and advances the
-// workspace's call epoch.
+// stops. The call's last launch, one workgroup that runs once every half has
+// finished, completes such rows from the published words, recomputing
+// whatever is missing with the same per-group steps and reductions
+// (bit-identical); it then averages the branch losses in a fixed order and
+// advances the workspace's call epoch.
 //
 // Definition (page title, section): "SpecOPD: Branch-Parallel On-Policy
 // Distillation for Speculative Decoding", prerequisite on acceptance length
@@ -40,6 +40,7 @@
 // dq(v)/dz(u) = q(v)(delta_uv - q(u)).
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstddef>
 #include <cstdint>
 
@@ -81,7 +82,7 @@ struct Args {
   float* loss;
   FusedCtl* ctl;
   uint64_t* words;       // [N][W][2][kSlotWords] tagged words
-  uint64_t* unfinished;  // [N][W] tagged: the row's dz is left to the repair launch
+  uint64_t* unfinished;  // [N][W] tagged: the row is left to the last launch
   double* branch_loss;   // [N]
 };
 
@@ -189,6 +190,7 @@ struct Shared {
   uint32_t words[LVTV_MAX_W * 2 * kSlotWords];
   uint8_t have[LVTV_MAX_W * 2 * kSlotWords];
   double coef[2];
+  int imin[kWaves];
 };
 
 __device__ __forceinline__ float block_max(float v, Shared& sh) {
@@ -226,7 +228,7 @@ __device__ __forceinline__ void block_sum3(double& a, double& b, double& c, Shar
 
 // ------------------------------------------------------------------ per-group steps
 //
-// Shared by the workgroups and the repair launch, so both give the same bits
+// Shared by the workgroups and the last launch, so both give the same bits
 // (same element order, same reduction tree).
 
 __device__ __forceinline__ float grp_max(const u32x4& g, float m) {
@@ -252,8 +254,8 @@ __device__ __forceinline__ uint32_t grp_overlap(const u32x4& g, const u32x4& pa,
   for (int j = 0; j < kVec; ++j) {
     const float q = qval(zelem(g, j), nm, inv_l);
     const float p = pelem(pa, pb, j);
-    a += fminf(q, p);
     const bool below = q < p;
+    a += below ? q : p;
     b += below ? q : 0.f;
     c += below ? 0.f : q;
     bits |= below ? (1u << j) : 0u;
@@ -279,7 +281,7 @@ __device__ __forceinline__ double block_sum1(double v, Shared& sh) {
 
 // Row statistics from the two halves' statistics, half 0 first: M = max,
 // L = sum_h l_h 2^((m_h - M) log2 e) in fp64 (a half of maximum -inf weighs
-// l_h * 0, which keeps a NaN). Both halves and the repair launch call this
+// l_h * 0, which keeps a NaN). Both halves and the last launch call this
 // with the same values, so they agree bit for bit.
 struct RowStats {
   float nm;     // -M log2 e (0 when M = -inf)
@@ -555,19 +557,16 @@ __device__ __forceinline__ void stream_half_parts(const uint16_t* z, const float
   block_sum3(al, sb, sa, sh);
 }
 
-// Rows a half left unfinished in this call. Every workgroup has stopped, so
-// every word that will ever be published is there; what is missing is
-// recomputed from the inputs with the same steps and reductions. Then both
-// halves' dz are written (the mask recomputed from z and p).
+// A row a half left unfinished in this call. Every half workgroup has
+// stopped, so every word that will ever be published is there; what is
+// missing is recomputed from the inputs with the same steps and reductions.
+// Then both halves' dz are written (the mask recomputed from z and p). Every
+// thread of the block calls it.
 template <bool kVecOk>
-__device__ __forceinline__ void repair_body(const Args& a) {
-  __shared__ Shared sh;
-  __shared__ uint32_t bw[LVTV_MAX_W * 2 * kSlotWords];  // the branch's words
+__device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag, Shared& sh,
+                                           uint32_t* bw) {
   const int W = a.W, V = a.V;
-  const uint32_t tag = tag_from_epoch(read_epoch(a.ctl));
-  const int rows = a.N * W;
-  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
-    if (uint32_t(tag_load(a.unfinished + row) >> 32) != tag) continue;
+  {
     const int n = row / W, j = row - n * W;
     // the branch's published words (stale ones recomputed below)
     uint64_t* base = a.words + size_t(n) * W * 2 * kSlotWords;
@@ -658,28 +657,57 @@ loss_halves(Args a) {
   half_body<kVecOk>(a);
 }
 
-template <bool kVecOk>
-__global__ __launch_bounds__(kThreads) void loss_repair(Args a) {
-  repair_body<kVecOk>(a);
+__device__ __forceinline__ int block_min(int v, Shared& sh) {
+  v = wmin(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) sh.imin[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int r = sh.imin[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = min(r, sh.imin[w]);
+  return r;
 }
 
-// Mean of the branch losses in a fixed order; then the call epoch advances
-// (every workgroup of this call has finished: they ran before this launch).
-__global__ __launch_bounds__(256) void loss_reduce(Args a) {
-  __shared__ double sd[256 / kWave];
-  const int per = (a.N + 255) / 256;
+// The call's last launch, one workgroup; every half workgroup has stopped.
+// (1) Rows a half left unfinished are completed, in row order: the flags of
+// up to 32 rows per thread are read at once, so the usual case (no flag) costs
+// one round of loads. (2) The loss is the mean of the branch losses, summed
+// in a fixed order. (3) The call epoch advances.
+template <bool kVecOk>
+__global__ __launch_bounds__(kThreads) void loss_finish(Args a) {
+  __shared__ Shared sh;
+  __shared__ uint32_t bw[LVTV_MAX_W * 2 * kSlotWords];  // a branch's words
+  __shared__ double sd[kWaves];
+  const uint32_t tag = tag_from_epoch(read_epoch(a.ctl));
+  const int rows = a.N * a.W;
+  for (int r0 = 0; r0 < rows; r0 += kThreads * 32) {
+    uint32_t mine = 0;  // bit i: row r0 + tid + i * kThreads is flagged
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+      const int row = r0 + int(threadIdx.x) + i * kThreads;
+      if (row < rows && uint32_t(tag_load(a.unfinished + row) >> 32) == tag) mine |= 1u << i;
+    }
+    while (__syncthreads_or(mine != 0)) {
+      const int cand = mine ? r0 + int(threadIdx.x) + __builtin_ctz(mine) * kThreads : INT_MAX;
+      const int row = block_min(cand, sh);
+      if (cand == row) mine &= mine - 1u;
+      repair_row<kVecOk>(a, row, tag, sh, bw);
+    }
+  }
+  const int per = (a.N + kThreads - 1) / kThreads;
   double x = 0.0;
   for (int n = threadIdx.x * per; n < min(a.N, (int(threadIdx.x) + 1) * per); ++n)
     x += a.branch_loss[n];
   x = wsum(x);
+  __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sd[threadIdx.x / kWave] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
     double t = 0.0;
-    for (int w = 0; w < 256 / kWave; ++w) t += sd[w];
+    for (int w = 0; w < kWaves; ++w) t += sd[w];
     a.loss[0] = float(t / double(a.N));
-    const uint32_t e = read_epoch(a.ctl);
-    __hip_atomic_store(&a.ctl->epoch, e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.ctl->epoch, read_epoch(a.ctl) + 1, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -737,14 +765,10 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
     hipLaunchKernelGGL(loss_halves<false>, dim3(2 * rows), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned rgrid = rows < 256u ? rows : 256u;
   if (c.vec_ok)
-    hipLaunchKernelGGL(loss_repair<true>, dim3(rgrid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(loss_finish<true>, dim3(1), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(loss_repair<false>, dim3(rgrid), dim3(kThreads), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(loss_reduce, dim3(1), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(loss_finish<false>, dim3(1), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
