@@ -54,11 +54,12 @@ def loss_bytes(n, w, vocab):
     return 8 * n * w * vocab
 
 
-def cpu_baseline(verify_cases, loss_case, n_verify_req=64, n_branches=96):
+def cpu_baseline(verify_cases, loss_case, verify_passes=2, n_branches=LOSS_N):
     """Time the fp64 oracle, as it stands, on a bounded sample of the same
-    workload (about 15 s of CPU work): every request of each temperature's
-    verify inputs and the first branches of the loss inputs. Single process,
-    one thread (numpy elementwise work is single-threaded)."""
+    workload (10-15 s of CPU work on the GPU host): every request of each
+    temperature's verify inputs, `verify_passes` times, and the first
+    `n_branches` branches of the loss inputs. Single process, one thread
+    (numpy elementwise work is single-threaded)."""
     sys.path.insert(0, ROOT)
     from oracle import bf16 as obf16
     from oracle import loss as ol
@@ -66,13 +67,14 @@ def cpu_baseline(verify_cases, loss_case, n_verify_req=64, n_branches=96):
 
     rows_v = 0
     t0 = time.perf_counter()
-    for case in verify_cases:
-        for b in range(n_verify_req):
-            ov.verify_request(ov.decode_rows(case.target[b], case.dtype),
-                              ov.decode_rows(case.draft[b], case.dtype), case.tokens[b],
-                              case.k[b], case.temperature[b], int(case.seed[b]), b,
-                              case.shape[1])
-            rows_v += int(case.k[b]) + 1
+    for _ in range(verify_passes):
+        for case in verify_cases:
+            for b in range(case.shape[0]):
+                ov.verify_request(ov.decode_rows(case.target[b], case.dtype),
+                                  ov.decode_rows(case.draft[b], case.dtype), case.tokens[b],
+                                  case.k[b], case.temperature[b], int(case.seed[b]), b,
+                                  case.shape[1])
+                rows_v += int(case.k[b]) + 1
     t_v = time.perf_counter() - t0
     t0 = time.perf_counter()
     for n in range(n_branches):
@@ -87,10 +89,10 @@ def cpu_baseline(verify_cases, loss_case, n_verify_req=64, n_branches=96):
         "unit": "vocab-rows/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"{n_verify_req} requests x {len(verify_cases)} temperatures of the "
-                   f"verify workload ({rows_v} vocab-rows, {t_v:.1f} s) and {n_branches} "
-                   f"branches of the loss workload ({rows_l} vocab-rows, {t_l:.1f} s), "
-                   f"fp64 numpy, one process; scaled to the step's row mix"),
+        "sample": (f"{verify_passes} passes over all requests x {len(verify_cases)} "
+                   f"temperatures of the verify workload ({rows_v} vocab-rows, {t_v:.1f} s) "
+                   f"and {n_branches} branches of the loss workload ({rows_l} vocab-rows, "
+                   f"{t_l:.1f} s), fp64 numpy, one process; scaled to the step's row mix"),
         "verify_rows_per_s": rows_v / t_v,
         "loss_rows_per_s": rows_l / t_l,
         "host_cpus": os.cpu_count(),
@@ -252,7 +254,7 @@ def main():
         },
         "achieved_hbm_gbs": (len(TEMPS) * vb + lb) / (ms_step * 1e-3) / 1e9,
         "roofline": {
-            "kernel": "loss_rows (e2e_tv_loss_fwd_bwd)",
+            "kernel": "loss_halves (e2e_tv_loss_fwd_bwd)",
             "bound": "hbm",
             "achieved": loss_gbs,
             "peak": HBM_PEAK_GBS,

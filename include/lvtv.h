@@ -73,11 +73,12 @@ const char* lvtv_strerror(int code);
 
 /*
  * Zero-fill a workspace on `stream` (a plain fill kernel, so it may sit in a
- * captured graph). A workspace must be zero-filled once before its first
- * use: the single-read kernels keep a call counter and per-request counters
- * there and leave them ready for the next call, so later calls need no
- * reset. Returns LVTV_ERR_NULL / LVTV_ERR_WORKSPACE (misaligned) before
- * enqueueing anything.
+ * captured graph). e2e_tv_loss_fwd_bwd needs this once before a workspace's
+ * first use: it keeps a call epoch there and tags the words its workgroups
+ * exchange with it, so that a later call (of any shape, either op) never
+ * takes an earlier call's word for its own and needs no reset. spec_verify
+ * does not depend on the contents. Returns LVTV_ERR_NULL /
+ * LVTV_ERR_WORKSPACE (misaligned) before enqueueing anything.
  */
 int lvtv_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
@@ -167,7 +168,10 @@ size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V);
  *   alpha          float [N, W] out.
  *   dlogits        bfloat16 (uint16) [N, W, V] out.
  *   workspace      device scratch of >= e2e_tv_loss_workspace_bytes(...)
- *                  bytes, 256-byte aligned, no initialisation needed.
+ *                  bytes, 256-byte aligned, zero-filled once before its
+ *                  first use (lvtv_workspace_reset); after that it needs no
+ *                  reset between calls of any shape. Calls sharing a
+ *                  workspace must be ordered on one stream.
  *   stream         hipStream_t.
  * NaN or infinite inputs propagate into the outputs; there is no status.
  */

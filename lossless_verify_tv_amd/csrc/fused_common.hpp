@@ -10,17 +10,16 @@
 //
 // Calls are told apart by an epoch counter in the workspace control block;
 // the tag is derived from it and is never 0, so a zero-filled workspace
-// holds no fresh word. The last unit of work to complete in a call (a
-// request of the verify step, a branch of the loss) bumps the epoch and
-// clears the completion counter; everything else a call leaves behind is
-// either tagged or reset by its own last user. The workspace must therefore
-// be zero-filled once before its first use (lvtv_workspace_reset).
+// holds no fresh word. The call's last launch advances the epoch, so the
+// next call's tag differs and nothing a call leaves behind is ever taken for
+// fresh. The workspace must therefore be zero-filled once before its first
+// use (lvtv_workspace_reset).
 //
 // Every wait is bounded: a workgroup that polls a word for `spin_limit`
-// rounds without seeing it gives up and recomputes the missing value from
-// the inputs with the same function (same element order, same reduction
-// tree) its producer uses, so the result is bit-identical either way and no
-// schedule of workgroups can deadlock.
+// rounds without seeing it gives up, and the missing values are recomputed
+// from the inputs with the same functions (same element order, same
+// reduction tree) their producers use, so the result is bit-identical either
+// way and no schedule of workgroups can deadlock.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,17 +31,15 @@ namespace lvtv {
 
 struct FusedCtl {
   uint32_t epoch;  // bumped once per completed call
-  uint32_t done;   // completed units in the running call
+  uint32_t unused;
   uint32_t pad[62];
 };
 static_assert(sizeof(FusedCtl) == 256, "control block is one 256-byte line");
 
 // Every workspace starts with a region of fixed layout, whatever the call's
-// shapes: the control block, then one arrival counter per unit of work (a
-// request or a branch; at most 65535 of them). Counters return to zero by the
-// end of each call, so the region stays valid across calls of any shape;
-// the shape-dependent arrays (tagged words, or the two-read pipeline's
-// partial sums) come after it.
+// shapes: the control block, then room for one 32-bit counter per unit of
+// work (a request or a branch; the current kernels keep none there). The
+// shape-dependent arrays (tagged words, partial sums) come after it.
 constexpr int kMaxUnits = 65536;
 constexpr size_t kReservedBytes = sizeof(FusedCtl) + sizeof(uint32_t) * size_t(kMaxUnits);
 static_assert(kReservedBytes % 256 == 0, "reserved region keeps 256-byte alignment");
@@ -67,34 +64,6 @@ __device__ __forceinline__ void tag_store(uint64_t* p, uint32_t tag, uint32_t bi
 
 __device__ __forceinline__ uint64_t tag_load(uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Block-wide poll of n consecutive tagged words. Payloads land in `dst`,
-// `have[i]` says whether word i was seen fresh. Returns true when all were.
-// Every thread of the block must call it.
-__device__ __forceinline__ bool poll_tagged(uint64_t* src, int n, uint32_t tag, uint32_t* dst,
-                                            uint8_t* have, int spin_limit) {
-  for (int i = threadIdx.x; i < n; i += kBlock) have[i] = 0;
-  __syncthreads();
-  int round = 0;
-  while (true) {
-    int missing = 0;
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-      if (!have[i]) {
-        const uint64_t w = tag_load(src + i);
-        if (uint32_t(w >> 32) == tag) {
-          dst[i] = uint32_t(w);
-          have[i] = 1;
-        } else {
-          missing = 1;
-        }
-      }
-    }
-    const int any = __syncthreads_or(missing);
-    if (!any) return true;
-    if (++round > spin_limit) return false;
-    __builtin_amdgcn_s_sleep(2);
-  }
 }
 
 // Nontemporal 16-byte vector loads/stores: streamed data is read once.
