@@ -11,11 +11,13 @@ import pytest
 
 import oracle.bf16
 import oracle.loss
+import oracle.objectives
 import oracle.philox
 import oracle.verify
 
 from . import test_oracle_bf16 as t_bf16
 from . import test_oracle_loss as t_loss
+from . import test_oracle_objectives as t_obj
 from . import test_oracle_philox as t_philox
 from . import test_oracle_verify as t_verify
 
@@ -79,6 +81,20 @@ CASES = [
      '"loss": total / n_br,', '"loss": total,',
      t_loss, "ol", "test_worked_examples",
      ({"alphas": [0.8, 0.8, 0.8, 0.8], "expected_emitted": 3.3616},)),
+    ("CE gradient drops the sum of p", oracle.objectives,
+     "dz = (q * np.sum(p64, axis=1, keepdims=True) - p64) / n_branches",
+     "dz = (q - p64) / n_branches",
+     t_obj, "ob", "test_gradient_central_differences", ("ce",)),
+    ("KL drops the p log p term", oracle.objectives,
+     "per_pos = ce + np.sum(plogp, axis=1)", "per_pos = ce",
+     t_obj, "ob", "test_kl_vanishes_at_q_equal_p", ()),
+    ("per-step TV gradient sign flipped", oracle.objectives,
+     "dz = np.where(below, -q * s_above, q * s_below) / n_branches",
+     "dz = np.where(below, q * s_above, -q * s_below) / n_branches",
+     t_obj, "ob", "test_gradient_central_differences", ("step_tv",)),
+    ("per-step TV loss sums alpha", oracle.objectives,
+     "loss_n = float(np.sum(1.0 - alpha))", "loss_n = float(np.sum(alpha))",
+     t_obj, "ob", "test_step_tv_is_half_l1_and_matches_e2e_at_one_position", ()),
     ("Philox key not bumped between rounds", oracle.philox,
      "k0 = (k0 + _WEYL_A) & _MASK64", "k0 = k0",
      t_philox, "philox", "test_block_matches_numpy_random_counters", ()),
