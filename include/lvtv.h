@@ -55,6 +55,14 @@ extern "C" {
 #define LVTV_ERR_DTYPE (-3)     /* unknown dtype                         */
 #define LVTV_ERR_WORKSPACE (-4) /* workspace NULL or smaller than queried */
 #define LVTV_ERR_LAUNCH (-5)    /* the HIP runtime rejected a launch     */
+#define LVTV_ERR_OBJECTIVE (-6) /* unknown loss objective                */
+
+/* Objectives of draft_loss_fwd_bwd, each summed over a branch's W positions
+ * and averaged over the N branches. */
+#define LVTV_OBJ_E2E_TV 0  /* -sum_j prod_{k<=j} alpha_k (e2e_tv_loss_fwd_bwd) */
+#define LVTV_OBJ_STEP_TV 1 /* sum_j (1 - alpha_j), the per-step TV loss      */
+#define LVTV_OBJ_CE 2      /* sum_j -sum_v p log q, cross-entropy            */
+#define LVTV_OBJ_KL 3      /* sum_j sum_v p log(p / q), KL(p || q)           */
 
 /* Supported ranges. */
 #define LVTV_MAX_K 16         /* draft positions per request (Kmax)      */
@@ -179,6 +187,44 @@ int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
                         int32_t N, int32_t W, int32_t V, float* loss,
                         float* alpha, uint16_t* dlogits, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes draft_loss_fwd_bwd needs (0 if out of range; the same as
+ * e2e_tv_loss_workspace_bytes). Host only.
+ */
+size_t draft_loss_workspace_bytes(int32_t N, int32_t W, int32_t V);
+
+/*
+ * draft_loss_fwd_bwd -- the E2E-TV loss or one of the per-position
+ * objectives the pages set against it, with the gradient with respect to
+ * the draft logits ("Reading Qwen Bebop and DeepSeek DSpark", section
+ * "Bebop's solution": CE = -sum_y p log q, KL(p || q) = sum_y p log(p / q),
+ * L_TV = d_TV(p, q) = 1 - sum_y min(p, q); the "SpecOPD" summary's ablation,
+ * Figure 8, compares the E2E-TV objective with CE).
+ *
+ *   objective      LVTV_OBJ_*: per branch n the loss is summed over the W
+ *                  positions, loss = (1/N) sum_n L_n:
+ *                    E2E_TV   L_n = -sum_j prod_{k<=j} alpha_{n,k} (exactly
+ *                             e2e_tv_loss_fwd_bwd);
+ *                    STEP_TV  L_n = sum_k (1 - alpha_{n,k});
+ *                    CE       L_n = sum_k -sum_v p log q_{n,k}(v);
+ *                    KL       L_n = sum_k sum_v p log(p / q_{n,k}(v)),
+ *                             p log p = 0 where p = 0.
+ *                  Gradients: STEP_TV as E2E_TV with dL_n/dalpha_k = -1;
+ *                  CE and KL: dlogits[n,k,u] = (q(u) sum_v p(v) - p(u)) / N.
+ *   alpha          float [N, W] out: alpha_{n,k} = sum_v min(q, p) for every
+ *                  objective.
+ *   Other arguments, layouts, workspace rules and errors as for
+ *   e2e_tv_loss_fwd_bwd; an unknown objective returns LVTV_ERR_OBJECTIVE
+ *   before enqueueing anything.
+ * The TV objectives run the single-read kernel when V <= 155648 (one read of
+ * z and p, one write of dz); CE and KL run the multi-pass pipeline (z read
+ * three times, p twice).
+ */
+int draft_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
+                       int32_t N, int32_t W, int32_t V, int objective,
+                       float* loss, float* alpha, uint16_t* dlogits,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

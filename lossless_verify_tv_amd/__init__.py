@@ -4,7 +4,7 @@ AMD MI355X (gfx950).
 The work runs in hand-written HIP kernels behind a C ABI (``include/lvtv.h``,
 ``liblvtv.so``). This package holds the kernels and the ABI
 (``csrc/``), the build script (``build``), a thin ctypes binding
-(``spec_verify``, ``e2e_tv_loss_fwd_bwd``) and the seeded synthetic input
+(``spec_verify``, ``e2e_tv_loss_fwd_bwd``, ``draft_loss_fwd_bwd``) and the seeded synthetic input
 generators (``synth``).
 
 The binding loads the library lazily, on first call, and raises if it is
@@ -19,7 +19,10 @@ from ._binding import (  # noqa: F401
     STATUS_BAD_TEMPERATURE,
     STATUS_BAD_TOKEN,
     STATUS_NONFINITE,
+    OBJECTIVES,
     LvtvError,
+    draft_loss_fwd_bwd,
+    draft_loss_workspace_bytes,
     e2e_tv_loss_fwd_bwd,
     e2e_tv_loss_workspace_bytes,
     load_library,

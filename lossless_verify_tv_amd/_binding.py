@@ -34,7 +34,12 @@ EXPORTS = (
     "spec_verify",
     "e2e_tv_loss_workspace_bytes",
     "e2e_tv_loss_fwd_bwd",
+    "draft_loss_workspace_bytes",
+    "draft_loss_fwd_bwd",
 )
+
+# Objectives of draft_loss_fwd_bwd (include/lvtv.h, LVTV_OBJ_*).
+OBJECTIVES = {"e2e_tv": 0, "step_tv": 1, "ce": 2, "kl": 3}
 
 _lib = None
 _lock = threading.Lock()
@@ -70,6 +75,11 @@ def load_library(path: str = LIB_PATH):
         lib.e2e_tv_loss_workspace_bytes.argtypes = [i32, i32, i32]
         lib.e2e_tv_loss_fwd_bwd.restype = ctypes.c_int
         lib.e2e_tv_loss_fwd_bwd.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        lib.draft_loss_workspace_bytes.restype = sz
+        lib.draft_loss_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.draft_loss_fwd_bwd.restype = ctypes.c_int
+        lib.draft_loss_fwd_bwd.argtypes = [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp,
+                                           sz, vp]
         _lib = lib
         return lib
 
@@ -213,4 +223,41 @@ def e2e_tv_loss_fwd_bwd(draft_logits, target_probs, workspace=None, out=None):
                                        _ptr(loss), _ptr(alpha), _ptr(dlogits), _ptr(ws),
                                        ws.numel(), _stream(dev))
     _check(code, "e2e_tv_loss_fwd_bwd")
+    return loss, alpha, dlogits
+
+
+def draft_loss_workspace_bytes(N, W, V) -> int:
+    return int(load_library().draft_loss_workspace_bytes(N, W, V))
+
+
+def draft_loss_fwd_bwd(draft_logits, target_probs, objective, workspace=None, out=None):
+    """The E2E-TV loss or a per-position comparator (per-step TV, CE, KL) and
+    its gradient (see include/lvtv.h). ``objective`` is a key of OBJECTIVES
+    or its LVTV_OBJ_* value; otherwise as e2e_tv_loss_fwd_bwd."""
+    lib = load_library()
+    obj = OBJECTIVES.get(objective, objective)
+    _require(isinstance(obj, int), f"unknown objective {objective!r}")
+    dev = draft_logits.device
+    _require(dev.type == "cuda", "draft_loss_fwd_bwd needs GPU tensors")
+    _require(draft_logits.dtype == torch.bfloat16, "draft_logits must be bfloat16")
+    _require(target_probs.dtype == torch.float32, "target_probs must be float32")
+    _require(draft_logits.dim() == 3 and tuple(target_probs.shape) == tuple(draft_logits.shape),
+             "draft_logits and target_probs must both be [N, W, V]")
+    for t in (draft_logits, target_probs):
+        _require(t.device == dev and t.is_contiguous(), "inputs must be contiguous on one GPU")
+    N, W, V = draft_logits.shape
+    need = lib.draft_loss_workspace_bytes(N, W, V)
+    _require(need > 0, f"sizes out of range: N={N} W={W} V={V}")
+    ws = workspace if workspace is not None else _workspace("loss", dev, need)
+    if out is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        alpha = torch.empty(N, W, dtype=torch.float32, device=dev)
+        dlogits = torch.empty(N, W, V, dtype=torch.bfloat16, device=dev)
+    else:
+        loss, alpha, dlogits = out
+    with torch.cuda.device(dev):
+        code = lib.draft_loss_fwd_bwd(_ptr(draft_logits), _ptr(target_probs), N, W, V, obj,
+                                      _ptr(loss), _ptr(alpha), _ptr(dlogits), _ptr(ws),
+                                      ws.numel(), _stream(dev))
+    _check(code, "draft_loss_fwd_bwd")
     return loss, alpha, dlogits

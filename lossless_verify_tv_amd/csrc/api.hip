@@ -44,6 +44,7 @@ extern "C" const char* lvtv_strerror(int code) {
     case LVTV_ERR_DTYPE: return "unknown dtype";
     case LVTV_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than required";
     case LVTV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case LVTV_ERR_OBJECTIVE: return "unknown loss objective";
     default: return "unknown error code";
   }
 }

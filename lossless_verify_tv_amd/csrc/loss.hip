@@ -1,4 +1,6 @@
-// e2e_tv_loss_fwd_bwd: E2E-TV prefix-product loss and its gradient on gfx950.
+// e2e_tv_loss_fwd_bwd: E2E-TV prefix-product loss and its gradient on gfx950,
+// and draft_loss_fwd_bwd: the same machinery under the per-position
+// comparators the pages set against it (per-step TV, CE, KL).
 //
 // Definition (page title, section): "SpecOPD: Branch-Parallel On-Policy
 // Distillation for Speculative Decoding", prerequisite "Acceptance length and
@@ -21,6 +23,15 @@
 //   4. reduce     one workgroup: loss = (1/N) sum_n L_n in fixed order.
 //   5. grad       grid (slice, position, branch): dz = q (G/N) S' where q < p,
 //                 -q (G/N) S elsewhere; bfloat16 round-to-nearest-even.
+//
+// Comparators ("Reading Qwen Bebop and DeepSeek DSpark", section "Bebop's
+// solution": CE = -sum p log q, KL(p || q) = sum p log(p / q), per-step
+// L_TV = 1 - sum min(p, q)), each summed over a branch's positions and
+// averaged over branches:
+//   * per-step TV: G = -1 for every position, the rest as above;
+//   * CE and KL: the overlap pass also sums p, p z and (KL) p ln p per row;
+//     CE_k = -sum p z + (M + ln L) sum p (log q = z - M - ln L), KL_k = CE_k +
+//     sum p ln p; dz = q (sum p)/N - p/N, one fused multiply-add.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -37,17 +48,19 @@ namespace lvtv {
 namespace {
 
 constexpr int kSlice = kBlock * kVec * 4;  // 8192 elements per slice
+constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kSteps = kSlice / (kBlock * kVec);
 
 struct RowFinal {
   float neg_m_log2e;  // -M log2(e)
   float inv_l;        // 1 / L
-  float c_below;      // (G/N) S'   applied where q < p
-  float c_above;      // -(G/N) S   applied where q >= p
+  float c_below;      // (G/N) S'   applied where q < p    (CE, KL: (sum p)/N, the weight of q)
+  float c_above;      // -(G/N) S   applied where q >= p   (CE, KL: 1/N, the weight of p)
 };
 
 struct Part {
   double alpha, s_below, s_above;
+  double sp, spz, splp;  // CE and KL: sum p, sum p z, sum p ln p (0 otherwise)
 };
 
 struct Layout {
@@ -78,6 +91,7 @@ struct Args {
   const uint16_t* z;
   const float* p;
   int N, W, V;
+  int objective;  // LVTV_OBJ_*
   bool vec_ok;
   float* loss;
   float* alpha;
@@ -152,7 +166,9 @@ __global__ __launch_bounds__(kBlock) void overlap_kernel(Args a) {
   const float inv_l = float(1.0 / L);
   const uint16_t* z = a.z + row * a.V;
   const float* p = a.p + row * a.V;
-  double al = 0.0, sb = 0.0, sa = 0.0;
+  const bool xent = a.objective == LVTV_OBJ_CE || a.objective == LVTV_OBJ_KL;
+  const bool kl = a.objective == LVTV_OBJ_KL;
+  double al = 0.0, sb = 0.0, sa = 0.0, sp = 0.0, spz = 0.0, splp = 0.0;
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
     const int64_t e = elem_index(s, it);
@@ -171,11 +187,32 @@ __global__ __launch_bounds__(kBlock) void overlap_kernel(Args a) {
     al += a_min;
     sb += a_below;
     sa += a_above;
+    if (xent) {
+      float b_p = 0.f, b_pz = 0.f, b_plp = 0.f;
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        const int64_t v = e + i;
+        // tokens past V read z = -inf and p = 0: they add nothing
+        if (v < a.V) {
+          b_p += xp[i];
+          b_pz += xp[i] * xz[i];
+          if (kl && xp[i] > 0.f) b_plp += xp[i] * logf(xp[i]);
+        }
+      }
+      sp += b_p;
+      spz += b_pz;
+      splp += b_plp;
+    }
   }
   al = block_sum(al, sd);
   sb = block_sum(sb, sd);
   sa = block_sum(sa, sd);
-  if (threadIdx.x == 0) a.part[row * a.L.S + s] = Part{al, sb, sa};
+  if (xent) {
+    sp = block_sum(sp, sd);
+    spz = block_sum(spz, sd);
+    splp = block_sum(splp, sd);
+  }
+  if (threadIdx.x == 0) a.part[row * a.L.S + s] = Part{al, sb, sa, sp, spz, splp};
 }
 
 __global__ __launch_bounds__(kBlock) void branch_kernel(Args a) {
@@ -185,30 +222,62 @@ __global__ __launch_bounds__(kBlock) void branch_kernel(Args a) {
   __shared__ float sf[kWavesPerBlock];
   __shared__ double al[LVTV_MAX_W], sb[LVTV_MAX_W], sa[LVTV_MAX_W];
   __shared__ double Ms[LVTV_MAX_W], Ls[LVTV_MAX_W];
+  __shared__ double sps[LVTV_MAX_W], spzs[LVTV_MAX_W], splps[LVTV_MAX_W];
   for (int k = 0; k < W; ++k) {
     const size_t row = size_t(n) * W + k;
     double M, L;
     combine_row_stats(a.stat + row * a.L.S, a.L.S, sd, sf, M, L);
-    double x = 0.0, y = 0.0, w = 0.0;
+    double x = 0.0, y = 0.0, w = 0.0, u = 0.0, t = 0.0, r = 0.0;
     for (int s = threadIdx.x; s < a.L.S; s += kBlock) {
       const Part pt = a.part[row * a.L.S + s];
       x += pt.alpha;
       y += pt.s_below;
       w += pt.s_above;
+      u += pt.sp;
+      t += pt.spz;
+      r += pt.splp;
     }
     x = block_sum(x, sd);
     y = block_sum(y, sd);
     w = block_sum(w, sd);
+    u = block_sum(u, sd);
+    t = block_sum(t, sd);
+    r = block_sum(r, sd);
     if (threadIdx.x == 0) {
       al[k] = x;
       sb[k] = y;
       sa[k] = w;
       Ms[k] = M;
       Ls[k] = L;
+      sps[k] = u;
+      spzs[k] = t;
+      splps[k] = r;
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && a.objective != LVTV_OBJ_E2E_TV) {
+    const double inv_n = 1.0 / double(a.N);
+    double loss_n = 0.0;
+    for (int k = 0; k < W; ++k) {
+      const size_t row = size_t(n) * W + k;
+      RowFinal fin{-float(Ms[k]) * kLog2e, float(1.0 / Ls[k]), 0.f, 0.f};
+      if (a.objective == LVTV_OBJ_STEP_TV) {
+        loss_n += 1.0 - al[k];
+        fin.c_below = float(-inv_n * sa[k]);
+        fin.c_above = float(inv_n * sb[k]);
+      } else {
+        // log q = z - M - ln L, so -sum p log q = -sum p z + (M + ln L) sum p
+        const double ce = -spzs[k] + (Ms[k] + log(Ls[k])) * sps[k];
+        loss_n += a.objective == LVTV_OBJ_KL ? ce + splps[k] : ce;
+        fin.c_below = float(sps[k] * inv_n);
+        fin.c_above = float(inv_n);
+      }
+      a.fin[row] = fin;
+      a.alpha[row] = float(al[k]);
+    }
+    a.branch_loss[n] = loss_n;
+  }
+  if (threadIdx.x == 0 && a.objective == LVTV_OBJ_E2E_TV) {
     double prefix[LVTV_MAX_W], suffix[LVTV_MAX_W];
     double run = 1.0, loss_n = 0.0;
     for (int k = 0; k < W; ++k) {
@@ -245,6 +314,7 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
   const int s = blockIdx.x;
   const size_t row = size_t(blockIdx.z) * a.W + blockIdx.y;
   const RowFinal f = a.fin[row];
+  const bool xent = a.objective == LVTV_OBJ_CE || a.objective == LVTV_OBJ_KL;
   const uint16_t* z = a.z + row * a.V;
   const float* p = a.p + row * a.V;
   uint16_t* dz = a.dz + row * a.V;
@@ -256,11 +326,19 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
     load8<1>(z, e, a.V, a.vec_ok, xz);
     load8_p(p, e, a.V, a.vec_ok, xp);
     uint16_t out[kVec];
+    if (xent) {
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      const float q = exp_shifted(xz[i], f.neg_m_log2e) * f.inv_l;
-      const float g = q * (q < xp[i] ? f.c_below : f.c_above);
-      out[i] = f32_to_bf16_rne(g);
+      for (int i = 0; i < kVec; ++i) {
+        const float q = exp_shifted(xz[i], f.neg_m_log2e) * f.inv_l;
+        out[i] = f32_to_bf16_rne(__builtin_fmaf(q, f.c_below, -(xp[i] * f.c_above)));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) {
+        const float q = exp_shifted(xz[i], f.neg_m_log2e) * f.inv_l;
+        const float g = q * (q < xp[i] ? f.c_below : f.c_above);
+        out[i] = f32_to_bf16_rne(g);
+      }
     }
     if (a.vec_ok && e + kVec <= a.V) {
       uint4 w;
@@ -309,38 +387,44 @@ bool use_fused(int32_t N, int32_t W, int32_t V) {
 }  // namespace
 }  // namespace lvtv
 
-extern "C" size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V) {
-  if (!lvtv::sizes_ok(N, W, V)) return 0;
-  size_t n = lvtv::make_layout(N, W, V).total;
-  if (lvtv::lf::applicable(N, W, V)) {
-    const size_t f = lvtv::lf::workspace_bytes(N, W, V);
+namespace lvtv {
+namespace {
+
+size_t loss_workspace_bytes(int32_t N, int32_t W, int32_t V) {
+  if (!sizes_ok(N, W, V)) return 0;
+  size_t n = make_layout(N, W, V).total;
+  if (lf::applicable(N, W, V)) {
+    const size_t f = lf::workspace_bytes(N, W, V);
     if (f > n) n = f;
   }
   return n;
 }
 
-extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
-                                   int32_t N, int32_t W, int32_t V, float* loss, float* alpha,
-                                   uint16_t* dlogits, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
-  using namespace lvtv;
+int run_loss(const uint16_t* draft_logits, const float* target_probs, int32_t N, int32_t W,
+             int32_t V, int objective, float* loss, float* alpha, uint16_t* dlogits,
+             void* workspace, size_t workspace_bytes, void* stream) {
   if (!sizes_ok(N, W, V)) return LVTV_ERR_SHAPE;
+  if (objective < LVTV_OBJ_E2E_TV || objective > LVTV_OBJ_KL) return LVTV_ERR_OBJECTIVE;
   if (!draft_logits || !target_probs || !loss || !alpha || !dlogits) return LVTV_ERR_NULL;
   const Layout L = make_layout(N, W, V);
-  if (!workspace || workspace_bytes < e2e_tv_loss_workspace_bytes(N, W, V) ||
+  if (!workspace || workspace_bytes < loss_workspace_bytes(N, W, V) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
-  const uintptr_t mis0 = reinterpret_cast<uintptr_t>(draft_logits) |
-                         reinterpret_cast<uintptr_t>(target_probs) |
-                         reinterpret_cast<uintptr_t>(dlogits);
-  if (use_fused(N, W, V)) {
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(draft_logits) |
+                        reinterpret_cast<uintptr_t>(target_probs) |
+                        reinterpret_cast<uintptr_t>(dlogits);
+  const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
+  // the single-read kernel serves the TV objectives (their gradients need
+  // only the held z, the mask and per-row scalars)
+  if ((objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV) && use_fused(N, W, V)) {
     lf::LossCall c;
     c.z = draft_logits;
     c.p = target_probs;
     c.N = N;
     c.W = W;
     c.V = V;
-    c.vec_ok = (V % kVec == 0) && ((mis0 & 15) == 0);
+    c.objective = objective;
+    c.vec_ok = vec_ok;
     c.spin_limit = spin_limit();
     c.loss = loss;
     c.alpha = alpha;
@@ -354,10 +438,8 @@ extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* ta
   a.N = N;
   a.W = W;
   a.V = V;
-  const uintptr_t mis = reinterpret_cast<uintptr_t>(draft_logits) |
-                        reinterpret_cast<uintptr_t>(target_probs) |
-                        reinterpret_cast<uintptr_t>(dlogits);
-  a.vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
+  a.objective = objective;
+  a.vec_ok = vec_ok;
   a.loss = loss;
   a.alpha = alpha;
   a.dz = dlogits;
@@ -375,4 +457,31 @@ extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* ta
   hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(kBlock), 0, s, a);
   hipLaunchKernelGGL(grad_kernel, grid, dim3(kBlock), 0, s, a);
   return hipGetLastError() == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace lvtv
+
+extern "C" size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V) {
+  return lvtv::loss_workspace_bytes(N, W, V);
+}
+
+extern "C" size_t draft_loss_workspace_bytes(int32_t N, int32_t W, int32_t V) {
+  return lvtv::loss_workspace_bytes(N, W, V);
+}
+
+extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
+                                   int32_t N, int32_t W, int32_t V, float* loss, float* alpha,
+                                   uint16_t* dlogits, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return lvtv::run_loss(draft_logits, target_probs, N, W, V, LVTV_OBJ_E2E_TV, loss, alpha,
+                        dlogits, workspace, workspace_bytes, stream);
+}
+
+extern "C" int draft_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
+                                  int32_t N, int32_t W, int32_t V, int objective, float* loss,
+                                  float* alpha, uint16_t* dlogits, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return lvtv::run_loss(draft_logits, target_probs, N, W, V, objective, loss, alpha, dlogits,
+                        workspace, workspace_bytes, stream);
 }

@@ -76,6 +76,7 @@ struct Args {
   const uint16_t* z;
   const float* p;
   int N, W, V;
+  int objective;  // LVTV_OBJ_E2E_TV or LVTV_OBJ_STEP_TV
   int spin_limit;
   float* alpha;
   uint16_t* dz;
@@ -356,15 +357,22 @@ __device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size
       const int b1 = (k * 2 + 1) * kSlotWords + 4 + 2 * which;
       return word_f64(sh.words, b0) + word_f64(sh.words, b1);
     };
-    double run = 1.0, loss_n = 0.0, before = 1.0;
-    for (int k = 0; k < W; ++k) {
-      if (k == j) before = run;
-      run *= part(k, 0);
-      loss_n -= run;
+    double loss_n = 0.0, g;
+    if (a.objective == LVTV_OBJ_STEP_TV) {
+      // sum_k (1 - alpha_k); d/dalpha_j = -1
+      for (int k = 0; k < W; ++k) loss_n += 1.0 - part(k, 0);
+      g = -1.0 / double(a.N);
+    } else {
+      double run = 1.0, before = 1.0;
+      for (int k = 0; k < W; ++k) {
+        if (k == j) before = run;
+        run *= part(k, 0);
+        loss_n -= run;
+      }
+      double suffix = 1.0;  // R_{W-1} = 1, R_k = 1 + alpha_{k+1} R_{k+1}
+      for (int k = W - 2; k >= j; --k) suffix = 1.0 + part(k + 1, 0) * suffix;
+      g = -before * suffix / double(a.N);
     }
-    double suffix = 1.0;  // R_{W-1} = 1, R_k = 1 + alpha_{k+1} R_{k+1}
-    for (int k = W - 2; k >= j; --k) suffix = 1.0 + part(k + 1, 0) * suffix;
-    const double g = -before * suffix / double(a.N);
     sh.coef[0] = g * part(j, 2);   // S'_j
     sh.coef[1] = -g * part(j, 1);  // S_j
     a.alpha[row] = float(part(j, 0));
@@ -749,6 +757,7 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   a.N = c.N;
   a.W = c.W;
   a.V = c.V;
+  a.objective = c.objective;
   a.spin_limit = c.spin_limit;
   a.alpha = c.alpha;
   a.dz = c.dz;

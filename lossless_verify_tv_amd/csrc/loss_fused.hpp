@@ -18,6 +18,7 @@ struct LossCall {
   const uint16_t* z;
   const float* p;
   int N, W, V;
+  int objective;  // LVTV_OBJ_E2E_TV or LVTV_OBJ_STEP_TV
   bool vec_ok;
   int spin_limit;
   float* loss;

@@ -67,3 +67,12 @@ def run_loss(z_u16, p_f32, dev=None):
     torch.cuda.synchronize(dev)
     return {"loss": float(loss.cpu().numpy()[0]), "alpha": alpha.cpu().numpy(),
             "dlogits": dl.view(torch.int16).cpu().numpy().view(np.uint16)}
+
+
+def run_draft_loss(z_u16, p_f32, objective, dev=None):
+    dev = dev or device()
+    z, p = loss_to_device(z_u16, p_f32, dev)
+    loss, alpha, dl = lv.draft_loss_fwd_bwd(z, p, objective)
+    torch.cuda.synchronize(dev)
+    return {"loss": float(loss.cpu().numpy()[0]), "alpha": alpha.cpu().numpy(),
+            "dlogits": dl.view(torch.int16).cpu().numpy().view(np.uint16)}

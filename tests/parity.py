@@ -146,16 +146,22 @@ def rel_close(a, b, rtol):
     return np.abs(a - b) <= rtol * np.abs(b)
 
 
-def compare_branch(gpu_u16, z_u16, p32, n_branches):
+def compare_branch(gpu_u16, z_u16, p32, n_branches, grad=None):
     """Compare the GPU gradient rows of one branch ([W, V] bf16) with the
     oracle, with the tie alternatives described in the module docstring.
-    Returns (n_bad, n_midpoint, n_tie, n_rows_on_alternative, first_bad)."""
+    ``grad(z64, p64)`` gives the oracle's fp64 gradient of the branch
+    ([W, V]); the default is the E2E-TV loss's (the per-step TV loss passes
+    its own). Returns (n_bad, n_midpoint, n_tie, n_rows_on_alternative,
+    first_bad)."""
     from oracle import bf16 as obf16
     from oracle import loss as ol
 
+    if grad is None:
+        def grad(zz, pp):
+            return ol.branch(zz, pp, n_branches)[4]
     z64 = obf16.decode(z_u16)
     p64 = np.asarray(p32, dtype=np.float64)
-    _, _, _, _, dz = ol.branch(z64, p64, n_branches)
+    dz = grad(z64, p64)
     q = np.exp(z64 - z64.max(-1, keepdims=True))
     q /= q.sum(-1, keepdims=True)
     tie = np.abs(q - p64) <= TIE_RTOL * np.maximum(q, p64)
@@ -172,7 +178,7 @@ def compare_branch(gpu_u16, z_u16, p32, n_branches):
                 p_alt = p64.copy()
                 below = q[k, sub] < p64[k, sub]
                 p_alt[k, sub] = np.where(below, q[k, sub] * (1 - 1e-12), q[k, sub] * (1 + 1e-12))
-                cands.append(ol.branch(z64, p_alt, n_branches)[4][k])
+                cands.append(grad(z64, p_alt)[k])
         best = None
         for ci, cand in enumerate(cands):
             res = compare_dlogits(gpu_u16[k], obf16.encode_rne(cand), cand, q[k], p64[k])
@@ -186,3 +192,40 @@ def compare_branch(gpu_u16, z_u16, p32, n_branches):
         if first is None and fb is not None:
             first = (k, fb)
     return tot_bad, tot_mid, tot_tie, alt_rows, first
+
+
+XENT_QTOL = 4e-6
+
+
+def compare_xent_branch(gpu_u16, z_u16, p32, n_branches, objective):
+    """Gradient rows of one branch under CE or KL: dz = (q sum p - p) / N.
+
+    The GPU evaluates q in fp32 from an exponent whose reference is rounded
+    (about 1e-6 relative in q) and forms q sum p - p with one fused
+    multiply-add, which cancels where q sum p is close to p. A GPU value
+    passes when it is the bf16 round-to-nearest-even of some value within
+    XENT_QTOL (q sum p + p) / N of the oracle's fp64 gradient (that bound
+    covers both effects), or equal to the oracle's rounding. Returns (n_bad,
+    n_within_bound_but_unequal, first_bad)."""
+    from oracle import bf16 as obf16
+    from oracle import objectives as ob
+
+    z64 = obf16.decode(z_u16)
+    p64 = np.asarray(p32, dtype=np.float64)
+    dz = ob.branch(z64, p64, n_branches, objective)[2]
+    q = np.exp(z64 - z64.max(-1, keepdims=True))
+    q /= q.sum(-1, keepdims=True)
+    err = XENT_QTOL * (q * p64.sum(-1, keepdims=True) + p64) / n_branches
+    g = np.asarray(gpu_u16, dtype=np.uint16)
+    exact = g == obf16.encode_rne(dz)
+    lo = bf16_bits_to_f64(obf16.encode_rne(dz - err))
+    hi = bf16_bits_to_f64(obf16.encode_rne(dz + err))
+    gv = bf16_bits_to_f64(g)
+    within = (gv >= np.minimum(lo, hi)) & (gv <= np.maximum(lo, hi))
+    tiny = (np.abs(dz) < FP32_MIN_NORMAL) & (np.abs(gv) < FP32_MIN_NORMAL)
+    bad = ~(exact | within | tiny)
+    first = None
+    if bad.any():
+        i = int(np.flatnonzero(bad.ravel())[0])
+        first = (np.unravel_index(i, bad.shape), float(gv.ravel()[i]), float(dz.ravel()[i]))
+    return int(bad.sum()), int((within & ~exact).sum()), first

@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_strerror(lib):
     assert lib.lvtv_version() >= 1
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lv.strerror(code)
     assert "unknown" in lv.strerror(-99)
 
@@ -55,6 +55,9 @@ def test_workspace_queries(lib):
     assert lv.e2e_tv_loss_workspace_bytes(512, 7, 151936) > 0
     assert lv.e2e_tv_loss_workspace_bytes(512, 17, 151936) == 0
     assert lv.e2e_tv_loss_workspace_bytes(0, 7, 100) == 0
+    assert lv.draft_loss_workspace_bytes(512, 7, 151936) == lv.e2e_tv_loss_workspace_bytes(
+        512, 7, 151936)
+    assert lv.draft_loss_workspace_bytes(512, 17, 151936) == 0
     small = lv.spec_verify_workspace_bytes(8, 4, 1000)
     big = lv.spec_verify_workspace_bytes(8, 4, 100000)
     assert big > small
@@ -100,6 +103,18 @@ def test_loss_host_errors(lib):
     assert call(wsb=need - 1) == -4
 
 
+def test_draft_loss_host_errors(lib):
+    need = lv.draft_loss_workspace_bytes(4, 3, 100)
+    call = lambda **kw: lib.draft_loss_fwd_bwd(*{**dict(
+        z=FAKE, p=FAKE, N=4, W=3, V=100, obj=2, loss=FAKE, alpha=FAKE, dz=FAKE, ws=FAKE,
+        wsb=need, stream=NULL), **kw}.values())
+    assert call(obj=4) == -6
+    assert call(obj=-1) == -6
+    assert call(N=0) == -2
+    assert call(z=NULL) == -1
+    assert call(wsb=need - 1) == -4
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     t = torch.zeros(2, 3, 10)
@@ -109,3 +124,5 @@ def test_binding_rejects_cpu_tensors():
                        torch.zeros(2, dtype=torch.int64))
     with pytest.raises(ValueError):
         lv.e2e_tv_loss_fwd_bwd(t.to(torch.bfloat16), t)
+    with pytest.raises(ValueError):
+        lv.draft_loss_fwd_bwd(t.to(torch.bfloat16), t, "ce")
