@@ -277,6 +277,25 @@ def main():
     result["components"]["e2e_tv_loss_fwd_bwd"] = {
         "ms": loss_ms, "rows_per_s": LOSS_N * LOSS_W / (loss_ms * 1e-3), "gbs": loss_gbs,
         "frac": loss_gbs / HBM_PEAK_GBS, "algorithmic_bytes": lb}
+    # The per-position comparators of the loss on the same inputs, outside
+    # the step: each timed over as many calls as the step count.
+    variants = {}
+    for name in ("step_tv", "ce", "kl"):
+        lv.draft_loss_fwd_bwd(z, p, name, workspace=lws, out=lout)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            lv.draft_loss_fwd_bwd(z, p, name, workspace=lws, out=lout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        variants[f"draft_loss_{name}"] = {
+            "ms": ms, "gbs": lb / (ms * 1e-3) / 1e9,
+            "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb}
+    result["loss_variants"] = variants
+    log("loss variants: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in variants.items()))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(vcases, lcase)
