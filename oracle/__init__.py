@@ -30,8 +30,11 @@ Modules:
   residual / bonus draw, greedy rule, per-request status).
 * ``loss``    -- the E2E-TV prefix-product loss and its gradient with respect
   to the draft logits.
+* ``objectives`` -- the per-position comparators (per-step TV, CE, KL) with
+  their gradients.
+* ``schedule`` -- confidence-scheduled verify lengths (DSpark).
 
 Parity status of each function is stated in its module header.
 """
 
-from . import bf16, loss, philox, verify  # noqa: F401
+from . import bf16, loss, objectives, philox, schedule, verify  # noqa: F401

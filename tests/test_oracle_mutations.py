@@ -13,12 +13,14 @@ import oracle.bf16
 import oracle.loss
 import oracle.objectives
 import oracle.philox
+import oracle.schedule
 import oracle.verify
 
 from . import test_oracle_bf16 as t_bf16
 from . import test_oracle_loss as t_loss
 from . import test_oracle_objectives as t_obj
 from . import test_oracle_philox as t_philox
+from . import test_oracle_schedule as t_sched
 from . import test_oracle_verify as t_verify
 
 
@@ -95,6 +97,18 @@ CASES = [
     ("per-step TV loss sums alpha", oracle.objectives,
      "loss_n = float(np.sum(1.0 - alpha))", "loss_n = float(np.sum(alpha))",
      t_obj, "ob", "test_step_tv_is_half_l1_and_matches_e2e_at_one_position", ()),
+    ("schedule takes the smallest survivals first", oracle.schedule,
+     "order = np.lexsort((np.arange(flat.size), -flat.astype(np.float64)))",
+     "order = np.lexsort((np.arange(flat.size), flat.astype(np.float64)))",
+     t_sched, "osch", "test_matches_exhaustive_search", ("steps", 3, 3)),
+    ("schedule prices the batch without the bonus tokens", oracle.schedule,
+     "theta = (R + s) * sps[R + np.arange(flat.size + 1)]",
+     "theta = (R + s) * sps[np.arange(flat.size + 1)]",
+     t_sched, "osch", "test_matches_exhaustive_search", ("steps", 3, 3)),
+    ("schedule drops the guaranteed token per request", oracle.schedule,
+     "theta = (R + s) * sps[R + np.arange(flat.size + 1)]",
+     "theta = s * sps[R + np.arange(flat.size + 1)]",
+     t_sched, "osch", "test_flat_curve_verifies_everything_and_collapse_verifies_nothing", ()),
     ("Philox key not bumped between rounds", oracle.philox,
      "k0 = (k0 + _WEYL_A) & _MASK64", "k0 = k0",
      t_philox, "philox", "test_block_matches_numpy_random_counters", ()),
