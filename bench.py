@@ -296,6 +296,28 @@ def main():
             "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb}
     result["loss_variants"] = variants
     log("loss variants: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in variants.items()))
+    # Confidence-scheduled verify lengths for 256 requests x 16 positions
+    # (one workgroup; latency-bound, reported as time per call).
+    srng = np.random.default_rng([7, 1])
+    sR, sL = 256, 16
+    conf = torch.from_numpy(srng.uniform(0.05, 1.0, (sR, sL)).astype(np.float32)).to(dev)
+    Bs = np.arange(sR * (sL + 1) + 1, dtype=np.float64)
+    sps = torch.from_numpy((4000.0 / (1.0 + np.floor(Bs / 128.0))).astype(np.float32)).to(dev)
+    sout = (torch.empty(sR, dtype=torch.int32, device=dev),
+            torch.empty(2, dtype=torch.float64, device=dev))
+    lv.dspark_schedule(conf, sps, out=sout)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 100
+    e0.record(stream)
+    for _ in range(reps):
+        lv.dspark_schedule(conf, sps, out=sout)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    result["dspark_schedule"] = {"us": e0.elapsed_time(e1) / reps * 1e3, "requests": sR,
+                                 "positions": sL}
+    log(f"dspark_schedule R={sR} L={sL}: {result['dspark_schedule']['us']:.1f} us")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(vcases, lcase)

@@ -226,6 +226,36 @@ int draft_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
                        float* loss, float* alpha, uint16_t* dlogits,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * dspark_schedule -- confidence-scheduled verify lengths ("Reading Qwen
+ * Bebop and DeepSeek DSpark", section "DSpark's second piece:
+ * confidence-scheduled verify length").
+ *
+ * Request r has confidences c_{r,j}, j < L (the chance that draft token j
+ * survives once every earlier one did; the pages' soft label is 1 - d_TV,
+ * which is spec_verify's alpha). With prefix survivals
+ * a_{r,j} = prod_{i<=j} c_{r,i}, verifying l_r tokens of each request feeds
+ * B = sum_r (1 + l_r) tokens to the target model and yields
+ * tau = sum_r (1 + sum_{j<l_r} a_{r,j}) tokens in expectation. The call picks
+ * the l_r maximising Theta = tau * SPS(B).
+ *
+ * Arguments (device pointers):
+ *   confidence   float [R, L]; clamped to [0, 1], NaN read as 0.
+ *   sps          float [R (L + 1) + 1]: decode steps per second at batch
+ *                size B (entry B; entries below R are not read).
+ *   R, L         1 <= R, 1 <= L, R L <= LVTV_SCHED_MAX_ITEMS.
+ *   verify_len   int32 [R] out: l_r in 0..L.
+ *   best         double [2] out: Theta at the optimum and its B.
+ *   stream       hipStream_t. One workgroup; no workspace.
+ * Arithmetic: survivals in binary32, left to right; equal survivals are
+ * taken in flat index order r L + j; tau and Theta in fp64; among equal
+ * Theta the smallest B wins, and a NaN Theta never wins (all NaN: B = R).
+ * Returns LVTV_ERR_SHAPE / LVTV_ERR_NULL before enqueueing anything.
+ */
+#define LVTV_SCHED_MAX_ITEMS 8192 /* R L of one dspark_schedule call */
+int dspark_schedule(const float* confidence, const float* sps, int32_t R,
+                    int32_t L, int32_t* verify_len, double* best, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     LvtvError,
     draft_loss_fwd_bwd,
     draft_loss_workspace_bytes,
+    dspark_schedule,
     e2e_tv_loss_fwd_bwd,
     e2e_tv_loss_workspace_bytes,
     load_library,

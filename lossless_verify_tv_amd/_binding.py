@@ -36,7 +36,10 @@ EXPORTS = (
     "e2e_tv_loss_fwd_bwd",
     "draft_loss_workspace_bytes",
     "draft_loss_fwd_bwd",
+    "dspark_schedule",
 )
+
+SCHED_MAX_ITEMS = 8192  # LVTV_SCHED_MAX_ITEMS
 
 # Objectives of draft_loss_fwd_bwd (include/lvtv.h, LVTV_OBJ_*).
 OBJECTIVES = {"e2e_tv": 0, "step_tv": 1, "ce": 2, "kl": 3}
@@ -80,6 +83,8 @@ def load_library(path: str = LIB_PATH):
         lib.draft_loss_fwd_bwd.restype = ctypes.c_int
         lib.draft_loss_fwd_bwd.argtypes = [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp,
                                            sz, vp]
+        lib.dspark_schedule.restype = ctypes.c_int
+        lib.dspark_schedule.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         _lib = lib
         return lib
 
@@ -261,3 +266,32 @@ def draft_loss_fwd_bwd(draft_logits, target_probs, objective, workspace=None, ou
                                       ws.numel(), _stream(dev))
     _check(code, "draft_loss_fwd_bwd")
     return loss, alpha, dlogits
+
+
+def dspark_schedule(confidence, sps, out=None):
+    """Confidence-scheduled verify lengths (see include/lvtv.h).
+
+    confidence float32 [R, L] and sps float32 [R (L + 1) + 1], contiguous on
+    one GPU. Returns (verify_len int32 [R], best float64 [2]: Theta at the
+    optimum and its batch size) on the device; no synchronisation."""
+    lib = load_library()
+    dev = confidence.device
+    _require(dev.type == "cuda", "dspark_schedule needs GPU tensors")
+    _require(confidence.dtype == torch.float32 and sps.dtype == torch.float32,
+             "confidence and sps must be float32")
+    _require(confidence.dim() == 2, "confidence must be [R, L]")
+    R, L = confidence.shape
+    _require(sps.dim() == 1 and sps.numel() >= R * (L + 1) + 1,
+             "sps needs R (L + 1) + 1 entries, indexed by batch size")
+    for t in (confidence, sps):
+        _require(t.device == dev and t.is_contiguous(), "inputs must be contiguous on one GPU")
+    if out is None:
+        lens = torch.empty(R, dtype=torch.int32, device=dev)
+        best = torch.empty(2, dtype=torch.float64, device=dev)
+    else:
+        lens, best = out
+    with torch.cuda.device(dev):
+        code = lib.dspark_schedule(_ptr(confidence), _ptr(sps), R, L, _ptr(lens), _ptr(best),
+                                   _stream(dev))
+    _check(code, "dspark_schedule")
+    return lens, best

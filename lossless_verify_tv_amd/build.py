@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblvtv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "verify_rows.hip", "loss.hip", "loss_fused.hip"]
+SOURCES = ["api.hip", "verify_rows.hip", "loss.hip", "loss_fused.hip", "schedule.hip"]
 
 # -ffp-contract=off: products that must round on their own (the canonical
 # scaled logit) are never fused; kernels request fused multiply-adds

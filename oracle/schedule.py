@@ -23,7 +23,8 @@ Readings (the pages are silent on them):
   precision, since they decide an integer: the order);
 * equal survivals are taken in flat index order r * L + j (so every
   request's selection stays a prefix);
-* tau and Theta are fp64; among equal Theta the smallest B wins.
+* tau and Theta are fp64; among equal Theta the smallest B wins, and a NaN
+  Theta (a NaN throughput) never wins.
 """
 
 from __future__ import annotations
@@ -54,6 +55,7 @@ def schedule(conf, sps):
     s = np.concatenate(([0.0], np.cumsum(flat[order].astype(np.float64))))
     sps = np.asarray(sps, dtype=np.float64)
     theta = (R + s) * sps[R + np.arange(flat.size + 1)]
+    theta = np.where(np.isnan(theta), -np.inf, theta)   # a NaN never wins
     t = int(np.argmax(theta))
     taken = order[:t]
     lens = np.zeros(R, dtype=np.int64)

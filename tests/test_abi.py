@@ -115,6 +115,17 @@ def test_draft_loss_host_errors(lib):
     assert call(wsb=need - 1) == -4
 
 
+def test_schedule_host_errors(lib):
+    call = lambda **kw: lib.dspark_schedule(*{**dict(
+        c=FAKE, sps=FAKE, R=4, L=3, lens=FAKE, best=FAKE, stream=NULL), **kw}.values())
+    assert call(R=0) == -2
+    assert call(L=0) == -2
+    assert call(R=8193, L=1) == -2
+    assert call(R=1024, L=9) == -2
+    assert call(c=NULL) == -1
+    assert call(best=NULL) == -1
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     t = torch.zeros(2, 3, 10)
