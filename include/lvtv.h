@@ -150,6 +150,46 @@ int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace bytes spec_verify_packed needs (0 if out of range). Host only.
+ */
+size_t spec_verify_packed_workspace_bytes(int32_t B, int32_t total_rows, int32_t V,
+                                          int dtype);
+
+/*
+ * spec_verify_packed -- spec_verify on a packed, variable-length layout:
+ * each request's rows are stored back to back with no padding for a ragged
+ * K ("Reading Qwen Bebop and DeepSeek DSpark", "DSpark's second piece":
+ * every request gets its own verify length).
+ *
+ * Layout (device pointers; rows V contiguous):
+ *   row_offsets    int32 [B + 1]: request b owns the target rows
+ *                  [row_offsets[b], row_offsets[b+1]), so
+ *                  K_b = row_offsets[b+1] - row_offsets[b] - 1 (0..LVTV_MAX_K);
+ *                  row_offsets[0] = 0 and row_offsets[B] = total_rows.
+ *   target_logits  [total_rows, V] of `dtype`.
+ *   draft_logits   [total_rows - B, V]: request b's draft rows start at
+ *                  row_offsets[b] - b (K_b of them).
+ *   draft_tokens   int32 [total_rows - B], packed like the draft rows.
+ *   accepted_len   int32 [B] out.
+ *   out_tokens     int32 [total_rows] out: request b's K_b + 1 slots at
+ *                  row_offsets[b] (accepted drafts, the drawn token, then -1).
+ *   alpha          float [total_rows - B] out, packed like the draft rows.
+ *   temperature, seed, status, workspace, stream: as spec_verify (Philox
+ *                  counters use the request index b and the position k, so a
+ *                  request gives the same result in either layout).
+ * Offsets that break the rules above fault every request
+ * (LVTV_STATUS_BAD_K, accepted_len -1) and no out_tokens or alpha slot is
+ * written. Three kernels are enqueued: one workgroup maps rows to requests
+ * and checks the offsets, then the row and finalize kernels of spec_verify.
+ */
+int spec_verify_packed(const void* target_logits, const void* draft_logits, int dtype,
+                       const int32_t* draft_tokens, const int32_t* row_offsets,
+                       const float* temperature, const uint64_t* seed, int32_t B,
+                       int32_t total_rows, int32_t V, int32_t* accepted_len,
+                       int32_t* out_tokens, float* alpha, int32_t* status,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Workspace bytes e2e_tv_loss_fwd_bwd needs (0 if out of range). Host only.
  */
 size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V);

@@ -29,6 +29,8 @@ from ._binding import (  # noqa: F401
     load_library,
     new_workspace,
     spec_verify,
+    spec_verify_packed,
+    spec_verify_packed_workspace_bytes,
     spec_verify_workspace_bytes,
     strerror,
 )

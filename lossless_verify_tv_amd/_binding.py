@@ -32,6 +32,8 @@ EXPORTS = (
     "lvtv_workspace_reset",
     "spec_verify_workspace_bytes",
     "spec_verify",
+    "spec_verify_packed_workspace_bytes",
+    "spec_verify_packed",
     "e2e_tv_loss_workspace_bytes",
     "e2e_tv_loss_fwd_bwd",
     "draft_loss_workspace_bytes",
@@ -74,6 +76,11 @@ def load_library(path: str = LIB_PATH):
         lib.spec_verify.restype = ctypes.c_int
         lib.spec_verify.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32,
                                     vp, vp, vp, vp, vp, sz, vp]
+        lib.spec_verify_packed_workspace_bytes.restype = sz
+        lib.spec_verify_packed_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
+        lib.spec_verify_packed.restype = ctypes.c_int
+        lib.spec_verify_packed.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32,
+                                           vp, vp, vp, vp, vp, sz, vp]
         lib.e2e_tv_loss_workspace_bytes.restype = sz
         lib.e2e_tv_loss_workspace_bytes.argtypes = [i32, i32, i32]
         lib.e2e_tv_loss_fwd_bwd.restype = ctypes.c_int
@@ -96,6 +103,14 @@ def strerror(code: int) -> str:
 def _check(code: int, what: str):
     if code != 0:
         raise LvtvError(f"{what} failed: {strerror(code)} (code {code})")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return LVTV_BF16
+    if t.dtype == torch.float32:
+        return LVTV_F32
+    raise ValueError("logits must be float32 or bfloat16")
 
 
 def _ptr(t):
@@ -295,3 +310,54 @@ def dspark_schedule(confidence, sps, out=None):
                                    _stream(dev))
     _check(code, "dspark_schedule")
     return lens, best
+
+
+def spec_verify_packed_workspace_bytes(B, total_rows, V, dtype=LVTV_BF16) -> int:
+    return int(load_library().spec_verify_packed_workspace_bytes(B, total_rows, V, dtype))
+
+
+def spec_verify_packed(target_logits, draft_logits, draft_tokens, row_offsets, temperature, seed,
+                       workspace=None, out=None):
+    """Verify step on the packed layout (see include/lvtv.h): target_logits
+    [total_rows, V], draft_logits [total_rows - B, V] (same dtype, bf16 or
+    fp32), draft_tokens int32 [total_rows - B], row_offsets int32 [B + 1],
+    temperature float32 [B], seed int64/uint64 [B]. Returns (accepted_len
+    [B], out_tokens [total_rows], alpha [total_rows - B], status [B])."""
+    lib = load_library()
+    dev = target_logits.device
+    _require(dev.type == "cuda", "spec_verify_packed needs GPU tensors")
+    dtype = _dtype_code(target_logits)
+    _require(target_logits.dim() == 2, "target_logits must be [total_rows, V]")
+    total_rows, V = target_logits.shape
+    B = row_offsets.numel() - 1
+    _require(B >= 1 and row_offsets.dtype == torch.int32, "row_offsets must be int32 [B + 1]")
+    nd = total_rows - B
+    _require(draft_logits.dtype == target_logits.dtype and draft_logits.dim() == 2 and
+             tuple(draft_logits.shape) == (nd, V), "draft_logits must be [total_rows - B, V]")
+    _require(draft_tokens.dtype == torch.int32 and draft_tokens.numel() == nd,
+             "draft_tokens must be int32 [total_rows - B]")
+    _require(temperature.dtype == torch.float32 and temperature.numel() == B,
+             "temperature must be float32 [B]")
+    _require(seed.dtype in (torch.int64, torch.uint64) and seed.numel() == B,
+             "seed must be 64-bit [B]")
+    for t in (target_logits, draft_logits, draft_tokens, row_offsets, temperature, seed):
+        _require(t.device == dev and t.is_contiguous(), "inputs must be contiguous on one GPU")
+    need = lib.spec_verify_packed_workspace_bytes(B, total_rows, V, dtype)
+    _require(need > 0, f"sizes out of range: B={B} total_rows={total_rows} V={V}")
+    ws = workspace if workspace is not None else _workspace("verify_packed", dev, need)
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty(total_rows, dtype=torch.int32, device=dev)
+        alpha = torch.empty(max(nd, 1), dtype=torch.float32, device=dev)[:nd]
+        status = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        acc, toks, alpha, status = out
+    with torch.cuda.device(dev):
+        code = lib.spec_verify_packed(_ptr(target_logits), _ptr(draft_logits if nd else None),
+                                      dtype, _ptr(draft_tokens if nd else None),
+                                      _ptr(row_offsets), _ptr(temperature), _ptr(seed), B,
+                                      total_rows, V, _ptr(acc), _ptr(toks),
+                                      _ptr(alpha if nd else None), _ptr(status), _ptr(ws),
+                                      ws.numel(), _stream(dev))
+    _check(code, "spec_verify_packed")
+    return acc, toks, alpha, status

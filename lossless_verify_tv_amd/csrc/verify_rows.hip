@@ -86,16 +86,33 @@ struct Args {
   int32_t* out_tokens;
   float* alpha;
   int32_t* status;
-  RowOut* rows;  // [B][Kmax+1]
-  float* chunk;  // [B][Kmax+1][NC]
+  RowOut* rows;  // one per target row: [B][Kmax+1] (padded) or [total_rows] (packed)
+  float* chunk;  // [target rows][NC]
+  // Packed layout (toff == nullptr for the padded one): request b owns the
+  // target rows [toff[b], toff[b+1]), K_b = toff[b+1] - toff[b] - 1, and the
+  // draft rows, draft tokens and alphas from toff[b] - b on.
+  const int32_t* toff;
+  const int32_t* rowmap;     // [total_rows]: the request of each target row (-1: bad offsets)
+  const int32_t* packed_ok;  // the offsets tile [0, total_rows) (written by packed_map)
+  int total_rows;
 };
 
 __device__ __forceinline__ bool temperature_ok(float t) { return (t >= 0.f) && !isinf(t); }
 
+// Index of request b's target row k, and of its draft row k (also the index
+// of draft token k and of alpha k), in either layout.
+__device__ __forceinline__ int64_t target_row(const Args& a, int b, int k) {
+  return a.toff ? int64_t(a.toff[b]) + k : int64_t(b) * (a.Kmax + 1) + k;
+}
+
+__device__ __forceinline__ int64_t draft_row(const Args& a, int b, int k) {
+  return a.toff ? int64_t(a.toff[b]) - b + k : int64_t(b) * a.Kmax + k;
+}
+
 template <int kDtype>
 __device__ __forceinline__ const void* row_ptr(const Args& a, int b, bool target, int k) {
   constexpr int kSize = kDtype == 1 ? 2 : 4;
-  const int64_t row = target ? (int64_t(b) * (a.Kmax + 1) + k) : (int64_t(b) * a.Kmax + k);
+  const int64_t row = target ? target_row(a, b, k) : draft_row(a, b, k);
   return static_cast<const char*>(target ? a.target : a.draft) + row * int64_t(a.V) * kSize;
 }
 
@@ -381,7 +398,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
   const float nrd = kPair ? float(-((double)Rd + log2((double)ld))) : 0.f;
 
   // ---- pass 2: the partial tile, the held tiles, the rest back to front
-  float* chunk_row = a.chunk + (size_t(b) * (a.Kmax + 1) + k) * a.NC;
+  float* chunk_row = a.chunk + size_t(target_row(a, b, k)) * a.NC;
   float sa = 0.f;
   if (tail) overlap_tile<kDtype, kPair>(tt[0], td[0], c, nrt, nrd, sa, chunk_row, nfull);
 #pragma unroll
@@ -416,7 +433,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
     o.arg_t = -1;
     o.arg_d = -1;
     o.nan = 0;
-    a.rows[size_t(b) * (a.Kmax + 1) + k] = o;
+    a.rows[target_row(a, b, k)] = o;
   }
 }
 
@@ -500,7 +517,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, int b, int k, bool pai
     o.arg_t = bt.i;
     o.arg_d = pair ? bd.i : -1;
     o.nan = (bt.nan ? 1 : 0) | (pair && bd.nan ? 2 : 0);
-    a.rows[size_t(b) * (a.Kmax + 1) + k] = o;
+    a.rows[target_row(a, b, k)] = o;
   }
 }
 
@@ -509,9 +526,17 @@ __device__ __forceinline__ void greedy_row(const Args& a, int b, int k, bool pai
 template <int kDtype, bool kVecOk>
 __device__ __forceinline__ void rows_body(const Args& a) {
   __shared__ Shared sh;
-  const int b = blockIdx.x / (a.Kmax + 1);
-  const int k = blockIdx.x - b * (a.Kmax + 1);
-  const int kb = a.kreq[b];
+  int b, k, kb;
+  if (a.toff) {
+    b = a.rowmap[blockIdx.x];
+    if (b < 0) return;  // the offsets are bad: every request is faulted
+    k = int(blockIdx.x) - a.toff[b];
+    kb = a.toff[b + 1] - a.toff[b] - 1;
+  } else {
+    b = blockIdx.x / (a.Kmax + 1);
+    k = blockIdx.x - b * (a.Kmax + 1);
+    kb = a.kreq[b];
+  }
   const float T = a.temp[b];
   if (!(kb >= 0 && kb <= a.Kmax && temperature_ok(T)) || k > kb) return;
   if (T == 0.f) {
@@ -662,11 +687,18 @@ __device__ __forceinline__ void p_chunk_masses(const void* trow, int V, int NC, 
   __syncthreads();
 }
 
-__device__ __forceinline__ void write_fault(const Args& a, int b, int status) {
-  int32_t* out_tok = a.out_tokens + size_t(b) * (a.Kmax + 1);
-  float* out_alpha = a.alpha + size_t(b) * a.Kmax;
-  for (int k = threadIdx.x; k <= a.Kmax; k += kThreads) out_tok[k] = -1;
-  for (int k = threadIdx.x; k < a.Kmax; k += kThreads) out_alpha[k] = 0.f;
+// A request's output slots: out_tokens [ntok] and alpha [nalpha] (padded:
+// Kmax + 1 and Kmax; packed: K_b + 1 and K_b; none when the packed offsets
+// are bad).
+struct Slots {
+  int32_t* tok;
+  float* alpha;
+  int ntok, nalpha;
+};
+
+__device__ __forceinline__ void write_fault(const Args& a, int b, int status, const Slots& o) {
+  for (int k = threadIdx.x; k < o.ntok; k += kThreads) o.tok[k] = -1;
+  for (int k = threadIdx.x; k < o.nalpha; k += kThreads) o.alpha[k] = 0.f;
   if (threadIdx.x == 0) {
     a.status[b] = status;
     a.acc_len[b] = -1;
@@ -685,18 +717,31 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   __shared__ FinShared fs;
   Shared& sh = fs.red;
   const int b = blockIdx.x;
-  const int kb = a.kreq[b];
   const float T = a.temp[b];
   const int Kmax = a.Kmax;
+  int kb;
+  Slots o;
+  if (a.toff) {
+    if (*a.packed_ok) {
+      kb = a.toff[b + 1] - a.toff[b] - 1;
+      o = Slots{a.out_tokens + a.toff[b], a.alpha + (a.toff[b] - b), kb + 1, kb};
+    } else {
+      kb = -1;
+      o = Slots{a.out_tokens, a.alpha, 0, 0};
+    }
+  } else {
+    kb = a.kreq[b];
+    o = Slots{a.out_tokens + size_t(b) * (Kmax + 1), a.alpha + size_t(b) * Kmax, Kmax + 1, Kmax};
+  }
   if (!(kb >= 0 && kb <= Kmax && temperature_ok(T))) {
     int st = 0;
     if (!temperature_ok(T)) st |= LVTV_STATUS_BAD_TEMPERATURE;
     if (kb < 0 || kb > Kmax) st |= LVTV_STATUS_BAD_K;
-    write_fault(a, b, st);
+    write_fault(a, b, st, o);
     return;
   }
-  const int32_t* y = a.tokens + size_t(b) * Kmax;
-  const RowOut* rows = a.rows + size_t(b) * (Kmax + 1);
+  const int32_t* y = a.tokens + draft_row(a, b, 0);
+  const RowOut* rows = a.rows + target_row(a, b, 0);
   const bool greedy = (T == 0.f);
   int bad = 0, fault = 0;
   for (int k = threadIdx.x; k <= kb; k += kThreads) {
@@ -713,11 +758,11 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const int status = (__syncthreads_or(bad) ? LVTV_STATUS_BAD_TOKEN : 0) |
                      (__syncthreads_or(fault) ? LVTV_STATUS_NONFINITE : 0);
   if (status) {
-    write_fault(a, b, status);
+    write_fault(a, b, status, o);
     return;
   }
-  int32_t* out_tok = a.out_tokens + size_t(b) * (Kmax + 1);
-  float* out_alpha = a.alpha + size_t(b) * Kmax;
+  int32_t* out_tok = o.tok;
+  float* out_alpha = o.alpha;
 
   if (greedy) {
     if (threadIdx.x == 0) {
@@ -727,9 +772,9 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
           j = k;
           break;
         }
-      for (int k = 0; k < Kmax; ++k)
+      for (int k = 0; k < o.nalpha; ++k)
         out_alpha[k] = (k < kb) ? (rows[k].arg_t == rows[k].arg_d ? 1.f : 0.f) : 0.f;
-      for (int k = 0; k <= Kmax; ++k) out_tok[k] = k < j ? y[k] : (k == j ? rows[j].arg_t : -1);
+      for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? y[k] : (k == j ? rows[j].arg_t : -1);
       a.acc_len[b] = j;
       a.status[b] = 0;
     }
@@ -752,7 +797,7 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int k = 0; k < Kmax; ++k) out_alpha[k] = k < kb ? rows[k].alpha : 0.f;
+    for (int k = 0; k < o.nalpha; ++k) out_alpha[k] = k < kb ? rows[k].alpha : 0.f;
     int j = kb;
     for (int k = 0; k < kb; ++k)
       if (!(fs.uacc[k] < fs.ratio[k])) {
@@ -771,7 +816,7 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const RowOut r = rows[j];
   const void* trow = row_ptr<kDtype>(a, b, true, j);
   const void* drow = residual ? row_ptr<kDtype>(a, b, false, j) : nullptr;
-  float* m = a.chunk + (size_t(b) * (Kmax + 1) + j) * a.NC;
+  float* m = a.chunk + size_t(target_row(a, b, j)) * a.NC;
   const int NC = a.NC;
   int any = 0;
   for (int c = threadIdx.x; c < NC; c += kThreads) any |= m[c] > 0.f;
@@ -787,7 +832,7 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
                                r.Ld, sh);
   if (v < 0 || v >= a.V) v = a.V - 1;  // unreachable: the chosen chunk has positive mass
   if (threadIdx.x == 0) {
-    for (int k = 0; k <= Kmax; ++k) out_tok[k] = k < j ? y[k] : (k == j ? v : -1);
+    for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? y[k] : (k == j ? v : -1);
     a.acc_len[b] = j;
     a.status[b] = 0;
   }
@@ -804,18 +849,22 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   int n_tiles, NC;
-  size_t off_rows, off_chunk, total;
+  size_t off_rows, off_chunk, off_map, total;
 };
 
-Layout make_layout(int B, int Kmax, int V) {
+// `rows` target rows (B (Kmax + 1) padded, total_rows packed); the row map
+// and its validity flag only for the packed layout.
+Layout make_layout(size_t rows, int V, bool packed) {
   Layout L;
   L.n_tiles = (V + kTile - 1) / kTile;
   L.NC = L.n_tiles * kWaves;
   size_t off = kReservedBytes;
   L.off_rows = off;
-  off = align256(off + sizeof(RowOut) * size_t(B) * (Kmax + 1));
+  off = align256(off + sizeof(RowOut) * rows);
   L.off_chunk = off;
-  off = align256(off + sizeof(float) * size_t(B) * (Kmax + 1) * L.NC);
+  off = align256(off + sizeof(float) * rows * L.NC);
+  L.off_map = off;
+  if (packed) off = align256(off + sizeof(int32_t) * (rows + 1));
   L.total = off;
   return L;
 }
@@ -824,9 +873,43 @@ bool sizes_ok(int32_t B, int32_t Kmax, int32_t V) {
   return B >= 1 && B <= 65535 && Kmax >= 0 && Kmax <= LVTV_MAX_K && V >= 1 && V <= LVTV_MAX_V;
 }
 
+bool packed_sizes_ok(int32_t B, int32_t total_rows, int32_t V) {
+  return B >= 1 && B <= 65535 && total_rows >= B && total_rows <= B * (LVTV_MAX_K + 1) &&
+         V >= 1 && V <= LVTV_MAX_V;
+}
+
+// Checks the packed offsets (toff[0] = 0, toff[B] = total_rows, 1 to
+// LVTV_MAX_K + 1 target rows per request, so the requests tile the rows
+// exactly) and writes the request of every target row, or -1 everywhere if
+// the offsets are bad. One workgroup.
+__global__ __launch_bounds__(1024) void packed_map(const int32_t* toff, int B, int total_rows,
+                                                   int32_t* rowmap, int32_t* ok) {
+  int bad = 0;
+  for (int b = threadIdx.x; b < B; b += 1024) {
+    const int n = toff[b + 1] - toff[b];
+    bad |= !(n >= 1 && n <= LVTV_MAX_K + 1);
+  }
+  if (threadIdx.x == 0) bad |= (toff[0] != 0) || (toff[B] != total_rows);
+  const bool good = !__syncthreads_or(bad);
+  if (good) {
+    for (int b = threadIdx.x; b < B; b += 1024)
+      for (int g = toff[b]; g < toff[b + 1]; ++g) rowmap[g] = b;
+  } else {
+    for (int g = threadIdx.x; g < total_rows; g += 1024) rowmap[g] = -1;
+  }
+  if (threadIdx.x == 0) *ok = good ? 1 : 0;
+}
+
 template <int kDtype, bool kVecOk>
 hipError_t launch(const Args& a, hipStream_t stream) {
-  const unsigned grid = unsigned(a.B) * unsigned(a.Kmax + 1);
+  if (a.toff) {
+    hipLaunchKernelGGL(packed_map, dim3(1), dim3(1024), 0, stream, a.toff, a.B, a.total_rows,
+                       const_cast<int32_t*>(a.rowmap), const_cast<int32_t*>(a.packed_ok));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const unsigned grid =
+      a.toff ? unsigned(a.total_rows) : unsigned(a.B) * unsigned(a.Kmax + 1);
   if constexpr (kDtype == 1)
     hipLaunchKernelGGL(verify_rows_bf16<kVecOk>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
@@ -843,7 +926,14 @@ hipError_t launch(const Args& a, hipStream_t stream) {
 
 extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype) {
   if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
-  return lvtv::vr::make_layout(B, Kmax, V).total;
+  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false).total;
+}
+
+extern "C" size_t spec_verify_packed_workspace_bytes(int32_t B, int32_t total_rows, int32_t V,
+                                                      int dtype) {
+  if (!lvtv::vr::packed_sizes_ok(B, total_rows, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16))
+    return 0;
+  return lvtv::vr::make_layout(size_t(total_rows), V, true).total;
 }
 
 extern "C" int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
@@ -860,7 +950,7 @@ extern "C" int spec_verify(const void* target_logits, const void* draft_logits, 
       !status)
     return LVTV_ERR_NULL;
   if (Kmax > 0 && (!draft_logits || !draft_tokens || !alpha)) return LVTV_ERR_NULL;
-  const Layout L = make_layout(B, Kmax, V);
+  const Layout L = make_layout(size_t(B) * (Kmax + 1), V, false);
   if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
   Args a;
@@ -882,6 +972,62 @@ extern "C" int spec_verify(const void* target_logits, const void* draft_logits, 
   char* ws = static_cast<char*>(workspace);
   a.rows = reinterpret_cast<RowOut*>(ws + L.off_rows);
   a.chunk = reinterpret_cast<float*>(ws + L.off_chunk);
+  a.toff = nullptr;
+  a.rowmap = nullptr;
+  a.packed_ok = nullptr;
+  a.total_rows = B * (Kmax + 1);
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
+                        reinterpret_cast<uintptr_t>(draft_logits);
+  const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == LVTV_BF16)
+    e = vec_ok ? launch<1, true>(a, s) : launch<1, false>(a, s);
+  else
+    e = vec_ok ? launch<0, true>(a, s) : launch<0, false>(a, s);
+  return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+}
+
+extern "C" int spec_verify_packed(const void* target_logits, const void* draft_logits, int dtype,
+                                  const int32_t* draft_tokens, const int32_t* row_offsets,
+                                  const float* temperature, const uint64_t* seed, int32_t B,
+                                  int32_t total_rows, int32_t V, int32_t* accepted_len,
+                                  int32_t* out_tokens, float* alpha, int32_t* status,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace lvtv;
+  using namespace lvtv::vr;
+  if (dtype != LVTV_F32 && dtype != LVTV_BF16) return LVTV_ERR_DTYPE;
+  if (!packed_sizes_ok(B, total_rows, V)) return LVTV_ERR_SHAPE;
+  if (!target_logits || !row_offsets || !temperature || !seed || !accepted_len || !out_tokens ||
+      !status)
+    return LVTV_ERR_NULL;
+  if (total_rows > B && (!draft_logits || !draft_tokens || !alpha)) return LVTV_ERR_NULL;
+  const Layout L = make_layout(size_t(total_rows), V, true);
+  if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return LVTV_ERR_WORKSPACE;
+  Args a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.kreq = nullptr;
+  a.temp = temperature;
+  a.seed = seed;
+  a.B = B;
+  a.Kmax = LVTV_MAX_K;
+  a.V = V;
+  a.n_tiles = L.n_tiles;
+  a.NC = L.NC;
+  a.acc_len = accepted_len;
+  a.out_tokens = out_tokens;
+  a.alpha = alpha;
+  a.status = status;
+  char* ws = static_cast<char*>(workspace);
+  a.rows = reinterpret_cast<RowOut*>(ws + L.off_rows);
+  a.chunk = reinterpret_cast<float*>(ws + L.off_chunk);
+  a.toff = row_offsets;
+  a.rowmap = reinterpret_cast<int32_t*>(ws + L.off_map);
+  a.packed_ok = reinterpret_cast<int32_t*>(ws + L.off_map) + total_rows;
+  a.total_rows = total_rows;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
                         reinterpret_cast<uintptr_t>(draft_logits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);

@@ -115,6 +115,23 @@ def test_draft_loss_host_errors(lib):
     assert call(wsb=need - 1) == -4
 
 
+def test_packed_verify_host_errors(lib):
+    need = lv.spec_verify_packed_workspace_bytes(4, 10, 100)
+    assert need > 0
+    assert lv.spec_verify_packed_workspace_bytes(4, 3, 100) == 0        # fewer rows than requests
+    assert lv.spec_verify_packed_workspace_bytes(4, 4 * 17 + 1, 100) == 0
+    call = lambda **kw: lib.spec_verify_packed(*{**dict(
+        t=FAKE, d=FAKE, dtype=1, y=FAKE, off=FAKE, T=FAKE, seed=FAKE, B=4, rows=10, V=100,
+        acc=FAKE, tok=FAKE, alpha=FAKE, status=FAKE, ws=FAKE, wsb=need, stream=NULL),
+        **kw}.values())
+    assert call(dtype=2) == -3
+    assert call(rows=3) == -2
+    assert call(off=NULL) == -1
+    assert call(d=NULL) == -1
+    assert call(rows=4, d=NULL, y=NULL, alpha=NULL, wsb=0) == -4   # K_b = 0 for all: drafts optional
+    assert call(wsb=need - 1) == -4
+
+
 def test_schedule_host_errors(lib):
     call = lambda **kw: lib.dspark_schedule(*{**dict(
         c=FAKE, sps=FAKE, R=4, L=3, lens=FAKE, best=FAKE, stream=NULL), **kw}.values())
