@@ -33,8 +33,9 @@ Modules:
 * ``objectives`` -- the per-position comparators (per-step TV, CE, KL) with
   their gradients.
 * ``schedule`` -- confidence-scheduled verify lengths (DSpark).
+* ``truncate`` -- top-k / top-p truncation of p and q before the verify step.
 
 Parity status of each function is stated in its module header.
 """
 
-from . import bf16, loss, objectives, philox, schedule, verify  # noqa: F401
+from . import bf16, loss, objectives, philox, schedule, truncate, verify  # noqa: F401

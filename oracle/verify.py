@@ -59,7 +59,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16, philox
+from . import bf16, philox, truncate
 
 F32 = "f32"
 BF16 = "bf16"
@@ -68,6 +68,7 @@ STATUS_BAD_K = 1
 STATUS_BAD_TOKEN = 2
 STATUS_BAD_TEMPERATURE = 4
 STATUS_NONFINITE = 8
+STATUS_BAD_TRUNCATION = 16
 
 
 def decode_rows(raw, dtype):
@@ -138,7 +139,7 @@ def _row_fault(s):
 
 
 def verify_request(t_rows, d_rows, y, k_b, temperature, seed, b, kmax,
-                   uniforms=None):
+                   uniforms=None, top_k=0, top_p=1.0):
     """Verify one request.
 
     ``t_rows`` float32 [>= K_b+1, V], ``d_rows`` float32 [>= K_b, V] (decoded
@@ -148,6 +149,10 @@ def verify_request(t_rows, d_rows, y, k_b, temperature, seed, b, kmax,
     where no decision was taken), ``draw_margin``, ``residual`` (Z_k),
     ``greedy``. ``uniforms(seed, b, k) -> (u_accept, u_draw)`` defaults to
     the Philox mapping; the enumeration tests substitute lattice values.
+    ``top_k`` / ``top_p`` truncate p and q first (``truncate``; the defaults
+    keep every token); ``trunc_margin`` then reports the closest top-p
+    decision of the request's rows. A top_p that is NaN or <= 0 faults the
+    request with status 16.
     """
     if uniforms is None:
         uniforms = philox.verify_uniforms
@@ -160,8 +165,11 @@ def verify_request(t_rows, d_rows, y, k_b, temperature, seed, b, kmax,
         "draw_margin": np.nan,
         "status": 0,
         "greedy": False,
+        "trunc_margin": np.inf,
     }
     status = 0
+    if not (float(np.float32(top_p)) > 0.0):
+        status |= STATUS_BAD_TRUNCATION
     t_val = float(np.float32(temperature))
     if not (t_val >= 0.0) or np.isinf(t_val):
         status |= STATUS_BAD_TEMPERATURE
@@ -191,8 +199,12 @@ def verify_request(t_rows, d_rows, y, k_b, temperature, seed, b, kmax,
 
     s_t = [scale(t_rows[k], t_val) for k in range(k_b + 1)]
     s_d = [scale(d_rows[k], t_val) for k in range(k_b)]
-    p = [softmax64(s)[0] for s in s_t]
-    q = [softmax64(s)[0] for s in s_d]
+    top_p = float(np.float32(top_p))
+    pt = [truncate.truncated_softmax(s, top_k, top_p) for s in s_t]
+    qt = [truncate.truncated_softmax(s, top_k, top_p) for s in s_d]
+    p = [x[0] for x in pt]
+    q = [x[0] for x in qt]
+    out["trunc_margin"] = min([x[3] for x in pt + qt] + [np.inf])
 
     for k in range(k_b):
         out["alpha"][k], out["residual"][k] = overlap(p[k], q[k])
@@ -239,21 +251,24 @@ def _greedy(out, t_rows, d_rows, y, k_b):
 
 
 def spec_verify(target_logits, draft_logits, dtype, draft_tokens, k_per_req,
-                temperature, seed):
+                temperature, seed, top_k=None, top_p=None):
     """Batched verify.
 
     ``target_logits`` [B, Kmax+1, V] and ``draft_logits`` [B, Kmax, V] stored
     as float32 (dtype "f32") or uint16 bfloat16 patterns (dtype "bf16");
     ``draft_tokens`` int [B, Kmax]; ``k_per_req`` int [B]; ``temperature``
-    float [B]; ``seed`` uint64 [B]. Returns a dict of stacked per-request
-    results (see ``verify_request``).
+    float [B]; ``seed`` uint64 [B]; ``top_k`` int [B] and ``top_p`` float
+    [B] are optional (``truncate``; omitted: every token kept). Returns a dict
+    of stacked per-request results (see ``verify_request``).
     """
     batch = target_logits.shape[0]
     kmax = draft_logits.shape[1]
     res = [verify_request(decode_rows(target_logits[b], dtype),
                           decode_rows(draft_logits[b], dtype),
                           draft_tokens[b], k_per_req[b], temperature[b],
-                          int(seed[b]), b, kmax)
+                          int(seed[b]), b, kmax,
+                          top_k=0 if top_k is None else int(top_k[b]),
+                          top_p=1.0 if top_p is None else float(top_p[b]))
            for b in range(batch)]
     return {
         "accepted_len": np.array([r["accepted_len"] for r in res], dtype=np.int64),
@@ -264,6 +279,7 @@ def spec_verify(target_logits, draft_logits, dtype, draft_tokens, k_per_req,
         "draw_margin": np.array([r["draw_margin"] for r in res]),
         "status": np.array([r["status"] for r in res], dtype=np.int64),
         "greedy": np.array([r["greedy"] for r in res]),
+        "trunc_margin": np.array([r["trunc_margin"] for r in res]),
     }
 
 

@@ -14,6 +14,7 @@ import oracle.loss
 import oracle.objectives
 import oracle.philox
 import oracle.schedule
+import oracle.truncate
 import oracle.verify
 
 from . import test_oracle_bf16 as t_bf16
@@ -21,6 +22,7 @@ from . import test_oracle_loss as t_loss
 from . import test_oracle_objectives as t_obj
 from . import test_oracle_philox as t_philox
 from . import test_oracle_schedule as t_sched
+from . import test_oracle_truncate as t_trunc
 from . import test_oracle_verify as t_verify
 
 
@@ -109,6 +111,17 @@ CASES = [
      "theta = (R + s) * sps[R + np.arange(flat.size + 1)]",
      "theta = s * sps[R + np.arange(flat.size + 1)]",
      t_sched, "osch", "test_flat_curve_verifies_everything_and_collapse_verifies_nothing", ()),
+    ("top-p keeps one token too few", oracle.truncate,
+     'n = int(np.searchsorted(c, target, side="left")) + 1',
+     'n = int(np.searchsorted(c, target, side="left"))',
+     t_trunc, "ot", "test_top_p_matches_the_ascending_formulation", (0.5,)),
+    ("top-p measured against the untruncated mass", oracle.truncate,
+     "w = np.exp(s[idx[:m]] - np.max(s))", "w = np.exp(s[idx] - np.max(s))",
+     t_trunc, "ot", "test_top_k_then_top_p_uses_the_top_k_mass", ()),
+    ("equal logits kept in reverse token order", oracle.truncate,
+     "return np.lexsort((np.arange(s.size), -s))",
+     "return np.lexsort((-np.arange(s.size), -s))",
+     t_trunc, "ot", "test_equal_logits_kept_in_token_order", ()),
     ("Philox key not bumped between rounds", oracle.philox,
      "k0 = (k0 + _WEYL_A) & _MASK64", "k0 = k0",
      t_philox, "philox", "test_block_matches_numpy_random_counters", ()),
