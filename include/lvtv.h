@@ -75,6 +75,7 @@ extern "C" {
 #define LVTV_STATUS_BAD_TEMPERATURE 4 /* T_b negative, NaN or infinite         */
 #define LVTV_STATUS_NONFINITE 8       /* a used row holds NaN or +inf, or is
                                          entirely -inf (after scaling)         */
+#define LVTV_STATUS_BAD_TRUNCATION 16 /* top_p_b NaN or <= 0 (spec_verify_topkp) */
 
 int lvtv_version(void);
 const char* lvtv_strerror(int code);
@@ -188,6 +189,47 @@ int spec_verify_packed(const void* target_logits, const void* draft_logits, int 
                        int32_t total_rows, int32_t V, int32_t* accepted_len,
                        int32_t* out_tokens, float* alpha, int32_t* status,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes spec_verify_topkp needs (0 if out of range). Host only.
+ */
+size_t spec_verify_topkp_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype);
+
+/*
+ * spec_verify_topkp -- spec_verify with top-k / top-p truncation of p and q.
+ *
+ * The "Speculative Decoding and MTP" survey, section 4, has the verify step
+ * compare p and q after the same temperature and top-p / top-k transforms.
+ * The transforms (this library's reading; the pages do not spell them out),
+ * applied to every used row on its own, the target rows for p and the draft
+ * rows for q:
+ *   order the tokens by scaled logit s = fl32(x * fl32(1/T)) descending, the
+ *   lower token id first among equal s;
+ *   top-k: keep the first top_k[b] tokens (top_k[b] <= 0 or >= V: all);
+ *   top-p: of those, with weights e^(s - max s), keep the shortest prefix
+ *   whose weight reaches top_p[b] times their total (top_p[b] >= 1: all);
+ *   p (or q) is the softmax over the kept tokens, 0 elsewhere.
+ * The verify step then runs unchanged on the truncated p and q. Greedy
+ * requests (T = 0) are unaffected: the argmax is always kept.
+ *
+ * Arguments: as spec_verify, plus (device pointers)
+ *   top_k          int32 [B].
+ *   top_p          float [B]; NaN or <= 0 faults the request with
+ *                  LVTV_STATUS_BAD_TRUNCATION (combined with any other bits).
+ * The workspace must hold spec_verify_topkp_workspace_bytes(...) bytes.
+ * Which prefix top-p keeps is a floating-point decision: the kernel forms
+ * the weights in 64-bit fixed point to about 3e-7 of the kept total, so a
+ * request whose cumulative weight lies that close to top_p times the total
+ * may keep one token more or fewer than an exact computation would.
+ * Three kernels are enqueued: one radix selection per used row (a few
+ * passes over the row), then the row and finalize kernels of spec_verify.
+ */
+int spec_verify_topkp(const void* target_logits, const void* draft_logits, int dtype,
+                      const int32_t* draft_tokens, const int32_t* k_per_req,
+                      const float* temperature, const uint64_t* seed, const int32_t* top_k,
+                      const float* top_p, int32_t B, int32_t Kmax, int32_t V,
+                      int32_t* accepted_len, int32_t* out_tokens, float* alpha,
+                      int32_t* status, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes e2e_tv_loss_fwd_bwd needs (0 if out of range). Host only.

@@ -25,6 +25,7 @@ STATUS_BAD_K = 1
 STATUS_BAD_TOKEN = 2
 STATUS_BAD_TEMPERATURE = 4
 STATUS_NONFINITE = 8
+STATUS_BAD_TRUNCATION = 16
 
 EXPORTS = (
     "lvtv_version",
@@ -34,6 +35,8 @@ EXPORTS = (
     "spec_verify",
     "spec_verify_packed_workspace_bytes",
     "spec_verify_packed",
+    "spec_verify_topkp_workspace_bytes",
+    "spec_verify_topkp",
     "e2e_tv_loss_workspace_bytes",
     "e2e_tv_loss_fwd_bwd",
     "draft_loss_workspace_bytes",
@@ -81,6 +84,11 @@ def load_library(path: str = LIB_PATH):
         lib.spec_verify_packed.restype = ctypes.c_int
         lib.spec_verify_packed.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32,
                                            vp, vp, vp, vp, vp, sz, vp]
+        lib.spec_verify_topkp_workspace_bytes.restype = sz
+        lib.spec_verify_topkp_workspace_bytes.argtypes = [i32, i32, i32, ctypes.c_int]
+        lib.spec_verify_topkp.restype = ctypes.c_int
+        lib.spec_verify_topkp.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32,
+                                          i32, vp, vp, vp, vp, vp, sz, vp]
         lib.e2e_tv_loss_workspace_bytes.restype = sz
         lib.e2e_tv_loss_workspace_bytes.argtypes = [i32, i32, i32]
         lib.e2e_tv_loss_fwd_bwd.restype = ctypes.c_int
@@ -156,7 +164,7 @@ def spec_verify_workspace_bytes(B, Kmax, V, dtype=LVTV_BF16) -> int:
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperature, seed,
-                workspace=None, out=None):
+                workspace=None, out=None, top_k=None, top_p=None):
     """Verify step for B requests (see include/lvtv.h for the contract).
 
     target_logits [B, Kmax+1, V] and draft_logits [B, Kmax, V]: float32 or
@@ -165,9 +173,16 @@ def spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperatur
     (bit pattern used as the 64-bit Philox key). Returns (accepted_len
     int32 [B], out_tokens int32 [B, Kmax+1], alpha float32 [B, Kmax],
     status int32 [B]) on the device; no synchronisation.
+
+    With ``top_k`` (int32 [B]) and ``top_p`` (float32 [B]) the call is
+    spec_verify_topkp: p and q are truncated to each row's top-k, then top-p,
+    tokens before the verify step.
     """
     lib = load_library()
     dev = target_logits.device
+    trunc = top_k is not None or top_p is not None
+    _require(top_k is not None and top_p is not None or not trunc,
+             "top_k and top_p go together")
     _require(dev.type == "cuda", "spec_verify needs GPU tensors")
     _require(target_logits.dim() == 3 and draft_logits.dim() == 3, "logits must be 3-D")
     B, K1, V = target_logits.shape
@@ -183,13 +198,16 @@ def spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperatur
     for name, t, dt, shape in (("draft_tokens", draft_tokens, (torch.int32,), (B, Kmax)),
                                ("k_per_req", k_per_req, (torch.int32,), (B,)),
                                ("temperature", temperature, (torch.float32,), (B,)),
-                               ("seed", seed, (torch.int64, torch.uint64), (B,))):
+                               ("seed", seed, (torch.int64, torch.uint64), (B,))) + (
+            (("top_k", top_k, (torch.int32,), (B,)),
+             ("top_p", top_p, (torch.float32,), (B,))) if trunc else ()):
         _require(t.dtype in dt, f"{name} must be {dt}")
         _require(tuple(t.shape) == shape, f"{name} must have shape {shape}")
         _require(t.device == dev and t.is_contiguous(), f"{name} must be contiguous on {dev}")
     for t in (target_logits, draft_logits):
         _require(t.device == dev and t.is_contiguous(), "logits must be contiguous on one GPU")
-    need = lib.spec_verify_workspace_bytes(B, Kmax, V, dtype)
+    need = (lib.spec_verify_topkp_workspace_bytes if trunc else
+            lib.spec_verify_workspace_bytes)(B, Kmax, V, dtype)
     _require(need > 0, f"sizes out of range: B={B} Kmax={Kmax} V={V}")
     ws = workspace if workspace is not None else _workspace("verify", dev, need)
     if out is None:
@@ -200,12 +218,32 @@ def spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperatur
     else:
         acc, toks, alpha, status = out
     with torch.cuda.device(dev):
-        code = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype,
-                               _ptr(draft_tokens), _ptr(k_per_req), _ptr(temperature),
-                               _ptr(seed), B, Kmax, V, _ptr(acc), _ptr(toks), _ptr(alpha),
-                               _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
-    _check(code, "spec_verify")
+        if trunc:
+            code = lib.spec_verify_topkp(_ptr(target_logits), _ptr(draft_logits), dtype,
+                                         _ptr(draft_tokens), _ptr(k_per_req), _ptr(temperature),
+                                         _ptr(seed), _ptr(top_k), _ptr(top_p), B, Kmax, V,
+                                         _ptr(acc), _ptr(toks), _ptr(alpha), _ptr(status),
+                                         _ptr(ws), ws.numel(), _stream(dev))
+        else:
+            code = lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype,
+                                   _ptr(draft_tokens), _ptr(k_per_req), _ptr(temperature),
+                                   _ptr(seed), B, Kmax, V, _ptr(acc), _ptr(toks), _ptr(alpha),
+                                   _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
+    _check(code, "spec_verify_topkp" if trunc else "spec_verify")
     return acc, toks, alpha, status
+
+
+def spec_verify_topkp_workspace_bytes(B, Kmax, V, dtype=LVTV_BF16) -> int:
+    return int(load_library().spec_verify_topkp_workspace_bytes(B, Kmax, V, dtype))
+
+
+def spec_verify_topkp(target_logits, draft_logits, draft_tokens, k_per_req, temperature, seed,
+                      top_k, top_p, workspace=None, out=None):
+    """spec_verify with per-request top-k (int32 [B]; <= 0 or >= V: off) and
+    top-p (float32 [B]; >= 1: off, NaN or <= 0 faults the request with
+    STATUS_BAD_TRUNCATION) applied to p and q first."""
+    return spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperature, seed,
+                       workspace=workspace, out=out, top_k=top_k, top_p=top_p)
 
 
 def e2e_tv_loss_workspace_bytes(N, W, V) -> int:

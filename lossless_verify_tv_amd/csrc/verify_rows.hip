@@ -72,6 +72,36 @@ struct RowOut {
 };
 static_assert(sizeof(RowOut) == 32, "row record is 32 bytes");
 
+// Tokens a row keeps after top-k / top-p truncation: with d the order key of
+// a token's scaled logit s (larger s, smaller d), token v is kept iff
+// d < key, or d == key and v <= idx (equal s are kept in token order).
+struct KeepRow {
+  uint32_t key;
+  int32_t idx;
+};
+struct KeepPair {
+  KeepRow t, d;  // the target row and the draft row of one position
+};
+static_assert(sizeof(KeepPair) == 16, "keep record is 16 bytes");
+
+// Order key of a scaled logit: unsigned order of the key is descending order
+// of s (-0 and +0 share one key).
+__device__ __forceinline__ uint32_t desc_key(float s) {
+  const uint32_t u = (s == 0.f) ? 0u : __float_as_uint(s);
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+
+__device__ __forceinline__ float key_value(uint32_t d) {
+  const uint32_t asc = ~d;
+  return __uint_as_float((asc & 0x80000000u) ? (asc & 0x7fffffffu) : ~asc);
+}
+
+__device__ __forceinline__ bool keeps(const KeepRow& k, float s, int v) {
+  const uint32_t d = desc_key(s);
+  return d < k.key || (d == k.key && v <= k.idx);
+}
+
 struct Args {
   const void* target;
   const void* draft;
@@ -95,7 +125,13 @@ struct Args {
   const int32_t* rowmap;     // [total_rows]: the request of each target row (-1: bad offsets)
   const int32_t* packed_ok;  // the offsets tile [0, total_rows) (written by packed_map)
   int total_rows;
+  // top-k / top-p truncation (null when off)
+  const int32_t* top_k;  // [B]
+  const float* top_p;    // [B]
+  KeepPair* keep;        // one per target row, written by trunc_rows
 };
+
+__device__ __forceinline__ KeepRow keep_all() { return KeepRow{0xffffffffu, INT_MAX}; }
 
 __device__ __forceinline__ bool temperature_ok(float t) { return (t >= 0.f) && !isinf(t); }
 
@@ -323,7 +359,27 @@ __device__ __forceinline__ void load_tail(const void* row, int V, int t, Grp<kDt
   }
 }
 
-template <int kDtype, bool kVecOk, bool kPair>
+// Tokens of a group (first token e) that the row's truncation drops read as
+// -inf from here on.
+template <int kDtype>
+__device__ __forceinline__ void apply_keep(Grp<kDtype>& g, int e, const KeepRow& kr, float inv_t,
+                                           bool unit) {
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const float s = scale_logit(gelem(g, j), inv_t, unit);
+    if (!keeps(kr, s, e + j)) {
+      if constexpr (kDtype == 1) {
+        const uint32_t w = g.q[0][j >> 1];
+        g.q[0][j >> 1] =
+            (j & 1) ? ((w & 0x0000ffffu) | 0xff800000u) : ((w & 0xffff0000u) | 0x0000ff80u);
+      } else {
+        g.q[j >> 2][j & 3] = 0xff800000u;
+      }
+    }
+  }
+}
+
+template <int kDtype, bool kVecOk, bool kPair, bool kTrunc>
 __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float T, Shared& sh) {
   constexpr int kHold = hold_tiles<kDtype>();
   const int V = a.V;
@@ -334,6 +390,17 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
   const float c = (T == 1.f) ? kL2E : __fmul_rn(kL2E, __fdiv_rn(1.f, T));
   const void* trow = row_ptr<kDtype>(a, b, true, k);
   const void* drow = kPair ? row_ptr<kDtype>(a, b, false, k) : nullptr;
+  const float inv_t = __fdiv_rn(1.f, T);
+  const bool unit = (T == 1.f);
+  KeepPair kp{keep_all(), keep_all()};
+  if constexpr (kTrunc) kp = a.keep[target_row(a, b, k)];
+  // drops the truncated tokens of a loaded group of tile t
+  auto mk = [&](Grp<kDtype>& gt, Grp<kDtype>& gd, int tt) {
+    if constexpr (kTrunc) {
+      apply_keep<kDtype>(gt, tile_elem(tt), kp.t, inv_t, unit);
+      if constexpr (kPair) apply_keep<kDtype>(gd, tile_elem(tt), kp.d, inv_t, unit);
+    }
+  };
 
   // ---- pass 1: streamed full tiles, held full tiles, the partial tile
   float mt = -INFINITY, lt = 0.f, md = -INFINITY, ld = 0.f;
@@ -344,6 +411,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
     for (int n = 0; n < kBatch; ++n) {
       load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t + n), gt[n]);
       if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t + n), gd[n]);
+      mk(gt[n], gd[n], t + n);
     }
     online_batch<kDtype, kBatch>(gt, c, mt, lt);
     if constexpr (kPair) online_batch<kDtype, kBatch>(gd, c, md, ld);
@@ -352,6 +420,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
     Grp<kDtype> gt[1], gd[1];
     load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t), gt[0]);
     if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t), gd[0]);
+    mk(gt[0], gd[0], t);
     online_batch<kDtype, 1>(gt, c, mt, lt);
     if constexpr (kPair) online_batch<kDtype, 1>(gd, c, md, ld);
   }
@@ -361,6 +430,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
     for (int h = 0; h < kHold; ++h) {
       load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(nstream + h), ht[h]);
       if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(nstream + h), hd[h]);
+      mk(ht[h], hd[h], nstream + h);
     }
     online_batch<kDtype, kHold>(ht, c, mt, lt);
     if constexpr (kPair) online_batch<kDtype, kHold>(hd, c, md, ld);
@@ -371,6 +441,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
         Grp<kDtype> g1[1], g2[1];
         load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(nstream + h), g1[0]);
         if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(nstream + h), g2[0]);
+        mk(g1[0], g2[0], nstream + h);
         online_batch<kDtype, 1>(g1, c, mt, lt);
         if constexpr (kPair) online_batch<kDtype, 1>(g2, c, md, ld);
         ht[h] = g1[0];
@@ -380,6 +451,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
   if (tail) {
     load_tail<kDtype, kVecOk>(trow, V, nfull, tt[0]);
     if constexpr (kPair) load_tail<kDtype, kVecOk>(drow, V, nfull, td[0]);
+    mk(tt[0], td[0], nfull);
     online_batch<kDtype, 1>(tt, c, mt, lt);
     if constexpr (kPair) online_batch<kDtype, 1>(td, c, md, ld);
   }
@@ -411,6 +483,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
     for (int n = 0; n < kBatch; ++n) {
       load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t - 1 - n), gt[n]);
       if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t - 1 - n), gd[n]);
+      mk(gt[n], gd[n], t - 1 - n);
     }
 #pragma unroll
     for (int n = 0; n < kBatch; ++n)
@@ -420,6 +493,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
     Grp<kDtype> gt, gd;
     load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t - 1), gt);
     if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t - 1), gd);
+    mk(gt, gd, t - 1);
     overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, t - 1);
   }
   const float alpha = kPair ? block_sum1(sa, sh) : 0.f;
@@ -523,7 +597,7 @@ __device__ __forceinline__ void greedy_row(const Args& a, int b, int k, bool pai
 
 // ------------------------------------------------------------------ row kernel
 
-template <int kDtype, bool kVecOk>
+template <int kDtype, bool kVecOk, bool kTrunc>
 __device__ __forceinline__ void rows_body(const Args& a) {
   __shared__ Shared sh;
   int b, k, kb;
@@ -542,21 +616,418 @@ __device__ __forceinline__ void rows_body(const Args& a) {
   if (T == 0.f) {
     greedy_row<kDtype, kVecOk>(a, b, k, k < kb, sh);
   } else if (k < kb) {
-    sampling_row<kDtype, kVecOk, true>(a, b, k, T, sh);
+    sampling_row<kDtype, kVecOk, true, kTrunc>(a, b, k, T, sh);
   } else {
-    sampling_row<kDtype, kVecOk, false>(a, b, k, T, sh);
+    sampling_row<kDtype, kVecOk, false, kTrunc>(a, b, k, T, sh);
   }
 }
 
-template <bool kVecOk>
+template <bool kVecOk, bool kTrunc>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 verify_rows_bf16(Args a) {
-  rows_body<1, kVecOk>(a);
+  rows_body<1, kVecOk, kTrunc>(a);
 }
 
-template <bool kVecOk>
+template <bool kVecOk, bool kTrunc>
 __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
-  rows_body<0, kVecOk>(a);
+  rows_body<0, kVecOk, kTrunc>(a);
+}
+
+// ------------------------------------------------------------------ truncation
+//
+// trunc_rows finds, for each used row of a sampling request, the prefix of
+// the row's tokens (scaled logit descending, then token id) that top-k and
+// then top-p keep, as a KeepRow. Radix selection on the 32-bit order key d in
+// three levels, bits [21, 32), [10, 21) and [0, 10): one pass over the row per
+// level builds LDS histograms of token counts (top-k) or of fixed-point
+// masses (top-p) of the tokens under the prefix chosen so far, and a block
+// scan picks the bucket where the running count or mass reaches its target.
+// A level ends the search early when its bucket holds a single key (with
+// bf16 logits the second level always does). When the kept prefix ends
+// inside a run of equal keys, a last pass finds the token id it ends at.
+//
+// Masses are e^(s - M) 2^E truncated to integers (M the row maximum, E = 63 -
+// bits(V) so that a row's total cannot pass 2^63), formed to about two
+// binary32 ulps whatever s - M is and summed exactly in 64 bits: the sums are
+// deterministic, and within about 3e-7 of the exact ones relative to the kept
+// total for vocabularies up to a few million.
+
+constexpr int kL1Shift = 21, kL2Shift = 10;
+constexpr int kL1Buckets = 2048, kL2Buckets = 2048, kL3Buckets = 1024;
+constexpr float kL2ELo = 1.925963033e-8f;  // log2(e) - fl32(log2(e))
+
+struct TruncShared {
+  uint32_t cnt[kL1Buckets];
+  unsigned long long mass[kL1Buckets];
+  uint32_t kmin[kL2Buckets], kmax[kL2Buckets];
+  unsigned long long part[kWaves];
+  unsigned long long res64;
+  int32_t res32;
+  float fmax[kWaves];
+};
+
+// e^(s - M) 2^E truncated, `scale` = 2^E; s <= M, both finite (or s = -inf:
+// 0). The difference is split exactly (two-sum) and the base change by an
+// FMA, so the exponent's rounding does not grow with M - s.
+__device__ __forceinline__ uint64_t fixed_mass(float s, float M, float scale) {
+  const float d = s - M;
+  const float sv = d + M;
+  const float dlo = (s - sv) + (-M - (d - sv));
+  const float th = __fmul_rn(d, kL2E);
+  if (!(th > -64.f)) return 0;
+  const float tl = __builtin_fmaf(d, kL2E, -th) + __builtin_fmaf(d, kL2ELo, dlo * kL2E);
+  const float w = __builtin_amdgcn_exp2f(th) * __builtin_fmaf(tl, 0.693147182f, 1.f);
+  return (uint64_t)(w * scale);
+}
+
+// One pass over a row: f(s, v) for every token v < V with its scaled logit,
+// four tiles of loads in flight.
+template <int kDtype, bool kVecOk, class F>
+__device__ __forceinline__ void row_pass(const void* row, int V, float inv_t, bool unit, F&& f) {
+  const int nt = (V + kTile - 1) / kTile;
+  int t = 0;
+  for (; t + kBatch <= nt; t += kBatch) {
+    Grp<kDtype> g[kBatch];
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n) load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t + n), g[n]);
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n)
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int v = tile_elem(t + n) + j;
+        if (v < V) f(scale_logit(gelem(g[n], j), inv_t, unit), v);
+      }
+  }
+  for (; t < nt; ++t) {
+    Grp<kDtype> g;
+    load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t), g);
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const int v = tile_elem(t) + j;
+      if (v < V) f(scale_logit(gelem(g, j), inv_t, unit), v);
+    }
+  }
+}
+
+// Block-wide exclusive scan of 64-bit integers; `total` gets the sum.
+__device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, TruncShared& ts,
+                                                     uint64_t& total) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  uint64_t inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint64_t n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) ts.part[wave] = inc;
+  __syncthreads();
+  uint64_t pre = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) pre += ts.part[w];
+    total += ts.part[w];
+  }
+  return pre + inc - v;
+}
+
+// The bucket b of h[0, nb) whose running sum reaches r (sum h[< b] < r <=
+// sum h[<= b], r >= 1), with sum h[< b] in `before`; the last bucket if the
+// total is below r. nb is a multiple of the block size.
+template <class T>
+__device__ __forceinline__ int select_bucket(const T* h, int nb, uint64_t r, uint64_t& before,
+                                             TruncShared& ts) {
+  const int per = nb / kThreads;
+  const int b0 = threadIdx.x * per;
+  uint64_t mine = 0;
+  for (int i = 0; i < per; ++i) mine += h[b0 + i];
+  uint64_t total;
+  const uint64_t exc = block_exscan_u64(mine, ts, total);
+  if (exc < r && r <= exc + mine) {
+    uint64_t run = exc;
+    int b = b0 + per - 1;
+    for (int i = 0; i < per; ++i) {
+      if (run + h[b0 + i] >= r) {
+        b = b0 + i;
+        break;
+      }
+      run += h[b0 + i];
+    }
+    ts.res32 = b;
+    ts.res64 = run;
+  } else if (r > total && threadIdx.x == kThreads - 1) {
+    ts.res32 = nb - 1;
+    ts.res64 = total - h[nb - 1];
+  }
+  __syncthreads();
+  before = ts.res64;
+  const int b = ts.res32;
+  __syncthreads();
+  return b;
+}
+
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, TruncShared& ts) {
+  uint64_t total;
+  (void)block_exscan_u64(v, ts, total);
+  return total;
+}
+
+__device__ __forceinline__ float block_max_f(float v, TruncShared& ts) {
+  v = wmax(v);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) ts.fmax[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float r = ts.fmax[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, ts.fmax[w]);
+  return r;
+}
+
+__device__ __forceinline__ void clear_hist(TruncShared& ts, bool minmax) {
+  for (int i = threadIdx.x; i < kL1Buckets; i += kThreads) {
+    ts.cnt[i] = 0;
+    ts.mass[i] = 0;
+    if (minmax) {
+      ts.kmin[i] = 0xffffffffu;
+      ts.kmax[i] = 0;
+    }
+  }
+  __syncthreads();
+}
+
+// Token id of the n-th token (in id order, n >= 1) whose key is `key`; every
+// thread gets it.
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t, bool unit,
+                                            uint32_t key, uint64_t n, TruncShared& ts) {
+  if (threadIdx.x == 0) ts.res32 = INT_MAX;
+  const int nt = (V + kTile - 1) / kTile;
+  uint64_t run = 0;  // matches in the tiles before t
+  for (int t = 0; t < nt && run < n; t += 4) {
+    Grp<kDtype> g[4];
+    uint64_t mine = 0;  // this thread's matches per tile, 16 bits each
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (t + i < nt)
+        load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t + i), g[i]);
+      else
+        fill_grp(g[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint64_t c = 0;
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int v = tile_elem(t + i) + j;
+        c += (t + i < nt && v < V && desc_key(scale_logit(gelem(g[i], j), inv_t, unit)) == key);
+      }
+      mine |= c << (16 * i);
+    }
+    uint64_t total;
+    const uint64_t exc = block_exscan_u64(mine, ts, total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t before = run + ((exc >> (16 * i)) & 0xffff);
+      const uint64_t c = (mine >> (16 * i)) & 0xffff;
+      if (before < n && n <= before + c) {
+        uint64_t seen = before;
+        for (int j = 0; j < kVec; ++j) {
+          const int v = tile_elem(t + i) + j;
+          if (v < V && desc_key(scale_logit(gelem(g[i], j), inv_t, unit)) == key && ++seen == n) {
+            ts.res32 = v;
+            break;
+          }
+        }
+      }
+      run += (total >> (16 * i)) & 0xffff;
+    }
+  }
+  __syncthreads();
+  return ts.res32;
+}
+
+template <int kDtype, bool kVecOk>
+__device__ __forceinline__ void trunc_body(const Args& a) {
+  __shared__ TruncShared ts;
+  const bool draft = blockIdx.x & 1;
+  const int slot = blockIdx.x >> 1;  // target row slot
+  int b, k, kb;
+  if (a.toff) {
+    b = a.rowmap[slot];
+    if (b < 0) return;
+    k = slot - a.toff[b];
+    kb = a.toff[b + 1] - a.toff[b] - 1;
+  } else {
+    b = slot / (a.Kmax + 1);
+    k = slot - b * (a.Kmax + 1);
+    kb = a.kreq[b];
+  }
+  const float T = a.temp[b];
+  if (!(kb >= 0 && kb <= a.Kmax && temperature_ok(T)) || T == 0.f || k > kb || (draft && k == kb))
+    return;  // a row the rows kernel does not sample
+  KeepRow* out = draft ? &a.keep[target_row(a, b, k)].d : &a.keep[target_row(a, b, k)].t;
+  const int V = a.V;
+  const int top_k = a.top_k[b];
+  const float top_p = a.top_p[b];
+  const bool k_on = top_k >= 1 && top_k < V;
+  const bool p_on = top_p < 1.f;
+  if (!(top_p > 0.f) || !(k_on || p_on)) {  // a bad top_p faults the request
+    if (threadIdx.x == 0) *out = keep_all();
+    return;
+  }
+  const void* row = row_ptr<kDtype>(a, b, !draft, k);
+  const float inv_t = __fdiv_rn(1.f, T);
+  const bool unit = (T == 1.f);
+  const float scale = __builtin_ldexpf(1.f, 63 - (32 - __clz(V)));
+
+  // ---- pass 1: the maximum, faults, top-k's first-level counts
+  clear_hist(ts, false);
+  float mx = -INFINITY;
+  int bad = 0;
+  row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
+    bad |= (s != s) | (s == INFINITY);
+    mx = fmaxf(mx, s);
+    if (k_on) atomicAdd(&ts.cnt[desc_key(s) >> kL1Shift], 1u);
+  });
+  bad = __syncthreads_or(bad);
+  const float M = block_max_f(mx, ts);
+  if (bad || M == -INFINITY) {  // the rows kernel faults the row: leave it whole
+    if (threadIdx.x == 0) *out = keep_all();
+    return;
+  }
+
+  // ---- top-k: the top_k-th token's key, its rank among equal keys, and how
+  // many tokens share the key
+  uint32_t keyK = 0xffffffffu;
+  uint64_t nK = 0, tieK = 0;
+  if (k_on) {
+    uint64_t before, rank = uint64_t(top_k);
+    const uint32_t b1 = select_bucket(ts.cnt, kL1Buckets, rank, before, ts);
+    rank -= before;
+    clear_hist(ts, true);
+    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
+      const uint32_t d = desc_key(s);
+      if ((d >> kL1Shift) == b1) {
+        const uint32_t i = (d >> kL2Shift) & (kL2Buckets - 1);
+        atomicAdd(&ts.cnt[i], 1u);
+        atomicMin(&ts.kmin[i], d);
+        atomicMax(&ts.kmax[i], d);
+      }
+    });
+    __syncthreads();
+    const uint32_t b2 = select_bucket(ts.cnt, kL2Buckets, rank, before, ts);
+    rank -= before;
+    const uint32_t lo = ts.kmin[b2], hi = ts.kmax[b2], n2 = ts.cnt[b2];
+    __syncthreads();
+    if (lo == hi) {
+      keyK = lo;
+      tieK = n2;
+    } else {
+      const uint32_t pre = (b1 << 11) | b2;
+      clear_hist(ts, false);
+      row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
+        const uint32_t d = desc_key(s);
+        if ((d >> kL2Shift) == pre) atomicAdd(&ts.cnt[d & (kL3Buckets - 1)], 1u);
+      });
+      __syncthreads();
+      const uint32_t b3 = select_bucket(ts.cnt, kL3Buckets, rank, before, ts);
+      rank -= before;
+      keyK = (pre << kL2Shift) | b3;
+      tieK = ts.cnt[b3];
+      __syncthreads();
+    }
+    nK = rank;
+  }
+
+  // ---- top-p over the top-k set: the key where the running mass reaches
+  // top_p times the set's mass, and its rank among equal keys
+  uint32_t key = keyK;
+  uint64_t n = nK, ties = tieK;
+  if (p_on) {
+    // tokens of key keyK beyond the top_k-th are outside the set
+    const uint64_t excess = k_on ? (tieK - nK) * fixed_mass(key_value(keyK), M, scale) : 0;
+    clear_hist(ts, false);
+    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
+      const uint32_t d = desc_key(s);
+      if (d <= keyK) {
+        const uint64_t m = fixed_mass(s, M, scale);
+        if (m) atomicAdd(&ts.mass[d >> kL1Shift], (unsigned long long)m);
+      }
+    });
+    __syncthreads();
+    if (k_on && threadIdx.x == 0) ts.mass[keyK >> kL1Shift] -= excess;
+    __syncthreads();
+    uint64_t mine = 0;
+    for (int i = 0; i < kL1Buckets / kThreads; ++i) mine += ts.mass[threadIdx.x * (kL1Buckets / kThreads) + i];
+    const uint64_t W = block_sum_u64(mine, ts);
+    uint64_t need = (uint64_t)ceil((double)top_p * (double)W);
+    need = need < 1 ? 1 : (need > W ? W : need);
+    uint64_t before;
+    const uint32_t b1 = select_bucket(ts.mass, kL1Buckets, need, before, ts);
+    uint64_t rem = need - before;
+    clear_hist(ts, true);
+    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
+      const uint32_t d = desc_key(s);
+      if ((d >> kL1Shift) == b1 && d <= keyK) {
+        const uint32_t i = (d >> kL2Shift) & (kL2Buckets - 1);
+        const uint64_t m = fixed_mass(s, M, scale);
+        if (m) atomicAdd(&ts.mass[i], (unsigned long long)m);
+        atomicMin(&ts.kmin[i], d);
+        atomicMax(&ts.kmax[i], d);
+      }
+    });
+    __syncthreads();
+    if (k_on && threadIdx.x == 0 && (keyK >> kL1Shift) == b1)
+      ts.mass[(keyK >> kL2Shift) & (kL2Buckets - 1)] -= excess;
+    __syncthreads();
+    const uint32_t b2 = select_bucket(ts.mass, kL2Buckets, rem, before, ts);
+    rem -= before;
+    const uint32_t lo = ts.kmin[b2], hi = ts.kmax[b2];
+    uint64_t bucket_mass = ts.mass[b2];
+    __syncthreads();
+    if (lo == hi) {
+      key = lo;
+    } else {
+      const uint32_t pre = (b1 << 11) | b2;
+      clear_hist(ts, false);
+      row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
+        const uint32_t d = desc_key(s);
+        if ((d >> kL2Shift) == pre && d <= keyK) {
+          const uint64_t m = fixed_mass(s, M, scale);
+          if (m) atomicAdd(&ts.mass[d & (kL3Buckets - 1)], (unsigned long long)m);
+        }
+      });
+      __syncthreads();
+      if (k_on && threadIdx.x == 0 && (keyK >> kL2Shift) == pre)
+        ts.mass[keyK & (kL3Buckets - 1)] -= excess;
+      __syncthreads();
+      const uint32_t b3 = select_bucket(ts.mass, kL3Buckets, rem, before, ts);
+      rem -= before;
+      key = (pre << kL2Shift) | b3;
+      bucket_mass = ts.mass[b3];
+      __syncthreads();
+    }
+    // every token of one key has the same mass; the bucket reached holds
+    // positive mass, so w > 0
+    const uint64_t w = fixed_mass(key_value(key), M, scale);
+    if (w == 0) {  // not reached: kept for a defined result
+      n = 1;
+      ties = 1;
+    } else {
+      n = (rem + w - 1) / w;
+      ties = (k_on && key == keyK) ? tieK : bucket_mass / w;
+    }
+  }
+
+  const int idx = (n < ties) ? nth_with_key<kDtype, kVecOk>(row, V, inv_t, unit, key, n, ts)
+                             : INT_MAX;
+  if (threadIdx.x == 0) *out = KeepRow{key, idx};
+}
+
+template <int kDtype, bool kVecOk>
+__global__ __launch_bounds__(kThreads) void trunc_rows(Args a) {
+  trunc_body<kDtype, kVecOk>(a);
 }
 
 // ------------------------------------------------------------------ finalize
@@ -594,11 +1065,13 @@ __device__ __forceinline__ int block_min(int v, Shared& sh) {
   return r;
 }
 
-// fp64 probability of token v under a row's (R, L), base-2 convention.
+// fp64 probability of token v under a row's (R, L), base-2 convention; 0 for
+// a token the row's truncation drops.
 template <int kDtype>
 __device__ __forceinline__ double prob64(const void* row, int v, float inv_t, bool unit, float R,
-                                         float L) {
+                                         float L, const KeepRow& kr) {
   const float s = scale_logit(load1<kDtype>(row, v), inv_t, unit);
+  if (!keeps(kr, s, v)) return 0.0;
   return exp2((double)s * (double)kL2E - (double)R) / (double)L;
 }
 
@@ -645,16 +1118,18 @@ __device__ __forceinline__ int pick_chunk(const float* m, int NC, double u, Shar
 // Token of chunk c at remaining mass `rem`: fp64 weights of the chunk's 512
 // tokens (one per thread), rescaled so they sum to the chunk's mass `cmass`
 // (the unit the chunk was chosen in); the first token whose running weight
-// passes `rem`, else the last token of positive weight.
+// passes `rem`, else the last token of positive weight; -1 if no token of
+// the chunk has positive weight.
 template <int kDtype>
 __device__ __forceinline__ int search_chunk(const void* trow, const void* drow, int V, int c,
                                             double rem, double cmass, float inv_t, bool unit,
-                                            float Rt, float Lt, float Rd, float Ld, Shared& sh) {
+                                            float Rt, float Lt, float Rd, float Ld,
+                                            const KeepPair& kp, Shared& sh) {
   const int v = c * kChunk + (int)threadIdx.x;
   double w = 0.0;
   if (threadIdx.x < kChunk && v < V) {
-    const double p = prob64<kDtype>(trow, v, inv_t, unit, Rt, Lt);
-    w = drow ? fmax(0.0, p - prob64<kDtype>(drow, v, inv_t, unit, Rd, Ld)) : p;
+    const double p = prob64<kDtype>(trow, v, inv_t, unit, Rt, Lt, kp.t);
+    w = drow ? fmax(0.0, p - prob64<kDtype>(drow, v, inv_t, unit, Rd, Ld, kp.d)) : p;
   }
   double total;
   const double exc = block_exscan(w, sh, total);
@@ -662,7 +1137,7 @@ __device__ __forceinline__ int search_chunk(const void* trow, const void* drow, 
   int pick = block_min((w > 0.0 && (exc + w) * f > rem) ? v : INT_MAX, sh);
   if (pick == INT_MAX) {
     const int last = -block_min(w > 0.0 ? -v : INT_MAX, sh);
-    pick = (last == -INT_MAX) ? c * kChunk : last;
+    pick = (last == -INT_MAX) ? -1 : last;
   }
   return pick;
 }
@@ -671,7 +1146,8 @@ __device__ __forceinline__ int search_chunk(const void* trow, const void* drow, 
 // rejection meets an all-zero residual, p_j == q_j).
 template <int kDtype>
 __device__ __forceinline__ void p_chunk_masses(const void* trow, int V, int NC, float inv_t,
-                                               bool unit, float Rt, float Lt, float* m) {
+                                               bool unit, float Rt, float Lt, const KeepRow& kr,
+                                               float* m) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   for (int c = wave; c < NC; c += kWaves) {
     float s = 0.f;
@@ -679,7 +1155,7 @@ __device__ __forceinline__ void p_chunk_masses(const void* trow, int V, int NC, 
     for (int j = 0; j < kVec; ++j) {
       const int v = c * kChunk + lane * kVec + j;
       if (v < V)
-        s += (float)prob64<kDtype>(trow, v, inv_t, unit, Rt, Lt);
+        s += (float)prob64<kDtype>(trow, v, inv_t, unit, Rt, Lt, kr);
     }
     s = wsum(s);
     if (lane == 0) m[c] = s;
@@ -733,29 +1209,30 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
     kb = a.kreq[b];
     o = Slots{a.out_tokens + size_t(b) * (Kmax + 1), a.alpha + size_t(b) * Kmax, Kmax + 1, Kmax};
   }
-  if (!(kb >= 0 && kb <= Kmax && temperature_ok(T))) {
-    int st = 0;
-    if (!temperature_ok(T)) st |= LVTV_STATUS_BAD_TEMPERATURE;
-    if (kb < 0 || kb > Kmax) st |= LVTV_STATUS_BAD_K;
-    write_fault(a, b, st, o);
-    return;
-  }
+  // faults: the draft tokens are checked whenever K_b is valid, the rows
+  // only when the temperature is valid too (they are not computed otherwise)
+  const bool k_ok = kb >= 0 && kb <= Kmax, t_ok = temperature_ok(T);
+  const bool greedy = (T == 0.f);
   const int32_t* y = a.tokens + draft_row(a, b, 0);
   const RowOut* rows = a.rows + target_row(a, b, 0);
-  const bool greedy = (T == 0.f);
   int bad = 0, fault = 0;
-  for (int k = threadIdx.x; k <= kb; k += kThreads) {
-    const RowOut r = rows[k];
-    if (k < kb) bad |= (y[k] < 0 || y[k] >= a.V);
-    if (greedy) {
-      fault |= (r.nan & 1) || !isfinite(r.Rt);
-      if (k < kb) fault |= (r.nan & 2) || !isfinite(r.Rd);
-    } else {
-      fault |= !isfinite(r.Rt) || !isfinite(r.Lt) || !(r.Lt > 0.f);
-      if (k < kb) fault |= !isfinite(r.Rd) || !isfinite(r.Ld) || !(r.Ld > 0.f);
+  if (k_ok) {
+    for (int k = threadIdx.x; k <= kb; k += kThreads) {
+      if (k < kb) bad |= (y[k] < 0 || y[k] >= a.V);
+      if (!t_ok) continue;
+      const RowOut r = rows[k];
+      if (greedy) {
+        fault |= (r.nan & 1) || !isfinite(r.Rt);
+        if (k < kb) fault |= (r.nan & 2) || !isfinite(r.Rd);
+      } else {
+        fault |= !isfinite(r.Rt) || !isfinite(r.Lt) || !(r.Lt > 0.f);
+        if (k < kb) fault |= !isfinite(r.Rd) || !isfinite(r.Ld) || !(r.Ld > 0.f);
+      }
     }
   }
-  const int status = (__syncthreads_or(bad) ? LVTV_STATUS_BAD_TOKEN : 0) |
+  const int status = (k_ok ? 0 : LVTV_STATUS_BAD_K) | (t_ok ? 0 : LVTV_STATUS_BAD_TEMPERATURE) |
+                     ((a.top_p && !(a.top_p[b] > 0.f)) ? LVTV_STATUS_BAD_TRUNCATION : 0) |
+                     (__syncthreads_or(bad) ? LVTV_STATUS_BAD_TOKEN : 0) |
                      (__syncthreads_or(fault) ? LVTV_STATUS_NONFINITE : 0);
   if (status) {
     write_fault(a, b, status, o);
@@ -790,8 +1267,11 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
     verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
     fs.uacc[k] = u;
     const RowOut r = rows[k];
-    const double p = prob64<kDtype>(row_ptr<kDtype>(a, b, true, k), y[k], inv_t, unit, r.Rt, r.Lt);
-    const double q = prob64<kDtype>(row_ptr<kDtype>(a, b, false, k), y[k], inv_t, unit, r.Rd, r.Ld);
+    const KeepPair kp = a.keep ? a.keep[target_row(a, b, k)] : KeepPair{keep_all(), keep_all()};
+    const double p =
+        prob64<kDtype>(row_ptr<kDtype>(a, b, true, k), y[k], inv_t, unit, r.Rt, r.Lt, kp.t);
+    const double q =
+        prob64<kDtype>(row_ptr<kDtype>(a, b, false, k), y[k], inv_t, unit, r.Rd, r.Ld, kp.d);
     // q == 0: accept iff p > 0, encoded as an infinite or zero ratio
     fs.ratio[k] = (q == 0.0) ? (p > 0.0 ? INFINITY : 0.0) : p / q;
   }
@@ -818,18 +1298,28 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const void* drow = residual ? row_ptr<kDtype>(a, b, false, j) : nullptr;
   float* m = a.chunk + size_t(target_row(a, b, j)) * a.NC;
   const int NC = a.NC;
+  const KeepPair kp = a.keep ? a.keep[target_row(a, b, j)] : KeepPair{keep_all(), keep_all()};
   int any = 0;
   for (int c = threadIdx.x; c < NC; c += kThreads) any |= m[c] > 0.f;
   if (residual && !__syncthreads_or(any)) {
     // residual zero everywhere: draw from p_j
-    p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, m);
+    p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, kp.t, m);
     drow = nullptr;
   }
   double rem;
   const int c = pick_chunk(m, NC, u_draw, sh, rem);
   const double cmass = (double)m[c];
   int v = search_chunk<kDtype>(trow, drow, a.V, c, rem, cmass, inv_t, unit, r.Rt, r.Lt, r.Rd,
-                               r.Ld, sh);
+                               r.Ld, kp, sh);
+  if (v < 0 && drow) {
+    // The chunk's residual mass was rounding noise (p_j and q_j agree to
+    // within it, as when both are truncated to one token): the residual is
+    // zero, draw from p_j.
+    p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, kp.t, m);
+    const int c2 = pick_chunk(m, NC, u_draw, sh, rem);
+    v = search_chunk<kDtype>(trow, nullptr, a.V, c2, rem, (double)m[c2], inv_t, unit, r.Rt, r.Lt,
+                             r.Rd, r.Ld, kp, sh);
+  }
   if (v < 0 || v >= a.V) v = a.V - 1;  // unreachable: the chosen chunk has positive mass
   if (threadIdx.x == 0) {
     for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? y[k] : (k == j ? v : -1);
@@ -849,12 +1339,13 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   int n_tiles, NC;
-  size_t off_rows, off_chunk, off_map, total;
+  size_t off_rows, off_chunk, off_map, off_keep, total;
 };
 
 // `rows` target rows (B (Kmax + 1) padded, total_rows packed); the row map
-// and its validity flag only for the packed layout.
-Layout make_layout(size_t rows, int V, bool packed) {
+// and its validity flag only for the packed layout, the keep records only
+// with truncation.
+Layout make_layout(size_t rows, int V, bool packed, bool trunc = false) {
   Layout L;
   L.n_tiles = (V + kTile - 1) / kTile;
   L.NC = L.n_tiles * kWaves;
@@ -865,6 +1356,8 @@ Layout make_layout(size_t rows, int V, bool packed) {
   off = align256(off + sizeof(float) * rows * L.NC);
   L.off_map = off;
   if (packed) off = align256(off + sizeof(int32_t) * (rows + 1));
+  L.off_keep = off;
+  if (trunc) off = align256(off + sizeof(KeepPair) * rows);
   L.total = off;
   return L;
 }
@@ -910,47 +1403,45 @@ hipError_t launch(const Args& a, hipStream_t stream) {
   }
   const unsigned grid =
       a.toff ? unsigned(a.total_rows) : unsigned(a.B) * unsigned(a.Kmax + 1);
-  if constexpr (kDtype == 1)
-    hipLaunchKernelGGL(verify_rows_bf16<kVecOk>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(verify_rows_f32<kVecOk>, dim3(grid), dim3(kThreads), 0, stream, a);
+  if (a.keep) {
+    hipLaunchKernelGGL((trunc_rows<kDtype, kVecOk>), dim3(2 * grid), dim3(kThreads), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if constexpr (kDtype == 1)
+      hipLaunchKernelGGL((verify_rows_bf16<kVecOk, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((verify_rows_f32<kVecOk, true>), dim3(grid), dim3(kThreads), 0, stream, a);
+  } else {
+    if constexpr (kDtype == 1)
+      hipLaunchKernelGGL((verify_rows_bf16<kVecOk, false>), dim3(grid), dim3(kThreads), 0, stream,
+                         a);
+    else
+      hipLaunchKernelGGL((verify_rows_f32<kVecOk, false>), dim3(grid), dim3(kThreads), 0, stream,
+                         a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(verify_finalize<kDtype>, dim3(unsigned(a.B)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-}  // namespace
-}  // namespace vr
-}  // namespace lvtv
-
-extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype) {
-  if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
-  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false).total;
-}
-
-extern "C" size_t spec_verify_packed_workspace_bytes(int32_t B, int32_t total_rows, int32_t V,
-                                                      int dtype) {
-  if (!lvtv::vr::packed_sizes_ok(B, total_rows, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16))
-    return 0;
-  return lvtv::vr::make_layout(size_t(total_rows), V, true).total;
-}
-
-extern "C" int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
-                           const int32_t* draft_tokens, const int32_t* k_per_req,
-                           const float* temperature, const uint64_t* seed, int32_t B,
-                           int32_t Kmax, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
-                           float* alpha, int32_t* status, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  using namespace lvtv;
-  using namespace lvtv::vr;
+// The padded-layout verify, with top-k / top-p truncation when top_k and
+// top_p are given.
+int verify_padded(const void* target_logits, const void* draft_logits, int dtype,
+                  const int32_t* draft_tokens, const int32_t* k_per_req, const float* temperature,
+                  const uint64_t* seed, const int32_t* top_k, const float* top_p, int32_t B,
+                  int32_t Kmax, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                  float* alpha, int32_t* status, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   if (dtype != LVTV_F32 && dtype != LVTV_BF16) return LVTV_ERR_DTYPE;
   if (!sizes_ok(B, Kmax, V)) return LVTV_ERR_SHAPE;
   if (!target_logits || !k_per_req || !temperature || !seed || !accepted_len || !out_tokens ||
       !status)
     return LVTV_ERR_NULL;
   if (Kmax > 0 && (!draft_logits || !draft_tokens || !alpha)) return LVTV_ERR_NULL;
-  const Layout L = make_layout(size_t(B) * (Kmax + 1), V, false);
+  const bool trunc = top_k || top_p;
+  if (trunc && !(top_k && top_p)) return LVTV_ERR_NULL;
+  const Layout L = make_layout(size_t(B) * (Kmax + 1), V, false, trunc);
   if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
   Args a;
@@ -976,6 +1467,9 @@ extern "C" int spec_verify(const void* target_logits, const void* draft_logits, 
   a.rowmap = nullptr;
   a.packed_ok = nullptr;
   a.total_rows = B * (Kmax + 1);
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.keep = trunc ? reinterpret_cast<KeepPair*>(ws + L.off_keep) : nullptr;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
                         reinterpret_cast<uintptr_t>(draft_logits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
@@ -986,6 +1480,52 @@ extern "C" int spec_verify(const void* target_logits, const void* draft_logits, 
   else
     e = vec_ok ? launch<0, true>(a, s) : launch<0, false>(a, s);
   return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace vr
+}  // namespace lvtv
+
+extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype) {
+  if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
+  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false).total;
+}
+
+extern "C" size_t spec_verify_packed_workspace_bytes(int32_t B, int32_t total_rows, int32_t V,
+                                                      int dtype) {
+  if (!lvtv::vr::packed_sizes_ok(B, total_rows, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16))
+    return 0;
+  return lvtv::vr::make_layout(size_t(total_rows), V, true).total;
+}
+
+extern "C" int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
+                           const int32_t* draft_tokens, const int32_t* k_per_req,
+                           const float* temperature, const uint64_t* seed, int32_t B,
+                           int32_t Kmax, int32_t V, int32_t* accepted_len, int32_t* out_tokens,
+                           float* alpha, int32_t* status, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return lvtv::vr::verify_padded(target_logits, draft_logits, dtype, draft_tokens, k_per_req,
+                                 temperature, seed, nullptr, nullptr, B, Kmax, V, accepted_len,
+                                 out_tokens, alpha, status, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t spec_verify_topkp_workspace_bytes(int32_t B, int32_t Kmax, int32_t V,
+                                                     int dtype) {
+  if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
+  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false, true).total;
+}
+
+extern "C" int spec_verify_topkp(const void* target_logits, const void* draft_logits, int dtype,
+                                 const int32_t* draft_tokens, const int32_t* k_per_req,
+                                 const float* temperature, const uint64_t* seed,
+                                 const int32_t* top_k, const float* top_p, int32_t B,
+                                 int32_t Kmax, int32_t V, int32_t* accepted_len,
+                                 int32_t* out_tokens, float* alpha, int32_t* status,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!top_k || !top_p) return LVTV_ERR_NULL;
+  return lvtv::vr::verify_padded(target_logits, draft_logits, dtype, draft_tokens, k_per_req,
+                                 temperature, seed, top_k, top_p, B, Kmax, V, accepted_len,
+                                 out_tokens, alpha, status, workspace, workspace_bytes, stream);
 }
 
 extern "C" int spec_verify_packed(const void* target_logits, const void* draft_logits, int dtype,
@@ -1028,6 +1568,9 @@ extern "C" int spec_verify_packed(const void* target_logits, const void* draft_l
   a.rowmap = reinterpret_cast<int32_t*>(ws + L.off_map);
   a.packed_ok = reinterpret_cast<int32_t*>(ws + L.off_map) + total_rows;
   a.total_rows = total_rows;
+  a.top_k = nullptr;
+  a.top_p = nullptr;
+  a.keep = nullptr;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
                         reinterpret_cast<uintptr_t>(draft_logits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);

@@ -132,6 +132,23 @@ def test_packed_verify_host_errors(lib):
     assert call(wsb=need - 1) == -4
 
 
+def test_topkp_verify_host_errors(lib):
+    need = lv.spec_verify_topkp_workspace_bytes(4, 3, 100, 1)
+    assert need > lv.spec_verify_workspace_bytes(4, 3, 100, 1)    # the keep records
+    assert lv.spec_verify_topkp_workspace_bytes(4, 17, 100, 1) == 0
+    call = lambda **kw: lib.spec_verify_topkp(*{**dict(
+        t=FAKE, d=FAKE, dtype=1, y=FAKE, k=FAKE, T=FAKE, seed=FAKE, tk=FAKE, tp=FAKE, B=4, K=3,
+        V=100, acc=FAKE, tok=FAKE, alpha=FAKE, status=FAKE, ws=FAKE, wsb=need, stream=NULL),
+        **kw}.values())
+    assert call(tk=NULL) == -1
+    assert call(tp=NULL) == -1
+    assert call(dtype=2) == -3
+    assert call(K=17) == -2
+    assert call(wsb=need - 1) == -4
+    # the plain verify's workspace is too small for the truncating one
+    assert call(wsb=lv.spec_verify_workspace_bytes(4, 3, 100, 1)) == -4
+
+
 def test_schedule_host_errors(lib):
     call = lambda **kw: lib.dspark_schedule(*{**dict(
         c=FAKE, sps=FAKE, R=4, L=3, lens=FAKE, best=FAKE, stream=NULL), **kw}.values())

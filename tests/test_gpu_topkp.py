@@ -1,0 +1,228 @@
+"""GPU parity of spec_verify_topkp (top-k / top-p truncation before the
+verify step) against the oracle, through the C ABI.
+
+Each request gets its own (top_k, top_p) from a mix that covers truncation
+off, top-k alone (1, small, large, V - 1, beyond V, negative), top-p alone
+(0.3 to 0.999999) and both together. Inputs: ragged bf16 and fp32 batches
+at several temperatures (greedy included), the full-vocabulary workload
+(every request run on the GPU, a sample checked against the oracle),
+logits on a coarse grid so that top-k and top-p cut through runs of equal
+values, rows holding -inf, and bad top_p values.
+
+Which prefix top-p keeps is decided by floating point. The kernel forms
+each token's weight e^(s - max s) to within about 2.4e-7 relative (the
+exponent split exactly, one v_exp_f32 of at most 1 ulp, two binary32
+roundings) and sums the weights exactly in fixed point, so its cumulative
+weight and the top-p target are each within 2.4e-7 of the kept total: its
+decision can differ from the exact one only where the oracle's decision
+margin (``trunc_margin``, relative to the kept total) is below 4.8e-7. Such
+requests are excused and counted (their outputs must still be well formed);
+every other request must meet the verify parity rules."""
+
+import numpy as np
+import pytest
+import torch
+
+import lossless_verify_tv_amd as lv
+from lossless_verify_tv_amd import synth
+from oracle import verify as ov
+
+from .gpu_util import announce, device, run_verify, verify_inputs
+from .parity import compare_verify
+
+pytestmark = pytest.mark.gpu
+
+TRUNC_MARGIN = 5e-7
+
+
+def _settings(B, V, rotate=0):
+    mix = [(0, 1.0), (1, 1.0), (5, 1.0), (50, 1.0), (1000, 1.0), (V - 1, 1.0), (V + 3, 1.0),
+           (-1, 0.3), (0, 0.5), (0, 0.9), (0, 0.95), (0, 0.999), (7, 0.999999), (20, 0.8),
+           (3000, 0.95), (100000, 0.9), (2, 0.6)]
+    mix = mix[rotate % len(mix):] + mix[:rotate % len(mix)]
+    top_k = np.array([mix[b % len(mix)][0] for b in range(B)], dtype=np.int32)
+    top_p = np.array([mix[b % len(mix)][1] for b in range(B)], dtype=np.float32)
+    return top_k, top_p
+
+
+def _run_gpu(case, top_k, top_p, dev):
+    inp = verify_inputs(case, dev)
+    acc, toks, alpha, status = lv.spec_verify_topkp(
+        **inp, top_k=torch.from_numpy(top_k).to(dev), top_p=torch.from_numpy(top_p).to(dev))
+    torch.cuda.synchronize(dev)
+    return {"accepted_len": acc.cpu().numpy(), "tokens": toks.cpu().numpy(),
+            "alpha": alpha.cpu().numpy(), "status": status.cpu().numpy()}
+
+
+def _oracle(case, top_k, top_p, requests):
+    kmax = case.draft.shape[1]
+    res = [ov.verify_request(ov.decode_rows(case.target[b], case.dtype),
+                             ov.decode_rows(case.draft[b], case.dtype), case.tokens[b],
+                             case.k[b], case.temperature[b], int(case.seed[b]), b, kmax,
+                             top_k=int(top_k[b]), top_p=float(top_p[b]))
+           for b in requests]
+    keys = ("accepted_len", "tokens", "alpha", "accept_margin", "draw_margin", "status",
+            "greedy", "trunc_margin")
+    return {k: np.array([r[k] for r in res]) for k in keys}
+
+
+def _compare(case, gpu, top_k, top_p, tag, requests=None):
+    B = case.shape[0]
+    requests = list(range(B)) if requests is None else list(requests)
+    orc = _oracle(case, top_k, top_p, requests)
+    keep = [i for i, _ in enumerate(requests) if not orc["trunc_margin"][i] < TRUNC_MARGIN]
+    excused = len(requests) - len(keep)
+    V = case.shape[2]
+    for i, b in enumerate(requests):
+        if i in keep:
+            continue
+        # an excused request: same status, well-formed outputs
+        assert gpu["status"][b] == orc["status"][i], (tag, b)
+        j, kb = int(gpu["accepted_len"][b]), int(case.k[b])
+        assert 0 <= j <= kb, (tag, b)
+        t = gpu["tokens"][b]
+        assert np.array_equal(t[:j], case.tokens[b][:j]) and 0 <= t[j] < V \
+            and np.all(t[j + 1:] == -1), (tag, b)
+        assert np.all((gpu["alpha"][b][:kb] >= 0) & (gpu["alpha"][b][:kb] <= 1 + 1e-6)), (tag, b)
+    sel = [requests[i] for i in keep]
+    g = {k: v[sel] for k, v in gpu.items()}
+    o = {k: v[keep] for k, v in orc.items()}
+    rep = compare_verify(g, o, case.k[sel], case.shape[1])
+    announce(f"topkp {tag}: {len(requests)} requests, {rep['stochastic']} stochastic, "
+             f"{rep['greedy']} greedy, {rep['faulted']} faulted, truncation near-ties "
+             f"excused {excused}, accept {rep['excused_accept']}, draw {rep['excused_draw']}")
+    assert not rep["failures"], (tag, [(sel[i], why) for i, why in rep["failures"][:5]])
+    return rep, excused
+
+
+@pytest.mark.parametrize("dtype_case,temperature", [(3, 1.0), (3, 0.6), (3, 1.7), (1, 1.0)])
+def test_topkp_ragged_against_oracle(dtype_case, temperature):
+    dev = device()
+    if dtype_case == 3:
+        case = synth.verify_case(3, temperature=temperature, batch=34, vocab=9001,
+                                 k_values=[(b * 5) % 8 for b in range(34)])
+    else:
+        case = synth.verify_case(1, temperature=temperature, batch=17, vocab=4096, kmax=4)
+    top_k, top_p = _settings(case.shape[0], case.shape[2], rotate=int(temperature * 10))
+    announce(f"topkp ragged case={dtype_case} T={temperature} shape={case.shape}")
+    _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p,
+             f"ragged case={dtype_case} T={temperature}")
+
+
+def test_topkp_greedy_and_mixed_temperatures():
+    dev = device()
+    case = synth.verify_case(3, batch=17, vocab=5000, kmax=5)
+    case.temperature[:] = np.array([0.0, 1.0, 0.5, 2.0] * 5, dtype=np.float32)[:17]
+    case = synth.redraw_tokens(case, 1.0)
+    case.temperature[:] = np.array([0.0, 1.0, 0.5, 2.0] * 5, dtype=np.float32)[:17]
+    top_k, top_p = _settings(17, 5000, rotate=3)
+    announce(f"topkp mixed temperatures shape={case.shape}")
+    rep, _ = _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p, "mixed T")
+    assert rep["greedy"] >= 4
+
+
+def _grid_case(dtype, step, V=6000, B=17, K=3, with_ninf=False):
+    """Logits on a grid of `step` (many exact ties), in `dtype`."""
+    rng = np.random.default_rng(int(step * 100) + (dtype == "bf16"))
+    t = np.round(rng.standard_normal((B, K + 1, V)) * 2.0 / step) * step
+    d = np.round((t[:, :K] + 0.7 * rng.standard_normal((B, K, V))) / step) * step
+    t = t.astype(np.float32)
+    d = d.astype(np.float32)
+    if with_ninf:
+        t[:, :, ::7] = -np.inf
+        d[:, :, 3::11] = -np.inf
+    case = synth.verify_case(1, batch=B, vocab=V, kmax=K)
+    case.dtype = dtype
+    case.target = synth.to_bf16(t) if dtype == "bf16" else t
+    case.draft = synth.to_bf16(d) if dtype == "bf16" else d
+    dec = ov.decode_rows(case.draft.reshape(-1, V), dtype).reshape(B, K, V)
+    case.tokens = np.argmax(dec + rng.gumbel(size=dec.shape), axis=-1).astype(np.int32)
+    case.k = np.full(B, K, dtype=np.int32)
+    case.temperature = np.full(B, 1.0, dtype=np.float32)
+    case.seed = rng.integers(0, 2**63, size=B).astype(np.uint64)
+    return case
+
+
+@pytest.mark.parametrize("dtype,step,ninf", [("bf16", 0.25, False), ("f32", 0.5, False),
+                                             ("f32", 0.125, True), ("bf16", 1.0, True)])
+def test_topkp_cuts_through_equal_logits(dtype, step, ninf):
+    dev = device()
+    case = _grid_case(dtype, step, with_ninf=ninf)
+    B, _, V = case.shape
+    top_k, top_p = _settings(B, V, rotate=5)
+    top_k[::3] = [3, 17, 250, 999, 4000, 31][:len(top_k[::3])]
+    announce(f"topkp ties dtype={dtype} step={step} -inf={ninf} shape={case.shape}")
+    _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p,
+             f"ties {dtype} step={step} ninf={ninf}")
+
+
+def test_topkp_constant_rows_keep_lowest_ids():
+    """All logits equal: top-k keeps ids 0..k-1, top-p the shortest prefix of
+    ids; with k = 1 every draw is token 0."""
+    dev = device()
+    B, K, V = 6, 2, 1000
+    case = synth.verify_case(1, batch=B, vocab=V, kmax=K)
+    case.target = np.zeros((B, K + 1, V), np.float32)
+    case.draft = np.zeros((B, K, V), np.float32)
+    case.tokens = np.array([[0, 1], [5, 0], [0, 0], [999, 3], [2, 2], [0, 9]], np.int32)
+    case.k = np.full(B, K, np.int32)
+    case.temperature = np.ones(B, np.float32)
+    case.seed = np.arange(B, dtype=np.uint64) * 7919
+    top_k = np.array([1, 10, 1, 0, 3, 0], np.int32)
+    top_p = np.array([1.0, 1.0, 0.5, 0.0105, 1.0, 0.3517], np.float32)
+    announce("topkp constant rows")
+    gpu = _run_gpu(case, top_k, top_p, dev)
+    _compare(case, gpu, top_k, top_p, "constant rows")
+    for b in (0, 2):   # k = 1 keeps token 0 only: the draw is 0
+        j = gpu["accepted_len"][b]
+        assert gpu["tokens"][b][j] == 0
+
+
+def test_bad_top_p_faults_with_other_bits():
+    dev = device()
+    case = synth.verify_case(3, batch=6, vocab=3000, kmax=2)
+    case.temperature[3] = -1.0            # also a bad temperature
+    case.tokens[4, 0] = 3000              # also a bad token
+    top_k = np.zeros(6, np.int32)
+    top_p = np.array([0.0, -0.5, np.nan, 0.0, 0.0, 0.9], np.float32)
+    announce("topkp bad top_p")
+    gpu = _run_gpu(case, top_k, top_p, dev)
+    orc = _oracle(case, top_k, top_p, range(6))
+    assert list(gpu["status"]) == list(orc["status"])
+    assert gpu["status"][0] == lv.STATUS_BAD_TRUNCATION
+    assert gpu["status"][3] == lv.STATUS_BAD_TRUNCATION | lv.STATUS_BAD_TEMPERATURE
+    assert gpu["status"][4] == lv.STATUS_BAD_TRUNCATION | lv.STATUS_BAD_TOKEN
+    assert gpu["status"][5] == 0
+    assert np.all(gpu["accepted_len"][:5] == -1)
+
+
+def test_truncation_off_equals_plain_verify():
+    """top_k <= 0 or >= V and top_p >= 1 keep every token: the outputs are
+    bit-identical to spec_verify's on the full-vocabulary workload."""
+    dev = device()
+    case = synth.verify_case(3, temperature=0.6, batch=16)
+    B, _, V = case.shape
+    top_k = np.where(np.arange(B) % 2 == 0, 0, V).astype(np.int32)
+    top_p = np.where(np.arange(B) % 3 == 0, 1.0, 2.5).astype(np.float32)
+    announce(f"topkp off vs plain shape={case.shape}")
+    plain = run_verify(case, dev)
+    trunc = _run_gpu(case, top_k, top_p, dev)
+    for key in ("accepted_len", "status", "tokens", "alpha"):
+        assert np.array_equal(plain[key], trunc[key]), key
+
+
+def test_topkp_full_vocabulary_workload():
+    """The full batch (B = 64, Kmax = 7, V = 151936, bf16) on the GPU in one
+    call; 16 requests spread over the batch checked against the oracle."""
+    dev = device()
+    case = synth.verify_case(3)
+    B, _, V = case.shape
+    top_k, top_p = _settings(B, V)
+    announce(f"topkp full workload shape={case.shape}")
+    gpu = _run_gpu(case, top_k, top_p, dev)
+    sample = list(range(0, B, 4))
+    _compare(case, gpu, top_k, top_p, "full workload (sample)", requests=sample)
+    # a rerun is bit-identical
+    again = _run_gpu(case, top_k, top_p, dev)
+    for key in ("accepted_len", "tokens", "alpha", "status"):
+        assert np.array_equal(gpu[key], again[key]), key
