@@ -74,15 +74,19 @@ static_assert(sizeof(RowOut) == 32, "row record is 32 bytes");
 
 // Tokens a row keeps after top-k / top-p truncation: with d the order key of
 // a token's scaled logit s (larger s, smaller d), token v is kept iff
-// d < key, or d == key and v <= idx (equal s are kept in token order).
+// d < key, or d == key and v <= idx (equal s are kept in token order). R and
+// L are the row's statistics over the kept tokens in the row kernel's
+// convention (R = fl32(max s log2 e), L = sum 2^(s log2 e - R)), so that the
+// row kernel needs a single pass over a truncated row.
 struct KeepRow {
   uint32_t key;
   int32_t idx;
+  float R, L;
 };
 struct KeepPair {
   KeepRow t, d;  // the target row and the draft row of one position
 };
-static_assert(sizeof(KeepPair) == 16, "keep record is 16 bytes");
+static_assert(sizeof(KeepPair) == 32, "keep record is 32 bytes");
 
 // Order key of a scaled logit: unsigned order of the key is descending order
 // of s (-0 and +0 share one key).
@@ -131,7 +135,7 @@ struct Args {
   KeepPair* keep;        // one per target row, written by trunc_rows
 };
 
-__device__ __forceinline__ KeepRow keep_all() { return KeepRow{0xffffffffu, INT_MAX}; }
+__device__ __forceinline__ KeepRow keep_all() { return KeepRow{0xffffffffu, INT_MAX, 0.f, 0.f}; }
 
 __device__ __forceinline__ bool temperature_ok(float t) { return (t >= 0.f) && !isinf(t); }
 
@@ -360,21 +364,29 @@ __device__ __forceinline__ void load_tail(const void* row, int V, int t, Grp<kDt
 }
 
 // Tokens of a group (first token e) that the row's truncation drops read as
-// -inf from here on.
+// -inf from here on. The kept prefix ends at the token of scaled logit sk and
+// id idx: a token is kept iff s > sk, or s == sk and its id is at most idx
+// (the order key's order, compared as floats).
 template <int kDtype>
-__device__ __forceinline__ void apply_keep(Grp<kDtype>& g, int e, const KeepRow& kr, float inv_t,
+__device__ __forceinline__ void apply_keep(Grp<kDtype>& g, int e, float sk, int idx, float inv_t,
                                            bool unit) {
+  if constexpr (kDtype == 1) {
 #pragma unroll
-  for (int j = 0; j < kVec; ++j) {
-    const float s = scale_logit(gelem(g, j), inv_t, unit);
-    if (!keeps(kr, s, e + j)) {
-      if constexpr (kDtype == 1) {
-        const uint32_t w = g.q[0][j >> 1];
-        g.q[0][j >> 1] =
-            (j & 1) ? ((w & 0x0000ffffu) | 0xff800000u) : ((w & 0xffff0000u) | 0x0000ff80u);
-      } else {
-        g.q[j >> 2][j & 3] = 0xff800000u;
-      }
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t w = g.q[0][h];
+      const float s0 = scale_logit(__uint_as_float(w << 16), inv_t, unit);
+      const float s1 = scale_logit(__uint_as_float(w & 0xffff0000u), inv_t, unit);
+      const bool k0 = s0 > sk || (s0 == sk && e + 2 * h <= idx);
+      const bool k1 = s1 > sk || (s1 == sk && e + 2 * h + 1 <= idx);
+      const uint32_t drop = (k0 ? 0u : 0x0000ffffu) | (k1 ? 0u : 0xffff0000u);
+      g.q[0][h] = (w & ~drop) | (0xff80ff80u & drop);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const float s = scale_logit(__uint_as_float(g.q[j >> 2][j & 3]), inv_t, unit);
+      const bool kp = s > sk || (s == sk && e + j <= idx);
+      if (!kp) g.q[j >> 2][j & 3] = 0xff800000u;
     }
   }
 }
@@ -394,13 +406,63 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
   const bool unit = (T == 1.f);
   KeepPair kp{keep_all(), keep_all()};
   if constexpr (kTrunc) kp = a.keep[target_row(a, b, k)];
+  // a row that keeps every token is left as it is
+  const bool cut_t = kTrunc && kp.t.key != keep_all().key;
+  const bool cut_d = kTrunc && kPair && kp.d.key != keep_all().key;
+  const float sk_t = key_value(kp.t.key), sk_d = key_value(kp.d.key);
   // drops the truncated tokens of a loaded group of tile t
   auto mk = [&](Grp<kDtype>& gt, Grp<kDtype>& gd, int tt) {
     if constexpr (kTrunc) {
-      apply_keep<kDtype>(gt, tile_elem(tt), kp.t, inv_t, unit);
-      if constexpr (kPair) apply_keep<kDtype>(gd, tile_elem(tt), kp.d, inv_t, unit);
+      if (cut_t) apply_keep<kDtype>(gt, tile_elem(tt), sk_t, kp.t.idx, inv_t, unit);
+      if constexpr (kPair)
+        if (cut_d) apply_keep<kDtype>(gd, tile_elem(tt), sk_d, kp.d.idx, inv_t, unit);
     }
   };
+
+  if constexpr (kTrunc) {
+    if (cut_t && (!kPair || cut_d)) {
+      // A truncated row (pair): the selection kernel has the statistics of
+      // the kept tokens, so one pass over the row does.
+      const float Rt = kp.t.R, Lt = kp.t.L;
+      const float Rd = kPair ? kp.d.R : 0.f, Ld = kPair ? kp.d.L : 1.f;
+      const float nrt = float(-((double)Rt + log2((double)Lt)));
+      const float nrd = kPair ? float(-((double)Rd + log2((double)Ld))) : 0.f;
+      float* chunk_row = a.chunk + size_t(target_row(a, b, k)) * a.NC;
+      float sa = 0.f;
+      int t = 0;
+      for (; t + kBatch <= nfull; t += kBatch) {
+        Grp<kDtype> gt[kBatch], gd[kBatch];
+#pragma unroll
+        for (int n = 0; n < kBatch; ++n) {
+          load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t + n), gt[n]);
+          if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t + n), gd[n]);
+        }
+#pragma unroll
+        for (int n = 0; n < kBatch; ++n) {
+          mk(gt[n], gd[n], t + n);
+          overlap_tile<kDtype, kPair>(gt[n], gd[n], c, nrt, nrd, sa, chunk_row, t + n);
+        }
+      }
+      for (; t < nfull; ++t) {
+        Grp<kDtype> gt, gd;
+        load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t), gt);
+        if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t), gd);
+        mk(gt, gd, t);
+        overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, t);
+      }
+      if (tail) {
+        Grp<kDtype> gt, gd;
+        load_tail<kDtype, kVecOk>(trow, V, nfull, gt);
+        if constexpr (kPair) load_tail<kDtype, kVecOk>(drow, V, nfull, gd);
+        mk(gt, gd, nfull);
+        overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, nfull);
+      }
+      const float alpha = kPair ? block_sum1(sa, sh) : 0.f;
+      if (threadIdx.x == 0)
+        a.rows[target_row(a, b, k)] = RowOut{Rt, Lt, Rd, Ld, alpha, -1, -1, 0};
+      return;
+    }
+  }
 
   // ---- pass 1: streamed full tiles, held full tiles, the partial tile
   float mt = -INFINITY, lt = 0.f, md = -INFINITY, ld = 0.f;
@@ -636,33 +698,48 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 // ------------------------------------------------------------------ truncation
 //
 // trunc_rows finds, for each used row of a sampling request, the prefix of
-// the row's tokens (scaled logit descending, then token id) that top-k and
-// then top-p keep, as a KeepRow. Radix selection on the 32-bit order key d in
-// three levels, bits [21, 32), [10, 21) and [0, 10): one pass over the row per
-// level builds LDS histograms of token counts (top-k) or of fixed-point
-// masses (top-p) of the tokens under the prefix chosen so far, and a block
-// scan picks the bucket where the running count or mass reaches its target.
-// A level ends the search early when its bucket holds a single key (with
-// bf16 logits the second level always does). When the kept prefix ends
-// inside a run of equal keys, a last pass finds the token id it ends at.
+// the row's tokens (scaled logit s descending, then token id) that top-k and
+// then top-p keep, and stores its last token as a KeepRow. Three passes over
+// the row in the common case:
+//   1. the row maximum M (and faults: such rows are left whole);
+//   2. first-level LDS histograms over the distance below the maximum in
+//      1/32-nat bins, floor((M - s) 32) (the last bin takes everything
+//      further down): token counts for top-k, fixed-point masses for top-p.
+//      Bins follow the order of s and spread the LDS atomics of clustered
+//      logits over many addresses. A block scan picks the bin where the
+//      running count reaches top_k, and the bin where the running mass
+//      reaches top_p times the mass top-k keeps, when the part of top-k's
+//      own bin it keeps does not leave that open;
+//   3. the tokens of the chosen bins are gathered into LDS (order key and
+//      token id) and the boundary is resolved there: radix selection on the
+//      32-bit order key, 10 bits a level, then on the token id among equal
+//      keys.
+// A bin with more tokens than LDS holds is refined by further passes over
+// the row instead (a level a pass, then one pass to split equal keys).
 //
-// Masses are e^(s - M) 2^E truncated to integers (M the row maximum, E = 63 -
-// bits(V) so that a row's total cannot pass 2^63), formed to about two
-// binary32 ulps whatever s - M is and summed exactly in 64 bits: the sums are
-// deterministic, and within about 3e-7 of the exact ones relative to the kept
-// total for vocabularies up to a few million.
+// Masses are e^(s - M) 2^E truncated to integers (E = 63 - bits(V), so that a
+// row's total cannot pass 2^63), formed to about two binary32 ulps whatever
+// s - M is and summed exactly in 64 bits: the sums are deterministic, and
+// within about 2.4e-7 of the exact ones relative to the kept total.
 
-constexpr int kL1Shift = 21, kL2Shift = 10;
-constexpr int kL1Buckets = 2048, kL2Buckets = 2048, kL3Buckets = 1024;
+constexpr int kRes = 32;       // first-level bins per nat below the row maximum
+constexpr int kNB1 = 2048;     // first-level bins
+constexpr int kNB = 1024;      // buckets of a refinement level
+constexpr int kCand = 4096;    // tokens gathered into LDS
 constexpr float kL2ELo = 1.925963033e-8f;  // log2(e) - fl32(log2(e))
 
 struct TruncShared {
-  uint32_t cnt[kL1Buckets];
-  unsigned long long mass[kL1Buckets];
-  uint32_t kmin[kL2Buckets], kmax[kL2Buckets];
-  unsigned long long part[kWaves];
-  unsigned long long res64;
-  int32_t res32;
+  uint32_t cnt1[kNB1];
+  unsigned long long mass1[kNB1];
+  uint32_t ckey[kCand];
+  int32_t cidx[kCand];
+  uint32_t cnt[kNB];
+  unsigned long long mass[kNB];
+  uint32_t vmin[kNB], vmax[kNB];
+  unsigned long long part[kWaves][2];
+  unsigned long long r64[2];
+  int32_t r32;
+  uint32_t ncand;
   float fmax[kWaves];
 };
 
@@ -678,6 +755,21 @@ __device__ __forceinline__ uint64_t fixed_mass(float s, float M, float scale) {
   const float tl = __builtin_fmaf(d, kL2E, -th) + __builtin_fmaf(d, kL2ELo, dlo * kL2E);
   const float w = __builtin_amdgcn_exp2f(th) * __builtin_fmaf(tl, 0.693147182f, 1.f);
   return (uint64_t)(w * scale);
+}
+
+// First-level bin of a token: floor((M - s) 32), the last bin also taking
+// everything further down (and -inf). Non-decreasing in the order key.
+__device__ __forceinline__ uint32_t l1_bin(float s, float M) {
+  const float g = __fmul_rn(M - s, float(kRes));
+  return g < float(kNB1 - 1) ? uint32_t(g) : uint32_t(kNB1 - 1);
+}
+
+// Order keys that bin b can hold, with slack for the rounding of M - s.
+__device__ __forceinline__ void l1_key_range(uint32_t b, float M, uint32_t& lo, uint32_t& hi) {
+  const double e = 1.0 / 4194304.0;  // 2^-22, above the 2^-24 relative error of fl(M - s)
+  lo = desc_key(__double2float_ru((double)M - (double(b) / kRes) * (1.0 - e)));
+  hi = (b >= kNB1 - 1) ? 0xff800000u
+                       : desc_key(__double2float_rd((double)M - (double(b + 1) / kRes) * (1.0 + e)));
 }
 
 // One pass over a row: f(s, v) for every token v < V with its scaled logit,
@@ -709,68 +801,138 @@ __device__ __forceinline__ void row_pass(const void* row, int V, float inv_t, bo
   }
 }
 
-// Block-wide exclusive scan of 64-bit integers; `total` gets the sum.
-__device__ __forceinline__ uint64_t block_exscan_u64(uint64_t v, TruncShared& ts,
-                                                     uint64_t& total) {
+// Gathers (order key, token id) of the tokens `want(s)` admits into the LDS
+// list (ts.ncand counts them all, also past kCand). Wave-aggregated: one LDS
+// atomic per wave and token slot.
+template <int kDtype, bool kVecOk, class F>
+__device__ __forceinline__ void gather_pass(const void* row, int V, float inv_t, bool unit, F&& want,
+                                            TruncShared& ts) {
+  const int nt = (V + kTile - 1) / kTile;
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int t = 0; t < nt; t += kBatch) {
+    Grp<kDtype> g[kBatch];
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n) {
+      if (t + n < nt)
+        load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t + n), g[n]);
+      else
+        fill_grp(g[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < kBatch; ++n)
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int v = tile_elem(t + n) + j;
+        const float s = scale_logit(gelem(g[n], j), inv_t, unit);
+        const bool w = (t + n < nt) && v < V && want(s);
+        const uint64_t mask = __ballot(w);
+        if (mask) {
+          const int leader = __ffsll((unsigned long long)mask) - 1;
+          uint32_t base = 0;
+          if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
+          base = (uint32_t)__shfl((int)base, leader, kWave);
+          if (w) {
+            const uint32_t pos = base + (uint32_t)__popcll(mask & below);
+            if (pos < uint32_t(kCand)) {
+              ts.ckey[pos] = desc_key(s);
+              ts.cidx[pos] = v;
+            }
+          }
+        }
+      }
+  }
+}
+
+// Block-wide exclusive scans of two 64-bit integers; totals in ta, tb.
+__device__ __forceinline__ void block_exscan2_u64(uint64_t a, uint64_t b, uint64_t& ea,
+                                                  uint64_t& eb, uint64_t& ta, uint64_t& tb,
+                                                  TruncShared& ts) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  uint64_t inc = v;
+  uint64_t ia = a, ib = b;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
-    const uint64_t n = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += n;
+    const uint64_t na = __shfl_up(ia, o, kWave), nb = __shfl_up(ib, o, kWave);
+    if (lane >= o) {
+      ia += na;
+      ib += nb;
+    }
   }
   __syncthreads();
-  if (lane == kWave - 1) ts.part[wave] = inc;
+  if (lane == kWave - 1) {
+    ts.part[wave][0] = ia;
+    ts.part[wave][1] = ib;
+  }
   __syncthreads();
-  uint64_t pre = 0;
-  total = 0;
+  uint64_t pa = 0, pb = 0;
+  ta = tb = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) pre += ts.part[w];
-    total += ts.part[w];
+    if (w < wave) {
+      pa += ts.part[w][0];
+      pb += ts.part[w][1];
+    }
+    ta += ts.part[w][0];
+    tb += ts.part[w][1];
   }
-  return pre + inc - v;
+  ea = pa + ia - a;
+  eb = pb + ib - b;
 }
 
 // The bucket b of h[0, nb) whose running sum reaches r (sum h[< b] < r <=
-// sum h[<= b], r >= 1), with sum h[< b] in `before`; the last bucket if the
-// total is below r. nb is a multiple of the block size.
-template <class T>
-__device__ __forceinline__ int select_bucket(const T* h, int nb, uint64_t r, uint64_t& before,
-                                             TruncShared& ts) {
+// sum h[<= b], r >= 1; the last bucket if the total is below r), with the
+// sums of h and of g before it. nb is a multiple of the block size.
+template <class T, class U>
+__device__ __forceinline__ int select2(const T* h, const U* g, int nb, uint64_t r, uint64_t& bh,
+                                       uint64_t& bg, TruncShared& ts) {
   const int per = nb / kThreads;
   const int b0 = threadIdx.x * per;
-  uint64_t mine = 0;
-  for (int i = 0; i < per; ++i) mine += h[b0 + i];
-  uint64_t total;
-  const uint64_t exc = block_exscan_u64(mine, ts, total);
-  if (exc < r && r <= exc + mine) {
-    uint64_t run = exc;
+  uint64_t mh = 0, mg = 0;
+  for (int i = 0; i < per; ++i) {
+    mh += h[b0 + i];
+    mg += g[b0 + i];
+  }
+  uint64_t eh, eg, th, tg;
+  block_exscan2_u64(mh, mg, eh, eg, th, tg, ts);
+  if (eh < r && r <= eh + mh) {
+    uint64_t rh = eh, rg = eg;
     int b = b0 + per - 1;
     for (int i = 0; i < per; ++i) {
-      if (run + h[b0 + i] >= r) {
+      if (rh + h[b0 + i] >= r) {
         b = b0 + i;
         break;
       }
-      run += h[b0 + i];
+      rh += h[b0 + i];
+      rg += g[b0 + i];
     }
-    ts.res32 = b;
-    ts.res64 = run;
-  } else if (r > total && threadIdx.x == kThreads - 1) {
-    ts.res32 = nb - 1;
-    ts.res64 = total - h[nb - 1];
+    ts.r32 = b;
+    ts.r64[0] = rh;
+    ts.r64[1] = rg;
+  } else if (r > th && threadIdx.x == kThreads - 1) {
+    ts.r32 = nb - 1;
+    ts.r64[0] = th - h[nb - 1];
+    ts.r64[1] = tg - g[nb - 1];
   }
   __syncthreads();
-  before = ts.res64;
-  const int b = ts.res32;
+  bh = ts.r64[0];
+  bg = ts.r64[1];
+  const int b = ts.r32;
   __syncthreads();
   return b;
 }
 
-__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, TruncShared& ts) {
-  uint64_t total;
-  (void)block_exscan_u64(v, ts, total);
-  return total;
+// Sum of h[0, b).
+template <class T>
+__device__ __forceinline__ uint64_t sum_before(const T* h, int nb, int b, TruncShared& ts) {
+  const int per = nb / kThreads;
+  uint64_t m = 0;
+  for (int i = 0; i < per; ++i) {
+    const int j = threadIdx.x * per + i;
+    if (j < b) m += h[j];
+  }
+  uint64_t e0, e1, t0, t1;
+  block_exscan2_u64(m, 0, e0, e1, t0, t1, ts);
+  return t0;
 }
 
 __device__ __forceinline__ float block_max_f(float v, TruncShared& ts) {
@@ -784,24 +946,75 @@ __device__ __forceinline__ float block_max_f(float v, TruncShared& ts) {
   return r;
 }
 
-__device__ __forceinline__ void clear_hist(TruncShared& ts, bool minmax) {
-  for (int i = threadIdx.x; i < kL1Buckets; i += kThreads) {
-    ts.cnt[i] = 0;
-    ts.mass[i] = 0;
-    if (minmax) {
-      ts.kmin[i] = 0xffffffffu;
-      ts.kmax[i] = 0;
+// Result of a selection: the value (order key or token id) where the
+// running count or mass of the admitted tokens reaches the target, what of
+// the target is left at that value, and the admitted totals before it and
+// at it.
+struct Sel {
+  uint32_t val;
+  uint64_t rest;
+  uint64_t bcnt, bmass;
+  uint64_t acnt, amass;
+};
+
+// Radix selection over the tokens `src` yields and `adm` admits, on the
+// order key (or the token id, by_idx) within [lo, hi], 10 bits a level: by
+// count, or by mass (by_mass; want_mass also sums masses in count mode).
+template <class Src, class Adm>
+__device__ __forceinline__ Sel select_value(Src&& src, Adm&& adm, bool by_idx, bool by_mass,
+                                            bool want_mass, uint64_t target, uint32_t lo,
+                                            uint32_t hi, float M, float scale, TruncShared& ts) {
+  Sel r{0, target, 0, 0, 0, 0};
+  for (int level = 0; level < 6; ++level) {  // 4 levels cover 32 bits
+    const uint32_t span = hi - lo;
+    const int sh = span < uint32_t(kNB) ? 0 : (32 - __clz(span)) - 10;
+    for (int i = threadIdx.x; i < kNB; i += kThreads) {
+      ts.cnt[i] = 0;
+      ts.mass[i] = 0;
+      ts.vmin[i] = 0xffffffffu;
+      ts.vmax[i] = 0;
     }
+    __syncthreads();
+    src([&](float s, int v, uint32_t d) {
+      const uint32_t u = by_idx ? uint32_t(v) : d;
+      if (u < lo || u > hi || !adm(s, v, d)) return;
+      const uint32_t i = (u - lo) >> sh;
+      atomicAdd(&ts.cnt[i], 1u);
+      if (want_mass) {
+        const uint64_t m = fixed_mass(s, M, scale);
+        if (m) atomicAdd(&ts.mass[i], (unsigned long long)m);
+      }
+      atomicMin(&ts.vmin[i], u);
+      atomicMax(&ts.vmax[i], u);
+    });
+    __syncthreads();
+    uint64_t bp, bo;
+    const int b = by_mass ? select2(ts.mass, ts.cnt, kNB, r.rest, bp, bo, ts)
+                          : select2(ts.cnt, ts.mass, kNB, r.rest, bp, bo, ts);
+    r.rest -= bp;
+    r.bcnt += by_mass ? bo : bp;
+    r.bmass += by_mass ? bp : bo;
+    const uint32_t vlo = ts.vmin[b], vhi = ts.vmax[b], c = ts.cnt[b];
+    const uint64_t m = ts.mass[b];
+    __syncthreads();
+    if (vlo == vhi || c == 0) {
+      r.val = vlo;
+      r.acnt = c;
+      r.amass = m;
+      return r;
+    }
+    lo += uint32_t(b) << sh;
+    hi = min(hi, lo + ((1u << sh) - 1u));
   }
-  __syncthreads();
+  return r;
 }
 
 // Token id of the n-th token (in id order, n >= 1) whose key is `key`; every
-// thread gets it.
+// thread gets it. One pass over the row.
 template <int kDtype, bool kVecOk>
 __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t, bool unit,
                                             uint32_t key, uint64_t n, TruncShared& ts) {
-  if (threadIdx.x == 0) ts.res32 = INT_MAX;
+  if (threadIdx.x == 0) ts.r32 = INT_MAX;
   const int nt = (V + kTile - 1) / kTile;
   uint64_t run = 0;  // matches in the tiles before t
   for (int t = 0; t < nt && run < n; t += 4) {
@@ -824,8 +1037,8 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
       }
       mine |= c << (16 * i);
     }
-    uint64_t total;
-    const uint64_t exc = block_exscan_u64(mine, ts, total);
+    uint64_t exc, e1, total, t1;
+    block_exscan2_u64(mine, 0, exc, e1, total, t1, ts);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t before = run + ((exc >> (16 * i)) & 0xffff);
@@ -835,7 +1048,7 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
         for (int j = 0; j < kVec; ++j) {
           const int v = tile_elem(t + i) + j;
           if (v < V && desc_key(scale_logit(gelem(g[i], j), inv_t, unit)) == key && ++seen == n) {
-            ts.res32 = v;
+            ts.r32 = v;
             break;
           }
         }
@@ -844,7 +1057,15 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
     }
   }
   __syncthreads();
-  return ts.res32;
+  const int r = ts.r32;
+  __syncthreads();
+  return r;
+}
+
+// ceil(top_p W), clamped to [1, W].
+__device__ __forceinline__ uint64_t top_p_need(float top_p, uint64_t W) {
+  uint64_t n = (uint64_t)ceil((double)top_p * (double)W);
+  return n < 1 ? 1 : (n > W ? W : n);
 }
 
 template <int kDtype, bool kVecOk>
@@ -880,15 +1101,16 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   const float inv_t = __fdiv_rn(1.f, T);
   const bool unit = (T == 1.f);
   const float scale = __builtin_ldexpf(1.f, 63 - (32 - __clz(V)));
+  auto hbm = [&](auto&& f) {
+    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int v) { f(s, v, desc_key(s)); });
+  };
 
-  // ---- pass 1: the maximum, faults, top-k's first-level counts
-  clear_hist(ts, false);
+  // ---- pass 1: the maximum, faults
   float mx = -INFINITY;
   int bad = 0;
   row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
     bad |= (s != s) | (s == INFINITY);
     mx = fmaxf(mx, s);
-    if (k_on) atomicAdd(&ts.cnt[desc_key(s) >> kL1Shift], 1u);
   });
   bad = __syncthreads_or(bad);
   const float M = block_max_f(mx, ts);
@@ -897,132 +1119,156 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     return;
   }
 
-  // ---- top-k: the top_k-th token's key, its rank among equal keys, and how
-  // many tokens share the key
-  uint32_t keyK = 0xffffffffu;
-  uint64_t nK = 0, tieK = 0;
+  // ---- pass 2: first-level histograms
+  for (int i = threadIdx.x; i < kNB1; i += kThreads) {
+    ts.cnt1[i] = 0;
+    ts.mass1[i] = 0;
+  }
+  __syncthreads();
+  row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
+    const uint32_t i = l1_bin(s, M);
+    if (k_on) atomicAdd(&ts.cnt1[i], 1u);
+    const uint64_t m = fixed_mass(s, M, scale);
+    if (m) atomicAdd(&ts.mass1[i], (unsigned long long)m);
+  });
+  __syncthreads();
+
+  int binK = -1, binP = -1;
+  uint64_t rankK = 0, W0 = 0, needP = 0, beforeP = 0;
   if (k_on) {
-    uint64_t before, rank = uint64_t(top_k);
-    const uint32_t b1 = select_bucket(ts.cnt, kL1Buckets, rank, before, ts);
-    rank -= before;
-    clear_hist(ts, true);
-    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
-      const uint32_t d = desc_key(s);
-      if ((d >> kL1Shift) == b1) {
-        const uint32_t i = (d >> kL2Shift) & (kL2Buckets - 1);
-        atomicAdd(&ts.cnt[i], 1u);
-        atomicMin(&ts.kmin[i], d);
-        atomicMax(&ts.kmax[i], d);
+    uint64_t bc, bm;
+    binK = select2(ts.cnt1, ts.mass1, kNB1, uint64_t(top_k), bc, bm, ts);
+    rankK = uint64_t(top_k) - bc;
+    W0 = bm;  // mass of the bins above top-k's own
+    if (p_on) {
+      // top-p's bin is settled now if even the most top-k can keep of its
+      // own bin leaves the target above it, in one bin
+      const uint64_t n_hi = top_p_need(top_p, W0 + ts.mass1[binK]);
+      if (n_hi <= W0) {
+        uint64_t b0, b1, c0, c1;
+        const int lo_bin = select2(ts.mass1, ts.cnt1, kNB1, top_p_need(top_p, W0), b0, c0, ts);
+        const int hi_bin = select2(ts.mass1, ts.cnt1, kNB1, n_hi, b1, c1, ts);
+        if (lo_bin == hi_bin) binP = lo_bin;
       }
-    });
-    __syncthreads();
-    const uint32_t b2 = select_bucket(ts.cnt, kL2Buckets, rank, before, ts);
-    rank -= before;
-    const uint32_t lo = ts.kmin[b2], hi = ts.kmax[b2], n2 = ts.cnt[b2];
-    __syncthreads();
-    if (lo == hi) {
-      keyK = lo;
-      tieK = n2;
-    } else {
-      const uint32_t pre = (b1 << 11) | b2;
-      clear_hist(ts, false);
-      row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
-        const uint32_t d = desc_key(s);
-        if ((d >> kL2Shift) == pre) atomicAdd(&ts.cnt[d & (kL3Buckets - 1)], 1u);
-      });
-      __syncthreads();
-      const uint32_t b3 = select_bucket(ts.cnt, kL3Buckets, rank, before, ts);
-      rank -= before;
-      keyK = (pre << kL2Shift) | b3;
-      tieK = ts.cnt[b3];
-      __syncthreads();
     }
-    nK = rank;
+  } else {
+    uint64_t W = 0, t0 = 0;
+    {
+      uint64_t e0, e1, t1;
+      uint64_t m = 0;
+      for (int i = 0; i < kNB1 / kThreads; ++i) m += ts.mass1[threadIdx.x * (kNB1 / kThreads) + i];
+      block_exscan2_u64(m, 0, e0, e1, W, t1, ts);
+    }
+    needP = top_p_need(top_p, W);
+    uint64_t bc;
+    binP = select2(ts.mass1, ts.cnt1, kNB1, needP, beforeP, bc, ts);
+    (void)t0;
   }
 
-  // ---- top-p over the top-k set: the key where the running mass reaches
-  // top_p times the set's mass, and its rank among equal keys
+  // ---- pass 3: gather the tokens of the open bins into LDS
+  if (threadIdx.x == 0) ts.ncand = 0;
+  __syncthreads();
+  gather_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s) {
+    const int i = int(l1_bin(s, M));
+    return i == binK || i == binP;
+  }, ts);
+  __syncthreads();
+  uint32_t nc = ts.ncand;
+  bool in_lds = nc <= uint32_t(kCand);
+  __syncthreads();
+  auto lds = [&](auto&& f) {
+    for (uint32_t i = threadIdx.x; i < nc; i += kThreads) {
+      const uint32_t d = ts.ckey[i];
+      f(key_value(d), ts.cidx[i], d);
+    }
+  };
+
+  // ---- top-k: the top_k-th token
+  uint32_t keyK = 0xffffffffu;
+  int idxK = INT_MAX;
+  uint64_t WK = 0;  // mass of the tokens top-k keeps
+  if (k_on) {
+    auto adm = [&](float s, int, uint32_t) { return int(l1_bin(s, M)) == binK; };
+    uint32_t lo = 0, hi = 0xffffffffu;
+    if (!in_lds) l1_key_range(uint32_t(binK), M, lo, hi);
+    const Sel sk = in_lds ? select_value(lds, adm, false, false, true, rankK, lo, hi, M, scale, ts)
+                          : select_value(hbm, adm, false, false, true, rankK, lo, hi, M, scale, ts);
+    keyK = sk.val;
+    const uint64_t nK = sk.rest;
+    if (nK < sk.acnt) {
+      if (in_lds) {
+        auto tie = [&](float, int, uint32_t d) { return d == keyK; };
+        idxK = int(select_value(lds, tie, true, false, false, nK, 0, uint32_t(V - 1), M, scale, ts).val);
+      } else {
+        idxK = nth_with_key<kDtype, kVecOk>(row, V, inv_t, unit, keyK, nK, ts);
+      }
+    }
+    WK = W0 + sk.bmass + nK * (sk.acnt ? sk.amass / sk.acnt : 0);
+  }
+
+  // ---- top-p over the top-k set
   uint32_t key = keyK;
-  uint64_t n = nK, ties = tieK;
+  int idx = idxK;
+  uint64_t kept = WK;  // mass of the kept tokens
   if (p_on) {
-    // tokens of key keyK beyond the top_k-th are outside the set
-    const uint64_t excess = k_on ? (tieK - nK) * fixed_mass(key_value(keyK), M, scale) : 0;
-    clear_hist(ts, false);
-    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
-      const uint32_t d = desc_key(s);
-      if (d <= keyK) {
-        const uint64_t m = fixed_mass(s, M, scale);
-        if (m) atomicAdd(&ts.mass[d >> kL1Shift], (unsigned long long)m);
-      }
-    });
-    __syncthreads();
-    if (k_on && threadIdx.x == 0) ts.mass[keyK >> kL1Shift] -= excess;
-    __syncthreads();
-    uint64_t mine = 0;
-    for (int i = 0; i < kL1Buckets / kThreads; ++i) mine += ts.mass[threadIdx.x * (kL1Buckets / kThreads) + i];
-    const uint64_t W = block_sum_u64(mine, ts);
-    uint64_t need = (uint64_t)ceil((double)top_p * (double)W);
-    need = need < 1 ? 1 : (need > W ? W : need);
-    uint64_t before;
-    const uint32_t b1 = select_bucket(ts.mass, kL1Buckets, need, before, ts);
-    uint64_t rem = need - before;
-    clear_hist(ts, true);
-    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
-      const uint32_t d = desc_key(s);
-      if ((d >> kL1Shift) == b1 && d <= keyK) {
-        const uint32_t i = (d >> kL2Shift) & (kL2Buckets - 1);
-        const uint64_t m = fixed_mass(s, M, scale);
-        if (m) atomicAdd(&ts.mass[i], (unsigned long long)m);
-        atomicMin(&ts.kmin[i], d);
-        atomicMax(&ts.kmax[i], d);
-      }
-    });
-    __syncthreads();
-    if (k_on && threadIdx.x == 0 && (keyK >> kL1Shift) == b1)
-      ts.mass[(keyK >> kL2Shift) & (kL2Buckets - 1)] -= excess;
-    __syncthreads();
-    const uint32_t b2 = select_bucket(ts.mass, kL2Buckets, rem, before, ts);
-    rem -= before;
-    const uint32_t lo = ts.kmin[b2], hi = ts.kmax[b2];
-    uint64_t bucket_mass = ts.mass[b2];
-    __syncthreads();
-    if (lo == hi) {
-      key = lo;
-    } else {
-      const uint32_t pre = (b1 << 11) | b2;
-      clear_hist(ts, false);
-      row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
-        const uint32_t d = desc_key(s);
-        if ((d >> kL2Shift) == pre && d <= keyK) {
-          const uint64_t m = fixed_mass(s, M, scale);
-          if (m) atomicAdd(&ts.mass[d & (kL3Buckets - 1)], (unsigned long long)m);
+    if (k_on) {
+      needP = top_p_need(top_p, WK);
+      if (needP > W0) {
+        binP = binK;
+        beforeP = W0;
+      } else {
+        if (binP < 0) {
+          uint64_t bc;
+          binP = select2(ts.mass1, ts.cnt1, kNB1, needP, beforeP, bc, ts);
+          // not gathered yet: gather it alone
+          if (threadIdx.x == 0) ts.ncand = 0;
+          __syncthreads();
+          gather_pass<kDtype, kVecOk>(row, V, inv_t, unit,
+                                      [&](float s) { return int(l1_bin(s, M)) == binP; }, ts);
+          __syncthreads();
+          nc = ts.ncand;
+          in_lds = nc <= uint32_t(kCand);
+          __syncthreads();
+        } else {
+          beforeP = sum_before(ts.mass1, kNB1, binP, ts);
         }
-      });
-      __syncthreads();
-      if (k_on && threadIdx.x == 0 && (keyK >> kL2Shift) == pre)
-        ts.mass[keyK & (kL3Buckets - 1)] -= excess;
-      __syncthreads();
-      const uint32_t b3 = select_bucket(ts.mass, kL3Buckets, rem, before, ts);
-      rem -= before;
-      key = (pre << kL2Shift) | b3;
-      bucket_mass = ts.mass[b3];
-      __syncthreads();
+      }
     }
+    const uint64_t rem = needP - beforeP;
+    auto adm = [&](float s, int v, uint32_t d) {
+      return int(l1_bin(s, M)) == binP && (d < keyK || (d == keyK && v <= idxK));
+    };
+    uint32_t lo = 0, hi = 0xffffffffu;
+    if (!in_lds) l1_key_range(uint32_t(binP), M, lo, hi);
+    const Sel sp = in_lds ? select_value(lds, adm, false, true, true, rem, lo, hi, M, scale, ts)
+                          : select_value(hbm, adm, false, true, true, rem, lo, hi, M, scale, ts);
+    key = sp.val;
     // every token of one key has the same mass; the bucket reached holds
-    // positive mass, so w > 0
-    const uint64_t w = fixed_mass(key_value(key), M, scale);
-    if (w == 0) {  // not reached: kept for a defined result
-      n = 1;
-      ties = 1;
+    // positive mass
+    const uint64_t w = sp.acnt ? sp.amass / sp.acnt : 0;
+    const uint64_t n = w ? (sp.rest + w - 1) / w : 1;
+    kept = beforeP + sp.bmass + n * w;
+    if (n < sp.acnt) {
+      if (in_lds) {
+        auto tie = [&](float, int v, uint32_t d) {
+          return d == key && (d != keyK || v <= idxK);
+        };
+        idx = int(select_value(lds, tie, true, false, false, n, 0, uint32_t(V - 1), M, scale, ts).val);
+      } else {
+        // the admitted tokens of the key are its first ones in id order
+        idx = nth_with_key<kDtype, kVecOk>(row, V, inv_t, unit, key, n, ts);
+      }
     } else {
-      n = (rem + w - 1) / w;
-      ties = (k_on && key == keyK) ? tieK : bucket_mass / w;
+      idx = (key == keyK) ? idxK : INT_MAX;
     }
   }
-
-  const int idx = (n < ties) ? nth_with_key<kDtype, kVecOk>(row, V, inv_t, unit, key, n, ts)
-                             : INT_MAX;
-  if (threadIdx.x == 0) *out = KeepRow{key, idx};
+  if (threadIdx.x == 0) {
+    // kept mass in the row kernel's convention: sum 2^(s log2e - R) =
+    // 2^(M log2e - R) sum e^(s - M), log2e as the kernels round it
+    const float R = __fmul_rn(M, kL2E);
+    const double L = (double)kept / (double)scale * exp2((double)M * (double)kL2E - (double)R);
+    *out = KeepRow{key, idx, R, (float)L};
+  }
 }
 
 template <int kDtype, bool kVecOk>

@@ -178,6 +178,32 @@ def test_topkp_constant_rows_keep_lowest_ids():
         assert gpu["tokens"][b][j] == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_topkp_crowded_bins(dtype):
+    """Rows of a few distinct logits with V = 30000: the bin holding the
+    top-k or top-p boundary has more tokens than one workgroup gathers, so
+    the selection refines it by passes over the row instead."""
+    dev = device()
+    B, K, V = 8, 2, 30000
+    rng = np.random.default_rng(17 if dtype == "bf16" else 18)
+    vals = np.array([1.0, 0.5, 0.0, -3.0], np.float32)
+    t = vals[rng.integers(0, 4, (B, K + 1, V))]
+    d = vals[rng.integers(0, 4, (B, K, V))]
+    t[:, :, 123] = 2.0           # one clear maximum per row
+    case = synth.verify_case(1, batch=B, vocab=V, kmax=K)
+    case.dtype = dtype
+    case.target = synth.to_bf16(t) if dtype == "bf16" else t
+    case.draft = synth.to_bf16(d) if dtype == "bf16" else d
+    case.tokens = rng.integers(0, V, (B, K)).astype(np.int32)
+    case.k = np.full(B, K, np.int32)
+    case.temperature = np.array([1.0, 0.7, 1.0, 1.3, 1.0, 1.0, 0.9, 1.0], np.float32)
+    case.seed = rng.integers(0, 2**63, size=B).astype(np.uint64)
+    top_k = np.array([9000, 20000, 0, 0, 15000, 29999, 1, 12000], np.int32)
+    top_p = np.array([1.0, 1.0, 0.4, 0.77, 0.6, 0.3, 1.0, 0.93], np.float32)
+    announce(f"topkp crowded bins dtype={dtype} shape={case.shape}")
+    _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p, f"crowded {dtype}")
+
+
 def test_bad_top_p_faults_with_other_bits():
     dev = device()
     case = synth.verify_case(3, batch=6, vocab=3000, kmax=2)
