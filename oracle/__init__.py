@@ -31,7 +31,8 @@ Modules:
 * ``loss``    -- the E2E-TV prefix-product loss and its gradient with respect
   to the draft logits.
 * ``objectives`` -- the per-position comparators (per-step TV, CE, KL) with
-  their gradients.
+  their gradients, and every objective with the target given as logits and
+  a temperature on both sides.
 * ``schedule`` -- confidence-scheduled verify lengths (DSpark).
 * ``truncate`` -- top-k / top-p truncation of p and q before the verify step.
 

@@ -101,3 +101,58 @@ def draft_loss(draft_logits_bf16, target_probs, objective):
                                       objective)
         total += l_n
     return {"loss": total / n_br, "alpha": alpha, "dz": dz, "dlogits": bf16.encode_rne(dz)}
+
+
+# ---------------------------------------------------------------------------
+# Target given as logits, with a temperature.
+#
+# The verify step compares p and q after one temperature transform applied to
+# both sides ("Speculative Decoding and MTP" survey, section 4), and the
+# overlap the loss drives up is that same alpha ("Reading Qwen Bebop and
+# DeepSeek DSpark", section "Formulas", eq. alpha_RS; "SpecOPD" summary,
+# prerequisite on the E2E-TV objective). Readings taken here, where the
+# pages are silent:
+#
+# * both logit rows are scaled by the verify step's transform,
+#   s = fl32(x * fl32(1/T)) (``oracle.verify.scale``); p_k = softmax(s_target),
+#   q_k = softmax(s_draft), both in fp64;
+# * T > 0 only (a greedy target has no gradient);
+# * the gradient is taken with respect to the raw draft logits through the
+#   linear map s = x * fl32(1/T), i.e. d/dx = fl32(1/T) * d/ds (the rounding
+#   of s is not differentiated);
+# * p is a constant (SpecOPD, method step (6)).
+# ---------------------------------------------------------------------------
+
+def branch_scaled(s_z, s_t, inv_t, n_branches, objective):
+    """One branch from fp64 scaled logits ``s_z`` [W, V] (draft) and ``s_t``
+    [W, V] (target), with the chain factor ``inv_t`` = fl32(1/T). Returns
+    (L_n, alpha [W], dz [W, V]), dz with respect to the raw draft logits."""
+    s_t = np.asarray(s_t, dtype=np.float64)
+    p = np.stack([e2e.softmax64(s_t[k]) for k in range(s_t.shape[0])])
+    loss_n, alpha, ds = branch(s_z, p, n_branches, objective)
+    return loss_n, alpha, float(inv_t) * ds
+
+
+def scaled_logits(raw_bf16, temperature):
+    """fp64 copy of fl32(x * fl32(1/T)) for bfloat16 logits."""
+    from . import verify as ov
+    return ov.scale(bf16.decode(raw_bf16).astype(np.float32), temperature).astype(np.float64)
+
+
+def draft_loss_logits(draft_logits_bf16, target_logits_bf16, temperature, objective):
+    """Full loss over [N, W, V] with the target given as bfloat16 logits and
+    the temperature ``temperature`` > 0 on both sides. Returns a dict as
+    ``draft_loss``."""
+    if not (np.isfinite(temperature) and temperature > 0):
+        raise ValueError("the temperature must be finite and > 0")
+    n_br, width, vocab = draft_logits_bf16.shape
+    inv_t = float(np.float32(1.0) / np.float32(temperature))
+    alpha = np.zeros((n_br, width))
+    dz = np.zeros((n_br, width, vocab))
+    total = 0.0
+    for n in range(n_br):
+        l_n, alpha[n], dz[n] = branch_scaled(scaled_logits(draft_logits_bf16[n], temperature),
+                                             scaled_logits(target_logits_bf16[n], temperature),
+                                             inv_t, n_br, objective)
+        total += l_n
+    return {"loss": total / n_br, "alpha": alpha, "dz": dz, "dlogits": bf16.encode_rne(dz)}

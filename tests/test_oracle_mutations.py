@@ -19,6 +19,7 @@ import oracle.verify
 
 from . import test_oracle_bf16 as t_bf16
 from . import test_oracle_loss as t_loss
+from . import test_oracle_loss_logits as t_logits
 from . import test_oracle_objectives as t_obj
 from . import test_oracle_philox as t_philox
 from . import test_oracle_schedule as t_sched
@@ -99,6 +100,16 @@ CASES = [
     ("per-step TV loss sums alpha", oracle.objectives,
      "loss_n = float(np.sum(1.0 - alpha))", "loss_n = float(np.sum(alpha))",
      t_obj, "ob", "test_step_tv_is_half_l1_and_matches_e2e_at_one_position", ()),
+    ("logits-target gradient drops the 1/T chain factor", oracle.objectives,
+     "return loss_n, alpha, float(inv_t) * ds", "return loss_n, alpha, ds",
+     t_logits, "ob", "test_gradient_central_differences_through_the_scaling", ("e2e_tv",)),
+    ("target logits left unscaled by the temperature", oracle.objectives,
+     "scaled_logits(target_logits_bf16[n], temperature)",
+     "bf16.decode(target_logits_bf16[n]).astype(np.float64)",
+     t_logits, "ob", "test_alpha_is_the_verify_overlap_at_the_same_temperature", (0.6,)),
+    ("target softmax taken over the draft row", oracle.objectives,
+     "p = np.stack([e2e.softmax64(s_t[k])", "p = np.stack([e2e.softmax64(np.asarray(s_z)[k])",
+     t_logits, "ob", "test_matches_torch_autograd_at_an_exact_temperature", ("ce",)),
     ("schedule takes the smallest survivals first", oracle.schedule,
      "order = np.lexsort((np.arange(flat.size), -flat.astype(np.float64)))",
      "order = np.lexsort((np.arange(flat.size), flat.astype(np.float64)))",
