@@ -56,6 +56,7 @@ extern "C" {
 #define LVTV_ERR_WORKSPACE (-4) /* workspace NULL or smaller than queried */
 #define LVTV_ERR_LAUNCH (-5)    /* the HIP runtime rejected a launch     */
 #define LVTV_ERR_OBJECTIVE (-6) /* unknown loss objective                */
+#define LVTV_ERR_TEMPERATURE (-7) /* loss temperature not finite and > 0 */
 
 /* Objectives of draft_loss_fwd_bwd, each summed over a branch's W positions
  * and averaged over the N branches. */
@@ -307,6 +308,45 @@ int draft_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
                        int32_t N, int32_t W, int32_t V, int objective,
                        float* loss, float* alpha, uint16_t* dlogits,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes draft_loss_logits_fwd_bwd needs (0 if out of range; the
+ * same as e2e_tv_loss_workspace_bytes). Host only.
+ */
+size_t draft_loss_logits_workspace_bytes(int32_t N, int32_t W, int32_t V);
+
+/*
+ * draft_loss_logits_fwd_bwd -- draft_loss_fwd_bwd with the target given as
+ * bfloat16 logits and a temperature: the target softmax is computed inside
+ * the kernels, so the target costs 2 bytes per token instead of 4 and no
+ * probability tensor is ever written.
+ *
+ * What it computes: both rows take the verify step's temperature transform
+ * ("Speculative Decoding and MTP" survey, section 4: p and q after the same
+ * transform), s = fl32(x * fl32(1/T)); p_{n,k} = softmax(s_target[n,k]) and
+ * q_{n,k} = softmax(s_draft[n,k]), so alpha_{n,k} = sum_v min(q, p) is the
+ * overlap the verify step sees at temperature T ("Reading Qwen Bebop and
+ * DeepSeek DSpark", section "Formulas", eq. alpha_RS). The objective and its
+ * reduction are as draft_loss_fwd_bwd's. The gradient is taken with respect
+ * to the raw draft logits through s = x * fl32(1/T): every dlogits value of
+ * draft_loss_fwd_bwd is multiplied by fl32(1/T). p is a constant ("SpecOPD"
+ * summary, method step (6)).
+ *
+ * Arguments (device pointers; row-major, V contiguous):
+ *   draft_logits   bfloat16 (uint16) [N, W, V].
+ *   target_logits  bfloat16 (uint16) [N, W, V], constants.
+ *   temperature    host float, finite and > 0 with fl32(1/T) finite, else
+ *                  LVTV_ERR_TEMPERATURE before enqueueing anything.
+ *   objective, N, W, V, loss, alpha, dlogits, workspace, stream: as
+ *                  draft_loss_fwd_bwd (the workspace needs the same
+ *                  one-time zero fill).
+ * The TV objectives run the single-read kernel when V <= 155648; CE, KL and
+ * larger V run the multi-pass pipeline.
+ */
+int draft_loss_logits_fwd_bwd(const uint16_t* draft_logits, const uint16_t* target_logits,
+                              float temperature, int32_t N, int32_t W, int32_t V,
+                              int objective, float* loss, float* alpha, uint16_t* dlogits,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dspark_schedule -- confidence-scheduled verify lengths ("Reading Qwen

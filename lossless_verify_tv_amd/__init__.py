@@ -24,6 +24,8 @@ from ._binding import (  # noqa: F401
     OBJECTIVES,
     LvtvError,
     draft_loss_fwd_bwd,
+    draft_loss_logits_fwd_bwd,
+    draft_loss_logits_workspace_bytes,
     draft_loss_workspace_bytes,
     dspark_schedule,
     e2e_tv_loss_fwd_bwd,

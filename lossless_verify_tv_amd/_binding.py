@@ -41,6 +41,8 @@ EXPORTS = (
     "e2e_tv_loss_fwd_bwd",
     "draft_loss_workspace_bytes",
     "draft_loss_fwd_bwd",
+    "draft_loss_logits_workspace_bytes",
+    "draft_loss_logits_fwd_bwd",
     "dspark_schedule",
 )
 
@@ -98,6 +100,11 @@ def load_library(path: str = LIB_PATH):
         lib.draft_loss_fwd_bwd.restype = ctypes.c_int
         lib.draft_loss_fwd_bwd.argtypes = [vp, vp, i32, i32, i32, ctypes.c_int, vp, vp, vp, vp,
                                            sz, vp]
+        lib.draft_loss_logits_workspace_bytes.restype = sz
+        lib.draft_loss_logits_workspace_bytes.argtypes = [i32, i32, i32]
+        lib.draft_loss_logits_fwd_bwd.restype = ctypes.c_int
+        lib.draft_loss_logits_fwd_bwd.argtypes = [vp, vp, ctypes.c_float, i32, i32, i32,
+                                                  ctypes.c_int, vp, vp, vp, vp, sz, vp]
         lib.dspark_schedule.restype = ctypes.c_int
         lib.dspark_schedule.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         _lib = lib
@@ -318,6 +325,45 @@ def draft_loss_fwd_bwd(draft_logits, target_probs, objective, workspace=None, ou
                                       _ptr(loss), _ptr(alpha), _ptr(dlogits), _ptr(ws),
                                       ws.numel(), _stream(dev))
     _check(code, "draft_loss_fwd_bwd")
+    return loss, alpha, dlogits
+
+
+def draft_loss_logits_workspace_bytes(N, W, V) -> int:
+    return int(load_library().draft_loss_logits_workspace_bytes(N, W, V))
+
+
+def draft_loss_logits_fwd_bwd(draft_logits, target_logits, temperature, objective="e2e_tv",
+                              workspace=None, out=None):
+    """draft_loss_fwd_bwd with the target given as bfloat16 logits and a
+    temperature applied to both rows (see include/lvtv.h). ``temperature`` is
+    a host float; otherwise as draft_loss_fwd_bwd."""
+    lib = load_library()
+    obj = OBJECTIVES.get(objective, objective)
+    _require(isinstance(obj, int), f"unknown objective {objective!r}")
+    dev = draft_logits.device
+    _require(dev.type == "cuda", "draft_loss_logits_fwd_bwd needs GPU tensors")
+    _require(draft_logits.dtype == torch.bfloat16, "draft_logits must be bfloat16")
+    _require(target_logits.dtype == torch.bfloat16, "target_logits must be bfloat16")
+    _require(draft_logits.dim() == 3 and tuple(target_logits.shape) == tuple(draft_logits.shape),
+             "draft_logits and target_logits must both be [N, W, V]")
+    for t in (draft_logits, target_logits):
+        _require(t.device == dev and t.is_contiguous(), "inputs must be contiguous on one GPU")
+    N, W, V = draft_logits.shape
+    need = lib.draft_loss_logits_workspace_bytes(N, W, V)
+    _require(need > 0, f"sizes out of range: N={N} W={W} V={V}")
+    ws = workspace if workspace is not None else _workspace("loss", dev, need)
+    if out is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        alpha = torch.empty(N, W, dtype=torch.float32, device=dev)
+        dlogits = torch.empty(N, W, V, dtype=torch.bfloat16, device=dev)
+    else:
+        loss, alpha, dlogits = out
+    with torch.cuda.device(dev):
+        code = lib.draft_loss_logits_fwd_bwd(_ptr(draft_logits), _ptr(target_logits),
+                                             float(temperature), N, W, V, obj, _ptr(loss),
+                                             _ptr(alpha), _ptr(dlogits), _ptr(ws), ws.numel(),
+                                             _stream(dev))
+    _check(code, "draft_loss_logits_fwd_bwd")
     return loss, alpha, dlogits
 
 

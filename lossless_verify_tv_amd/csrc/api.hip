@@ -45,6 +45,7 @@ extern "C" const char* lvtv_strerror(int code) {
     case LVTV_ERR_WORKSPACE: return "workspace is NULL, misaligned or smaller than required";
     case LVTV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case LVTV_ERR_OBJECTIVE: return "unknown loss objective";
+    case LVTV_ERR_TEMPERATURE: return "temperature not finite and > 0 (or 1/T overflows)";
     default: return "unknown error code";
   }
 }

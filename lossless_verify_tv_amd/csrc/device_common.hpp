@@ -178,12 +178,13 @@ struct SliceStat {
 };
 
 // Combine per-slice (m, l) into the row's (M, L): M = max m_s,
-// L = sum_s l_s exp(m_s - M), in fp64, in slice order. Every thread of the
+// L = sum_s l_s exp((m_s - M) scale), in fp64, in slice order (scale is the
+// natural-log factor of the exponent: 1 for exp(x - m)). Every thread of the
 // block gets the same values.
 __device__ __forceinline__ void combine_row_stats(const SliceStat* parts, int n,
                                                   double* scratch_d,
                                                   float* scratch_f, double& M,
-                                                  double& L) {
+                                                  double& L, double scale) {
   float mloc = -INFINITY;
   for (int s = threadIdx.x; s < n; s += kBlock) mloc = fmaxf(mloc, (float)parts[s].m);
   const float mf = block_max(mloc, scratch_f);
@@ -193,7 +194,7 @@ __device__ __forceinline__ void combine_row_stats(const SliceStat* parts, int n,
     const double ms = parts[s].m;
     // slices that are entirely -inf weigh 0 (their l is 0, or NaN if a NaN
     // was present, which must propagate)
-    const double wgt = (ms == -INFINITY) ? 0.0 : exp(ms - M);
+    const double wgt = (ms == -INFINITY) ? 0.0 : exp((ms - M) * scale);
     lloc += (ms == -INFINITY) ? parts[s].l * 0.0 : parts[s].l * wgt;
   }
   L = block_sum(lloc, scratch_d);

@@ -42,6 +42,7 @@
 #include "fused_common.hpp"
 #include "loss_fused.hpp"
 
+#include <cmath>
 #include <cstdlib>
 
 namespace lvtv {
@@ -52,10 +53,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kSteps = kSlice / (kBlock * kVec);
 
 struct RowFinal {
-  float neg_m_log2e;  // -M log2(e)
+  float neg_m_log2e;  // -M c (c = log2(e) fl32(1/T), log2(e) without a temperature)
   float inv_l;        // 1 / L
   float c_below;      // (G/N) S'   applied where q < p    (CE, KL: (sum p)/N, the weight of q)
   float c_above;      // -(G/N) S   applied where q >= p   (CE, KL: 1/N, the weight of p)
+  float neg_t;        // target given as logits: -M_t c of the target row
+  float inv_lt;       // ... and 1 / L_t
 };
 
 struct Part {
@@ -68,6 +71,10 @@ struct Layout {
   size_t off_stat, off_part, off_fin, off_branch, total;
 };
 
+// Statistics are kept for two rows per (branch, position): the draft row,
+// then (target given as logits) the target row.
+constexpr int kStatSets = 2;
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 Layout make_layout(int N, int W, int V) {
@@ -76,7 +83,7 @@ Layout make_layout(int N, int W, int V) {
   const size_t rows = size_t(N) * W;
   size_t off = kReservedBytes;
   L.off_stat = off;
-  off = align256(off + sizeof(SliceStat) * rows * L.S);
+  off = align256(off + sizeof(SliceStat) * rows * L.S * kStatSets);
   L.off_part = off;
   off = align256(off + sizeof(Part) * rows * L.S);
   L.off_fin = off;
@@ -89,7 +96,11 @@ Layout make_layout(int N, int W, int V) {
 
 struct Args {
   const uint16_t* z;
-  const float* p;
+  const float* p;         // target probabilities (null when the target is logits)
+  const uint16_t* t;      // target logits (null when the target is probabilities)
+  float c;                // exponent scale log2(e) fl32(1/T) (log2(e) at T = 1)
+  double stat_scale;      // c ln 2 (1 at T = 1): weight of a shift of the maximum
+  double inv_t;           // chain factor fl32(1/T) of the gradient (1 at T = 1)
   int N, W, V;
   int objective;  // LVTV_OBJ_*
   bool vec_ok;
@@ -126,10 +137,19 @@ __device__ __forceinline__ int64_t elem_index(int s, int it) {
   return int64_t(s) * kSlice + it * (kBlock * kVec) + threadIdx.x * kVec;
 }
 
+// 2^(x c + neg), c the exponent scale of the call.
+__device__ __forceinline__ float exp_c(float x, float c, float neg) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, neg));
+}
+
+// Grid (slice, position, branch); with a logits target the second half of
+// the slices' blocks take the target row.
 __global__ __launch_bounds__(kBlock) void row_stats_kernel(Args a) {
-  const int s = blockIdx.x;
+  const bool tgt = int(blockIdx.x) >= a.L.S;
+  const int s = int(blockIdx.x) - (tgt ? a.L.S : 0);
   const size_t row = size_t(blockIdx.z) * a.W + blockIdx.y;
-  const uint16_t* z = a.z + row * a.V;
+  const size_t rows = size_t(a.N) * a.W;
+  const uint16_t* z = (tgt ? a.t : a.z) + row * a.V;
   __shared__ double sd[kWavesPerBlock];
   __shared__ float sf[kWavesPerBlock];
   float x[kSteps][kVec];
@@ -142,17 +162,41 @@ __global__ __launch_bounds__(kBlock) void row_stats_kernel(Args a) {
   }
   m = block_max(m, sf);
   const float ref = (m == -INFINITY) ? 0.f : m;
-  const float neg = -ref * kLog2e;
+  const float neg = -ref * a.c;
   double l = 0.0;
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) acc += exp_shifted(x[it][i], neg);
+    for (int i = 0; i < kVec; ++i) acc += exp_c(x[it][i], a.c, neg);
     l += acc;
   }
   l = block_sum(l, sd);
-  if (threadIdx.x == 0) a.stat[row * a.L.S + s] = SliceStat{(double)m, l};
+  if (threadIdx.x == 0) a.stat[(tgt ? rows : 0) * a.L.S + row * a.L.S + s] = SliceStat{(double)m, l};
+}
+
+// Row statistics (M, L) of the draft row (set 0) or the target row (set 1),
+// L = sum 2^((x - M) c) over the row.
+__device__ __forceinline__ void row_stats(const Args& a, size_t row, int set, double* sd,
+                                          float* sf, double& M, double& L) {
+  const size_t rows = size_t(a.N) * a.W;
+  combine_row_stats(a.stat + (set ? rows : 0) * a.L.S + row * a.L.S, a.L.S, sd, sf, M, L,
+                    a.stat_scale);
+}
+
+// Target probabilities of the group at e: loaded (probability target) or
+// p = 2^(t c - M_t c) / L_t from the target logits; 0 past V either way.
+__device__ __forceinline__ void target_group(const Args& a, const float* p, const uint16_t* t,
+                                             int64_t e, float neg_t, float inv_lt,
+                                             float (&xp)[kVec]) {
+  if (t != nullptr) {
+    float xt[kVec];
+    load8<1>(t, e, a.V, a.vec_ok, xt);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) xp[i] = exp_c(xt[i], a.c, neg_t) * inv_lt;
+  } else {
+    load8_p(p, e, a.V, a.vec_ok, xp);
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void overlap_kernel(Args a) {
@@ -161,24 +205,39 @@ __global__ __launch_bounds__(kBlock) void overlap_kernel(Args a) {
   __shared__ double sd[kWavesPerBlock];
   __shared__ float sf[kWavesPerBlock];
   double M, L;
-  combine_row_stats(a.stat + row * a.L.S, a.L.S, sd, sf, M, L);
-  const float neg = -float(M) * kLog2e;
+  row_stats(a, row, 0, sd, sf, M, L);
+  const float neg = -float(M) * a.c;
   const float inv_l = float(1.0 / L);
   const uint16_t* z = a.z + row * a.V;
-  const float* p = a.p + row * a.V;
+  const bool logits = a.t != nullptr;
+  const float* p = logits ? nullptr : a.p + row * a.V;
+  const uint16_t* t = logits ? a.t + row * a.V : nullptr;
+  float neg_t = 0.f, inv_lt = 0.f;
+  if (logits) {
+    double Mt, Lt;
+    row_stats(a, row, 1, sd, sf, Mt, Lt);
+    neg_t = -float(Mt) * a.c;
+    inv_lt = float(1.0 / Lt);
+  }
   const bool xent = a.objective == LVTV_OBJ_CE || a.objective == LVTV_OBJ_KL;
   const bool kl = a.objective == LVTV_OBJ_KL;
   double al = 0.0, sb = 0.0, sa = 0.0, sp = 0.0, spz = 0.0, splp = 0.0;
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
     const int64_t e = elem_index(s, it);
-    float xz[kVec], xp[kVec];
+    float xz[kVec], xp[kVec], xt[kVec];
     load8<1>(z, e, a.V, a.vec_ok, xz);
-    load8_p(p, e, a.V, a.vec_ok, xp);
+    if (logits) {
+      load8<1>(t, e, a.V, a.vec_ok, xt);
+#pragma unroll
+      for (int i = 0; i < kVec; ++i) xp[i] = exp_c(xt[i], a.c, neg_t) * inv_lt;
+    } else {
+      load8_p(p, e, a.V, a.vec_ok, xp);
+    }
     float a_min = 0.f, a_below = 0.f, a_above = 0.f;
 #pragma unroll
     for (int i = 0; i < kVec; ++i) {
-      const float q = exp_shifted(xz[i], neg) * inv_l;
+      const float q = exp_c(xz[i], a.c, neg) * inv_l;
       a_min += fminf(q, xp[i]);
       const bool below = q < xp[i];
       a_below += below ? q : 0.f;
@@ -196,7 +255,11 @@ __global__ __launch_bounds__(kBlock) void overlap_kernel(Args a) {
         if (v < a.V) {
           b_p += xp[i];
           b_pz += xp[i] * xz[i];
-          if (kl && xp[i] > 0.f) b_plp += xp[i] * logf(xp[i]);
+          // KL: sum p ln p for a probability target; for a logits target
+          // sum p (t - z), from which the branch kernel forms
+          // sum p (ln p - ln q) without a cancellation against CE
+          if (kl && logits && xp[i] > 0.f) b_plp += xp[i] * (xt[i] - xz[i]);
+          if (kl && !logits && xp[i] > 0.f) b_plp += xp[i] * logf(xp[i]);
         }
       }
       sp += b_p;
@@ -221,12 +284,13 @@ __global__ __launch_bounds__(kBlock) void branch_kernel(Args a) {
   __shared__ double sd[kWavesPerBlock];
   __shared__ float sf[kWavesPerBlock];
   __shared__ double al[LVTV_MAX_W], sb[LVTV_MAX_W], sa[LVTV_MAX_W];
-  __shared__ double Ms[LVTV_MAX_W], Ls[LVTV_MAX_W];
+  __shared__ double Ms[LVTV_MAX_W], Ls[LVTV_MAX_W], Mts[LVTV_MAX_W], Lts[LVTV_MAX_W];
   __shared__ double sps[LVTV_MAX_W], spzs[LVTV_MAX_W], splps[LVTV_MAX_W];
   for (int k = 0; k < W; ++k) {
     const size_t row = size_t(n) * W + k;
-    double M, L;
-    combine_row_stats(a.stat + row * a.L.S, a.L.S, sd, sf, M, L);
+    double M, L, Mt = 0.0, Lt = 1.0;
+    row_stats(a, row, 0, sd, sf, M, L);
+    if (a.t != nullptr) row_stats(a, row, 1, sd, sf, Mt, Lt);
     double x = 0.0, y = 0.0, w = 0.0, u = 0.0, t = 0.0, r = 0.0;
     for (int s = threadIdx.x; s < a.L.S; s += kBlock) {
       const Part pt = a.part[row * a.L.S + s];
@@ -249,28 +313,47 @@ __global__ __launch_bounds__(kBlock) void branch_kernel(Args a) {
       sa[k] = w;
       Ms[k] = M;
       Ls[k] = L;
+      Mts[k] = Mt;
+      Lts[k] = Lt;
       sps[k] = u;
       spzs[k] = t;
       splps[k] = r;
     }
   }
   __syncthreads();
+  // the row's exponent references; gradient coefficients carry the chain
+  // factor of the temperature scaling
+  auto row_final = [&](int k) {
+    RowFinal f{-float(Ms[k]) * a.c, float(1.0 / Ls[k]), 0.f, 0.f, 0.f, 0.f};
+    if (a.t != nullptr) {
+      f.neg_t = -float(Mts[k]) * a.c;
+      f.inv_lt = float(1.0 / Lts[k]);
+    }
+    return f;
+  };
   if (threadIdx.x == 0 && a.objective != LVTV_OBJ_E2E_TV) {
     const double inv_n = 1.0 / double(a.N);
     double loss_n = 0.0;
     for (int k = 0; k < W; ++k) {
       const size_t row = size_t(n) * W + k;
-      RowFinal fin{-float(Ms[k]) * kLog2e, float(1.0 / Ls[k]), 0.f, 0.f};
+      RowFinal fin = row_final(k);
       if (a.objective == LVTV_OBJ_STEP_TV) {
         loss_n += 1.0 - al[k];
-        fin.c_below = float(-inv_n * sa[k]);
-        fin.c_above = float(inv_n * sb[k]);
+        fin.c_below = float(-inv_n * sa[k] * a.inv_t);
+        fin.c_above = float(inv_n * sb[k] * a.inv_t);
       } else {
-        // log q = z - M - ln L, so -sum p log q = -sum p z + (M + ln L) sum p
-        const double ce = -spzs[k] + (Ms[k] + log(Ls[k])) * sps[k];
-        loss_n += a.objective == LVTV_OBJ_KL ? ce + splps[k] : ce;
-        fin.c_below = float(sps[k] * inv_n);
-        fin.c_above = float(inv_n);
+        // log q = s - M_s - ln L with s = z fl32(1/T) and M_s = M fl32(1/T),
+        // so -sum p log q = -fl32(1/T) sum p z + (M_s + ln L) sum p
+        const double ce = -a.inv_t * spzs[k] + (a.inv_t * Ms[k] + log(Ls[k])) * sps[k];
+        if (a.objective == LVTV_OBJ_CE)
+          loss_n += ce;
+        else if (a.t == nullptr)
+          loss_n += ce + splps[k];
+        else  // ln p - ln q = (t - z)/T - (M_t - M)/T - ln L_t + ln L
+          loss_n += a.inv_t * splps[k] -
+                    (a.inv_t * (Mts[k] - Ms[k]) + log(Lts[k]) - log(Ls[k])) * sps[k];
+        fin.c_below = float(sps[k] * inv_n * a.inv_t);
+        fin.c_above = float(inv_n * a.inv_t);
       }
       a.fin[row] = fin;
       a.alpha[row] = float(al[k]);
@@ -289,10 +372,12 @@ __global__ __launch_bounds__(kBlock) void branch_kernel(Args a) {
     for (int k = W - 2; k >= 0; --k) suffix[k] = 1.0 + al[k + 1] * suffix[k + 1];
     const double inv_n = 1.0 / double(a.N);
     for (int k = 0; k < W; ++k) {
-      const double g = -(k > 0 ? prefix[k - 1] : 1.0) * suffix[k] * inv_n;
+      const double g = -(k > 0 ? prefix[k - 1] : 1.0) * suffix[k] * inv_n * a.inv_t;
       const size_t row = size_t(n) * W + k;
-      a.fin[row] = RowFinal{-float(Ms[k]) * kLog2e, float(1.0 / Ls[k]), float(g * sa[k]),
-                            float(-g * sb[k])};
+      RowFinal fin = row_final(k);
+      fin.c_below = float(g * sa[k]);
+      fin.c_above = float(-g * sb[k]);
+      a.fin[row] = fin;
       a.alpha[row] = float(al[k]);
     }
     a.branch_loss[n] = loss_n;
@@ -316,7 +401,9 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
   const RowFinal f = a.fin[row];
   const bool xent = a.objective == LVTV_OBJ_CE || a.objective == LVTV_OBJ_KL;
   const uint16_t* z = a.z + row * a.V;
-  const float* p = a.p + row * a.V;
+  const bool logits = a.t != nullptr;
+  const float* p = logits ? nullptr : a.p + row * a.V;
+  const uint16_t* t = logits ? a.t + row * a.V : nullptr;
   uint16_t* dz = a.dz + row * a.V;
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
@@ -324,18 +411,18 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
     if (e >= a.V) break;
     float xz[kVec], xp[kVec];
     load8<1>(z, e, a.V, a.vec_ok, xz);
-    load8_p(p, e, a.V, a.vec_ok, xp);
+    target_group(a, p, t, e, f.neg_t, f.inv_lt, xp);
     uint16_t out[kVec];
     if (xent) {
 #pragma unroll
       for (int i = 0; i < kVec; ++i) {
-        const float q = exp_shifted(xz[i], f.neg_m_log2e) * f.inv_l;
+        const float q = exp_c(xz[i], a.c, f.neg_m_log2e) * f.inv_l;
         out[i] = f32_to_bf16_rne(__builtin_fmaf(q, f.c_below, -(xp[i] * f.c_above)));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < kVec; ++i) {
-        const float q = exp_shifted(xz[i], f.neg_m_log2e) * f.inv_l;
+        const float q = exp_c(xz[i], a.c, f.neg_m_log2e) * f.inv_l;
         const float g = q * (q < xp[i] ? f.c_below : f.c_above);
         out[i] = f32_to_bf16_rne(g);
       }
@@ -400,41 +487,68 @@ size_t loss_workspace_bytes(int32_t N, int32_t W, int32_t V) {
   return n;
 }
 
-int run_loss(const uint16_t* draft_logits, const float* target_probs, int32_t N, int32_t W,
-             int32_t V, int objective, float* loss, float* alpha, uint16_t* dlogits,
-             void* workspace, size_t workspace_bytes, void* stream) {
+// The target of a call: probabilities used as given, or logits with a
+// temperature applied to both rows.
+struct Target {
+  const float* probs;
+  const uint16_t* logits;
+  float temperature;
+};
+
+int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t W, int32_t V,
+             int objective, float* loss, float* alpha, uint16_t* dlogits, void* workspace,
+             size_t workspace_bytes, void* stream) {
   if (!sizes_ok(N, W, V)) return LVTV_ERR_SHAPE;
   if (objective < LVTV_OBJ_E2E_TV || objective > LVTV_OBJ_KL) return LVTV_ERR_OBJECTIVE;
-  if (!draft_logits || !target_probs || !loss || !alpha || !dlogits) return LVTV_ERR_NULL;
+  const bool logits = tg.logits != nullptr || tg.probs == nullptr;
+  if (!draft_logits || (logits ? !tg.logits : !tg.probs) || !loss || !alpha || !dlogits)
+    return LVTV_ERR_NULL;
+  if (logits && !(tg.temperature > 0.f && std::isfinite(tg.temperature) &&
+                  std::isfinite(1.f / tg.temperature)))
+    return LVTV_ERR_TEMPERATURE;
   const Layout L = make_layout(N, W, V);
   if (!workspace || workspace_bytes < loss_workspace_bytes(N, W, V) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(draft_logits) |
-                        reinterpret_cast<uintptr_t>(target_probs) |
+                        reinterpret_cast<uintptr_t>(logits ? static_cast<const void*>(tg.logits)
+                                                           : static_cast<const void*>(tg.probs)) |
                         reinterpret_cast<uintptr_t>(dlogits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
+  // Exponent scale c = fl32(log2(e) fl32(1/T)) (log2(e) itself at T = 1, and
+  // for a probability target, which has no temperature).
+  const bool unit = !logits || tg.temperature == 1.f;
+  const float inv_t = unit ? 1.f : 1.f / tg.temperature;
+  const float c = unit ? kLog2e : kLog2e * inv_t;
   // the single-read kernel serves the TV objectives (their gradients need
   // only the held z, the mask and per-row scalars)
-  if ((objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV) && use_fused(N, W, V)) {
-    lf::LossCall c;
-    c.z = draft_logits;
-    c.p = target_probs;
-    c.N = N;
-    c.W = W;
-    c.V = V;
-    c.objective = objective;
-    c.vec_ok = vec_ok;
-    c.spin_limit = spin_limit();
-    c.loss = loss;
-    c.alpha = alpha;
-    c.dz = dlogits;
-    const hipError_t e = lf::run(c, workspace, static_cast<hipStream_t>(stream));
+  if ((objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV) && use_fused(N, W, V) &&
+      (!logits || lf::logits_supported())) {
+    lf::LossCall lc;
+    lc.z = draft_logits;
+    lc.p = logits ? nullptr : tg.probs;
+    lc.t = logits ? tg.logits : nullptr;
+    lc.c = c;
+    lc.inv_t = double(inv_t);
+    lc.N = N;
+    lc.W = W;
+    lc.V = V;
+    lc.objective = objective;
+    lc.vec_ok = vec_ok;
+    lc.spin_limit = spin_limit();
+    lc.loss = loss;
+    lc.alpha = alpha;
+    lc.dz = dlogits;
+    const hipError_t e = lf::run(lc, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
   }
   Args a;
   a.z = draft_logits;
-  a.p = target_probs;
+  a.p = logits ? nullptr : tg.probs;
+  a.t = logits ? tg.logits : nullptr;
+  a.c = c;
+  a.stat_scale = unit ? 1.0 : double(c) * 0.69314718055994530942;
+  a.inv_t = double(inv_t);
   a.N = N;
   a.W = W;
   a.V = V;
@@ -451,7 +565,8 @@ int run_loss(const uint16_t* draft_logits, const float* target_probs, int32_t N,
   a.branch_loss = reinterpret_cast<double*>(ws + L.off_branch);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(L.S, W, N);
-  hipLaunchKernelGGL(row_stats_kernel, grid, dim3(kBlock), 0, s, a);
+  const dim3 grid_stats(L.S * (logits ? 2 : 1), W, N);
+  hipLaunchKernelGGL(row_stats_kernel, grid_stats, dim3(kBlock), 0, s, a);
   hipLaunchKernelGGL(overlap_kernel, grid, dim3(kBlock), 0, s, a);
   hipLaunchKernelGGL(branch_kernel, dim3(N), dim3(kBlock), 0, s, a);
   hipLaunchKernelGGL(reduce_kernel, dim3(1), dim3(kBlock), 0, s, a);
@@ -474,14 +589,30 @@ extern "C" int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* ta
                                    int32_t N, int32_t W, int32_t V, float* loss, float* alpha,
                                    uint16_t* dlogits, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  return lvtv::run_loss(draft_logits, target_probs, N, W, V, LVTV_OBJ_E2E_TV, loss, alpha,
-                        dlogits, workspace, workspace_bytes, stream);
+  const lvtv::Target tg{target_probs, nullptr, 1.f};
+  return lvtv::run_loss(draft_logits, tg, N, W, V, LVTV_OBJ_E2E_TV, loss, alpha, dlogits,
+                        workspace, workspace_bytes, stream);
 }
 
 extern "C" int draft_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
                                   int32_t N, int32_t W, int32_t V, int objective, float* loss,
                                   float* alpha, uint16_t* dlogits, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  return lvtv::run_loss(draft_logits, target_probs, N, W, V, objective, loss, alpha, dlogits,
-                        workspace, workspace_bytes, stream);
+  const lvtv::Target tg{target_probs, nullptr, 1.f};
+  return lvtv::run_loss(draft_logits, tg, N, W, V, objective, loss, alpha, dlogits, workspace,
+                        workspace_bytes, stream);
+}
+
+extern "C" size_t draft_loss_logits_workspace_bytes(int32_t N, int32_t W, int32_t V) {
+  return lvtv::loss_workspace_bytes(N, W, V);
+}
+
+extern "C" int draft_loss_logits_fwd_bwd(const uint16_t* draft_logits,
+                                         const uint16_t* target_logits, float temperature,
+                                         int32_t N, int32_t W, int32_t V, int objective,
+                                         float* loss, float* alpha, uint16_t* dlogits,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  const lvtv::Target tg{nullptr, target_logits, temperature};
+  return lvtv::run_loss(draft_logits, tg, N, W, V, objective, loss, alpha, dlogits, workspace,
+                        workspace_bytes, stream);
 }

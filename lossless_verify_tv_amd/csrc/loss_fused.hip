@@ -740,6 +740,8 @@ Layout make_layout(int N, int W) {
 
 }  // namespace
 
+bool logits_supported() { return false; }
+
 bool applicable(int N, int W, int V) {
   return V <= kMaxV && size_t(N) * W * 2 < (size_t(1) << 31);
 }

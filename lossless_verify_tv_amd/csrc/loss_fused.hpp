@@ -16,7 +16,10 @@ constexpr int kMaxV = kMaxGroups * 1024 * 8;
 
 struct LossCall {
   const uint16_t* z;
-  const float* p;
+  const float* p;         // target probabilities, or null with ...
+  const uint16_t* t;      // ... target logits (temperature on both rows)
+  float c;                // exponent scale fl32(log2(e) fl32(1/T)) (log2(e) at T = 1)
+  double inv_t;           // chain factor fl32(1/T) of the gradient
   int N, W, V;
   int objective;  // LVTV_OBJ_E2E_TV or LVTV_OBJ_STEP_TV
   bool vec_ok;
@@ -27,6 +30,8 @@ struct LossCall {
 };
 
 bool applicable(int N, int W, int V);
+// Whether the single-read kernel takes a logits target.
+bool logits_supported();
 size_t workspace_bytes(int N, int W, int V);
 hipError_t run(const LossCall& c, void* workspace, hipStream_t stream);
 

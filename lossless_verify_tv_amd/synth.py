@@ -27,6 +27,8 @@ Workloads (numbers are the defaults; tests shrink B, K and V):
 4. Loss: N=512 branches, W=7, V=151936. Target logits from the workload-3
    Zipf generator; target probabilities = fp32 of their fp64 softmax;
    draft logits = bf16(target + N(0, sigma_n^2)), sigma_n = (0.3, 1, 2)[n mod 3].
+   With the target given as logits, the same target rows are stored as bf16
+   instead of probabilities.
 5. B=256, K_b ~ U{1..8}, Kmax=8, padded layout, V=129280, bf16 Zipf, sigma_b as
    in 3; T_b = 0 for even b and 1.0 for odd b; per-request uint64 seeds.
 
@@ -235,3 +237,43 @@ def loss_case(n_branches=512, width=7, vocab=151936, case=4, workers=1):
         for n in range(n_branches):
             z[n], p[n] = loss_branch(n, width, vocab, prior, case)
     return LossCase(z, p, meta={"N": n_branches, "W": width, "V": vocab})
+
+
+@dataclass
+class LossLogitsCase:
+    draft_logits: np.ndarray   # uint16 bf16 [N, W, V]
+    target_logits: np.ndarray  # uint16 bf16 [N, W, V]
+    meta: dict = field(default_factory=dict)
+
+
+def loss_logits_branch(n, width, vocab, prior, case=4):
+    """Rows of branch ``n`` with the target as logits: (bf16 draft logits
+    [W, V], bf16 target logits [W, V]); the same rows as ``loss_branch``,
+    the target stored in bf16 instead of as probabilities."""
+    z = np.empty((width, vocab), dtype=np.uint16)
+    t = np.empty((width, vocab), dtype=np.uint16)
+    sigma = SIGMAS[n % len(SIGMAS)]
+    for k in range(width):
+        t32 = _target_row(case, n, k, vocab, "zipf", prior)
+        t[k] = to_bf16(t32)
+        z[k] = to_bf16(_draft_row(case, n, k, vocab, t32, sigma))
+    return z, t
+
+
+def loss_logits_case(n_branches=512, width=7, vocab=151936, case=4, workers=1):
+    """The loss workload with the target given as bf16 logits (the
+    temperature is a call argument, not part of the inputs)."""
+    prior = zipf_prior(case, vocab)
+    z = np.empty((n_branches, width, vocab), dtype=np.uint16)
+    t = np.empty((n_branches, width, vocab), dtype=np.uint16)
+    if workers > 1 and n_branches > 1:
+        from concurrent.futures import ProcessPoolExecutor
+        with ProcessPoolExecutor(max_workers=workers) as pool:
+            futs = {n: pool.submit(loss_logits_branch, n, width, vocab, prior, case)
+                    for n in range(n_branches)}
+            for n, f in futs.items():
+                z[n], t[n] = f.result()
+    else:
+        for n in range(n_branches):
+            z[n], t[n] = loss_logits_branch(n, width, vocab, prior, case)
+    return LossLogitsCase(z, t, meta={"N": n_branches, "W": width, "V": vocab})

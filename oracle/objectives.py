@@ -116,7 +116,7 @@ def draft_loss(draft_logits_bf16, target_probs, objective):
 # * both logit rows are scaled by the verify step's transform,
 #   s = fl32(x * fl32(1/T)) (``oracle.verify.scale``); p_k = softmax(s_target),
 #   q_k = softmax(s_draft), both in fp64;
-# * T > 0 only (a greedy target has no gradient);
+# * T > 0 only (a greedy target has no gradient), with fl32(1/T) finite;
 # * the gradient is taken with respect to the raw draft logits through the
 #   linear map s = x * fl32(1/T), i.e. d/dx = fl32(1/T) * d/ds (the rounding
 #   of s is not differentiated);
@@ -143,10 +143,12 @@ def draft_loss_logits(draft_logits_bf16, target_logits_bf16, temperature, object
     """Full loss over [N, W, V] with the target given as bfloat16 logits and
     the temperature ``temperature`` > 0 on both sides. Returns a dict as
     ``draft_loss``."""
-    if not (np.isfinite(temperature) and temperature > 0):
-        raise ValueError("the temperature must be finite and > 0")
+    with np.errstate(over="ignore", divide="ignore"):
+        inv32 = np.float32(1.0) / np.float32(temperature)
+    if not (np.isfinite(temperature) and temperature > 0 and np.isfinite(inv32)):
+        raise ValueError("the temperature must be finite and > 0, with fl32(1/T) finite")
     n_br, width, vocab = draft_logits_bf16.shape
-    inv_t = float(np.float32(1.0) / np.float32(temperature))
+    inv_t = float(inv32)
     alpha = np.zeros((n_br, width))
     dz = np.zeros((n_br, width, vocab))
     total = 0.0

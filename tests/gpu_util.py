@@ -76,3 +76,13 @@ def run_draft_loss(z_u16, p_f32, objective, dev=None):
     torch.cuda.synchronize(dev)
     return {"loss": float(loss.cpu().numpy()[0]), "alpha": alpha.cpu().numpy(),
             "dlogits": dl.view(torch.int16).cpu().numpy().view(np.uint16)}
+
+
+def run_loss_logits(z_u16, t_u16, temperature, objective, dev=None):
+    dev = dev or device()
+    z = torch.from_numpy(np.ascontiguousarray(z_u16).view(np.int16)).view(torch.bfloat16).to(dev)
+    t = torch.from_numpy(np.ascontiguousarray(t_u16).view(np.int16)).view(torch.bfloat16).to(dev)
+    loss, alpha, dl = lv.draft_loss_logits_fwd_bwd(z, t, temperature, objective)
+    torch.cuda.synchronize(dev)
+    return {"loss": float(loss.cpu().numpy()[0]), "alpha": alpha.cpu().numpy(),
+            "dlogits": dl.view(torch.int16).cpu().numpy().view(np.uint16)}

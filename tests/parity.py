@@ -159,8 +159,15 @@ def compare_branch(gpu_u16, z_u16, p32, n_branches, grad=None):
     if grad is None:
         def grad(zz, pp):
             return ol.branch(zz, pp, n_branches)[4]
-    z64 = obf16.decode(z_u16)
-    p64 = np.asarray(p32, dtype=np.float64)
+    return _compare_tv_rows(gpu_u16, obf16.decode(z_u16), np.asarray(p32, dtype=np.float64),
+                            grad)
+
+
+def _compare_tv_rows(gpu_u16, z64, p64, grad):
+    """compare_branch on fp64 (scaled) draft logits z64 and probabilities
+    p64; q = softmax(z64)."""
+    from oracle import bf16 as obf16
+
     dz = grad(z64, p64)
     q = np.exp(z64 - z64.max(-1, keepdims=True))
     q /= q.sum(-1, keepdims=True)
@@ -213,9 +220,18 @@ def compare_xent_branch(gpu_u16, z_u16, p32, n_branches, objective):
     z64 = obf16.decode(z_u16)
     p64 = np.asarray(p32, dtype=np.float64)
     dz = ob.branch(z64, p64, n_branches, objective)[2]
+    return _compare_xent_rows(gpu_u16, z64, p64, dz, n_branches, 1.0)
+
+
+def _compare_xent_rows(gpu_u16, z64, p64, dz, n_branches, scale):
+    """compare_xent_branch on fp64 (scaled) draft logits z64 and
+    probabilities p64, with the oracle's gradient dz already formed and
+    carrying the chain factor ``scale``."""
+    from oracle import bf16 as obf16
+
     q = np.exp(z64 - z64.max(-1, keepdims=True))
     q /= q.sum(-1, keepdims=True)
-    err = XENT_QTOL * (q * p64.sum(-1, keepdims=True) + p64) / n_branches
+    err = XENT_QTOL * scale * (q * p64.sum(-1, keepdims=True) + p64) / n_branches
     g = np.asarray(gpu_u16, dtype=np.uint16)
     exact = g == obf16.encode_rne(dz)
     lo = bf16_bits_to_f64(obf16.encode_rne(dz - err))
@@ -229,3 +245,29 @@ def compare_xent_branch(gpu_u16, z_u16, p32, n_branches, objective):
         i = int(np.flatnonzero(bad.ravel())[0])
         first = (np.unravel_index(i, bad.shape), float(gv.ravel()[i]), float(dz.ravel()[i]))
     return int(bad.sum()), int((within & ~exact).sum()), first
+
+
+def compare_branch_logits(gpu_u16, z_u16, t_u16, temperature, n_branches, objective):
+    """Gradient rows of one branch of draft_loss_logits_fwd_bwd: the oracle
+    works on the scaled logits s = fl32(x fl32(1/T)) of both rows, with
+    p = softmax(s_target), and its gradient carries the chain factor
+    fl32(1/T). The TV objectives follow compare_branch's rules (ties
+    included), CE and KL compare_xent_branch's, with the tolerance scaled by
+    fl32(1/T); both q and p are formed on the GPU here, and those bounds
+    cover an error of that size in either. Returns (n_bad, n_excused,
+    first_bad)."""
+    from oracle import objectives as ob
+
+    s_z = ob.scaled_logits(z_u16, temperature)
+    s_t = ob.scaled_logits(t_u16, temperature)
+    inv = float(np.float32(1.0) / np.float32(temperature))
+    e = np.exp(s_t - s_t.max(-1, keepdims=True))
+    p64 = e / e.sum(-1, keepdims=True)
+    if objective in ("ce", "kl"):
+        dz = inv * ob.branch(s_z, p64, n_branches, objective)[2]
+        return _compare_xent_rows(gpu_u16, s_z, p64, dz, n_branches, inv)
+
+    def grad(zz, pp):
+        return inv * ob.branch(zz, pp, n_branches, objective)[2]
+    bad, mid, tie, _, first = _compare_tv_rows(gpu_u16, s_z, p64, grad)
+    return bad, mid + tie, first

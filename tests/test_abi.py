@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_strerror(lib):
     assert lib.lvtv_version() >= 1
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lv.strerror(code)
     assert "unknown" in lv.strerror(-99)
 
@@ -113,6 +113,24 @@ def test_draft_loss_host_errors(lib):
     assert call(N=0) == -2
     assert call(z=NULL) == -1
     assert call(wsb=need - 1) == -4
+
+
+def test_draft_loss_logits_host_errors(lib):
+    need = lv.draft_loss_logits_workspace_bytes(4, 3, 100)
+    assert need == lv.draft_loss_workspace_bytes(4, 3, 100)
+    call = lambda **kw: lib.draft_loss_logits_fwd_bwd(*{**dict(
+        z=FAKE, t=FAKE, T=0.7, N=4, W=3, V=100, obj=0, loss=FAKE, alpha=FAKE, dz=FAKE,
+        ws=FAKE, wsb=need, stream=NULL), **kw}.values())
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-39):
+        assert call(T=bad) == -7
+    assert call(obj=4) == -6
+    assert call(N=0) == -2
+    assert call(W=17) == -2
+    assert call(z=NULL) == -1
+    assert call(t=NULL) == -1
+    assert call(dz=NULL) == -1
+    assert call(wsb=need - 1) == -4
+    assert call(ws=ctypes.c_void_p(0x1010)) == -4
 
 
 def test_packed_verify_host_errors(lib):

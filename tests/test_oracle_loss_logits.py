@@ -123,7 +123,7 @@ def test_unit_temperature_is_the_probability_target(objective):
     assert np.allclose(out["dz"], ref["dz"], rtol=1e-4, atol=1e-9)
 
 
-@pytest.mark.parametrize("temperature", [0.0, -1.0, float("nan"), float("inf")])
+@pytest.mark.parametrize("temperature", [0.0, -1.0, float("nan"), float("inf"), 1e-39])
 def test_bad_temperature_is_refused(temperature):
     z, t = _case(6, 1, 1, 8)
     with pytest.raises(ValueError):
