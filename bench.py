@@ -294,6 +294,27 @@ def main():
         variants[f"draft_loss_{name}"] = {
             "ms": ms, "gbs": lb / (ms * 1e-3) / 1e9,
             "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb}
+    # The loss with the target given as bf16 logits (target softmax fused;
+    # algorithmic bytes 6 per token: z 2 + t 2 read, dz 2 written).
+    lgc = synth.loss_logits_case(workers=min(16, os.cpu_count() or 1))
+    tl = bf16_dev(lgc.target_logits)
+    del lgc
+    lb6 = 6 * LOSS_N * LOSS_W * VOCAB
+    for name, temp in (("e2e_tv", 1.0), ("e2e_tv", 0.7)):
+        lv.draft_loss_logits_fwd_bwd(z, tl, temp, name, workspace=lws, out=lout)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            lv.draft_loss_logits_fwd_bwd(z, tl, temp, name, workspace=lws, out=lout)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        variants[f"draft_loss_logits_{name}_T{temp}"] = {
+            "ms": ms, "gbs": lb6 / (ms * 1e-3) / 1e9,
+            "frac": lb6 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb6}
+    del tl
     result["loss_variants"] = variants
     log("loss variants: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in variants.items()))
     # Confidence-scheduled verify lengths for 256 requests x 16 positions

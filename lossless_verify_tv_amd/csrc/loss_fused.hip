@@ -22,6 +22,12 @@
 //      dz(u) = (G_j / N) q(u) ([q(u) < p(u)] - S_j), evaluated as
 //      (G_j/N) S'_j q(u) where the bit is set and -(G_j/N) S_j q(u) elsewhere,
 //      rounded to bf16 (nearest even) and written once.
+// With the target given as bf16 logits (draft_loss_logits_fwd_bwd), step 2
+// also streams the half of the target row once for its statistics (a running
+// maximum and sum per thread), swapped with the other half like the draft's,
+// and step 3 streams it again, forming p = softmax(t) per token instead of
+// loading it; both rows take the exponent scale c = log2(e) fl32(1/T), and
+// the gradient coefficients carry the chain factor fl32(1/T).
 // Every wait is bounded: a half that gives up marks its row unfinished and
 // stops. The call's last launch, one workgroup that runs once every half has
 // finished, completes such rows from the published words, recomputing
@@ -63,18 +69,21 @@ constexpr int kZL = 8;                           // ... of which in LDS (64 KB p
 constexpr int kZR = kZG - kZL;                   // ... and in registers
 constexpr int kMaskWords = (kZG * kVec + 31) / 32;
 constexpr int kPBatch = 4;                       // groups of p in flight together
-constexpr float kL2E = 1.44269504088896340736f;
 static_assert(2 * kHalf >= kMaxV, "two halves cover the largest V");
 
 // Tagged words per half row: the half's statistics, then its parts of the
 // branch sums.
 constexpr int kStatWords = 3;    // M_h (fp32), L_h (fp64)
 constexpr int kPartWords = 6;    // alpha_h, S_h, S'_h (fp64)
-constexpr int kSlotWords = 16;   // per half: [0,3) statistics, [4,10) parts
+constexpr int kSlotWords = 16;   // per half: [0,3) statistics, [4,10) parts,
+constexpr int kTStatWord = 10;   // [10,13) the target row's statistics (logits target)
 
 struct Args {
   const uint16_t* z;
-  const float* p;
+  const float* p;        // target probabilities, or
+  const uint16_t* t;     // target logits (kLogits)
+  float c;               // exponent scale log2(e) fl32(1/T) (log2(e) at T = 1)
+  double inv_t;          // chain factor fl32(1/T) of the gradient
   int N, W, V;
   int objective;  // LVTV_OBJ_E2E_TV or LVTV_OBJ_STEP_TV
   int spin_limit;
@@ -178,9 +187,9 @@ __device__ __forceinline__ void launder(Held& h) {
   for (int g = 0; g < kZR; ++g) asm volatile("" : "+v"(h.r[g]));
 }
 
-// q of one token: 2^(z log2 e - M log2 e) / L.
-__device__ __forceinline__ float qval(float z, float nm, float inv_l) {
-  return __builtin_amdgcn_exp2f(__builtin_fmaf(z, kL2E, nm)) * inv_l;
+// q of one token: 2^(z c - M c) / L (c = log2 e without a temperature).
+__device__ __forceinline__ float qval(float z, float c, float nm, float inv_l) {
+  return __builtin_amdgcn_exp2f(__builtin_fmaf(z, c, nm)) * inv_l;
 }
 
 // ------------------------------------------------------------------ block reductions
@@ -238,23 +247,32 @@ __device__ __forceinline__ float grp_max(const u32x4& g, float m) {
   return m;
 }
 
-__device__ __forceinline__ float grp_expsum(const u32x4& g, float nm) {
+__device__ __forceinline__ float grp_expsum(const u32x4& g, float c, float nm) {
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < kVec; ++j) s += __builtin_amdgcn_exp2f(__builtin_fmaf(zelem(g, j), kL2E, nm));
+  for (int j = 0; j < kVec; ++j) s += __builtin_amdgcn_exp2f(__builtin_fmaf(zelem(g, j), c, nm));
   return s;
 }
 
-// alpha, S and S' parts of a group, and its 8 mask bits.
+// Reference and inverse sum of a row's softmax: p or q = 2^(x c + nm) inv_l.
+struct RowStats {
+  float nm;     // -M c (0 when M = -inf)
+  float inv_l;  // fl32(1 / L)
+};
+
+// alpha, S and S' parts of a group, and its 8 mask bits. The target's group
+// is (pa, pb), 8 probabilities, or (kLogits) pa, 8 bf16 logits whose p is
+// formed with the target row's statistics ts.
+template <bool kLogits>
 __device__ __forceinline__ uint32_t grp_overlap(const u32x4& g, const u32x4& pa, const u32x4& pb,
-                                                float nm, float inv_l, double& al, double& sb,
-                                                double& sa) {
+                                                float cz, const RowStats& rs, const RowStats& ts,
+                                                double& al, double& sb, double& sa) {
   float a = 0.f, b = 0.f, c = 0.f;
   uint32_t bits = 0;
 #pragma unroll
   for (int j = 0; j < kVec; ++j) {
-    const float q = qval(zelem(g, j), nm, inv_l);
-    const float p = pelem(pa, pb, j);
+    const float q = qval(zelem(g, j), cz, rs.nm, rs.inv_l);
+    const float p = kLogits ? qval(zelem(pa, j), cz, ts.nm, ts.inv_l) : pelem(pa, pb, j);
     const bool below = q < p;
     a += below ? q : p;
     b += below ? q : 0.f;
@@ -284,19 +302,15 @@ __device__ __forceinline__ double block_sum1(double v, Shared& sh) {
 // L = sum_h l_h 2^((m_h - M) log2 e) in fp64 (a half of maximum -inf weighs
 // l_h * 0, which keeps a NaN). Both halves and the last launch call this
 // with the same values, so they agree bit for bit.
-struct RowStats {
-  float nm;     // -M log2 e (0 when M = -inf)
-  float inv_l;  // fl32(1 / L)
-};
-
-__device__ __forceinline__ RowStats combine_halves(float m0, double l0, float m1, double l1) {
+__device__ __forceinline__ RowStats combine_halves(float m0, double l0, float m1, double l1,
+                                                   float c) {
   const float M = fmaxf(m0, m1);
   const double w0 = (m0 == -INFINITY) ? l0 * 0.0
-                                      : l0 * (double)__builtin_amdgcn_exp2f((m0 - M) * kL2E);
+                                      : l0 * (double)__builtin_amdgcn_exp2f((m0 - M) * c);
   const double w1 = (m1 == -INFINITY) ? l1 * 0.0
-                                      : l1 * (double)__builtin_amdgcn_exp2f((m1 - M) * kL2E);
+                                      : l1 * (double)__builtin_amdgcn_exp2f((m1 - M) * c);
   RowStats r;
-  r.nm = (M == -INFINITY) ? 0.f : -(M * kL2E);
+  r.nm = (M == -INFINITY) ? 0.f : -(M * c);
   r.inv_l = float(1.0 / (w0 + w1));
   return r;
 }
@@ -305,6 +319,15 @@ __device__ __forceinline__ RowStats combine_halves(float m0, double l0, float m1
 __device__ __forceinline__ double word_f64(const uint32_t* w, int i) {
   return __longlong_as_double((long long)((uint64_t(w[i + 1]) << 32) | w[i]));
 }
+
+// Row statistics from the words [first, first + 3) of a row's two half
+// slots, laid out slot after slot from `w`.
+__device__ __forceinline__ RowStats row_stats_from(const uint32_t* w, int first, float c) {
+  return combine_halves(__uint_as_float(w[first]), word_f64(w, first + 1),
+                        __uint_as_float(w[kSlotWords + first]), word_f64(w, kSlotWords + first + 1),
+                        c);
+}
+
 
 __device__ __forceinline__ void f64_words(double v, uint32_t& lo, uint32_t& hi) {
   const uint64_t bits = uint64_t(__double_as_longlong(v));
@@ -373,8 +396,8 @@ __device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size
       for (int k = W - 2; k >= j; --k) suffix = 1.0 + part(k + 1, 0) * suffix;
       g = -before * suffix / double(a.N);
     }
-    sh.coef[0] = g * part(j, 2);   // S'_j
-    sh.coef[1] = -g * part(j, 1);  // S_j
+    sh.coef[0] = g * part(j, 2) * a.inv_t;   // S'_j
+    sh.coef[1] = -g * part(j, 1) * a.inv_t;  // S_j
     a.alpha[row] = float(part(j, 0));
     if (j == 0) a.branch_loss[n] = loss_n;
   }
@@ -385,8 +408,8 @@ __device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size
 // bits and the row's coefficients.
 template <bool kVecOk>
 __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e, int V,
-                                         const RowStats& rs, float c_below, float c_above,
-                                         uint16_t* dz) {
+                                         float cz, const RowStats& rs, float c_below,
+                                         float c_above, uint16_t* dz) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   u32x4 out;
@@ -397,7 +420,7 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e,
     for (int t = 0; t < 2; ++t) {
       const int jj = 2 * h + t;
       const bool below = (bits8 >> jj) & 1u;
-      v2[t] = qval(zelem(zv, jj), rs.nm, rs.inv_l) * (below ? c_below : c_above);
+      v2[t] = qval(zelem(zv, jj), cz, rs.nm, rs.inv_l) * (below ? c_below : c_above);
     }
     const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
     out[h] = __builtin_bit_cast(uint32_t, b);
@@ -415,9 +438,56 @@ __device__ __forceinline__ uint32_t mask_bits(const uint32_t (&mask)[kMaskWords]
   return (mask[(g * kVec) / 32] >> ((g * kVec) % 32)) & 0xffu;
 }
 
+// Statistics of half h of a target logits row, streamed once from memory:
+// per thread a running maximum m and sum l = sum 2^(t c - m c) over batches
+// of groups (the sum rescaled when the maximum moves), then the block's
+// maximum M_h and sum over threads of l 2^((m - M_h) c). The half workgroups
+// and the last launch call this with the same thread layout, so they agree
+// bit for bit.
+template <bool kVecOk>
+__device__ __forceinline__ HalfStats target_half_stats(const uint16_t* t, int V, int h, float c,
+                                                       Shared& sh) {
+  float m = -INFINITY;
+  double l = 0.0;
+  const int tb = opaque(group_elem(h, 0));
+#pragma unroll 1
+  for (int g0 = 0; g0 < kZG; g0 += kPBatch) {
+    u32x4 x[kPBatch];
+#pragma unroll
+    for (int i = 0; i < kPBatch; ++i)
+      if (g0 + i < kZG) x[i] = load_z<kVecOk>(t, V, opaque(tb) + (g0 + i) * kTile);
+    float bm = m;
+#pragma unroll
+    for (int i = 0; i < kPBatch; ++i)
+      if (g0 + i < kZG) bm = grp_max(x[i], bm);
+    if (bm > m) {
+      l = (m == -INFINITY) ? 0.0 : l * (double)__builtin_amdgcn_exp2f((m - bm) * c);
+      m = bm;
+    }
+    const float nm = (m == -INFINITY) ? 0.f : -(m * c);
+#pragma unroll
+    for (int i = 0; i < kPBatch; ++i)
+      if (g0 + i < kZG) l += (double)grp_expsum(x[i], c, nm);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float M = block_max(m, sh);
+  const double w = (m == -INFINITY) ? l * 0.0 : l * (double)__builtin_amdgcn_exp2f((m - M) * c);
+  return HalfStats{M, block_sum1(w, sh)};
+}
+
+// Publishes half statistics in words [first, first + 3) of a half slot.
+__device__ __forceinline__ void publish_stats(uint64_t* slot, int first, uint32_t tag,
+                                              const HalfStats& hs) {
+  uint32_t lo, hi;
+  f64_words(hs.l, lo, hi);
+  tag_store(slot + first, tag, __float_as_uint(hs.m));
+  tag_store(slot + first + 1, tag, lo);
+  tag_store(slot + first + 2, tag, hi);
+}
+
 // ------------------------------------------------------------------ half-row kernel
 
-template <bool kVecOk>
+template <bool kVecOk, bool kLogits>
 __device__ __forceinline__ void half_body(const Args& a) {
   __shared__ Shared sh;
   __shared__ u32x4 zl[kZL][kThreads];
@@ -429,7 +499,9 @@ __device__ __forceinline__ void half_body(const Args& a) {
   const int j = __builtin_amdgcn_readfirstlane(r - n * W);
   const size_t row = size_t(r);
   const uint16_t* z = a.z + row * V;
-  const float* p = a.p + row * V;
+  const float* p = kLogits ? nullptr : a.p + row * V;
+  const uint16_t* t = kLogits ? a.t + row * V : nullptr;
+  const float c = a.c;
   const uint32_t tag = tag_from_epoch(read_epoch(a.ctl));
   uint64_t* slot = a.words + (row * 2 + h) * kSlotWords;
 
@@ -453,28 +525,28 @@ __device__ __forceinline__ void half_body(const Args& a) {
   for (int g = 0; g < kZG; ++g) m = grp_max(zg.get(g), m);
   launder(zg);
   m = block_max(m, sh);
-  const float nm0 = (m == -INFINITY) ? 0.f : -(m * kL2E);
+  const float nm0 = (m == -INFINITY) ? 0.f : -(m * c);
   double l = 0.0;
 #pragma unroll
-  for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(zg.get(g), nm0);
+  for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(zg.get(g), c, nm0);
   launder(zg);
   l = block_sum1(l, sh);
-  if (threadIdx.x == 0) {
-    uint32_t lo, hi;
-    f64_words(l, lo, hi);
-    tag_store(slot + 0, tag, __float_as_uint(m));
-    tag_store(slot + 1, tag, lo);
-    tag_store(slot + 2, tag, hi);
+  if (threadIdx.x == 0) publish_stats(slot, 0, tag, HalfStats{m, l});
+  if constexpr (kLogits) {
+    const HalfStats ht = target_half_stats<kVecOk>(t, V, h, c, sh);
+    launder(zg);
+    if (threadIdx.x == 0) publish_stats(slot, kTStatWord, tag, ht);
   }
-  if (!poll_slots(a.words + row * 2 * kSlotWords, 2, 0, kStatWords, tag, a.spin_limit, sh)) {
+  uint64_t* rslots = a.words + row * 2 * kSlotWords;
+  if (!poll_slots(rslots, 2, 0, kStatWords, tag, a.spin_limit, sh) ||
+      (kLogits && !poll_slots(rslots, 2, kTStatWord, kStatWords, tag, a.spin_limit, sh))) {
     if (threadIdx.x == 0) tag_store(a.unfinished + row, tag, 1u);
     return;
   }
-  const RowStats rs =
-      combine_halves(__uint_as_float(sh.words[0]), word_f64(sh.words, 1),
-                     __uint_as_float(sh.words[kSlotWords]), word_f64(sh.words, kSlotWords + 1));
+  const RowStats rs = row_stats_from(sh.words, 0, c);
+  const RowStats ts = kLogits ? row_stats_from(sh.words, kTStatWord, c) : RowStats{0.f, 0.f};
 
-  // 3. one pass over this half of p
+  // 3. one pass over this half of p (or of the target logits)
   double al = 0.0, sb = 0.0, sa = 0.0;
   uint32_t mask[kMaskWords];
 #pragma unroll
@@ -485,12 +557,18 @@ __device__ __forceinline__ void half_body(const Args& a) {
     u32x4 pa[kPBatch], pb[kPBatch];
 #pragma unroll
     for (int i = 0; i < kPBatch; ++i)
-      if (g0 + i < kZG) load_p<kVecOk>(p, V, opaque(tbp) + (g0 + i) * kTile, pa[i], pb[i]);
+      if (g0 + i < kZG) {
+        if constexpr (kLogits)
+          pa[i] = load_z<kVecOk>(t, V, opaque(tbp) + (g0 + i) * kTile);
+        else
+          load_p<kVecOk>(p, V, opaque(tbp) + (g0 + i) * kTile, pa[i], pb[i]);
+      }
 #pragma unroll
     for (int i = 0; i < kPBatch; ++i)
       if (g0 + i < kZG) {
         const int g = g0 + i;
-        const uint32_t bits = grp_overlap(zg.get(g), pa[i], pb[i], rs.nm, rs.inv_l, al, sb, sa);
+        const uint32_t bits =
+            grp_overlap<kLogits>(zg.get(g), pa[i], pb[i], c, rs, ts, al, sb, sa);
         mask[(g * kVec) / 32] |= bits << ((g * kVec) % 32);
       }
     // keep the next batch's loads behind this batch's arithmetic
@@ -524,7 +602,7 @@ __device__ __forceinline__ void half_body(const Args& a) {
   const int tbd = opaque(group_elem(h, 0));
 #pragma unroll
   for (int g = 0; g < kZG; ++g) {
-    dz_group<kVecOk>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, rs, c_below,
+    dz_group<kVecOk>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, c, rs, c_below,
                      c_above, dz);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -535,34 +613,59 @@ __device__ __forceinline__ void half_body(const Args& a) {
 // Statistics of half h of a row, streamed from memory (same steps and
 // reductions as a half workgroup).
 template <bool kVecOk>
-__device__ __forceinline__ HalfStats stream_half_stats(const uint16_t* z, int V, int h,
+__device__ __forceinline__ HalfStats stream_half_stats(const uint16_t* z, int V, int h, float c,
                                                        Shared& sh) {
   float m = -INFINITY;
 #pragma unroll 1
   for (int g = 0; g < kZG; ++g) m = grp_max(load_z<kVecOk>(z, V, group_elem(h, g)), m);
   m = block_max(m, sh);
-  const float nm0 = (m == -INFINITY) ? 0.f : -(m * kL2E);
+  const float nm0 = (m == -INFINITY) ? 0.f : -(m * c);
   double l = 0.0;
 #pragma unroll 1
-  for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(load_z<kVecOk>(z, V, group_elem(h, g)), nm0);
+  for (int g = 0; g < kZG; ++g)
+    l += (double)grp_expsum(load_z<kVecOk>(z, V, group_elem(h, g)), c, nm0);
   l = block_sum1(l, sh);
   return HalfStats{m, l};
 }
 
+// The target's group at token e: 8 probabilities in (pa, pb), or (kLogits)
+// 8 bf16 logits in pa.
+template <bool kVecOk, bool kLogits>
+__device__ __forceinline__ void load_target(const Args& a, size_t row, int e, u32x4& pa,
+                                            u32x4& pb) {
+  if constexpr (kLogits) {
+    pa = load_z<kVecOk>(a.t + row * a.V, a.V, e);
+    pb = pa;
+  } else {
+    load_p<kVecOk>(a.p + row * a.V, a.V, e, pa, pb);
+  }
+}
+
 // Parts of half h of a row, streamed from memory.
-template <bool kVecOk>
-__device__ __forceinline__ void stream_half_parts(const uint16_t* z, const float* p, int V, int h,
-                                                  const RowStats& rs, double& al, double& sb,
-                                                  double& sa, Shared& sh) {
+template <bool kVecOk, bool kLogits>
+__device__ __forceinline__ void stream_half_parts(const Args& a, size_t row, int h,
+                                                  const RowStats& rs, const RowStats& ts,
+                                                  double& al, double& sb, double& sa, Shared& sh) {
   al = sb = sa = 0.0;
+  const uint16_t* z = a.z + row * a.V;
 #pragma unroll 1
   for (int g = 0; g < kZG; ++g) {
     const int e = group_elem(h, g);
     u32x4 pa, pb;
-    load_p<kVecOk>(p, V, e, pa, pb);
-    (void)grp_overlap(load_z<kVecOk>(z, V, e), pa, pb, rs.nm, rs.inv_l, al, sb, sa);
+    load_target<kVecOk, kLogits>(a, row, e, pa, pb);
+    (void)grp_overlap<kLogits>(load_z<kVecOk>(z, a.V, e), pa, pb, a.c, rs, ts, al, sb, sa);
   }
   block_sum3(al, sb, sa, sh);
+}
+
+// Writes half statistics into words [first, first + 3) of slot s of a
+// branch's word copy.
+__device__ __forceinline__ void put_stats(uint32_t* bw, int s, int first, const HalfStats& hs) {
+  uint32_t lo, hi;
+  f64_words(hs.l, lo, hi);
+  bw[s * kSlotWords + first] = __float_as_uint(hs.m);
+  bw[s * kSlotWords + first + 1] = lo;
+  bw[s * kSlotWords + first + 2] = hi;
 }
 
 // A row a half left unfinished in this call. Every half workgroup has
@@ -570,10 +673,11 @@ __device__ __forceinline__ void stream_half_parts(const uint16_t* z, const float
 // missing is recomputed from the inputs with the same steps and reductions.
 // Then both halves' dz are written (the mask recomputed from z and p). Every
 // thread of the block calls it.
-template <bool kVecOk>
+template <bool kVecOk, bool kLogits>
 __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag, Shared& sh,
                                            uint32_t* bw) {
   const int W = a.W, V = a.V;
+  const float c = a.c;
   {
     const int n = row / W, j = row - n * W;
     // the branch's published words (stale ones recomputed below)
@@ -581,43 +685,46 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
     for (int i = threadIdx.x; i < W * 2 * kSlotWords; i += kThreads)
       bw[i] = uint32_t(tag_load(base + i));
     __syncthreads();
+    // per half slot: 1 = draft statistics, 2 = parts, 4 = target statistics
+    // are fresh
     for (int s = threadIdx.x; s < 2 * W; s += kThreads) {
-      bool st = true, pt = true;
+      bool st = true, pt = true, tt = true;
       for (int k = 0; k < kStatWords; ++k)
         st &= uint32_t(tag_load(base + s * kSlotWords + k) >> 32) == tag;
       for (int k = 4; k < 4 + kPartWords; ++k)
         pt &= uint32_t(tag_load(base + s * kSlotWords + k) >> 32) == tag;
-      sh.have[s] = uint8_t((st ? 1 : 0) | (pt ? 2 : 0));
+      for (int k = kTStatWord; k < kTStatWord + kStatWords; ++k)
+        tt &= uint32_t(tag_load(base + s * kSlotWords + k) >> 32) == tag;
+      sh.have[s] = uint8_t((st ? 1 : 0) | (pt ? 2 : 0) | ((tt || !kLogits) ? 4 : 0));
     }
     __syncthreads();
     for (int k = 0; k < W; ++k) {
       const size_t rk = size_t(n) * W + k;
       const uint16_t* zk = a.z + rk * V;
-      const float* pk = a.p + rk * V;
       // statistics of both halves
       for (int hh = 0; hh < 2; ++hh) {
         const int s = 2 * k + hh;
         if (!(sh.have[s] & 1)) {
-          const HalfStats hs = stream_half_stats<kVecOk>(zk, V, hh, sh);
+          const HalfStats hs = stream_half_stats<kVecOk>(zk, V, hh, c, sh);
           __syncthreads();
-          if (threadIdx.x == 0) {
-            uint32_t lo, hi;
-            f64_words(hs.l, lo, hi);
-            bw[s * kSlotWords + 0] = __float_as_uint(hs.m);
-            bw[s * kSlotWords + 1] = lo;
-            bw[s * kSlotWords + 2] = hi;
-          }
+          if (threadIdx.x == 0) put_stats(bw, s, 0, hs);
+          __syncthreads();
+        }
+        if (!(sh.have[s] & 4)) {
+          const HalfStats hs = target_half_stats<kVecOk>(a.t + rk * V, V, hh, c, sh);
+          __syncthreads();
+          if (threadIdx.x == 0) put_stats(bw, s, kTStatWord, hs);
           __syncthreads();
         }
       }
-      const RowStats rs = combine_halves(
-          __uint_as_float(bw[(2 * k) * kSlotWords]), word_f64(bw, (2 * k) * kSlotWords + 1),
-          __uint_as_float(bw[(2 * k + 1) * kSlotWords]), word_f64(bw, (2 * k + 1) * kSlotWords + 1));
+      const RowStats rs = row_stats_from(bw + 2 * k * kSlotWords, 0, c);
+      const RowStats ts =
+          kLogits ? row_stats_from(bw + 2 * k * kSlotWords, kTStatWord, c) : RowStats{0.f, 0.f};
       for (int hh = 0; hh < 2; ++hh) {
         const int s = 2 * k + hh;
         if (!(sh.have[s] & 2)) {
           double x, y, w;
-          stream_half_parts<kVecOk>(zk, pk, V, hh, rs, x, y, w, sh);
+          stream_half_parts<kVecOk, kLogits>(a, rk, hh, rs, ts, x, y, w, sh);
           __syncthreads();
           if (threadIdx.x == 0) {
             const double v[3] = {x, y, w};
@@ -637,11 +744,10 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
     branch_scalars(a, n, j, size_t(row), sh);
     const float c_below = float(sh.coef[0]);
     const float c_above = float(sh.coef[1]);
-    const RowStats rs = combine_halves(
-        __uint_as_float(bw[(2 * j) * kSlotWords]), word_f64(bw, (2 * j) * kSlotWords + 1),
-        __uint_as_float(bw[(2 * j + 1) * kSlotWords]), word_f64(bw, (2 * j + 1) * kSlotWords + 1));
+    const RowStats rs = row_stats_from(bw + 2 * j * kSlotWords, 0, c);
+    const RowStats ts =
+        kLogits ? row_stats_from(bw + 2 * j * kSlotWords, kTStatWord, c) : RowStats{0.f, 0.f};
     const uint16_t* z = a.z + size_t(row) * V;
-    const float* p = a.p + size_t(row) * V;
     uint16_t* dz = a.dz + size_t(row) * V;
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll 1
@@ -649,20 +755,20 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
         const int e = group_elem(hh, g);
         const u32x4 zv = load_z<kVecOk>(z, V, e);
         u32x4 pa, pb;
-        load_p<kVecOk>(p, V, e, pa, pb);
+        load_target<kVecOk, kLogits>(a, size_t(row), e, pa, pb);
         double x = 0.0, y = 0.0, w = 0.0;
-        const uint32_t bits = grp_overlap(zv, pa, pb, rs.nm, rs.inv_l, x, y, w);
-        dz_group<kVecOk>(zv, bits, e, V, rs, c_below, c_above, dz);
+        const uint32_t bits = grp_overlap<kLogits>(zv, pa, pb, c, rs, ts, x, y, w);
+        dz_group<kVecOk>(zv, bits, e, V, c, rs, c_below, c_above, dz);
       }
     }
     __syncthreads();
   }
 }
 
-template <bool kVecOk>
+template <bool kVecOk, bool kLogits>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 loss_halves(Args a) {
-  half_body<kVecOk>(a);
+  half_body<kVecOk, kLogits>(a);
 }
 
 __device__ __forceinline__ int block_min(int v, Shared& sh) {
@@ -681,7 +787,7 @@ __device__ __forceinline__ int block_min(int v, Shared& sh) {
 // up to 32 rows per thread are read at once, so the usual case (no flag) costs
 // one round of loads. (2) The loss is the mean of the branch losses, summed
 // in a fixed order. (3) The call epoch advances.
-template <bool kVecOk>
+template <bool kVecOk, bool kLogits>
 __global__ __launch_bounds__(kThreads) void loss_finish(Args a) {
   __shared__ Shared sh;
   __shared__ uint32_t bw[LVTV_MAX_W * 2 * kSlotWords];  // a branch's words
@@ -699,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void loss_finish(Args a) {
       const int cand = mine ? r0 + int(threadIdx.x) + __builtin_ctz(mine) * kThreads : INT_MAX;
       const int row = block_min(cand, sh);
       if (cand == row) mine &= mine - 1u;
-      repair_row<kVecOk>(a, row, tag, sh, bw);
+      repair_row<kVecOk, kLogits>(a, row, tag, sh, bw);
     }
   }
   const int per = (a.N + kThreads - 1) / kThreads;
@@ -740,7 +846,7 @@ Layout make_layout(int N, int W) {
 
 }  // namespace
 
-bool logits_supported() { return false; }
+bool logits_supported() { return true; }
 
 bool applicable(int N, int W, int V) {
   return V <= kMaxV && size_t(N) * W * 2 < (size_t(1) << 31);
@@ -756,6 +862,9 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   Args a;
   a.z = c.z;
   a.p = c.p;
+  a.t = c.t;
+  a.c = c.c;
+  a.inv_t = c.inv_t;
   a.N = c.N;
   a.W = c.W;
   a.V = c.V;
@@ -770,16 +879,15 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   a.unfinished = reinterpret_cast<uint64_t*>(ws + L.off_unfinished);
   a.branch_loss = reinterpret_cast<double*>(ws + L.off_branch);
   const unsigned rows = unsigned(size_t(c.N) * c.W);
-  if (c.vec_ok)
-    hipLaunchKernelGGL(loss_halves<true>, dim3(2 * rows), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(loss_halves<false>, dim3(2 * rows), dim3(kThreads), 0, stream, a);
+  const bool logits = c.t != nullptr;
+  auto halves = c.vec_ok ? (logits ? loss_halves<true, true> : loss_halves<true, false>)
+                         : (logits ? loss_halves<false, true> : loss_halves<false, false>);
+  auto finish = c.vec_ok ? (logits ? loss_finish<true, true> : loss_finish<true, false>)
+                         : (logits ? loss_finish<false, true> : loss_finish<false, false>);
+  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (c.vec_ok)
-    hipLaunchKernelGGL(loss_finish<true>, dim3(1), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(loss_finish<false>, dim3(1), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(finish, dim3(1), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
