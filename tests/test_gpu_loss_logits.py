@@ -110,3 +110,30 @@ def test_full_workload_sampled(objective, T, full_case):
         assert rel_close(gpu["loss"], expect, 1e-5)
     else:
         assert np.isfinite(gpu["loss"]) and gpu["loss"] >= 0.0
+
+
+@pytest.mark.parametrize("objective", ["e2e_tv", "kl"])
+def test_vocab_above_the_single_read_limit(objective):
+    """V = 160000 exceeds what a half workgroup holds: the multi-pass
+    pipeline serves it."""
+    c = synth.loss_logits_case(n_branches=2, width=3, vocab=160000)
+    _check(c.draft_logits, c.target_logits, 0.8, objective, f"{objective} V=160000")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 16, 5), (2, 1, 40000)])
+def test_edge_shapes(shape):
+    """A single token, the widest branch (W = 16) and a single position."""
+    N, W, V = shape
+    c = synth.loss_logits_case(n_branches=N, width=W, vocab=V)
+    for obj in ("e2e_tv", "step_tv", "ce"):
+        _check(c.draft_logits, c.target_logits, 1.3, obj, f"{obj} N={N} W={W} V={V}")
+
+
+def test_target_row_of_one_hot_logits():
+    """A target row with one finite logit and the rest -inf (p one-hot):
+    alpha is q at that token, as the oracle computes it."""
+    c = synth.loss_logits_case(n_branches=2, width=2, vocab=3000)
+    t = c.target_logits.copy()
+    t[:, :, :] = 0xFF80                      # -inf
+    t[:, :, 17] = synth.to_bf16(np.float32([2.0]))[0]
+    _check(c.draft_logits, t, 0.9, "e2e_tv", "one-hot target")
