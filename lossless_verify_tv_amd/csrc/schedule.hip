@@ -18,7 +18,10 @@
 //      NaN read as 0), as 64-bit keys: the complement of the value's bits
 //      above the flat index r L + j, so that one ascending sort orders them
 //      largest first and equal values by index;
-//   2. a bitonic sort of the keys in LDS;
+//   2. a bitonic sort of the keys, held E = 1, 2, 4 or 8 per thread: stages
+//      whose partners share a thread swap in registers, partners in the
+//      same wave exchange through lane shuffles, and only the stages that
+//      cross waves go through LDS and a barrier (10 of 78 at R L = 4096);
 //   3. an fp64 block scan of the sorted survivals; Theta(B) for every B from
 //      R to R (1 + L), the largest kept (the smallest B among equals; a NaN
 //      Theta never wins);
@@ -41,8 +44,9 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 
 struct Shared {
-  uint64_t key[kMaxItems];
-  int32_t len[kMaxItems];  // per request (R <= R L)
+  uint64_t key[kMaxItems];  // survival keys, then (cross-wave stages) the sort's exchange
+  float conf[kMaxItems];
+  int32_t len[kMaxItems];   // per request (R <= R L)
   double wsum[kWaves];
   double wbest[kWaves];
   int32_t wt[kWaves];
@@ -59,51 +63,96 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(0xffffffffu - uint32_t(key >> 32));
 }
 
-__global__ __launch_bounds__(kThreads) void schedule_kernel(const float* conf, const float* sps,
-                                                            int R, int L, int32_t* verify_len,
-                                                            double* best) {
-  __shared__ Shared sh;
-  const int n = R * L;
-  int P = 1;
-  while (P < n) P <<= 1;
-  const int tid = threadIdx.x;
+// One compare-exchange step of the bitonic network for the key at index i
+// with partner value b (index i ^ j): the lower index of an ascending pair
+// (i & k == 0) keeps the smaller key, of a descending pair the larger.
+__device__ __forceinline__ uint64_t bitonic_pick(uint64_t a, uint64_t b, int i, int j, int k) {
+  const bool asc = (i & k) == 0, lower = (i & j) == 0;
+  return (asc == lower) ? (a < b ? a : b) : (a < b ? b : a);
+}
 
-  // 1. survivals as sort keys
+// Sorts the P = 1024 E keys held E per thread (thread t holds indices
+// t E .. t E + E - 1) ascending with the bitonic network: partners in the
+// same thread swap in registers, partners in the same wave through lane
+// shuffles, partners in other waves through LDS.
+template <int E>
+__device__ __forceinline__ void bitonic_sort(uint64_t (&x)[E], int P, Shared& sh) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+        uint64_t y[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) y[e] = bitonic_pick(x[e], x[e ^ j], tid * E + e, j, k);
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = y[e];
+      } else if (j < kWave * E) {
+        const int m = j / E;  // partner lane = lane ^ m
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t b = (uint64_t)__shfl_xor((long long)x[e], m, kWave);
+          x[e] = bitonic_pick(x[e], b, tid * E + e, j, k);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) sh.key[tid * E + e] = x[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          x[e] = bitonic_pick(x[e], sh.key[i ^ j], i, j, k);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+template <int E>
+__device__ __forceinline__ void schedule_body(const float* conf, const float* sps, int R, int L,
+                                              int32_t* verify_len, double* best, Shared& sh) {
+  const int n = R * L;
+  const int P = kThreads * E;
+  const int tid = threadIdx.x;
+  // the throughputs this thread's sorted items price (B = R + i + 1), loaded
+  // now so their latency hides behind the sort
+  float my_sps[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    my_sps[e] = i < n ? sps[R + i + 1] : 0.f;
+  }
+  const float sps0 = sps[R];
+
+  // 1. confidences into LDS (coalesced), survivals as sort keys
+  for (int i = tid; i < n; i += kThreads) sh.conf[i] = conf[i];
+  __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
     float run = 1.f;
     for (int j = 0; j < L; ++j) {
-      run = __fmul_rn(run, clamp_conf(conf[size_t(r) * L + j]));
+      run = __fmul_rn(run, clamp_conf(sh.conf[r * L + j]));
       const uint32_t idx = uint32_t(r * L + j);
       sh.key[idx] = (uint64_t(0xffffffffu - __float_as_uint(run)) << 32) | idx;
     }
     sh.len[r] = 0;
   }
-  for (int i = n + tid; i < P; i += kThreads) sh.key[i] = ~uint64_t(0);
+  __syncthreads();
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    x[e] = i < n ? sh.key[i] : ~uint64_t(0);
+  }
   __syncthreads();
 
-  // 2. bitonic sort, ascending
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t a = sh.key[i], b = sh.key[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > b) == up) {
-            sh.key[i] = b;
-            sh.key[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  // 2. sort, ascending: the largest survivals first, equal ones by index
+  bitonic_sort<E>(x, P, sh);
 
-  // 3. scan of the sorted survivals: thread t owns items [t q, t q + q)
-  const int q = (n + kThreads - 1) / kThreads;
-  const int i0 = tid * q;
+  // 3. scan of the sorted survivals: thread t owns items [t E, t E + E)
   double local = 0.0;
-  for (int i = i0; i < min(i0 + q, n); ++i) local += (double)key_value(sh.key[i]);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (tid * E + e < n) local += (double)key_value(x[e]);
   // exclusive prefix of the per-thread totals: within the wave, then waves
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   double inc = local;
@@ -116,23 +165,27 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const float* conf, c
   __syncthreads();
   double base = 0.0;
   for (int w = 0; w < wave; ++w) base += sh.wsum[w];
-  double s = base + inc - local;  // survivals taken before item i0
+  double s = base + inc - local;  // survivals taken before item t E
   // Theta for B = R + t, t = i + 1 over the thread's items (and t = 0)
   double bv = -INFINITY;
   int bt = INT_MAX;
   if (tid == 0) {
-    const double th = double(R) * (double)sps[R];
+    const double th = double(R) * (double)sps0;
     if (th == th) {
       bv = th;
       bt = 0;
     }
   }
-  for (int i = i0; i < min(i0 + q, n); ++i) {
-    s += (double)key_value(sh.key[i]);
-    const double th = (double(R) + s) * (double)sps[R + i + 1];
-    if (th > bv) {  // a NaN never wins; the first (smallest t) among equals stays
-      bv = th;
-      bt = i + 1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    if (i < n) {
+      s += (double)key_value(x[e]);
+      const double th = (double(R) + s) * (double)my_sps[e];
+      if (th > bv) {  // a NaN never wins; the first (smallest t) among equals stays
+        bv = th;
+        bt = i + 1;
+      }
     }
   }
   // block argmax: largest Theta, smallest t among equals
@@ -164,12 +217,16 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const float* conf, c
   }
   __syncthreads();
 
-  // 4. lengths
+  // 4. lengths: one past the last position of each request among the taken
   const int t = sh.best_t;
-  for (int i = tid; i < t; i += kThreads) {
-    const uint32_t idx = uint32_t(sh.key[i]);
-    const int r = int(idx) / L, j = int(idx) - r * L;
-    atomicMax(&sh.len[r], j + 1);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = tid * E + e;
+    if (i < t) {
+      const uint32_t idx = uint32_t(x[e]);
+      const int r = int(idx) / L, j = int(idx) - r * L;
+      atomicMax(&sh.len[r], j + 1);
+    }
   }
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) verify_len[r] = sh.len[r];
@@ -177,6 +234,21 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(const float* conf, c
     best[0] = sh.best_theta;
     best[1] = double(R + t);
   }
+}
+
+__global__ __launch_bounds__(kThreads) void schedule_kernel(const float* conf, const float* sps,
+                                                            int R, int L, int32_t* verify_len,
+                                                            double* best) {
+  __shared__ Shared sh;
+  const int n = R * L;
+  if (n <= kThreads)
+    schedule_body<1>(conf, sps, R, L, verify_len, best, sh);
+  else if (n <= 2 * kThreads)
+    schedule_body<2>(conf, sps, R, L, verify_len, best, sh);
+  else if (n <= 4 * kThreads)
+    schedule_body<4>(conf, sps, R, L, verify_len, best, sh);
+  else
+    schedule_body<8>(conf, sps, R, L, verify_len, best, sh);
 }
 
 }  // namespace
