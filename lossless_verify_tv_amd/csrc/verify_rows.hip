@@ -66,11 +66,24 @@ struct RowOut {
   float Rt, Lt;   // target row: R and L (greedy: max value, unused)
   float Rd, Ld;   // draft row
   float alpha;    // sum min(p, q) (greedy: unused)
-  int32_t arg_t;  // greedy argmax of the target row
-  int32_t arg_d;  // greedy argmax of the draft row
   int32_t nan;    // greedy: bit 0 target row, bit 1 draft row held a NaN
+  // greedy: the argmaxes of the target and the draft row; sampling draft
+  // rows: the bits of the accept ratio p(y_k) / q(y_k) in fp64 (low word in
+  // arg_t), see set_ratio
+  int32_t arg_t;
+  int32_t arg_d;
 };
 static_assert(sizeof(RowOut) == 32, "row record is 32 bytes");
+
+__device__ __forceinline__ void set_ratio(RowOut& o, double r) {
+  const uint64_t u = uint64_t(__double_as_longlong(r));
+  o.arg_t = int32_t(uint32_t(u));
+  o.arg_d = int32_t(uint32_t(u >> 32));
+}
+
+__device__ __forceinline__ double get_ratio(const RowOut& o) {
+  return __longlong_as_double((long long)((uint64_t(uint32_t(o.arg_d)) << 32) | uint32_t(o.arg_t)));
+}
 
 // Tokens a row keeps after top-k / top-p truncation: with d the order key of
 // a token's scaled logit s (larger s, smaller d), token v is kept iff
@@ -239,6 +252,8 @@ struct Shared {
   float f[kWaves][4];
   int i[kWaves][4];
   double d[kWaves];
+  float yx[2];  // sampling draft rows: the target and draft logits at y_k
+  int y;        // y_k, or -1 when it is out of range
 };
 
 // Block-wide combination of per-thread online statistics of two rows. A
@@ -291,6 +306,21 @@ __device__ __forceinline__ float block_sum1(float v, Shared& sh) {
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) r += sh.f[w][0];
   return r;
+}
+
+// fp64 probability of token v, logit x, under a row's (R, L), base-2
+// convention; 0 for a token the row's truncation drops.
+__device__ __forceinline__ double prob64_of(float x, int v, float inv_t, bool unit, float R,
+                                           float L, const KeepRow& kr) {
+  const float s = scale_logit(x, inv_t, unit);
+  if (!keeps(kr, s, v)) return 0.0;
+  return exp2((double)s * (double)kL2E - (double)R) / (double)L;
+}
+
+// The accept ratio p(y)/q(y) of a draft row, in fp64; q(y) = 0 encodes as
+// +inf when p(y) > 0 (accept) and 0 otherwise (reject).
+__device__ __forceinline__ double accept_ratio(double p, double q) {
+  return (q == 0.0) ? (p > 0.0 ? INFINITY : 0.0) : p / q;
 }
 
 // ------------------------------------------------------------------ sampling rows
@@ -410,6 +440,29 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
   const bool cut_t = kTrunc && kp.t.key != keep_all().key;
   const bool cut_d = kTrunc && kPair && kp.d.key != keep_all().key;
   const float sk_t = key_value(kp.t.key), sk_d = key_value(kp.d.key);
+  // the draft token's logits, for the accept ratio the row's statistics
+  // give at the end (an out-of-range token faults the request later)
+  if constexpr (kPair) {
+    if (threadIdx.x == 0) {
+      const int y = a.tokens[draft_row(a, b, k)];
+      const bool ok = y >= 0 && y < V;
+      sh.y = ok ? y : -1;
+      sh.yx[0] = ok ? load1<kDtype>(trow, y) : 0.f;
+      sh.yx[1] = ok ? load1<kDtype>(drow, y) : 0.f;
+    }
+  }
+  // the row record: statistics, alpha and (draft rows) the accept ratio
+  auto write_row = [&](float Rt_, float Lt_, float Rd_, float Ld_, float alpha_) {
+    if (threadIdx.x == 0) {
+      RowOut o{Rt_, Lt_, Rd_, Ld_, alpha_, 0, -1, -1};
+      if constexpr (kPair) {
+        if (sh.y >= 0)
+          set_ratio(o, accept_ratio(prob64_of(sh.yx[0], sh.y, inv_t, unit, Rt_, Lt_, kp.t),
+                                    prob64_of(sh.yx[1], sh.y, inv_t, unit, Rd_, Ld_, kp.d)));
+      }
+      a.rows[target_row(a, b, k)] = o;
+    }
+  };
   // drops the truncated tokens of a loaded group of tile t
   auto mk = [&](Grp<kDtype>& gt, Grp<kDtype>& gd, int tt) {
     if constexpr (kTrunc) {
@@ -458,8 +511,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
         overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, nfull);
       }
       const float alpha = kPair ? block_sum1(sa, sh) : 0.f;
-      if (threadIdx.x == 0)
-        a.rows[target_row(a, b, k)] = RowOut{Rt, Lt, Rd, Ld, alpha, -1, -1, 0};
+      write_row(Rt, Lt, Rd, Ld, alpha);
       return;
     }
   }
@@ -559,18 +611,7 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
     overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, t - 1);
   }
   const float alpha = kPair ? block_sum1(sa, sh) : 0.f;
-  if (threadIdx.x == 0) {
-    RowOut o;
-    o.Rt = Rt;
-    o.Lt = lt;
-    o.Rd = kPair ? Rd : 0.f;
-    o.Ld = kPair ? ld : 1.f;
-    o.alpha = alpha;
-    o.arg_t = -1;
-    o.arg_d = -1;
-    o.nan = 0;
-    a.rows[target_row(a, b, k)] = o;
-  }
+  write_row(Rt, lt, kPair ? Rd : 0.f, kPair ? ld : 1.f, alpha);
 }
 
 // ------------------------------------------------------------------ greedy rows
@@ -1316,9 +1357,7 @@ __device__ __forceinline__ int block_min(int v, Shared& sh) {
 template <int kDtype>
 __device__ __forceinline__ double prob64(const void* row, int v, float inv_t, bool unit, float R,
                                          float L, const KeepRow& kr) {
-  const float s = scale_logit(load1<kDtype>(row, v), inv_t, unit);
-  if (!keeps(kr, s, v)) return 0.0;
-  return exp2((double)s * (double)kL2E - (double)R) / (double)L;
+  return prob64_of(load1<kDtype>(row, v), v, inv_t, unit, R, L, kr);
 }
 
 // Inverse-CDF choice of a chunk from the masses m[0..NC) at u * total: the
@@ -1359,6 +1398,29 @@ __device__ __forceinline__ int pick_chunk(const float* m, int NC, double u, Shar
   }
   rem = INFINITY;
   return last >= 0 ? last : 0;
+}
+
+// pick_chunk for NC <= kThreads chunks in one block scan: thread c holds
+// chunk c's mass. Returns -1 (every thread) when no chunk has positive mass.
+__device__ __forceinline__ int pick_chunk_small(const float* m, int NC, double u, Shared& sh,
+                                                double& rem) {
+  const int c = threadIdx.x;
+  const double mc = c < NC ? (double)m[c] : 0.0;
+  double total;
+  const double exc = block_exscan(mc, sh, total);
+  const double target = u * total;
+  const int hit = block_min((mc > 0.0 && exc + mc > target) ? c : INT_MAX, sh);
+  if (hit != INT_MAX) {
+    if (c == hit) sh.d[0] = target - exc;
+    __syncthreads();
+    rem = sh.d[0];
+    __syncthreads();
+    return hit;
+  }
+  // rounding left no chunk past the target: the last chunk of positive mass
+  const int last = -block_min((c < NC && mc > 0.0) ? -c : INT_MAX, sh);
+  rem = INFINITY;
+  return last == -INT_MAX ? -1 : last;
 }
 
 // Token of chunk c at remaining mass `rem`: fp64 weights of the chunk's 512
@@ -1432,6 +1494,7 @@ struct FinShared {
   double ratio[LVTV_MAX_K];
   double uacc[LVTV_MAX_K];
   int j;
+  RowOut rc[LVTV_MAX_K + 1];  // the request's row records, read once
 };
 
 template <int kDtype>
@@ -1467,6 +1530,7 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
       if (k < kb) bad |= (y[k] < 0 || y[k] >= a.V);
       if (!t_ok) continue;
       const RowOut r = rows[k];
+      fs.rc[k] = r;
       if (greedy) {
         fault |= (r.nan & 1) || !isfinite(r.Rt);
         if (k < kb) fault |= (r.nan & 2) || !isfinite(r.Rd);
@@ -1506,24 +1570,18 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
 
   const bool unit = (T == 1.f);
   const float inv_t = __fdiv_rn(1.f, T);
-  // accept inputs for every position in parallel: u_k and p(y_k)/q(y_k)
+  // accept inputs for every position in parallel: u_k, and p(y_k)/q(y_k)
+  // as the row kernel evaluated it (prob64_of with the row's statistics)
   if (threadIdx.x < kb) {
     const int k = threadIdx.x;
     double u, u2;
     verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
     fs.uacc[k] = u;
-    const RowOut r = rows[k];
-    const KeepPair kp = a.keep ? a.keep[target_row(a, b, k)] : KeepPair{keep_all(), keep_all()};
-    const double p =
-        prob64<kDtype>(row_ptr<kDtype>(a, b, true, k), y[k], inv_t, unit, r.Rt, r.Lt, kp.t);
-    const double q =
-        prob64<kDtype>(row_ptr<kDtype>(a, b, false, k), y[k], inv_t, unit, r.Rd, r.Ld, kp.d);
-    // q == 0: accept iff p > 0, encoded as an infinite or zero ratio
-    fs.ratio[k] = (q == 0.0) ? (p > 0.0 ? INFINITY : 0.0) : p / q;
+    fs.ratio[k] = get_ratio(fs.rc[k]);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int k = 0; k < o.nalpha; ++k) out_alpha[k] = k < kb ? rows[k].alpha : 0.f;
+    for (int k = 0; k < o.nalpha; ++k) out_alpha[k] = k < kb ? fs.rc[k].alpha : 0.f;
     int j = kb;
     for (int k = 0; k < kb; ++k)
       if (!(fs.uacc[k] < fs.ratio[k])) {
@@ -1539,21 +1597,35 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   double u_acc, u_draw;
   verify_uniforms(a.seed[b], uint64_t(b), uint64_t(j), u_acc, u_draw);
   const bool residual = j < kb;
-  const RowOut r = rows[j];
+  const RowOut r = fs.rc[j];
   const void* trow = row_ptr<kDtype>(a, b, true, j);
   const void* drow = residual ? row_ptr<kDtype>(a, b, false, j) : nullptr;
   float* m = a.chunk + size_t(target_row(a, b, j)) * a.NC;
   const int NC = a.NC;
   const KeepPair kp = a.keep ? a.keep[target_row(a, b, j)] : KeepPair{keep_all(), keep_all()};
-  int any = 0;
-  for (int c = threadIdx.x; c < NC; c += kThreads) any |= m[c] > 0.f;
-  if (residual && !__syncthreads_or(any)) {
-    // residual zero everywhere: draw from p_j
-    p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, kp.t, m);
-    drow = nullptr;
-  }
   double rem;
-  const int c = pick_chunk(m, NC, u_draw, sh, rem);
+  int c;
+  if (NC <= kThreads) {
+    // one block scan of the chunk masses gives the total and every chunk's
+    // running mass
+    c = pick_chunk_small(m, NC, u_draw, sh, rem);
+    if (c < 0 && residual) {
+      // residual zero everywhere: draw from p_j
+      p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, kp.t, m);
+      drow = nullptr;
+      c = pick_chunk_small(m, NC, u_draw, sh, rem);
+    }
+    if (c < 0) c = 0;
+  } else {
+    int any = 0;
+    for (int cc = threadIdx.x; cc < NC; cc += kThreads) any |= m[cc] > 0.f;
+    if (residual && !__syncthreads_or(any)) {
+      // residual zero everywhere: draw from p_j
+      p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, kp.t, m);
+      drow = nullptr;
+    }
+    c = pick_chunk(m, NC, u_draw, sh, rem);
+  }
   const double cmass = (double)m[c];
   int v = search_chunk<kDtype>(trow, drow, a.V, c, rem, cmass, inv_t, unit, r.Rt, r.Lt, r.Rd,
                                r.Ld, kp, sh);
