@@ -203,45 +203,28 @@ struct Shared {
   int imin[kWaves];
 };
 
-// Workgroup barrier for data exchanged through LDS only: waits for this
-// wave's LDS accesses but not for its outstanding global loads (a full
-// __syncthreads would drain loads issued ahead of time).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <bool kLds>
-__device__ __forceinline__ void block_barrier() {
-  if constexpr (kLds)
-    lds_barrier();
-  else
-    __syncthreads();
-}
-
-template <bool kLds = false>
 __device__ __forceinline__ float block_max(float v, Shared& sh) {
   v = wmax(v);
-  block_barrier<kLds>();
+  __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) sh.f[threadIdx.x / kWave] = v;
-  block_barrier<kLds>();
+  __syncthreads();
   float r = sh.f[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) r = fmaxf(r, sh.f[w]);
   return r;
 }
 
-template <bool kLds = false>
 __device__ __forceinline__ void block_sum3(double& a, double& b, double& c, Shared& sh) {
   a = wsum(a);
   b = wsum(b);
   c = wsum(c);
-  block_barrier<kLds>();
+  __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) {
     sh.d[threadIdx.x / kWave][0] = a;
     sh.d[threadIdx.x / kWave][1] = b;
     sh.d[threadIdx.x / kWave][2] = c;
   }
-  block_barrier<kLds>();
+  __syncthreads();
   a = sh.d[0][0];
   b = sh.d[0][1];
   c = sh.d[0][2];
@@ -309,10 +292,9 @@ struct HalfStats {
   double l;  // sum of 2^((z - m) log2 e) over the half
 };
 
-template <bool kLds = false>
 __device__ __forceinline__ double block_sum1(double v, Shared& sh) {
   double u0 = 0.0, u1 = 0.0;
-  block_sum3<kLds>(v, u0, u1, sh);
+  block_sum3(v, u0, u1, sh);
   return v;
 }
 
@@ -462,19 +444,8 @@ __device__ __forceinline__ uint32_t mask_bits(const uint32_t (&mask)[kMaskWords]
 // maximum M_h and sum over threads of l 2^((m - M_h) c). The half workgroups
 // and the last launch call this with the same thread layout, so they agree
 // bit for bit.
-// The first batch of a half's target groups (loaded ahead of time by the
-// half workgroup, inside the function by the last launch).
-template <bool kVecOk>
-__device__ __forceinline__ void target_first_batch(const uint16_t* t, int V, int h,
-                                                   u32x4 (&x)[kPBatch]) {
-  const int tb = opaque(group_elem(h, 0));
-#pragma unroll
-  for (int i = 0; i < kPBatch; ++i) x[i] = load_z<kVecOk>(t, V, opaque(tb) + i * kTile);
-}
-
 template <bool kVecOk>
 __device__ __forceinline__ HalfStats target_half_stats(const uint16_t* t, int V, int h, float c,
-                                                       const u32x4 (&first)[kPBatch],
                                                        Shared& sh) {
   float m = -INFINITY;
   double l = 0.0;
@@ -483,12 +454,8 @@ __device__ __forceinline__ HalfStats target_half_stats(const uint16_t* t, int V,
   for (int g0 = 0; g0 < kZG; g0 += kPBatch) {
     u32x4 x[kPBatch];
 #pragma unroll
-    for (int i = 0; i < kPBatch; ++i) {
-      if (g0 == 0)
-        x[i] = first[i];
-      else if (g0 + i < kZG)
-        x[i] = load_z<kVecOk>(t, V, opaque(tb) + (g0 + i) * kTile);
-    }
+    for (int i = 0; i < kPBatch; ++i)
+      if (g0 + i < kZG) x[i] = load_z<kVecOk>(t, V, opaque(tb) + (g0 + i) * kTile);
     float bm = m;
 #pragma unroll
     for (int i = 0; i < kPBatch; ++i)
@@ -552,33 +519,21 @@ __device__ __forceinline__ void half_body(const Args& a) {
     for (int g = 0; g < kZL; ++g) zl[g][threadIdx.x] = tmp[g];
   }
 
-  // The first batch of p is loaded now, so that it arrives while the half
-  // statistics are computed (their reductions wait on LDS only).
-  const int tbp = opaque(group_elem(h, 0));
-  u32x4 pa0[kPBatch], pb0[kPBatch];
-  u32x4 tx0[kPBatch];
-  if constexpr (!kLogits) {
-#pragma unroll
-    for (int i = 0; i < kPBatch; ++i) load_p<kVecOk>(p, V, opaque(tbp) + i * kTile, pa0[i], pb0[i]);
-  } else {
-    target_first_batch<kVecOk>(t, V, h, tx0);
-  }
-
   // 2. half statistics, swapped with the other half
   float m = -INFINITY;
 #pragma unroll
   for (int g = 0; g < kZG; ++g) m = grp_max(zg.get(g), m);
   launder(zg);
-  m = block_max<true>(m, sh);
+  m = block_max(m, sh);
   const float nm0 = (m == -INFINITY) ? 0.f : -(m * c);
   double l = 0.0;
 #pragma unroll
   for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(zg.get(g), c, nm0);
   launder(zg);
-  l = block_sum1<true>(l, sh);
+  l = block_sum1(l, sh);
   if (threadIdx.x == 0) publish_stats(slot, 0, tag, HalfStats{m, l});
   if constexpr (kLogits) {
-    const HalfStats ht = target_half_stats<kVecOk>(t, V, h, c, tx0, sh);
+    const HalfStats ht = target_half_stats<kVecOk>(t, V, h, c, sh);
     launder(zg);
     if (threadIdx.x == 0) publish_stats(slot, kTStatWord, tag, ht);
   }
@@ -596,20 +551,17 @@ __device__ __forceinline__ void half_body(const Args& a) {
   uint32_t mask[kMaskWords];
 #pragma unroll
   for (int w = 0; w < kMaskWords; ++w) mask[w] = 0u;
+  const int tbp = opaque(group_elem(h, 0));
 #pragma unroll
   for (int g0 = 0; g0 < kZG; g0 += kPBatch) {
     u32x4 pa[kPBatch], pb[kPBatch];
 #pragma unroll
     for (int i = 0; i < kPBatch; ++i)
       if (g0 + i < kZG) {
-        if constexpr (kLogits) {
+        if constexpr (kLogits)
           pa[i] = load_z<kVecOk>(t, V, opaque(tbp) + (g0 + i) * kTile);
-        } else if (g0 == 0) {
-          pa[i] = pa0[i];
-          pb[i] = pb0[i];
-        } else {
+        else
           load_p<kVecOk>(p, V, opaque(tbp) + (g0 + i) * kTile, pa[i], pb[i]);
-        }
       }
 #pragma unroll
     for (int i = 0; i < kPBatch; ++i)
@@ -759,9 +711,7 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
           __syncthreads();
         }
         if (!(sh.have[s] & 4)) {
-          u32x4 first[kPBatch];
-          target_first_batch<kVecOk>(a.t + rk * V, V, hh, first);
-          const HalfStats hs = target_half_stats<kVecOk>(a.t + rk * V, V, hh, c, first, sh);
+          const HalfStats hs = target_half_stats<kVecOk>(a.t + rk * V, V, hh, c, sh);
           __syncthreads();
           if (threadIdx.x == 0) put_stats(bw, s, kTStatWord, hs);
           __syncthreads();
