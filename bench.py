@@ -317,6 +317,64 @@ def main():
     del tl
     result["loss_variants"] = variants
     log("loss variants: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in variants.items()))
+    # Verify variants, outside the step, each timed over as many calls as the
+    # step count: top-k / top-p truncation on the step's T = 1 inputs, and the
+    # ragged confidence-scheduled workload (B = 256, K_b in 1..8, V = 129280,
+    # half greedy) in the padded and the packed layouts.
+    vvar = {}
+
+    def time_calls(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    tk = torch.full((VERIFY_B,), 50, dtype=torch.int32, device=dev)
+    tp = torch.full((VERIFY_B,), 0.9, dtype=torch.float32, device=dev)
+    tws = lv.new_workspace(lv.spec_verify_topkp_workspace_bytes(VERIFY_B, VERIFY_K, VOCAB), dev)
+    ms = time_calls(lambda: lv.spec_verify_topkp(**vin[2], top_k=tk, top_p=tp, workspace=tws,
+                                                 out=vouts[2]))
+    vvar["spec_verify_topkp_T1.0_k50_p0.9"] = {
+        "ms": ms, "rows_per_s": VERIFY_B * (VERIFY_K + 1) / (ms * 1e-3),
+        "gbs": vb / (ms * 1e-3) / 1e9, "algorithmic_bytes": vb}
+    del tws
+    rc = synth.verify_case(5)
+    rvocab = rc.target.shape[2]
+    rb = verify_bytes(rc.k, rvocab)
+    rrows = int(sum(int(k) + 1 for k in rc.k))
+    rin = dict(target_logits=bf16_dev(rc.target), draft_logits=bf16_dev(rc.draft),
+               draft_tokens=torch.from_numpy(rc.tokens).to(dev),
+               k_per_req=torch.from_numpy(rc.k).to(dev),
+               temperature=torch.from_numpy(rc.temperature).to(dev),
+               seed=torch.from_numpy(rc.seed.view(np.int64)).to(dev))
+    ms = time_calls(lambda: lv.spec_verify(**rin))
+    vvar["spec_verify_ragged_padded"] = {
+        "ms": ms, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
+        "algorithmic_bytes": rb, "requests": int(rc.k.size), "rows": rrows, "vocab": rvocab}
+    kk = np.asarray(rc.k, dtype=np.int64)
+    off = np.zeros(kk.size + 1, dtype=np.int32)
+    off[1:] = np.cumsum(kk + 1)
+    pt = bf16_dev(np.concatenate([rc.target[b, :kk[b] + 1] for b in range(kk.size)]))
+    pdr = bf16_dev(np.concatenate([rc.draft[b, :kk[b]] for b in range(kk.size)]))
+    ptok = torch.from_numpy(np.concatenate([rc.tokens[b, :kk[b]]
+                                            for b in range(kk.size)]).astype(np.int32)).to(dev)
+    del rin
+    offd = torch.from_numpy(off).to(dev)
+    rtemp = torch.from_numpy(rc.temperature).to(dev)
+    rseed = torch.from_numpy(rc.seed.view(np.int64)).to(dev)
+    ms = time_calls(lambda: lv.spec_verify_packed(pt, pdr, ptok, offd, rtemp, rseed))
+    vvar["spec_verify_ragged_packed"] = {
+        "ms": ms, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
+        "algorithmic_bytes": rb, "requests": int(rc.k.size), "rows": rrows, "vocab": rvocab}
+    del pt, pdr, ptok, rc
+    result["verify_variants"] = vvar
+    log("verify variants: " + ", ".join(f"{k} {v['ms'] * 1e3:.1f} us" for k, v in vvar.items()))
     # Confidence-scheduled verify lengths for 256 requests x 16 positions
     # (one workgroup; latency-bound, reported as time per call).
     srng = np.random.default_rng([7, 1])
