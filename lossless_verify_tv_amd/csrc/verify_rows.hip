@@ -801,8 +801,13 @@ __device__ __forceinline__ uint64_t fixed_mass(float s, float M, float scale) {
 // First-level bin of a token: floor((M - s) 32), the last bin also taking
 // everything further down (and -inf). Non-decreasing in the order key.
 __device__ __forceinline__ uint32_t l1_bin(float s, float M) {
-  const float g = __fmul_rn(M - s, float(kRes));
-  return g < float(kNB1 - 1) ? uint32_t(g) : uint32_t(kNB1 - 1);
+  return uint32_t(fminf(__fmul_rn(M - s, float(kRes)), float(kNB1 - 1)));
+}
+
+// l1_bin(s, M) <= b for b below the last bin, as one comparison: `lim` =
+// b + 1.
+__device__ __forceinline__ bool l1_at_most(float s, float M, float lim) {
+  return __fmul_rn(M - s, float(kRes)) < lim;
 }
 
 // Order keys that bin b can hold, with slack for the rounding of M - s.
@@ -813,76 +818,67 @@ __device__ __forceinline__ void l1_key_range(uint32_t b, float M, uint32_t& lo, 
                        : desc_key(__double2float_rd((double)M - (double(b + 1) / kRes) * (1.0 + e)));
 }
 
-// One pass over a row: f(s, v) for every token v < V with its scaled logit,
-// four tiles of loads in flight.
+// One pass over a row: f(x, v) for every token v < V with its raw logit x,
+// four tiles of streaming loads in flight. The rows are read several times
+// here, but a re-read gains nothing from the caches on this part while
+// ordinary loads stream at about a third of the nontemporal rate, so every
+// pass streams. Tiles wholly inside the row take no bounds checks.
 template <int kDtype, bool kVecOk, class F>
-__device__ __forceinline__ void row_pass(const void* row, int V, float inv_t, bool unit, F&& f) {
+__device__ __forceinline__ void raw_pass(const void* row, int V, F&& f) {
   const int nt = (V + kTile - 1) / kTile;
+  const int nfull = V / kTile;
   int t = 0;
-  for (; t + kBatch <= nt; t += kBatch) {
+  for (; t + kBatch <= nfull; t += kBatch) {
     Grp<kDtype> g[kBatch];
 #pragma unroll
-    for (int n = 0; n < kBatch; ++n) load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t + n), g[n]);
+    for (int n = 0; n < kBatch; ++n) load_grp<kDtype, kVecOk, true>(row, V, tile_elem(t + n), g[n]);
 #pragma unroll
     for (int n = 0; n < kBatch; ++n)
 #pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        const int v = tile_elem(t + n) + j;
-        if (v < V) f(scale_logit(gelem(g[n], j), inv_t, unit), v);
-      }
+      for (int j = 0; j < kVec; ++j) f(gelem(g[n], j), tile_elem(t + n) + j);
   }
   for (; t < nt; ++t) {
     Grp<kDtype> g;
-    load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t), g);
+    load_grp<kDtype, kVecOk, true>(row, V, tile_elem(t), g);
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
       const int v = tile_elem(t) + j;
-      if (v < V) f(scale_logit(gelem(g, j), inv_t, unit), v);
+      if (v < V) f(gelem(g, j), v);
     }
   }
 }
 
+// The same with the scaled logit s = fl32(x inv_t) (x itself when inv_t = 1).
+template <int kDtype, bool kVecOk, class F>
+__device__ __forceinline__ void row_pass(const void* row, int V, float inv_t, F&& f) {
+  raw_pass<kDtype, kVecOk>(row, V, [&](float x, int v) { f(__fmul_rn(x, inv_t), v); });
+}
+
 // Gathers (order key, token id) of the tokens `want(s)` admits into the LDS
 // list (ts.ncand counts them all, also past kCand). Wave-aggregated: one LDS
-// atomic per wave and token slot.
+// atomic per wave and token slot, taken only where a token is admitted.
 template <int kDtype, bool kVecOk, class F>
-__device__ __forceinline__ void gather_pass(const void* row, int V, float inv_t, bool unit, F&& want,
+__device__ __forceinline__ void gather_pass(const void* row, int V, float inv_t, F&& want,
                                             TruncShared& ts) {
-  const int nt = (V + kTile - 1) / kTile;
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int t = 0; t < nt; t += kBatch) {
-    Grp<kDtype> g[kBatch];
-#pragma unroll
-    for (int n = 0; n < kBatch; ++n) {
-      if (t + n < nt)
-        load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t + n), g[n]);
-      else
-        fill_grp(g[n]);
-    }
-#pragma unroll
-    for (int n = 0; n < kBatch; ++n)
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        const int v = tile_elem(t + n) + j;
-        const float s = scale_logit(gelem(g[n], j), inv_t, unit);
-        const bool w = (t + n < nt) && v < V && want(s);
-        const uint64_t mask = __ballot(w);
-        if (mask) {
-          const int leader = __ffsll((unsigned long long)mask) - 1;
-          uint32_t base = 0;
-          if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
-          base = (uint32_t)__shfl((int)base, leader, kWave);
-          if (w) {
-            const uint32_t pos = base + (uint32_t)__popcll(mask & below);
-            if (pos < uint32_t(kCand)) {
-              ts.ckey[pos] = desc_key(s);
-              ts.cidx[pos] = v;
-            }
-          }
+  row_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s, int v) {
+    const bool w = want(s);
+    const uint64_t mask = __ballot(w);
+    if (mask) {
+      const int leader = __ffsll((unsigned long long)mask) - 1;
+      uint32_t base = 0;
+      if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
+      base = (uint32_t)__shfl((int)base, leader, kWave);
+      if (w) {
+        const uint32_t pos = base + (uint32_t)__popcll(mask & below);
+        if (pos < uint32_t(kCand)) {
+          ts.ckey[pos] = desc_key(s);
+          ts.cidx[pos] = v;
         }
       }
-  }
+    }
+  });
 }
 
 // Block-wide exclusive scans of two 64-bit integers; totals in ta, tb.
@@ -1053,8 +1049,8 @@ __device__ __forceinline__ Sel select_value(Src&& src, Adm&& adm, bool by_idx, b
 // Token id of the n-th token (in id order, n >= 1) whose key is `key`; every
 // thread gets it. One pass over the row.
 template <int kDtype, bool kVecOk>
-__device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t, bool unit,
-                                            uint32_t key, uint64_t n, TruncShared& ts) {
+__device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t, uint32_t key,
+                                            uint64_t n, TruncShared& ts) {
   if (threadIdx.x == 0) ts.r32 = INT_MAX;
   const int nt = (V + kTile - 1) / kTile;
   uint64_t run = 0;  // matches in the tiles before t
@@ -1064,7 +1060,7 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (t + i < nt)
-        load_grp<kDtype, kVecOk, false>(row, V, tile_elem(t + i), g[i]);
+        load_grp<kDtype, kVecOk, true>(row, V, tile_elem(t + i), g[i]);
       else
         fill_grp(g[i]);
     }
@@ -1074,7 +1070,7 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
 #pragma unroll
       for (int j = 0; j < kVec; ++j) {
         const int v = tile_elem(t + i) + j;
-        c += (t + i < nt && v < V && desc_key(scale_logit(gelem(g[i], j), inv_t, unit)) == key);
+        c += (t + i < nt && v < V && desc_key(__fmul_rn(gelem(g[i], j), inv_t)) == key);
       }
       mine |= c << (16 * i);
     }
@@ -1088,7 +1084,7 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
         uint64_t seen = before;
         for (int j = 0; j < kVec; ++j) {
           const int v = tile_elem(t + i) + j;
-          if (v < V && desc_key(scale_logit(gelem(g[i], j), inv_t, unit)) == key && ++seen == n) {
+          if (v < V && desc_key(__fmul_rn(gelem(g[i], j), inv_t)) == key && ++seen == n) {
             ts.r32 = v;
             break;
           }
@@ -1139,61 +1135,82 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     return;
   }
   const void* row = row_ptr<kDtype>(a, b, !draft, k);
+  // fl32(x * 1) = x, so the unit temperature needs no case of its own
   const float inv_t = __fdiv_rn(1.f, T);
-  const bool unit = (T == 1.f);
   const float scale = __builtin_ldexpf(1.f, 63 - (32 - __clz(V)));
   auto hbm = [&](auto&& f) {
-    row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int v) { f(s, v, desc_key(s)); });
+    row_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s, int v) { f(s, v, desc_key(s)); });
   };
 
-  // ---- pass 1: the maximum, faults
+  // ---- pass 1: the maximum, faults. fl32(x inv_t) is non-decreasing in x,
+  // so the maximum of s is the scaled maximum of x; s is NaN only where x
+  // is (inv_t = inf aside: then every s is +-inf or NaN and the row is
+  // left whole below either way), and +inf somewhere only if at the maximum.
   float mx = -INFINITY;
-  int bad = 0;
-  row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
-    bad |= (s != s) | (s == INFINITY);
-    mx = fmaxf(mx, s);
+  bool nan = false;
+  raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
+    nan |= (x != x);
+    mx = fmaxf(mx, x);
   });
-  bad = __syncthreads_or(bad);
-  const float M = block_max_f(mx, ts);
-  if (bad || M == -INFINITY) {  // the rows kernel faults the row: leave it whole
+  nan = __syncthreads_or(nan);
+  const float M = __fmul_rn(block_max_f(mx, ts), inv_t);
+  if (nan || !(M > -INFINITY && M < INFINITY)) {  // the rows kernel faults the row: leave it whole
     if (threadIdx.x == 0) *out = keep_all();
     return;
   }
+  // masses of the whole row into the first-level histogram
+  auto mass_pass = [&]() {
+    row_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s, int) {
+      const uint64_t m = fixed_mass(s, M, scale);
+      if (m) atomicAdd(&ts.mass1[l1_bin(s, M)], (unsigned long long)m);
+    });
+    __syncthreads();
+  };
 
-  // ---- pass 2: first-level histograms
+  // ---- pass 2: first-level histograms, token counts for top-k, masses for
+  // top-p alone (with top-k on, top-p only looks at the tokens top-k keeps,
+  // whose masses are taken from the gathered list below)
   for (int i = threadIdx.x; i < kNB1; i += kThreads) {
     ts.cnt1[i] = 0;
     ts.mass1[i] = 0;
   }
   __syncthreads();
-  row_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s, int) {
-    const uint32_t i = l1_bin(s, M);
-    if (k_on) atomicAdd(&ts.cnt1[i], 1u);
-    const uint64_t m = fixed_mass(s, M, scale);
-    if (m) atomicAdd(&ts.mass1[i], (unsigned long long)m);
-  });
-  __syncthreads();
+  if (k_on) {
+    row_pass<kDtype, kVecOk>(row, V, inv_t,
+                             [&](float s, int) { atomicAdd(&ts.cnt1[l1_bin(s, M)], 1u); });
+    __syncthreads();
+  } else {
+    mass_pass();
+  }
 
   int binK = -1, binP = -1;
   uint64_t rankK = 0, W0 = 0, needP = 0, beforeP = 0;
+  // all_in: top-k is on and every token of the bins down to top-k's own
+  // fits the LDS list; it is gathered whole and the masses of those bins
+  // come from it. Otherwise a mass pass fills the histogram for the row.
+  bool all_in = false;
   if (k_on) {
     uint64_t bc, bm;
     binK = select2(ts.cnt1, ts.mass1, kNB1, uint64_t(top_k), bc, bm, ts);
     rankK = uint64_t(top_k) - bc;
-    W0 = bm;  // mass of the bins above top-k's own
-    if (p_on) {
-      // top-p's bin is settled now if even the most top-k can keep of its
-      // own bin leaves the target above it, in one bin
-      const uint64_t n_hi = top_p_need(top_p, W0 + ts.mass1[binK]);
-      if (n_hi <= W0) {
-        uint64_t b0, b1, c0, c1;
-        const int lo_bin = select2(ts.mass1, ts.cnt1, kNB1, top_p_need(top_p, W0), b0, c0, ts);
-        const int hi_bin = select2(ts.mass1, ts.cnt1, kNB1, n_hi, b1, c1, ts);
-        if (lo_bin == hi_bin) binP = lo_bin;
+    all_in = bc + ts.cnt1[binK] <= uint64_t(kCand);
+    if (!all_in) {
+      mass_pass();
+      W0 = sum_before(ts.mass1, kNB1, binK, ts);  // mass of the bins above top-k's own
+      if (p_on) {
+        // top-p's bin is settled now if even the most top-k can keep of its
+        // own bin leaves the target above it, in one bin
+        const uint64_t n_hi = top_p_need(top_p, W0 + ts.mass1[binK]);
+        if (n_hi <= W0) {
+          uint64_t b0, b1, c0, c1;
+          const int lo_bin = select2(ts.mass1, ts.cnt1, kNB1, top_p_need(top_p, W0), b0, c0, ts);
+          const int hi_bin = select2(ts.mass1, ts.cnt1, kNB1, n_hi, b1, c1, ts);
+          if (lo_bin == hi_bin) binP = lo_bin;
+        }
       }
     }
   } else {
-    uint64_t W = 0, t0 = 0;
+    uint64_t W = 0;
     {
       uint64_t e0, e1, t1;
       uint64_t m = 0;
@@ -1203,16 +1220,22 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     needP = top_p_need(top_p, W);
     uint64_t bc;
     binP = select2(ts.mass1, ts.cnt1, kNB1, needP, beforeP, bc, ts);
-    (void)t0;
   }
 
   // ---- pass 3: gather the tokens of the open bins into LDS
   if (threadIdx.x == 0) ts.ncand = 0;
   __syncthreads();
-  gather_pass<kDtype, kVecOk>(row, V, inv_t, unit, [&](float s) {
-    const int i = int(l1_bin(s, M));
-    return i == binK || i == binP;
-  }, ts);
+  if (all_in) {
+    const bool every = binK >= kNB1 - 1;  // the last bin also takes g >= kNB1 and -inf
+    const float lim = float(binK + 1);
+    gather_pass<kDtype, kVecOk>(row, V, inv_t,
+                                [&](float s) { return every || l1_at_most(s, M, lim); }, ts);
+  } else {
+    gather_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s) {
+      const int i = int(l1_bin(s, M));
+      return i == binK || i == binP;
+    }, ts);
+  }
   __syncthreads();
   uint32_t nc = ts.ncand;
   bool in_lds = nc <= uint32_t(kCand);
@@ -1223,6 +1246,20 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
       f(key_value(d), ts.cidx[i], d);
     }
   };
+  if (all_in) {
+    if (in_lds) {
+      // the same masses, bins and exact sums as a pass over the row would
+      // give (key_value(desc_key(s)) = s, up to the sign of zero)
+      lds([&](float s, int, uint32_t) {
+        const uint64_t m = fixed_mass(s, M, scale);
+        if (m) atomicAdd(&ts.mass1[l1_bin(s, M)], (unsigned long long)m);
+      });
+      __syncthreads();
+    } else {
+      mass_pass();  // not reached: the list holds exactly the tokens counted
+    }
+    W0 = sum_before(ts.mass1, kNB1, binK, ts);
+  }
 
   // ---- top-k: the top_k-th token
   uint32_t keyK = 0xffffffffu;
@@ -1241,7 +1278,7 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
         auto tie = [&](float, int, uint32_t d) { return d == keyK; };
         idxK = int(select_value(lds, tie, true, false, false, nK, 0, uint32_t(V - 1), M, scale, ts).val);
       } else {
-        idxK = nth_with_key<kDtype, kVecOk>(row, V, inv_t, unit, keyK, nK, ts);
+        idxK = nth_with_key<kDtype, kVecOk>(row, V, inv_t, keyK, nK, ts);
       }
     }
     WK = W0 + sk.bmass + nK * (sk.acnt ? sk.amass / sk.acnt : 0);
@@ -1261,15 +1298,17 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
         if (binP < 0) {
           uint64_t bc;
           binP = select2(ts.mass1, ts.cnt1, kNB1, needP, beforeP, bc, ts);
-          // not gathered yet: gather it alone
-          if (threadIdx.x == 0) ts.ncand = 0;
-          __syncthreads();
-          gather_pass<kDtype, kVecOk>(row, V, inv_t, unit,
-                                      [&](float s) { return int(l1_bin(s, M)) == binP; }, ts);
-          __syncthreads();
-          nc = ts.ncand;
-          in_lds = nc <= uint32_t(kCand);
-          __syncthreads();
+          if (!all_in) {
+            // not gathered yet: gather it alone
+            if (threadIdx.x == 0) ts.ncand = 0;
+            __syncthreads();
+            gather_pass<kDtype, kVecOk>(row, V, inv_t,
+                                        [&](float s) { return int(l1_bin(s, M)) == binP; }, ts);
+            __syncthreads();
+            nc = ts.ncand;
+            in_lds = nc <= uint32_t(kCand);
+            __syncthreads();
+          }
         } else {
           beforeP = sum_before(ts.mass1, kNB1, binP, ts);
         }
@@ -1297,7 +1336,7 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
         idx = int(select_value(lds, tie, true, false, false, n, 0, uint32_t(V - 1), M, scale, ts).val);
       } else {
         // the admitted tokens of the key are its first ones in id order
-        idx = nth_with_key<kDtype, kVecOk>(row, V, inv_t, unit, key, n, ts);
+        idx = nth_with_key<kDtype, kVecOk>(row, V, inv_t, key, n, ts);
       }
     } else {
       idx = (key == keyK) ? idxK : INT_MAX;
