@@ -792,10 +792,16 @@ __device__ __forceinline__ uint64_t fixed_mass(float s, float M, float scale) {
   const float sv = d + M;
   const float dlo = (s - sv) + (-M - (d - sv));
   const float th = __fmul_rn(d, kL2E);
-  if (!(th > -64.f)) return 0;
   const float tl = __builtin_fmaf(d, kL2E, -th) + __builtin_fmaf(d, kL2ELo, dlo * kL2E);
   const float w = __builtin_amdgcn_exp2f(th) * __builtin_fmaf(tl, 0.693147182f, 1.f);
-  return (uint64_t)(w * scale);
+  // th <= -64 leaves w scale below 1 (scale <= 2^62) and s = -inf makes it
+  // NaN: 0 either way, chosen without a branch
+  const float x = th > -64.f ? __fmul_rn(w, scale) : 0.f;
+  // x in [0, 2^63) to an integer: the high word floor(x / 2^32), the low
+  // word x - hi 2^32 (exact), each truncated by one conversion
+  const float hi = floorf(x * 0x1p-32f);
+  const uint32_t lo = (uint32_t)__builtin_fmaf(hi, -0x1p32f, x);
+  return (uint64_t(uint32_t(hi)) << 32) | lo;
 }
 
 // First-level bin of a token: floor((M - s) 32), the last bin also taking
@@ -1161,8 +1167,7 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   // masses of the whole row into the first-level histogram
   auto mass_pass = [&]() {
     row_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s, int) {
-      const uint64_t m = fixed_mass(s, M, scale);
-      if (m) atomicAdd(&ts.mass1[l1_bin(s, M)], (unsigned long long)m);
+      atomicAdd(&ts.mass1[l1_bin(s, M)], (unsigned long long)fixed_mass(s, M, scale));
     });
     __syncthreads();
   };
