@@ -740,21 +740,30 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 //
 // trunc_rows finds, for each used row of a sampling request, the prefix of
 // the row's tokens (scaled logit s descending, then token id) that top-k and
-// then top-p keep, and stores its last token as a KeepRow. Three passes over
-// the row in the common case:
-//   1. the row maximum M (and faults: such rows are left whole);
-//   2. first-level LDS histograms over the distance below the maximum in
-//      1/32-nat bins, floor((M - s) 32) (the last bin takes everything
-//      further down): token counts for top-k, fixed-point masses for top-p.
-//      Bins follow the order of s and spread the LDS atomics of clustered
-//      logits over many addresses. A block scan picks the bin where the
-//      running count reaches top_k, and the bin where the running mass
-//      reaches top_p times the mass top-k keeps, when the part of top-k's
-//      own bin it keeps does not leave that open;
-//   3. the tokens of the chosen bins are gathered into LDS (order key and
-//      token id) and the boundary is resolved there: radix selection on the
-//      32-bit order key, 10 bits a level, then on the token id among equal
-//      keys.
+// then top-p keep, and stores its last token as a KeepRow. Every pass
+// streams the row (a re-read gains nothing from the caches here). Bins are
+// first-level LDS histograms over the distance below a reference value in
+// 1/32-nat bins, floor((ref - s) 32) (the last bin takes everything further
+// down); they follow the order of s and spread the LDS atomics of clustered
+// logits over many addresses.
+//
+// With top-k on, two passes in the common case:
+//   1. the row maximum M (and faults: such rows are left whole) and token
+//      counts per bin below R0, the largest s of the row's first tile
+//      (tokens above R0 share bin 0); a block scan finds the bin where the
+//      running count reaches top_k;
+//   2. if every token down to that bin fits the LDS list (4096 tokens), they
+//      are gathered (order key and token id): top-k's boundary and then
+//      top-p's, over the tokens top-k keeps, are resolved on the list by
+//      radix selection on the 32-bit order key, 10 bits a level, then on the
+//      token id among equal keys, with fixed-point masses below M.
+// Otherwise, and for top-p alone, the bins are redone below M:
+//   2'. token counts for top-k, or fixed-point masses for top-p alone; a
+//      block scan picks the bin where the running count reaches top_k, or
+//      the running mass top_p times the total;
+//   3'. the tokens of the open bins are gathered and resolved as above (with
+//      top-k on, all bins down to top-k's own when they fit, their masses
+//      taken from the list; else top-k's bin and top-p's, after a mass pass).
 // A bin with more tokens than LDS holds is refined by further passes over
 // the row instead (a level a pass, then one pass to split equal keys).
 //
@@ -763,7 +772,7 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 // s - M is and summed exactly in 64 bits: the sums are deterministic, and
 // within about 2.4e-7 of the exact ones relative to the kept total.
 
-constexpr int kRes = 32;       // first-level bins per nat below the row maximum
+constexpr int kRes = 32;       // first-level bins per nat below the reference
 constexpr int kNB1 = 2048;     // first-level bins
 constexpr int kNB = 1024;      // buckets of a refinement level
 constexpr int kCand = 4096;    // tokens gathered into LDS
@@ -810,8 +819,15 @@ __device__ __forceinline__ uint32_t l1_bin(float s, float M) {
   return uint32_t(fminf(__fmul_rn(M - s, float(kRes)), float(kNB1 - 1)));
 }
 
+// The first-level bin below a reference R0 that need not be the row
+// maximum: tokens above R0 fall into bin 0 with those just below it, so the
+// bins still follow the order of s.
+__device__ __forceinline__ uint32_t l1_bin_ref(float s, float R0) {
+  return uint32_t(fminf(fmaxf(__fmul_rn(R0 - s, float(kRes)), 0.f), float(kNB1 - 1)));
+}
+
 // l1_bin(s, M) <= b for b below the last bin, as one comparison: `lim` =
-// b + 1.
+// b + 1 (also l1_bin_ref(s, M) <= b).
 __device__ __forceinline__ bool l1_at_most(float s, float M, float lim) {
   return __fmul_rn(M - s, float(kRes)) < lim;
 }
@@ -830,10 +846,10 @@ __device__ __forceinline__ void l1_key_range(uint32_t b, float M, uint32_t& lo, 
 // ordinary loads stream at about a third of the nontemporal rate, so every
 // pass streams. Tiles wholly inside the row take no bounds checks.
 template <int kDtype, bool kVecOk, class F>
-__device__ __forceinline__ void raw_pass(const void* row, int V, F&& f) {
+__device__ __forceinline__ void raw_pass(const void* row, int V, F&& f, int t0 = 0) {
   const int nt = (V + kTile - 1) / kTile;
   const int nfull = V / kTile;
-  int t = 0;
+  int t = t0;
   for (; t + kBatch <= nfull; t += kBatch) {
     Grp<kDtype> g[kBatch];
 #pragma unroll
@@ -1152,17 +1168,61 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   // so the maximum of s is the scaled maximum of x; s is NaN only where x
   // is (inv_t = inf aside: then every s is +-inf or NaN and the row is
   // left whole below either way), and +inf somewhere only if at the maximum.
+  // With top-k on, the same pass counts tokens per first-level bin below R0,
+  // the largest scaled logit of the row's first tile (bins relative to it
+  // keep the order of s and spread clustered logits as the bins below the
+  // maximum do).
   float mx = -INFINITY;
   bool nan = false;
-  raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
-    nan |= (x != x);
-    mx = fmaxf(mx, x);
-  });
+  float R0 = 0.f;
+  if (k_on) {
+    Grp<kDtype> g0;
+    load_grp<kDtype, kVecOk, true>(row, V, tile_elem(0), g0);
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      const float x = gelem(g0, j);
+      if (tile_elem(0) + j < V) {
+        nan |= (x != x);
+        mx = fmaxf(mx, x);
+      }
+    }
+    for (int i = threadIdx.x; i < kNB1; i += kThreads) ts.cnt1[i] = 0;
+    R0 = __fmul_rn(block_max_f(mx, ts), inv_t);  // (its barriers also cover the zeroing)
+    if (!(R0 > -INFINITY && R0 < INFINITY)) R0 = 0.f;  // any finite reference keeps the order
+    auto count = [&](float x) { atomicAdd(&ts.cnt1[l1_bin_ref(__fmul_rn(x, inv_t), R0)], 1u); };
+#pragma unroll
+    for (int j = 0; j < kVec; ++j)
+      if (tile_elem(0) + j < V) count(gelem(g0, j));
+    raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
+      nan |= (x != x);
+      mx = fmaxf(mx, x);
+      count(x);
+    }, 1);
+  } else {
+    raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
+      nan |= (x != x);
+      mx = fmaxf(mx, x);
+    });
+  }
   nan = __syncthreads_or(nan);
   const float M = __fmul_rn(block_max_f(mx, ts), inv_t);
   if (nan || !(M > -INFINITY && M < INFINITY)) {  // the rows kernel faults the row: leave it whole
     if (threadIdx.x == 0) *out = keep_all();
     return;
+  }
+
+  // list: top-k is on and every token down to the bin (below R0) where the
+  // count reaches top_k fits the LDS list. One more pass gathers them (every
+  // token that top-k keeps is among them) and the rest works on the list.
+  bool list = false;
+  float limR = 0.f;
+  bool everyR = false;
+  if (k_on) {
+    uint64_t bc, bg;
+    const int binR = select2(ts.cnt1, ts.cnt1, kNB1, uint64_t(top_k), bc, bg, ts);
+    list = bc + ts.cnt1[binR] <= uint64_t(kCand);
+    everyR = binR >= kNB1 - 1;
+    limR = float(binR + 1);
   }
   // masses of the whole row into the first-level histogram
   auto mass_pass = [&]() {
@@ -1172,76 +1232,85 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     __syncthreads();
   };
 
-  // ---- pass 2: first-level histograms, token counts for top-k, masses for
-  // top-p alone (with top-k on, top-p only looks at the tokens top-k keeps,
-  // whose masses are taken from the gathered list below)
-  for (int i = threadIdx.x; i < kNB1; i += kThreads) {
-    ts.cnt1[i] = 0;
-    ts.mass1[i] = 0;
-  }
-  __syncthreads();
-  if (k_on) {
-    row_pass<kDtype, kVecOk>(row, V, inv_t,
-                             [&](float s, int) { atomicAdd(&ts.cnt1[l1_bin(s, M)], 1u); });
-    __syncthreads();
-  } else {
-    mass_pass();
-  }
-
   int binK = -1, binP = -1;
   uint64_t rankK = 0, W0 = 0, needP = 0, beforeP = 0;
   // all_in: top-k is on and every token of the bins down to top-k's own
   // fits the LDS list; it is gathered whole and the masses of those bins
   // come from it. Otherwise a mass pass fills the histogram for the row.
   bool all_in = false;
-  if (k_on) {
-    uint64_t bc, bm;
-    binK = select2(ts.cnt1, ts.mass1, kNB1, uint64_t(top_k), bc, bm, ts);
-    rankK = uint64_t(top_k) - bc;
-    all_in = bc + ts.cnt1[binK] <= uint64_t(kCand);
-    if (!all_in) {
+  if (list) {
+    if (threadIdx.x == 0) ts.ncand = 0;
+    __syncthreads();
+    gather_pass<kDtype, kVecOk>(row, V, inv_t,
+                                [&](float s) { return everyR || l1_at_most(s, R0, limR); }, ts);
+    __syncthreads();
+    rankK = uint64_t(top_k);
+  } else {
+    // ---- pass 2: first-level histograms, token counts for top-k, masses for
+    // top-p alone (with top-k on, top-p only looks at the tokens top-k keeps,
+    // whose masses are taken from the gathered list below)
+    for (int i = threadIdx.x; i < kNB1; i += kThreads) {
+      ts.cnt1[i] = 0;
+      ts.mass1[i] = 0;
+    }
+    __syncthreads();
+    if (k_on) {
+      row_pass<kDtype, kVecOk>(row, V, inv_t,
+                               [&](float s, int) { atomicAdd(&ts.cnt1[l1_bin(s, M)], 1u); });
+      __syncthreads();
+    } else {
       mass_pass();
-      W0 = sum_before(ts.mass1, kNB1, binK, ts);  // mass of the bins above top-k's own
-      if (p_on) {
-        // top-p's bin is settled now if even the most top-k can keep of its
-        // own bin leaves the target above it, in one bin
-        const uint64_t n_hi = top_p_need(top_p, W0 + ts.mass1[binK]);
-        if (n_hi <= W0) {
-          uint64_t b0, b1, c0, c1;
-          const int lo_bin = select2(ts.mass1, ts.cnt1, kNB1, top_p_need(top_p, W0), b0, c0, ts);
-          const int hi_bin = select2(ts.mass1, ts.cnt1, kNB1, n_hi, b1, c1, ts);
-          if (lo_bin == hi_bin) binP = lo_bin;
+    }
+
+    if (k_on) {
+      uint64_t bc, bm;
+      binK = select2(ts.cnt1, ts.mass1, kNB1, uint64_t(top_k), bc, bm, ts);
+      rankK = uint64_t(top_k) - bc;
+      all_in = bc + ts.cnt1[binK] <= uint64_t(kCand);
+      if (!all_in) {
+        mass_pass();
+        W0 = sum_before(ts.mass1, kNB1, binK, ts);  // mass of the bins above top-k's own
+        if (p_on) {
+          // top-p's bin is settled now if even the most top-k can keep of its
+          // own bin leaves the target above it, in one bin
+          const uint64_t n_hi = top_p_need(top_p, W0 + ts.mass1[binK]);
+          if (n_hi <= W0) {
+            uint64_t b0, b1, c0, c1;
+            const int lo_bin = select2(ts.mass1, ts.cnt1, kNB1, top_p_need(top_p, W0), b0, c0, ts);
+            const int hi_bin = select2(ts.mass1, ts.cnt1, kNB1, n_hi, b1, c1, ts);
+            if (lo_bin == hi_bin) binP = lo_bin;
+          }
         }
       }
+    } else {
+      uint64_t W = 0;
+      {
+        uint64_t e0, e1, t1;
+        uint64_t m = 0;
+        for (int i = 0; i < kNB1 / kThreads; ++i) m += ts.mass1[threadIdx.x * (kNB1 / kThreads) + i];
+        block_exscan2_u64(m, 0, e0, e1, W, t1, ts);
+      }
+      needP = top_p_need(top_p, W);
+      uint64_t bc;
+      binP = select2(ts.mass1, ts.cnt1, kNB1, needP, beforeP, bc, ts);
     }
-  } else {
-    uint64_t W = 0;
-    {
-      uint64_t e0, e1, t1;
-      uint64_t m = 0;
-      for (int i = 0; i < kNB1 / kThreads; ++i) m += ts.mass1[threadIdx.x * (kNB1 / kThreads) + i];
-      block_exscan2_u64(m, 0, e0, e1, W, t1, ts);
-    }
-    needP = top_p_need(top_p, W);
-    uint64_t bc;
-    binP = select2(ts.mass1, ts.cnt1, kNB1, needP, beforeP, bc, ts);
-  }
 
-  // ---- pass 3: gather the tokens of the open bins into LDS
-  if (threadIdx.x == 0) ts.ncand = 0;
-  __syncthreads();
-  if (all_in) {
-    const bool every = binK >= kNB1 - 1;  // the last bin also takes g >= kNB1 and -inf
-    const float lim = float(binK + 1);
-    gather_pass<kDtype, kVecOk>(row, V, inv_t,
-                                [&](float s) { return every || l1_at_most(s, M, lim); }, ts);
-  } else {
-    gather_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s) {
-      const int i = int(l1_bin(s, M));
-      return i == binK || i == binP;
-    }, ts);
+    // ---- pass 3: gather the tokens of the open bins into LDS
+    if (threadIdx.x == 0) ts.ncand = 0;
+    __syncthreads();
+    if (all_in) {
+      const bool every = binK >= kNB1 - 1;  // the last bin also takes g >= kNB1 and -inf
+      const float lim = float(binK + 1);
+      gather_pass<kDtype, kVecOk>(row, V, inv_t,
+                                  [&](float s) { return every || l1_at_most(s, M, lim); }, ts);
+    } else {
+      gather_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s) {
+        const int i = int(l1_bin(s, M));
+        return i == binK || i == binP;
+      }, ts);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   uint32_t nc = ts.ncand;
   bool in_lds = nc <= uint32_t(kCand);
   __syncthreads();
@@ -1271,7 +1340,7 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   int idxK = INT_MAX;
   uint64_t WK = 0;  // mass of the tokens top-k keeps
   if (k_on) {
-    auto adm = [&](float s, int, uint32_t) { return int(l1_bin(s, M)) == binK; };
+    auto adm = [&](float s, int, uint32_t) { return list || int(l1_bin(s, M)) == binK; };
     uint32_t lo = 0, hi = 0xffffffffu;
     if (!in_lds) l1_key_range(uint32_t(binK), M, lo, hi);
     const Sel sk = in_lds ? select_value(lds, adm, false, false, true, rankK, lo, hi, M, scale, ts)
@@ -1296,7 +1365,9 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   if (p_on) {
     if (k_on) {
       needP = top_p_need(top_p, WK);
-      if (needP > W0) {
+      if (list) {
+        beforeP = 0;
+      } else if (needP > W0) {
         binP = binK;
         beforeP = W0;
       } else {
@@ -1321,7 +1392,7 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     }
     const uint64_t rem = needP - beforeP;
     auto adm = [&](float s, int v, uint32_t d) {
-      return int(l1_bin(s, M)) == binP && (d < keyK || (d == keyK && v <= idxK));
+      return (list || int(l1_bin(s, M)) == binP) && (d < keyK || (d == keyK && v <= idxK));
     };
     uint32_t lo = 0, hi = 0xffffffffu;
     if (!in_lds) l1_key_range(uint32_t(binP), M, lo, hi);
