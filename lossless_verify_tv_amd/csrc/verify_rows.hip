@@ -53,6 +53,8 @@ constexpr int kWaves = kThreads / kWave;      // 8
 constexpr int kTile = kThreads * kVec;        // 4096 tokens: 8 per thread
 constexpr int kChunk = kWave * kVec;          // 512 tokens: one wave's part of a tile
 constexpr int kBatch = 4;                     // tiles whose loads are in flight together
+constexpr int kCand = 4096;                   // tokens a truncation's LDS list holds
+constexpr int kListNC = 1024;                 // chunks a row may have for the list path
 constexpr float kL2E = 1.44269504088896340736f;
 
 // Tiles kept in registers between the passes (the last ones of the row).
@@ -146,6 +148,11 @@ struct Args {
   const int32_t* top_k;  // [B]
   const float* top_p;    // [B]
   KeepPair* keep;        // one per target row, written by trunc_rows
+  // Ids of the tokens a target row keeps, when the selection had them all
+  // in its LDS list (klen > 0, in no particular order; 0: the row kernel
+  // streams the row). Written by trunc_rows for every row it truncates.
+  int32_t* klen;   // [target rows]
+  int32_t* klist;  // [target rows][kCand]
 };
 
 __device__ __forceinline__ KeepRow keep_all() { return KeepRow{0xffffffffu, INT_MAX, 0.f, 0.f}; }
@@ -252,6 +259,7 @@ struct Shared {
   float f[kWaves][4];
   int i[kWaves][4];
   double d[kWaves];
+  unsigned long long u[kWaves];
   float yx[2];  // sampling draft rows: the target and draft logits at y_k
   int y;        // y_k, or -1 when it is out of range
 };
@@ -481,6 +489,51 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
       const float nrt = float(-((double)Rt + log2((double)Lt)));
       const float nrd = kPair ? float(-((double)Rd + log2((double)Ld))) : 0.f;
       float* chunk_row = a.chunk + size_t(target_row(a, b, k)) * a.NC;
+      const int nlist = a.klen[target_row(a, b, k)];
+      if (nlist > 0 && nlist <= kCand && a.NC <= kListNC) {
+        // The target row's kept tokens are listed: only they carry p > 0,
+        // so alpha and the residual chunk masses are sums over them, each
+        // token's p and q formed as the streaming pass forms them (a token
+        // the draft row drops has q = 0). The sums are exact in 2^-62
+        // fixed point, so the list's order does not show.
+        __shared__ unsigned long long cacc[kListNC];
+        for (int i = threadIdx.x; i < a.NC; i += kThreads) cacc[i] = 0;
+        __syncthreads();
+        const int32_t* lst = a.klist + size_t(target_row(a, b, k)) * kCand;
+        uint64_t al = 0;
+        for (int i = threadIdx.x; i < nlist; i += kThreads) {
+          const int v = lst[i];
+          if (v < 0 || v >= V) continue;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(load1<kDtype>(trow, v), c, nrt));
+          float r = p;
+          if constexpr (kPair) {
+            const float xd = load1<kDtype>(drow, v);
+            const float q = keeps(kp.d, scale_logit(xd, inv_t, unit), v)
+                                ? __builtin_amdgcn_exp2f(__builtin_fmaf(xd, c, nrd))
+                                : 0.f;
+            const float mn = fminf(p, q);
+            al += (uint64_t)(mn * 0x1p62f);
+            r = p - mn;
+          }
+          atomicAdd(&cacc[v / kChunk], (unsigned long long)(r * 0x1p62f));
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < a.NC; i += kThreads)
+          chunk_row[i] = (float)((double)cacc[i] * 0x1p-62);
+        float alpha = 0.f;
+        if constexpr (kPair) {
+#pragma unroll
+          for (int o = kWave / 2; o > 0; o >>= 1) al += __shfl_xor(al, o, kWave);
+          if ((threadIdx.x & (kWave - 1)) == 0) sh.u[threadIdx.x / kWave] = al;
+          __syncthreads();
+          uint64_t tot = 0;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) tot += sh.u[w];
+          alpha = (float)((double)tot * 0x1p-62);
+        }
+        write_row(Rt, Lt, Rd, Ld, alpha);
+        return;
+      }
       float sa = 0.f;
       int t = 0;
       for (; t + kBatch <= nfull; t += kBatch) {
@@ -775,7 +828,6 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 constexpr int kRes = 32;       // first-level bins per nat below the reference
 constexpr int kNB1 = 2048;     // first-level bins
 constexpr int kNB = 1024;      // buckets of a refinement level
-constexpr int kCand = 4096;    // tokens gathered into LDS
 constexpr float kL2ELo = 1.925963033e-8f;  // log2(e) - fl32(log2(e))
 
 struct TruncShared {
@@ -1418,6 +1470,42 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
       idx = (key == keyK) ? idxK : INT_MAX;
     }
   }
+  if (!draft) {
+    // the kept tokens' ids for the row kernel, when every one of them is in
+    // the LDS list (top-k on: they are among the tokens gathered)
+    int32_t* klen = &a.klen[target_row(a, b, k)];
+    if (k_on && in_lds && (list || all_in)) {
+      int32_t* dst = a.klist + size_t(target_row(a, b, k)) * kCand;
+      __syncthreads();
+      if (threadIdx.x == 0) ts.ncand = 0;
+      __syncthreads();
+      const int lane = threadIdx.x & (kWave - 1);
+      const uint64_t below = (uint64_t(1) << lane) - 1;
+      for (uint32_t i0 = 0; i0 < nc; i0 += kThreads) {
+        const uint32_t i = i0 + threadIdx.x;
+        bool w = false;
+        int v = 0;
+        if (i < nc) {
+          const uint32_t d = ts.ckey[i];
+          v = ts.cidx[i];
+          w = d < key || (d == key && v <= idx);
+        }
+        const uint64_t mask = __ballot(w);
+        if (mask) {
+          const int leader = __ffsll((unsigned long long)mask) - 1;
+          uint32_t base = 0;
+          if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
+          base = (uint32_t)__shfl((int)base, leader, kWave);
+          const uint32_t pos = base + (uint32_t)__popcll(mask & below);
+          if (w && pos < uint32_t(kCand)) dst[pos] = v;
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x == 0) *klen = int32_t(min(ts.ncand, uint32_t(kCand)));
+    } else if (threadIdx.x == 0) {
+      *klen = 0;
+    }
+  }
   if (threadIdx.x == 0) {
     // kept mass in the row kernel's convention: sum 2^(s log2e - R) =
     // 2^(M log2e - R) sum e^(s - M), log2e as the kernels round it
@@ -1772,7 +1860,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
   int n_tiles, NC;
-  size_t off_rows, off_chunk, off_map, off_keep, total;
+  size_t off_rows, off_chunk, off_map, off_keep, off_klen, off_klist, total;
 };
 
 // `rows` target rows (B (Kmax + 1) padded, total_rows packed); the row map
@@ -1791,6 +1879,10 @@ Layout make_layout(size_t rows, int V, bool packed, bool trunc = false) {
   if (packed) off = align256(off + sizeof(int32_t) * (rows + 1));
   L.off_keep = off;
   if (trunc) off = align256(off + sizeof(KeepPair) * rows);
+  L.off_klen = off;
+  if (trunc) off = align256(off + sizeof(int32_t) * rows);
+  L.off_klist = off;
+  if (trunc) off = align256(off + sizeof(int32_t) * rows * kCand);
   L.total = off;
   return L;
 }
@@ -1903,6 +1995,8 @@ int verify_padded(const void* target_logits, const void* draft_logits, int dtype
   a.top_k = top_k;
   a.top_p = top_p;
   a.keep = trunc ? reinterpret_cast<KeepPair*>(ws + L.off_keep) : nullptr;
+  a.klen = trunc ? reinterpret_cast<int32_t*>(ws + L.off_klen) : nullptr;
+  a.klist = trunc ? reinterpret_cast<int32_t*>(ws + L.off_klist) : nullptr;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
                         reinterpret_cast<uintptr_t>(draft_logits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
@@ -2004,6 +2098,8 @@ extern "C" int spec_verify_packed(const void* target_logits, const void* draft_l
   a.top_k = nullptr;
   a.top_p = nullptr;
   a.keep = nullptr;
+  a.klen = nullptr;
+  a.klist = nullptr;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
                         reinterpret_cast<uintptr_t>(draft_logits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
