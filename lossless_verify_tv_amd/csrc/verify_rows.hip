@@ -800,16 +800,24 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 // down); they follow the order of s and spread the LDS atomics of clustered
 // logits over many addresses.
 //
-// With top-k on, two passes in the common case:
+// With top-k on, one or two passes in the common case:
 //   1. the row maximum M (and faults: such rows are left whole) and token
 //      counts per bin below R0, the largest s of the row's first tile
 //      (tokens above R0 share bin 0); a block scan finds the bin where the
-//      running count reaches top_k;
-//   2. if every token down to that bin fits the LDS list (4096 tokens), they
-//      are gathered (order key and token id): top-k's boundary and then
-//      top-p's, over the tokens top-k keeps, are resolved on the list by
-//      radix selection on the 32-bit order key, 10 bits a level, then on the
-//      token id among equal keys, with fixed-point masses below M.
+//      running count reaches top_k. For top_k <= 512 the pass also lists
+//      (order key and token id, in LDS) every token down to a bin chosen
+//      from the first tile's counts so that about 16 top_k tokens (fewer
+//      for a larger top_k) are expected; if top_k's bin lies within it, the
+//      list is complete;
+//   2. otherwise, if every token down to top_k's bin fits the LDS list
+//      (4096 tokens), a second pass gathers them.
+// On the list, top-k's boundary and then top-p's, over the tokens top-k
+// keeps, are resolved with fixed-point masses below M: for at most 256
+// tokens in the bins down to top_k's by ranking each against all the others
+// and summing masses in rank order, else by radix selection on the 32-bit
+// order key, 10 bits a level, then on the token id among equal keys. The
+// ids of the tokens kept are written out for the row kernel, which then
+// needs no pass over the row.
 // Otherwise, and for top-p alone, the bins are redone below M:
 //   2'. token counts for top-k, or fixed-point masses for top-p alone; a
 //      block scan picks the bin where the running count reaches top_k, or
@@ -828,6 +836,7 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 constexpr int kRes = 32;       // first-level bins per nat below the reference
 constexpr int kNB1 = 2048;     // first-level bins
 constexpr int kNB = 1024;      // buckets of a refinement level
+constexpr int kRankMax = 256;  // lists short enough to rank by comparing every pair
 constexpr float kL2ELo = 1.925963033e-8f;  // log2(e) - fl32(log2(e))
 
 struct TruncShared {
@@ -837,11 +846,13 @@ struct TruncShared {
   int32_t cidx[kCand];
   uint32_t cnt[kNB];
   unsigned long long mass[kNB];
-  uint32_t vmin[kNB], vmax[kNB];
+  alignas(16) uint32_t vmin[kNB];
+  alignas(16) uint32_t vmax[kNB];
   unsigned long long part[kWaves][2];
   unsigned long long r64[2];
   int32_t r32;
   uint32_t ncand;
+  uint32_t nrank;
   float fmax[kWaves];
 };
 
@@ -871,15 +882,22 @@ __device__ __forceinline__ uint32_t l1_bin(float s, float M) {
   return uint32_t(fminf(__fmul_rn(M - s, float(kRes)), float(kNB1 - 1)));
 }
 
-// The first-level bin below a reference R0 that need not be the row
-// maximum: tokens above R0 fall into bin 0 with those just below it, so the
-// bins still follow the order of s.
-__device__ __forceinline__ uint32_t l1_bin_ref(float s, float R0) {
-  return uint32_t(fminf(fmaxf(__fmul_rn(R0 - s, float(kRes)), 0.f), float(kNB1 - 1)));
+// First-level bins below a reference R0 that need not be the row maximum:
+// g = fl(32 R0 - 32 s) (one fused multiply-add; R0x32 = 32 R0) and the bin
+// floor(g) clamped to [0, kNB1 - 1], so that tokens above R0 fall into bin
+// 0 with those just below it and the bins still follow the order of s.
+__device__ __forceinline__ float l1_ref_g(float s, float R0x32) {
+  return __builtin_fmaf(s, -float(kRes), R0x32);
+}
+
+__device__ __forceinline__ uint32_t l1_bin_ref(float s, float R0x32) {
+  // the mask only matters for a NaN s, in rows that are left whole
+  return uint32_t(__builtin_amdgcn_fmed3f(l1_ref_g(s, R0x32), 0.f, float(kNB1 - 1))) &
+         uint32_t(kNB1 - 1);
 }
 
 // l1_bin(s, M) <= b for b below the last bin, as one comparison: `lim` =
-// b + 1 (also l1_bin_ref(s, M) <= b).
+// b + 1.
 __device__ __forceinline__ bool l1_at_most(float s, float M, float lim) {
   return __fmul_rn(M - s, float(kRes)) < lim;
 }
@@ -928,31 +946,34 @@ __device__ __forceinline__ void row_pass(const void* row, int V, float inv_t, F&
   raw_pass<kDtype, kVecOk>(row, V, [&](float x, int v) { f(__fmul_rn(x, inv_t), v); });
 }
 
-// Gathers (order key, token id) of the tokens `want(s)` admits into the LDS
-// list (ts.ncand counts them all, also past kCand). Wave-aggregated: one LDS
-// atomic per wave and token slot, taken only where a token is admitted.
+// Appends (order key, token id) of token v, scaled logit s, to the LDS list
+// on the lanes where w holds (ts.ncand counts every append, also past
+// kCand). Wave-aggregated: one LDS atomic per wave, taken only where some
+// lane appends.
+__device__ __forceinline__ void list_append(bool w, float s, int v, TruncShared& ts) {
+  const uint64_t mask = __ballot(w);
+  if (mask) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int leader = __ffsll((unsigned long long)mask) - 1;
+    uint32_t base = 0;
+    if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
+    base = (uint32_t)__shfl((int)base, leader, kWave);
+    if (w) {
+      const uint32_t pos = base + (uint32_t)__popcll(mask & ((uint64_t(1) << lane) - 1));
+      if (pos < uint32_t(kCand)) {
+        ts.ckey[pos] = desc_key(s);
+        ts.cidx[pos] = v;
+      }
+    }
+  }
+}
+
+// Gathers the tokens `want(s)` admits into the LDS list.
 template <int kDtype, bool kVecOk, class F>
 __device__ __forceinline__ void gather_pass(const void* row, int V, float inv_t, F&& want,
                                             TruncShared& ts) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint64_t below = (uint64_t(1) << lane) - 1;
-  row_pass<kDtype, kVecOk>(row, V, inv_t, [&](float s, int v) {
-    const bool w = want(s);
-    const uint64_t mask = __ballot(w);
-    if (mask) {
-      const int leader = __ffsll((unsigned long long)mask) - 1;
-      uint32_t base = 0;
-      if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
-      base = (uint32_t)__shfl((int)base, leader, kWave);
-      if (w) {
-        const uint32_t pos = base + (uint32_t)__popcll(mask & below);
-        if (pos < uint32_t(kCand)) {
-          ts.ckey[pos] = desc_key(s);
-          ts.cidx[pos] = v;
-        }
-      }
-    }
-  });
+  row_pass<kDtype, kVecOk>(row, V, inv_t,
+                           [&](float s, int v) { list_append(want(s), s, v, ts); });
 }
 
 // Block-wide exclusive scans of two 64-bit integers; totals in ta, tb.
@@ -1226,30 +1247,63 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   // maximum do).
   float mx = -INFINITY;
   bool nan = false;
-  float R0 = 0.f;
+  float R0x32 = 0.f;  // 32 R0
+  bool spec = false;  // pass 1 also lists the tokens of bins up to gb
+  uint32_t gb = 0;
   if (k_on) {
+    // NaN shows as an absolute value above +inf's bits
+    uint32_t amax = 0;
     Grp<kDtype> g0;
     load_grp<kDtype, kVecOk, true>(row, V, tile_elem(0), g0);
 #pragma unroll
     for (int j = 0; j < kVec; ++j) {
       const float x = gelem(g0, j);
       if (tile_elem(0) + j < V) {
-        nan |= (x != x);
+        amax = max(amax, __float_as_uint(x) & 0x7fffffffu);
         mx = fmaxf(mx, x);
       }
     }
     for (int i = threadIdx.x; i < kNB1; i += kThreads) ts.cnt1[i] = 0;
-    R0 = __fmul_rn(block_max_f(mx, ts), inv_t);  // (its barriers also cover the zeroing)
-    if (!(R0 > -INFINITY && R0 < INFINITY)) R0 = 0.f;  // any finite reference keeps the order
-    auto count = [&](float x) { atomicAdd(&ts.cnt1[l1_bin_ref(__fmul_rn(x, inv_t), R0)], 1u); };
+    const float R0 = __fmul_rn(block_max_f(mx, ts), inv_t);  // (its barriers cover the zeroing)
+    // any finite reference keeps the order; 32 R0 is exact unless it overflows
+    R0x32 = (R0 > -1e37f && R0 < 1e37f) ? R0 * float(kRes) : 0.f;
 #pragma unroll
     for (int j = 0; j < kVec; ++j)
-      if (tile_elem(0) + j < V) count(gelem(g0, j));
-    raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
-      nan |= (x != x);
+      if (tile_elem(0) + j < V)
+        atomicAdd(&ts.cnt1[l1_bin_ref(__fmul_rn(gelem(g0, j), inv_t), R0x32)], 1u);
+    // For a small top_k the same pass also lists every token down to the
+    // bin where the first tile's count reaches F top_k times the tile's
+    // share of the row (F = 16, less for a larger top_k, so that about half
+    // the list is expected to fill): if the bin where the whole row's count
+    // reaches top_k lies within it, the list is complete without a second
+    // pass.
+    const int F = min(16, kCand / (2 * top_k));
+    spec = F >= 4;
+    if (spec) {
+      __syncthreads();
+      const int n0 = V < kTile ? V : kTile;
+      const uint64_t kk =
+          (uint64_t(F) * uint64_t(top_k) * uint64_t(n0) + uint64_t(V) - 1) / uint64_t(V);
+      uint64_t b0, b1;
+      gb = uint32_t(select2(ts.cnt1, ts.cnt1, kNB1, kk < 1 ? 1 : kk, b0, b1, ts));
+      if (threadIdx.x == 0) ts.ncand = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        const int v = tile_elem(0) + j;
+        const float s = __fmul_rn(gelem(g0, j), inv_t);
+        list_append(v < V && l1_bin_ref(s, R0x32) <= gb, s, v, ts);
+      }
+    }
+    raw_pass<kDtype, kVecOk>(row, V, [&](float x, int v) {
+      amax = max(amax, __float_as_uint(x) & 0x7fffffffu);
       mx = fmaxf(mx, x);
-      count(x);
+      const float s = __fmul_rn(x, inv_t);
+      const uint32_t bin = l1_bin_ref(s, R0x32);
+      atomicAdd(&ts.cnt1[bin], 1u);
+      if (spec) list_append(bin <= gb, s, v, ts);
     }, 1);
+    nan = amax > 0x7f800000u;
   } else {
     raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
       nan |= (x != x);
@@ -1266,7 +1320,7 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   // list: top-k is on and every token down to the bin (below R0) where the
   // count reaches top_k fits the LDS list. One more pass gathers them (every
   // token that top-k keeps is among them) and the rest works on the list.
-  bool list = false;
+  bool list = false, listed = false;
   float limR = 0.f;
   bool everyR = false;
   if (k_on) {
@@ -1275,6 +1329,9 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     list = bc + ts.cnt1[binR] <= uint64_t(kCand);
     everyR = binR >= kNB1 - 1;
     limR = float(binR + 1);
+    // the list pass 1 made holds every token of the bins up to gb
+    listed = spec && uint32_t(binR) <= gb && ts.ncand <= uint32_t(kCand);
+    list = list || listed;
   }
   // masses of the whole row into the first-level histogram
   auto mass_pass = [&]() {
@@ -1291,11 +1348,13 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   // come from it. Otherwise a mass pass fills the histogram for the row.
   bool all_in = false;
   if (list) {
-    if (threadIdx.x == 0) ts.ncand = 0;
-    __syncthreads();
-    gather_pass<kDtype, kVecOk>(row, V, inv_t,
-                                [&](float s) { return everyR || l1_at_most(s, R0, limR); }, ts);
-    __syncthreads();
+    if (!listed) {
+      if (threadIdx.x == 0) ts.ncand = 0;
+      __syncthreads();
+      gather_pass<kDtype, kVecOk>(
+          row, V, inv_t, [&](float s) { return everyR || l1_ref_g(s, R0x32) < limR; }, ts);
+      __syncthreads();
+    }
     rankK = uint64_t(top_k);
   } else {
     // ---- pass 2: first-level histograms, token counts for top-k, masses for
@@ -1387,11 +1446,128 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     W0 = sum_before(ts.mass1, kNB1, binK, ts);
   }
 
-  // ---- top-k: the top_k-th token
+  // ---- small lists: every listed token's rank among the list in (key, id)
+  // order from comparisons with all the others, masses in rank order and
+  // their prefix sums. The list holds every token ranking at or above the
+  // top_k-th, so for those their rank in the list is their rank in the row.
   uint32_t keyK = 0xffffffffu;
   int idxK = INT_MAX;
   uint64_t WK = 0;  // mass of the tokens top-k keeps
-  if (k_on) {
+  uint32_t key = keyK;
+  int idx = idxK;
+  uint64_t kept = WK;  // mass of the kept tokens
+  bool ranked = false;
+  uint32_t* rk = ts.vmin;                                // keys of the ranked tokens
+  int32_t* ri = reinterpret_cast<int32_t*>(ts.vmax);     // their ids
+  if (k_on && in_lds && (list || all_in)) {
+    // the listed tokens of the bins down to top-k's own (a list pass 1 made
+    // also holds lower bins), copied out
+    if (threadIdx.x == 0) ts.nrank = 0;
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1);
+    for (uint32_t i0 = 0; i0 < nc; i0 += kThreads) {
+      const uint32_t i = i0 + threadIdx.x;
+      bool w = false;
+      uint32_t d = 0;
+      int v = 0;
+      if (i < nc) {
+        d = ts.ckey[i];
+        v = ts.cidx[i];
+        w = !listed || everyR || l1_ref_g(key_value(d), R0x32) < limR;
+      }
+      const uint64_t mask = __ballot(w);
+      if (mask) {
+        const int leader = __ffsll((unsigned long long)mask) - 1;
+        uint32_t base = 0;
+        if (lane == leader) base = atomicAdd(&ts.nrank, (uint32_t)__popcll(mask));
+        base = (uint32_t)__shfl((int)base, leader, kWave);
+        const uint32_t pos = base + (uint32_t)__popcll(mask & ((uint64_t(1) << lane) - 1));
+        if (w && pos < uint32_t(kNB)) {
+          rk[pos] = d;
+          ri[pos] = v;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nr = ts.nrank;
+    const uint32_t np = (nr + 7u) & ~7u;  // padded with keys above every real one
+    ranked = np <= uint32_t(kRankMax) && uint32_t(top_k) <= nr;
+    if (ranked && threadIdx.x < np - nr) {
+      rk[nr + threadIdx.x] = 0xffffffffu;
+      ri[nr + threadIdx.x] = INT_MAX;
+    }
+    __syncthreads();
+    if (ranked) {
+      for (uint32_t i = threadIdx.x; i < nr; i += kThreads) {
+        const uint64_t ci = (uint64_t(rk[i]) << 32) | uint32_t(ri[i]);
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < np; j += 8) {
+          const uint4 ka = *reinterpret_cast<const uint4*>(rk + j);
+          const uint4 kb = *reinterpret_cast<const uint4*>(rk + j + 4);
+          const uint4 ia = *reinterpret_cast<const uint4*>(ri + j);
+          const uint4 ib = *reinterpret_cast<const uint4*>(ri + j + 4);
+          r += ((uint64_t(ka.x) << 32) | ia.x) < ci;
+          r += ((uint64_t(ka.y) << 32) | ia.y) < ci;
+          r += ((uint64_t(ka.z) << 32) | ia.z) < ci;
+          r += ((uint64_t(ka.w) << 32) | ia.w) < ci;
+          r += ((uint64_t(kb.x) << 32) | ib.x) < ci;
+          r += ((uint64_t(kb.y) << 32) | ib.y) < ci;
+          r += ((uint64_t(kb.z) << 32) | ib.z) < ci;
+          r += ((uint64_t(kb.w) << 32) | ib.w) < ci;
+        }
+        if (r < uint32_t(top_k)) {
+          ts.cnt[r] = i;
+          ts.mass[r] = fixed_mass(key_value(rk[i]), M, scale);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (ranked) {
+    uint32_t* srt = ts.cnt;            // index of each rank below top_k
+    unsigned long long* pm = ts.mass;  // mass of each rank, then inclusive sums
+    constexpr int kPer = kNB / kThreads;
+    uint64_t m[kPer], own = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int r = threadIdx.x * kPer + q;
+      m[q] = r < top_k ? pm[r] : 0;
+      own += m[q];
+    }
+    uint64_t ex, e1, tot, t1;
+    block_exscan2_u64(own, 0, ex, e1, tot, t1, ts);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      ex += m[q];
+      pm[threadIdx.x * kPer + q] = ex;
+    }
+    __syncthreads();
+    WK = tot;
+    keyK = rk[srt[top_k - 1]];
+    idxK = ri[srt[top_k - 1]];
+    key = keyK;
+    idx = idxK;
+    kept = WK;
+    if (p_on) {
+      // the first rank whose running mass reaches top_p times WK
+      needP = top_p_need(top_p, WK);
+      if (threadIdx.x == 0) ts.r32 = top_k - 1;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int r = threadIdx.x * kPer + q;
+        if (r < top_k && pm[r] >= needP && (r == 0 || pm[r - 1] < needP)) ts.r32 = r;
+      }
+      __syncthreads();
+      const int rp = ts.r32;
+      key = rk[srt[rp]];
+      idx = ri[srt[rp]];
+      kept = pm[rp];
+    }
+  }
+
+  // ---- top-k: the top_k-th token
+  if (k_on && !ranked) {
     auto adm = [&](float s, int, uint32_t) { return list || int(l1_bin(s, M)) == binK; };
     uint32_t lo = 0, hi = 0xffffffffu;
     if (!in_lds) l1_key_range(uint32_t(binK), M, lo, hi);
@@ -1411,10 +1587,12 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   }
 
   // ---- top-p over the top-k set
-  uint32_t key = keyK;
-  int idx = idxK;
-  uint64_t kept = WK;  // mass of the kept tokens
-  if (p_on) {
+  if (!ranked) {
+    key = keyK;
+    idx = idxK;
+    kept = WK;
+  }
+  if (p_on && !ranked) {
     if (k_on) {
       needP = top_p_need(top_p, WK);
       if (list) {
