@@ -818,7 +818,8 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 // order key, 10 bits a level, then on the token id among equal keys. The
 // ids of the tokens kept are written out for the row kernel, which then
 // needs no pass over the row.
-// Otherwise, and for top-p alone, the bins are redone below M:
+// When the list cannot hold them, and for top-p alone, the bins are redone
+// below M:
 //   2'. token counts for top-k, or fixed-point masses for top-p alone; a
 //      block scan picks the bin where the running count reaches top_k, or
 //      the running mass top_p times the total;

@@ -204,6 +204,41 @@ def test_topkp_crowded_bins(dtype):
     _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p, f"crowded {dtype}")
 
 
+@pytest.mark.parametrize("temperature", [1.0, 0.7])
+def test_topkp_first_tile_holds_the_top_tokens(temperature):
+    """Most of the top-50 tokens sit in the row's first 4096 ids, so the
+    list the selection's first pass builds from the first tile's counts
+    stops above the 50th token and a second pass gathers the boundary;
+    other rows push that list past its capacity. Checked against the
+    oracle."""
+    dev = device()
+    B, K, V = 6, 2, 100000
+    rng = np.random.default_rng(61)
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + 0.5 * rng.standard_normal((B, K, V))).astype(np.float32)
+    for b in range(B):
+        for rows in (t[b], d[b]):
+            if b % 2 == 0:      # 40 high tokens in the first tile, 30 a little lower elsewhere
+                rows[:, rng.choice(4096, 40, replace=False)] = 6.0 + rng.random((rows.shape[0], 40))
+                rows[:, 4096 + rng.choice(V - 4096, 30, replace=False)] = 5.0 + rng.random((rows.shape[0], 30))
+            else:               # a few very high tokens in the first tile, its other tokens very low
+                rows[:, :4096] = -20.0
+                rows[:, rng.choice(4096, 30, replace=False)] = 10.0 + rng.random((rows.shape[0], 30))
+    case = synth.verify_case(1, batch=B, vocab=V, kmax=K)
+    case.dtype = "bf16"
+    case.target = synth.to_bf16(t)
+    case.draft = synth.to_bf16(d)
+    dec = ov.decode_rows(case.draft.reshape(-1, V), "bf16").reshape(B, K, V)
+    case.tokens = np.argmax(dec / temperature + rng.gumbel(size=dec.shape), axis=-1).astype(np.int32)
+    case.k = np.full(B, K, np.int32)
+    case.temperature = np.full(B, temperature, np.float32)
+    case.seed = rng.integers(0, 2**63, size=B).astype(np.uint64)
+    top_k = np.array([50, 50, 45, 60, 50, 35], np.int32)
+    top_p = np.array([1.0, 0.9, 0.95, 1.0, 0.8, 0.99], np.float32)
+    announce(f"topkp first tile heavy T={temperature} shape={case.shape}")
+    _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p, f"first tile T={temperature}")
+
+
 def test_bad_top_p_faults_with_other_bits():
     dev = device()
     case = synth.verify_case(3, batch=6, vocab=3000, kmax=2)
