@@ -257,6 +257,38 @@ def test_bad_top_p_faults_with_other_bits():
     assert np.all(gpu["accepted_len"][:5] == -1)
 
 
+def test_topkp_workspace_contents_do_not_matter():
+    """The kept prefixes, the kept-token lists and their lengths in the
+    workspace are written before they are read: a workspace full of garbage
+    gives the same outputs as a fresh one, and so does one that an earlier
+    call with other settings left behind."""
+    dev = device()
+    case = synth.verify_case(3, temperature=0.8, batch=12, vocab=40000)
+    B, kmax, V = case.shape
+    top_k, top_p = _settings(B, V, rotate=2)
+    nbytes = lv.spec_verify_topkp_workspace_bytes(B, kmax, V, lv.LVTV_BF16)
+    fresh = lv.new_workspace(nbytes, dev)
+    junk = lv.new_workspace(nbytes, dev)
+    junk.fill_(0xA7)
+    used = lv.new_workspace(nbytes, dev)
+    inp = verify_inputs(case, dev)
+    tk = torch.from_numpy(top_k).to(dev)
+    tp = torch.from_numpy(top_p).to(dev)
+    # an earlier call on `used` with every request truncated to top-k 3
+    lv.spec_verify_topkp(**inp, top_k=torch.full_like(tk, 3), top_p=torch.ones_like(tp),
+                         workspace=used)
+    announce(f"topkp workspace garbage shape={case.shape}")
+    outs = []
+    for ws in (fresh, junk, used):
+        acc, toks, alpha, status = lv.spec_verify_topkp(**inp, top_k=tk, top_p=tp, workspace=ws)
+        torch.cuda.synchronize(dev)
+        outs.append((acc.cpu().numpy(), toks.cpu().numpy(), alpha.cpu().numpy(),
+                     status.cpu().numpy()))
+    for other in outs[1:]:
+        for x, y in zip(outs[0], other):
+            assert np.array_equal(x, y)
+
+
 def test_truncation_off_equals_plain_verify():
     """top_k <= 0 or >= V and top_p >= 1 keep every token: the outputs are
     bit-identical to spec_verify's on the full-vocabulary workload."""
