@@ -711,25 +711,19 @@ __device__ __forceinline__ void greedy_row(const Args& a, int b, int k, bool pai
   // row); INT_MAX marks "none yet"
   float vt = -INFINITY, vd = -INFINITY;
   int it = INT_MAX, id = INT_MAX, nt = 0, nd = 0;
-  for (int t0 = 0; t0 < a.n_tiles; t0 += kBatch) {
-    Grp<kDtype> gt[kBatch], gd[kBatch];
-#pragma unroll
-    for (int n = 0; n < kBatch; ++n) {
-      const int t = t0 + n < a.n_tiles ? t0 + n : t0;
-      load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t), gt[n]);
-      if (pair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t), gd[n]);
-    }
-#pragma unroll
-    for (int n = 0; n < kBatch; ++n) {
-      const int e = tile_elem(t0 + n);
-      if (t0 + n < a.n_tiles) {
-        mask_grp<kDtype, kVecOk>(gt[n], e, V);
-        argmax_grp(gt[n], e, V, vt, it, nt);
-        if (pair) {
-          mask_grp<kDtype, kVecOk>(gd[n], e, V);
-          argmax_grp(gd[n], e, V, vd, id, nd);
-        }
-      }
+  // One tile of loads per step: with every row pair of the call resident at
+  // once there are enough loads in flight chip-wide, and batches of 2-8
+  // tiles measured slower (58-62 against 56 us per call).
+  for (int t = 0; t < a.n_tiles; ++t) {
+    const int e = tile_elem(t);
+    Grp<kDtype> gt, gd;
+    load_grp<kDtype, kVecOk, true>(trow, V, e, gt);
+    if (pair) load_grp<kDtype, kVecOk, true>(drow, V, e, gd);
+    mask_grp<kDtype, kVecOk>(gt, e, V);
+    argmax_grp(gt, e, V, vt, it, nt);
+    if (pair) {
+      mask_grp<kDtype, kVecOk>(gd, e, V);
+      argmax_grp(gd, e, V, vd, id, nd);
     }
   }
   // a thread whose tokens are all -inf reports its first in-range index
