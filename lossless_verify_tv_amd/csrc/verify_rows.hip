@@ -795,15 +795,16 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 // logits over many addresses.
 //
 // With top-k on, one or two passes in the common case:
-//   1. the row maximum M (and faults: such rows are left whole) and token
-//      counts per bin below R0, the largest s of the row's first tile
-//      (tokens above R0 share bin 0); a block scan finds the bin where the
-//      running count reaches top_k. For top_k <= 512 the pass also lists
-//      (order key and token id, in LDS) every token down to a bin chosen
-//      from the first tile's counts so that about 16 top_k tokens (fewer
-//      for a larger top_k) are expected; if top_k's bin lies within it, the
-//      list is complete;
-//   2. otherwise, if every token down to top_k's bin fits the LDS list
+//   1. the row maximum M (and faults: such rows are left whole), and R0,
+//      the largest s of the row's first tile. For top_k <= 512 the pass
+//      lists (order key and token id, in LDS) every token down to a bin
+//      below R0 chosen from the first tile's counts, so that about 16 top_k
+//      tokens (fewer for a larger top_k) are expected; if it lists at least
+//      top_k tokens (and no more than the list holds) it is complete. For a
+//      larger top_k the pass counts tokens per bin below R0 (tokens above R0
+//      share bin 0) and a block scan finds the bin where the count reaches
+//      top_k;
+//   2. in that case, if every token down to that bin fits the LDS list
 //      (4096 tokens), a second pass gathers them.
 // On the list, top-k's boundary and then top-p's, over the tokens top-k
 // keeps, are resolved with fixed-point masses below M: for at most 256
@@ -1266,12 +1267,12 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     for (int j = 0; j < kVec; ++j)
       if (tile_elem(0) + j < V)
         atomicAdd(&ts.cnt1[l1_bin_ref(__fmul_rn(gelem(g0, j), inv_t), R0x32)], 1u);
-    // For a small top_k the same pass also lists every token down to the
-    // bin where the first tile's count reaches F top_k times the tile's
-    // share of the row (F = 16, less for a larger top_k, so that about half
-    // the list is expected to fill): if the bin where the whole row's count
-    // reaches top_k lies within it, the list is complete without a second
-    // pass.
+    // For a small top_k the pass, instead of counting every token, lists
+    // every token down to the bin where the first tile's count reaches
+    // F top_k times the tile's share of the row (F = 16, less for a larger
+    // top_k, so that about half the list is expected to fill): if the list
+    // holds at least top_k tokens it is complete without a second pass, and
+    // no LDS atomic is spent on the tokens below it.
     const int F = min(16, kCand / (2 * top_k));
     spec = F >= 4;
     if (spec) {
@@ -1295,8 +1296,10 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
       mx = fmaxf(mx, x);
       const float s = __fmul_rn(x, inv_t);
       const uint32_t bin = l1_bin_ref(s, R0x32);
-      atomicAdd(&ts.cnt1[bin], 1u);
-      if (spec) list_append(bin <= gb, s, v, ts);
+      if (spec)
+        list_append(bin <= gb, s, v, ts);
+      else
+        atomicAdd(&ts.cnt1[bin], 1u);
     }, 1);
     nan = amax > 0x7f800000u;
   } else {
@@ -1318,15 +1321,32 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
   bool list = false, listed = false;
   float limR = 0.f;
   bool everyR = false;
-  if (k_on) {
+  if (k_on && spec) {
+    // The list holds every token of the bins up to gb, all ranking above the
+    // tokens it leaves out: with at least top_k of them it holds every token
+    // that top-k keeps. Their own bin counts give top_k's bin.
+    const uint32_t n = ts.ncand;
+    listed = n >= uint32_t(top_k) && n <= uint32_t(kCand);
+    if (listed) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < kNB1; i += kThreads) ts.cnt1[i] = 0;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < n; i += kThreads)
+        atomicAdd(&ts.cnt1[l1_bin_ref(key_value(ts.ckey[i]), R0x32)], 1u);
+      __syncthreads();
+      uint64_t bc, bg;
+      const int binR = select2(ts.cnt1, ts.cnt1, kNB1, uint64_t(top_k), bc, bg, ts);
+      everyR = binR >= kNB1 - 1;
+      limR = float(binR + 1);
+      list = true;
+    }
+    // otherwise the bins are redone below M
+  } else if (k_on) {
     uint64_t bc, bg;
     const int binR = select2(ts.cnt1, ts.cnt1, kNB1, uint64_t(top_k), bc, bg, ts);
     list = bc + ts.cnt1[binR] <= uint64_t(kCand);
     everyR = binR >= kNB1 - 1;
     limR = float(binR + 1);
-    // the list pass 1 made holds every token of the bins up to gb
-    listed = spec && uint32_t(binR) <= gb && ts.ncand <= uint32_t(kCand);
-    list = list || listed;
   }
   // masses of the whole row into the first-level histogram
   auto mass_pass = [&]() {
