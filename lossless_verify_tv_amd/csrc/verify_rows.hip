@@ -944,22 +944,14 @@ __device__ __forceinline__ void row_pass(const void* row, int V, float inv_t, F&
 
 // Appends (order key, token id) of token v, scaled logit s, to the LDS list
 // on the lanes where w holds (ts.ncand counts every append, also past
-// kCand). Wave-aggregated: one LDS atomic per wave, taken only where some
-// lane appends.
+// kCand). The compiler turns the per-lane increment into one LDS atomic per
+// wave and a lane prefix count.
 __device__ __forceinline__ void list_append(bool w, float s, int v, TruncShared& ts) {
-  const uint64_t mask = __ballot(w);
-  if (mask) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int leader = __ffsll((unsigned long long)mask) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
-    base = (uint32_t)__shfl((int)base, leader, kWave);
-    if (w) {
-      const uint32_t pos = base + (uint32_t)__popcll(mask & ((uint64_t(1) << lane) - 1));
-      if (pos < uint32_t(kCand)) {
-        ts.ckey[pos] = desc_key(s);
-        ts.cidx[pos] = v;
-      }
+  if (w) {
+    const uint32_t pos = atomicAdd(&ts.ncand, 1u);
+    if (pos < uint32_t(kCand)) {
+      ts.ckey[pos] = desc_key(s);
+      ts.cidx[pos] = v;
     }
   }
 }
@@ -1291,16 +1283,20 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
         list_append(v < V && l1_bin_ref(s, R0x32) <= gb, s, v, ts);
       }
     }
-    raw_pass<kDtype, kVecOk>(row, V, [&](float x, int v) {
-      amax = max(amax, __float_as_uint(x) & 0x7fffffffu);
-      mx = fmaxf(mx, x);
-      const float s = __fmul_rn(x, inv_t);
-      const uint32_t bin = l1_bin_ref(s, R0x32);
-      if (spec)
-        list_append(bin <= gb, s, v, ts);
-      else
-        atomicAdd(&ts.cnt1[bin], 1u);
-    }, 1);
+    if (spec) {
+      raw_pass<kDtype, kVecOk>(row, V, [&](float x, int v) {
+        amax = max(amax, __float_as_uint(x) & 0x7fffffffu);
+        mx = fmaxf(mx, x);
+        const float s = __fmul_rn(x, inv_t);
+        list_append(l1_bin_ref(s, R0x32) <= gb, s, v, ts);
+      }, 1);
+    } else {
+      raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
+        amax = max(amax, __float_as_uint(x) & 0x7fffffffu);
+        mx = fmaxf(mx, x);
+        atomicAdd(&ts.cnt1[l1_bin_ref(__fmul_rn(x, inv_t), R0x32)], 1u);
+      }, 1);
+    }
     nan = amax > 0x7f800000u;
   } else {
     raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
@@ -1479,27 +1475,13 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
     // also holds lower bins), copied out
     if (threadIdx.x == 0) ts.nrank = 0;
     __syncthreads();
-    const int lane = threadIdx.x & (kWave - 1);
-    for (uint32_t i0 = 0; i0 < nc; i0 += kThreads) {
-      const uint32_t i = i0 + threadIdx.x;
-      bool w = false;
-      uint32_t d = 0;
-      int v = 0;
-      if (i < nc) {
-        d = ts.ckey[i];
-        v = ts.cidx[i];
-        w = !listed || everyR || l1_ref_g(key_value(d), R0x32) < limR;
-      }
-      const uint64_t mask = __ballot(w);
-      if (mask) {
-        const int leader = __ffsll((unsigned long long)mask) - 1;
-        uint32_t base = 0;
-        if (lane == leader) base = atomicAdd(&ts.nrank, (uint32_t)__popcll(mask));
-        base = (uint32_t)__shfl((int)base, leader, kWave);
-        const uint32_t pos = base + (uint32_t)__popcll(mask & ((uint64_t(1) << lane) - 1));
-        if (w && pos < uint32_t(kNB)) {
+    for (uint32_t i = threadIdx.x; i < nc; i += kThreads) {
+      const uint32_t d = ts.ckey[i];
+      if (!listed || everyR || l1_ref_g(key_value(d), R0x32) < limR) {
+        const uint32_t pos = atomicAdd(&ts.nrank, 1u);
+        if (pos < uint32_t(kNB)) {
           rk[pos] = d;
-          ri[pos] = v;
+          ri[pos] = ts.cidx[i];
         }
       }
     }
@@ -1672,25 +1654,12 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
       __syncthreads();
       if (threadIdx.x == 0) ts.ncand = 0;
       __syncthreads();
-      const int lane = threadIdx.x & (kWave - 1);
-      const uint64_t below = (uint64_t(1) << lane) - 1;
-      for (uint32_t i0 = 0; i0 < nc; i0 += kThreads) {
-        const uint32_t i = i0 + threadIdx.x;
-        bool w = false;
-        int v = 0;
-        if (i < nc) {
-          const uint32_t d = ts.ckey[i];
-          v = ts.cidx[i];
-          w = d < key || (d == key && v <= idx);
-        }
-        const uint64_t mask = __ballot(w);
-        if (mask) {
-          const int leader = __ffsll((unsigned long long)mask) - 1;
-          uint32_t base = 0;
-          if (lane == leader) base = atomicAdd(&ts.ncand, (uint32_t)__popcll(mask));
-          base = (uint32_t)__shfl((int)base, leader, kWave);
-          const uint32_t pos = base + (uint32_t)__popcll(mask & below);
-          if (w && pos < uint32_t(kCand)) dst[pos] = v;
+      for (uint32_t i = threadIdx.x; i < nc; i += kThreads) {
+        const uint32_t d = ts.ckey[i];
+        const int v = ts.cidx[i];
+        if (d < key || (d == key && v <= idx)) {
+          const uint32_t pos = atomicAdd(&ts.ncand, 1u);
+          if (pos < uint32_t(kCand)) dst[pos] = v;
         }
       }
       __syncthreads();
