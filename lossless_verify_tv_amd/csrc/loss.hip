@@ -49,7 +49,6 @@ namespace lvtv {
 namespace {
 
 constexpr int kSlice = kBlock * kVec * 4;  // 8192 elements per slice
-constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kSteps = kSlice / (kBlock * kVec);
 
 struct RowFinal {

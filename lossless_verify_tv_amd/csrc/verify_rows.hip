@@ -1937,7 +1937,7 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const float inv_t = __fdiv_rn(1.f, T);
   // accept inputs for every position in parallel: u_k, and p(y_k)/q(y_k)
   // as the row kernel evaluated it (prob64_of with the row's statistics)
-  if (threadIdx.x < kb) {
+  if (int(threadIdx.x) < kb) {
     const int k = threadIdx.x;
     double u, u2;
     verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
