@@ -1276,19 +1276,23 @@ __device__ __forceinline__ void trunc_body(const Args& a) {
       gb = uint32_t(select2(ts.cnt1, ts.cnt1, kNB1, kk < 1 ? 1 : kk, b0, b1, ts));
       if (threadIdx.x == 0) ts.ncand = 0;
       __syncthreads();
+    }
+    // l1_bin_ref(s) <= gb as one comparison of its argument (the bin is not
+    // an index here): g < gb + 1, or every token when gb is the last bin
+    const bool every_g = gb >= uint32_t(kNB1 - 1);
+    const float lim_g = float(gb + 1);
+    if (spec) {
 #pragma unroll
       for (int j = 0; j < kVec; ++j) {
         const int v = tile_elem(0) + j;
         const float s = __fmul_rn(gelem(g0, j), inv_t);
-        list_append(v < V && l1_bin_ref(s, R0x32) <= gb, s, v, ts);
+        list_append(v < V && (every_g || l1_ref_g(s, R0x32) < lim_g), s, v, ts);
       }
-    }
-    if (spec) {
       raw_pass<kDtype, kVecOk>(row, V, [&](float x, int v) {
         amax = max(amax, __float_as_uint(x) & 0x7fffffffu);
         mx = fmaxf(mx, x);
         const float s = __fmul_rn(x, inv_t);
-        list_append(l1_bin_ref(s, R0x32) <= gb, s, v, ts);
+        list_append(every_g || l1_ref_g(s, R0x32) < lim_g, s, v, ts);
       }, 1);
     } else {
       raw_pass<kDtype, kVecOk>(row, V, [&](float x, int) {
