@@ -57,6 +57,7 @@ extern "C" {
 #define LVTV_ERR_LAUNCH (-5)    /* the HIP runtime rejected a launch     */
 #define LVTV_ERR_OBJECTIVE (-6) /* unknown loss objective                */
 #define LVTV_ERR_TEMPERATURE (-7) /* loss temperature not finite and > 0 */
+#define LVTV_ERR_OPTION (-8)    /* unknown debug option (lvtv_debug_draft_loss) */
 
 /* Objectives of draft_loss_fwd_bwd, each summed over a branch's W positions
  * and averaged over the N branches. */
@@ -69,6 +70,8 @@ extern "C" {
 #define LVTV_MAX_K 16         /* draft positions per request (Kmax)      */
 #define LVTV_MAX_W 16         /* positions per branch (W)                */
 #define LVTV_MAX_V (1 << 27)  /* vocabulary size                         */
+#define LVTV_MAX_B 65535      /* requests per verify call (B)            */
+#define LVTV_MAX_N 65535      /* branches per loss call (N)              */
 
 /* Per-request status bits written by spec_verify. */
 #define LVTV_STATUS_BAD_K 1           /* K_b outside [0, Kmax]                 */
@@ -83,12 +86,9 @@ const char* lvtv_strerror(int code);
 
 /*
  * Zero-fill a workspace on `stream` (a plain fill kernel, so it may sit in a
- * captured graph). e2e_tv_loss_fwd_bwd needs this once before a workspace's
- * first use: it keeps a call epoch there and tags the words its workgroups
- * exchange with it, so that a later call (of any shape, either op) never
- * takes an earlier call's word for its own and needs no reset. spec_verify
- * does not depend on the contents. Returns LVTV_ERR_NULL /
- * LVTV_ERR_WORKSPACE (misaligned) before enqueueing anything.
+ * captured graph). A utility only: no call depends on a workspace's
+ * contents on entry. Returns LVTV_ERR_NULL / LVTV_ERR_WORKSPACE (misaligned)
+ * before enqueueing anything.
  */
 int lvtv_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
@@ -130,7 +130,9 @@ size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype
  *   k_per_req      int32 [B], K_b in 0..Kmax (0 = one token sampled from p_0).
  *   temperature    float [B]; 0 = greedy, > 0 stochastic.
  *   seed           uint64 [B], Philox key word 0 for request b.
- *   B, Kmax, V     1 <= B, 0 <= Kmax <= LVTV_MAX_K, 1 <= V <= LVTV_MAX_V.
+ *   B, Kmax, V     1 <= B <= LVTV_MAX_B, 0 <= Kmax <= LVTV_MAX_K,
+ *                  1 <= V <= LVTV_MAX_V (else LVTV_ERR_SHAPE, and the workspace
+ *                  query returns 0).
  *   accepted_len   int32 [B] out: j (number of accepted drafts), -1 if faulted.
  *   out_tokens     int32 [B, Kmax+1] out: y_0..y_{j-1}, the drawn token, then -1.
  *   alpha          float [B, Kmax] out: alpha_k for k < K_b, 0 otherwise.
@@ -164,6 +166,7 @@ size_t spec_verify_packed_workspace_bytes(int32_t B, int32_t total_rows, int32_t
  * every request gets its own verify length).
  *
  * Layout (device pointers; rows V contiguous):
+ *   B              1 <= B <= LVTV_MAX_B; B <= total_rows <= B (LVTV_MAX_K + 1).
  *   row_offsets    int32 [B + 1]: request b owns the target rows
  *                  [row_offsets[b], row_offsets[b+1]), so
  *                  K_b = row_offsets[b+1] - row_offsets[b] - 1 (0..LVTV_MAX_K);
@@ -254,16 +257,20 @@ size_t e2e_tv_loss_workspace_bytes(int32_t N, int32_t W, int32_t V);
  * Arguments (device pointers; row-major, V contiguous):
  *   draft_logits   bfloat16 (uint16) [N, W, V].
  *   target_probs   float [N, W, V], constants.
- *   N, W, V        1 <= N, 1 <= W <= LVTV_MAX_W, 1 <= V <= LVTV_MAX_V.
+ *   N, W, V        1 <= N <= LVTV_MAX_N, 1 <= W <= LVTV_MAX_W,
+ *                  1 <= V <= LVTV_MAX_V.
  *   loss           float [1] out.
  *   alpha          float [N, W] out.
  *   dlogits        bfloat16 (uint16) [N, W, V] out.
  *   workspace      device scratch of >= e2e_tv_loss_workspace_bytes(...)
- *                  bytes, 256-byte aligned, zero-filled once before its
- *                  first use (lvtv_workspace_reset); after that it needs no
- *                  reset between calls of any shape. Calls sharing a
+ *                  bytes, 256-byte aligned. Its contents on entry do not
+ *                  matter: the call first clears the words its workgroups
+ *                  exchange, so a workspace left by any earlier call (of
+ *                  either op) or holding garbage is fine. Calls sharing a
  *                  workspace must be ordered on one stream.
- *   stream         hipStream_t.
+ *   stream         hipStream_t. For V <= 155648 three kernels are enqueued
+ *                  (the clear, one workgroup per half row, one finishing
+ *                  workgroup); larger V take the multi-pass pipeline.
  * NaN or infinite inputs propagate into the outputs; there is no status.
  */
 int e2e_tv_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
@@ -338,8 +345,7 @@ size_t draft_loss_logits_workspace_bytes(int32_t N, int32_t W, int32_t V);
  *   temperature    host float, finite and > 0 with fl32(1/T) finite, else
  *                  LVTV_ERR_TEMPERATURE before enqueueing anything.
  *   objective, N, W, V, loss, alpha, dlogits, workspace, stream: as
- *                  draft_loss_fwd_bwd (the workspace needs the same
- *                  one-time zero fill).
+ *                  draft_loss_fwd_bwd.
  * The TV objectives run the single-read kernel when V <= 155648; CE, KL and
  * larger V run the multi-pass pipeline.
  */
@@ -347,6 +353,34 @@ int draft_loss_logits_fwd_bwd(const uint16_t* draft_logits, const uint16_t* targ
                               float temperature, int32_t N, int32_t W, int32_t V,
                               int objective, float* loss, float* alpha, uint16_t* dlogits,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paths of lvtv_debug_draft_loss. */
+#define LVTV_PATH_AUTO 0       /* what the product entry points take        */
+#define LVTV_PATH_MULTI_PASS 2 /* force the multi-pass pipeline             */
+
+/*
+ * lvtv_debug_draft_loss -- test and debugging hook, not a product path.
+ *
+ * Runs draft_loss_fwd_bwd (target_probs given, target_logits NULL) or
+ * draft_loss_logits_fwd_bwd (target_logits given with `temperature`,
+ * target_probs NULL) with settings the product calls fix:
+ *   path         LVTV_PATH_AUTO or LVTV_PATH_MULTI_PASS (else LVTV_ERR_OPTION);
+ *   spin_limit   polling rounds a half-row workgroup of the single-read
+ *                kernel waits for the rest of its branch before leaving its
+ *                row to the finishing launch, which recomputes it
+ *                bit-identically (0: every row takes that repair path; the
+ *                product calls use 65536);
+ *   dlogits_f32  optional float [N, W, V] out: the gradient in fp32 before
+ *                its rounding to bfloat16 (NULL: not written).
+ * Everything else (arguments, workspace, errors) as the product calls;
+ * exactly one of target_probs and target_logits must be non-NULL
+ * (LVTV_ERR_NULL otherwise).
+ */
+int lvtv_debug_draft_loss(const uint16_t* draft_logits, const float* target_probs,
+                          const uint16_t* target_logits, float temperature, int32_t N,
+                          int32_t W, int32_t V, int objective, int path, int32_t spin_limit,
+                          float* loss, float* alpha, uint16_t* dlogits, float* dlogits_f32,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dspark_schedule -- confidence-scheduled verify lengths ("Reading Qwen

@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     STATUS_NONFINITE,
     OBJECTIVES,
     LvtvError,
+    PATHS,
+    debug_draft_loss,
     draft_loss_fwd_bwd,
     draft_loss_logits_fwd_bwd,
     draft_loss_logits_workspace_bytes,

@@ -44,12 +44,17 @@ EXPORTS = (
     "draft_loss_logits_workspace_bytes",
     "draft_loss_logits_fwd_bwd",
     "dspark_schedule",
+    "lvtv_debug_draft_loss",
 )
 
 SCHED_MAX_ITEMS = 8192  # LVTV_SCHED_MAX_ITEMS
 
 # Objectives of draft_loss_fwd_bwd (include/lvtv.h, LVTV_OBJ_*).
 OBJECTIVES = {"e2e_tv": 0, "step_tv": 1, "ce": 2, "kl": 3}
+
+# Paths of lvtv_debug_draft_loss (LVTV_PATH_*).
+PATHS = {"auto": 0, "multi-pass": 2}
+SPIN_LIMIT = 1 << 16  # what the product calls use
 
 _lib = None
 _lock = threading.Lock()
@@ -107,6 +112,10 @@ def load_library(path: str = LIB_PATH):
                                                   ctypes.c_int, vp, vp, vp, vp, sz, vp]
         lib.dspark_schedule.restype = ctypes.c_int
         lib.dspark_schedule.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+        lib.lvtv_debug_draft_loss.restype = ctypes.c_int
+        lib.lvtv_debug_draft_loss.argtypes = [vp, vp, vp, ctypes.c_float, i32, i32, i32,
+                                              ctypes.c_int, ctypes.c_int, i32, vp, vp, vp, vp,
+                                              vp, sz, vp]
         _lib = lib
         return lib
 
@@ -148,8 +157,9 @@ _workspaces: dict = {}
 
 
 def new_workspace(nbytes, device):
-    """A zero-filled workspace of at least `nbytes` bytes on `device`, as the
-    library requires before a workspace's first use."""
+    """A workspace of at least `nbytes` bytes on `device`, zero-filled by the
+    library's fill kernel (no call depends on the contents; zeros keep a
+    fresh workspace deterministic to look at)."""
     ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
     with torch.cuda.device(device):
         _check(load_library().lvtv_workspace_reset(_ptr(ws), ws.numel(), _stream(device)),
@@ -445,3 +455,45 @@ def spec_verify_packed(target_logits, draft_logits, draft_tokens, row_offsets, t
                                       ws.numel(), _stream(dev))
     _check(code, "spec_verify_packed")
     return acc, toks, alpha, status
+
+
+def debug_draft_loss(draft_logits, target_probs=None, target_logits=None, temperature=1.0,
+                     objective="e2e_tv", path="auto", spin_limit=SPIN_LIMIT, want_f32=False,
+                     workspace=None):
+    """Test and debugging hook (lvtv_debug_draft_loss): draft_loss_fwd_bwd
+    (``target_probs``) or draft_loss_logits_fwd_bwd (``target_logits`` and
+    ``temperature``) with the path forced ("auto" or "multi-pass"), the
+    single-read kernel's spin limit set (0: every row takes the repair
+    path) and, with ``want_f32``, the fp32 gradient before rounding.
+    Returns (loss, alpha, dlogits, dlogits_f32 or None)."""
+    lib = load_library()
+    obj = OBJECTIVES.get(objective, objective)
+    _require(isinstance(obj, int), f"unknown objective {objective!r}")
+    _require(path in PATHS, f"unknown path {path!r}")
+    _require((target_probs is None) != (target_logits is None),
+             "give exactly one of target_probs and target_logits")
+    target = target_probs if target_probs is not None else target_logits
+    dev = draft_logits.device
+    _require(dev.type == "cuda", "debug_draft_loss needs GPU tensors")
+    _require(draft_logits.dtype == torch.bfloat16, "draft_logits must be bfloat16")
+    _require(target.dtype == (torch.float32 if target_probs is not None else torch.bfloat16),
+             "target_probs must be float32, target_logits bfloat16")
+    _require(draft_logits.dim() == 3 and tuple(target.shape) == tuple(draft_logits.shape),
+             "draft_logits and the target must both be [N, W, V]")
+    for t in (draft_logits, target):
+        _require(t.device == dev and t.is_contiguous(), "inputs must be contiguous on one GPU")
+    N, W, V = draft_logits.shape
+    need = lib.draft_loss_workspace_bytes(N, W, V)
+    _require(need > 0, f"sizes out of range: N={N} W={W} V={V}")
+    ws = workspace if workspace is not None else _workspace("loss", dev, need)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    alpha = torch.empty(N, W, dtype=torch.float32, device=dev)
+    dlogits = torch.empty(N, W, V, dtype=torch.bfloat16, device=dev)
+    d32 = torch.empty(N, W, V, dtype=torch.float32, device=dev) if want_f32 else None
+    with torch.cuda.device(dev):
+        code = lib.lvtv_debug_draft_loss(
+            _ptr(draft_logits), _ptr(target_probs), _ptr(target_logits), float(temperature),
+            N, W, V, obj, PATHS[path], int(spin_limit), _ptr(loss), _ptr(alpha), _ptr(dlogits),
+            _ptr(d32), _ptr(ws), ws.numel(), _stream(dev))
+    _check(code, "lvtv_debug_draft_loss")
+    return loss, alpha, dlogits, d32

@@ -43,7 +43,6 @@
 #include "loss_fused.hpp"
 
 #include <cmath>
-#include <cstdlib>
 
 namespace lvtv {
 namespace {
@@ -106,6 +105,7 @@ struct Args {
   float* loss;
   float* alpha;
   uint16_t* dz;
+  float* dz32;  // debug: the fp32 gradient before rounding, or null
   Layout L;
   SliceStat* stat;
   Part* part;
@@ -404,6 +404,7 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
   const float* p = logits ? nullptr : a.p + row * a.V;
   const uint16_t* t = logits ? a.t + row * a.V : nullptr;
   uint16_t* dz = a.dz + row * a.V;
+  float* dz32 = a.dz32 ? a.dz32 + row * a.V : nullptr;
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
     const int64_t e = elem_index(s, it);
@@ -411,21 +412,23 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
     float xz[kVec], xp[kVec];
     load8<1>(z, e, a.V, a.vec_ok, xz);
     target_group(a, p, t, e, f.neg_t, f.inv_lt, xp);
-    uint16_t out[kVec];
+    float g[kVec];
     if (xent) {
 #pragma unroll
       for (int i = 0; i < kVec; ++i) {
         const float q = exp_c(xz[i], a.c, f.neg_m_log2e) * f.inv_l;
-        out[i] = f32_to_bf16_rne(__builtin_fmaf(q, f.c_below, -(xp[i] * f.c_above)));
+        g[i] = __builtin_fmaf(q, f.c_below, -(xp[i] * f.c_above));
       }
     } else {
 #pragma unroll
       for (int i = 0; i < kVec; ++i) {
         const float q = exp_c(xz[i], a.c, f.neg_m_log2e) * f.inv_l;
-        const float g = q * (q < xp[i] ? f.c_below : f.c_above);
-        out[i] = f32_to_bf16_rne(g);
+        g[i] = q * (q < xp[i] ? f.c_below : f.c_above);
       }
     }
+    uint16_t out[kVec];
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) out[i] = f32_to_bf16_rne(g[i]);
     if (a.vec_ok && e + kVec <= a.V) {
       uint4 w;
       w.x = uint32_t(out[0]) | (uint32_t(out[1]) << 16);
@@ -438,11 +441,16 @@ __global__ __launch_bounds__(kBlock) void grad_kernel(Args a) {
       for (int i = 0; i < kVec; ++i)
         if (e + i < a.V) dz[e + i] = out[i];
     }
+    if (dz32) {
+#pragma unroll
+      for (int i = 0; i < kVec; ++i)
+        if (e + i < a.V) dz32[e + i] = g[i];
+    }
   }
 }
 
 bool sizes_ok(int32_t N, int32_t W, int32_t V) {
-  return N >= 1 && N <= 65535 && W >= 1 && W <= LVTV_MAX_W && V >= 1 && V <= LVTV_MAX_V;
+  return N >= 1 && N <= LVTV_MAX_N && W >= 1 && W <= LVTV_MAX_W && V >= 1 && V <= LVTV_MAX_V;
 }
 
 }  // namespace
@@ -451,22 +459,23 @@ bool sizes_ok(int32_t N, int32_t W, int32_t V) {
 namespace lvtv {
 namespace {
 
-// Rounds a row workgroup of the single-read kernel polls for the rest of its
-// branch before recomputing the missing rows itself (LVTV_SPIN_LIMIT; 0
-// makes every wait take the recompute path, which the tests use).
-int spin_limit() {
-  const char* v = std::getenv("LVTV_SPIN_LIMIT");
-  if (!v || !*v) return 1 << 16;
-  const long n = std::strtol(v, nullptr, 10);
-  return n < 0 ? 0 : (n > (1 << 30) ? (1 << 30) : int(n));
-}
+// Rounds a half-row workgroup of the single-read kernel polls for the rest
+// of its branch before leaving its row to the call's last launch.
+constexpr int kSpinLimit = 1 << 16;
+
+// How a call is run. The product entry points take the defaults; the debug
+// entry point lvtv_debug_draft_loss sets them (the tests use it to compare
+// the two paths, to force the repair path and to read the fp32 gradient).
+struct Options {
+  int path = LVTV_PATH_AUTO;
+  int spin_limit = kSpinLimit;
+  float* dz32 = nullptr;
+};
 
 // The single-read kernel serves every V it can hold; the multi-pass
-// pipeline above serves the rest and can be forced with
-// LVTV_LOSS_PATH=multi-pass (used to cross-check the two).
-bool use_fused(int32_t N, int32_t W, int32_t V) {
-  const char* path = std::getenv("LVTV_LOSS_PATH");
-  if (path && path[0] == 'm') return false;
+// pipeline above serves the rest.
+bool use_fused(const Options& o, int32_t N, int32_t W, int32_t V) {
+  if (o.path == LVTV_PATH_MULTI_PASS) return false;
   return lf::applicable(N, W, V);
 }
 
@@ -496,7 +505,7 @@ struct Target {
 
 int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t W, int32_t V,
              int objective, float* loss, float* alpha, uint16_t* dlogits, void* workspace,
-             size_t workspace_bytes, void* stream) {
+             size_t workspace_bytes, void* stream, const Options& opt = Options()) {
   if (!sizes_ok(N, W, V)) return LVTV_ERR_SHAPE;
   if (objective < LVTV_OBJ_E2E_TV || objective > LVTV_OBJ_KL) return LVTV_ERR_OBJECTIVE;
   const bool logits = tg.logits != nullptr || tg.probs == nullptr;
@@ -521,7 +530,7 @@ int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t 
   const float c = unit ? kLog2e : kLog2e * inv_t;
   // the single-read kernel serves the TV objectives (their gradients need
   // only the held z, the mask and per-row scalars)
-  if ((objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV) && use_fused(N, W, V) &&
+  if ((objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV) && use_fused(opt, N, W, V) &&
       (!logits || lf::logits_supported())) {
     lf::LossCall lc;
     lc.z = draft_logits;
@@ -534,10 +543,11 @@ int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t 
     lc.V = V;
     lc.objective = objective;
     lc.vec_ok = vec_ok;
-    lc.spin_limit = spin_limit();
+    lc.spin_limit = opt.spin_limit;
     lc.loss = loss;
     lc.alpha = alpha;
     lc.dz = dlogits;
+    lc.dz32 = opt.dz32;
     const hipError_t e = lf::run(lc, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
   }
@@ -556,6 +566,7 @@ int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t 
   a.loss = loss;
   a.alpha = alpha;
   a.dz = dlogits;
+  a.dz32 = opt.dz32;
   a.L = L;
   char* ws = static_cast<char*>(workspace);
   a.stat = reinterpret_cast<SliceStat*>(ws + L.off_stat);
@@ -614,4 +625,21 @@ extern "C" int draft_loss_logits_fwd_bwd(const uint16_t* draft_logits,
   const lvtv::Target tg{nullptr, target_logits, temperature};
   return lvtv::run_loss(draft_logits, tg, N, W, V, objective, loss, alpha, dlogits, workspace,
                         workspace_bytes, stream);
+}
+
+extern "C" int lvtv_debug_draft_loss(const uint16_t* draft_logits, const float* target_probs,
+                                     const uint16_t* target_logits, float temperature, int32_t N,
+                                     int32_t W, int32_t V, int objective, int path,
+                                     int32_t spin_limit, float* loss, float* alpha,
+                                     uint16_t* dlogits, float* dlogits_f32, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (path != LVTV_PATH_AUTO && path != LVTV_PATH_MULTI_PASS) return LVTV_ERR_OPTION;
+  if ((target_probs == nullptr) == (target_logits == nullptr)) return LVTV_ERR_NULL;
+  lvtv::Options opt;
+  opt.path = path;
+  opt.spin_limit = spin_limit < 0 ? 0 : spin_limit;
+  opt.dz32 = dlogits_f32;
+  const lvtv::Target tg{target_probs, target_logits, target_logits ? temperature : 1.f};
+  return lvtv::run_loss(draft_logits, tg, N, W, V, objective, loss, alpha, dlogits, workspace,
+                        workspace_bytes, stream, opt);
 }

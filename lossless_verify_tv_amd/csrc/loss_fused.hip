@@ -89,6 +89,7 @@ struct Args {
   int spin_limit;
   float* alpha;
   uint16_t* dz;
+  float* dz32;           // debug output: the fp32 gradient before rounding (kDbg only)
   float* loss;
   FusedCtl* ctl;
   uint64_t* words;       // [N][W][2][kSlotWords] tagged words
@@ -405,14 +406,16 @@ __device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size
 }
 
 // dz of one group of 8 tokens, bf16 (nearest even), from z, the group's mask
-// bits and the row's coefficients.
-template <bool kVecOk>
+// bits and the row's coefficients. kDbg: the fp32 values before rounding go
+// to dz32 as well.
+template <bool kVecOk, bool kDbg>
 __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e, int V,
                                          float cz, const RowStats& rs, float c_below,
-                                         float c_above, uint16_t* dz) {
+                                         float c_above, uint16_t* dz, float* dz32) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   u32x4 out;
+  float g32[kVec];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     float v2[2];
@@ -421,6 +424,7 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e,
       const int jj = 2 * h + t;
       const bool below = (bits8 >> jj) & 1u;
       v2[t] = qval(zelem(zv, jj), cz, rs.nm, rs.inv_l) * (below ? c_below : c_above);
+      g32[jj] = v2[t];
     }
     const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
     out[h] = __builtin_bit_cast(uint32_t, b);
@@ -431,6 +435,11 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e,
 #pragma unroll
     for (int t = 0; t < kVec; ++t)
       if (e + t < V) dz[e + t] = uint16_t(out[t >> 1] >> (16 * (t & 1)));
+  }
+  if constexpr (kDbg) {
+#pragma unroll
+    for (int t = 0; t < kVec; ++t)
+      if (e + t < V) dz32[e + t] = g32[t];
   }
 }
 
@@ -487,7 +496,7 @@ __device__ __forceinline__ void publish_stats(uint64_t* slot, int first, uint32_
 
 // ------------------------------------------------------------------ half-row kernel
 
-template <bool kVecOk, bool kLogits>
+template <bool kVecOk, bool kLogits, bool kDbg>
 __device__ __forceinline__ void half_body(const Args& a) {
   __shared__ Shared sh;
   __shared__ u32x4 zl[kZL][kThreads];
@@ -602,8 +611,8 @@ __device__ __forceinline__ void half_body(const Args& a) {
   const int tbd = opaque(group_elem(h, 0));
 #pragma unroll
   for (int g = 0; g < kZG; ++g) {
-    dz_group<kVecOk>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, c, rs, c_below,
-                     c_above, dz);
+    dz_group<kVecOk, kDbg>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, c, rs,
+                           c_below, c_above, dz, kDbg ? a.dz32 + row * V : nullptr);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -673,7 +682,7 @@ __device__ __forceinline__ void put_stats(uint32_t* bw, int s, int first, const 
 // missing is recomputed from the inputs with the same steps and reductions.
 // Then both halves' dz are written (the mask recomputed from z and p). Every
 // thread of the block calls it.
-template <bool kVecOk, bool kLogits>
+template <bool kVecOk, bool kLogits, bool kDbg>
 __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag, Shared& sh,
                                            uint32_t* bw) {
   const int W = a.W, V = a.V;
@@ -758,17 +767,18 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
         load_target<kVecOk, kLogits>(a, size_t(row), e, pa, pb);
         double x = 0.0, y = 0.0, w = 0.0;
         const uint32_t bits = grp_overlap<kLogits>(zv, pa, pb, c, rs, ts, x, y, w);
-        dz_group<kVecOk>(zv, bits, e, V, c, rs, c_below, c_above, dz);
+        dz_group<kVecOk, kDbg>(zv, bits, e, V, c, rs, c_below, c_above, dz,
+                               kDbg ? a.dz32 + size_t(row) * V : nullptr);
       }
     }
     __syncthreads();
   }
 }
 
-template <bool kVecOk, bool kLogits>
+template <bool kVecOk, bool kLogits, bool kDbg>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 loss_halves(Args a) {
-  half_body<kVecOk, kLogits>(a);
+  half_body<kVecOk, kLogits, kDbg>(a);
 }
 
 __device__ __forceinline__ int block_min(int v, Shared& sh) {
@@ -787,7 +797,7 @@ __device__ __forceinline__ int block_min(int v, Shared& sh) {
 // up to 32 rows per thread are read at once, so the usual case (no flag) costs
 // one round of loads. (2) The loss is the mean of the branch losses, summed
 // in a fixed order. (3) The call epoch advances.
-template <bool kVecOk, bool kLogits>
+template <bool kVecOk, bool kLogits, bool kDbg>
 __global__ __launch_bounds__(kThreads) void loss_finish(Args a) {
   __shared__ Shared sh;
   __shared__ uint32_t bw[LVTV_MAX_W * 2 * kSlotWords];  // a branch's words
@@ -805,7 +815,7 @@ __global__ __launch_bounds__(kThreads) void loss_finish(Args a) {
       const int cand = mine ? r0 + int(threadIdx.x) + __builtin_ctz(mine) * kThreads : INT_MAX;
       const int row = block_min(cand, sh);
       if (cand == row) mine &= mine - 1u;
-      repair_row<kVecOk, kLogits>(a, row, tag, sh, bw);
+      repair_row<kVecOk, kLogits, kDbg>(a, row, tag, sh, bw);
     }
   }
   const int per = (a.N + kThreads - 1) / kThreads;
@@ -844,6 +854,37 @@ Layout make_layout(int N, int W) {
   return L;
 }
 
+// Zeroes the call's tagged words and row flags (16-byte stores; the region
+// is a multiple of 256 bytes), so that nothing a workspace held before the
+// call (an earlier call of either op, or garbage) can read as fresh: a zero
+// word never carries a tag.
+__global__ __launch_bounds__(256) void clear_words(u32x4* w, size_t n16) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    w[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+template <bool kDbg>
+hipError_t launch_all(const Args& a, bool vec_ok, bool logits, unsigned rows, size_t clear_bytes,
+                      void* clear_base, hipStream_t stream) {
+  const size_t n16 = clear_bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(clear_words, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     static_cast<u32x4*>(clear_base), n16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  auto halves = vec_ok ? (logits ? loss_halves<true, true, kDbg> : loss_halves<true, false, kDbg>)
+                       : (logits ? loss_halves<false, true, kDbg> : loss_halves<false, false, kDbg>);
+  auto finish = vec_ok ? (logits ? loss_finish<true, true, kDbg> : loss_finish<true, false, kDbg>)
+                       : (logits ? loss_finish<false, true, kDbg> : loss_finish<false, false, kDbg>);
+  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(finish, dim3(1), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool logits_supported() { return true; }
@@ -872,6 +913,7 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   a.spin_limit = c.spin_limit;
   a.alpha = c.alpha;
   a.dz = c.dz;
+  a.dz32 = c.dz32;
   a.loss = c.loss;
   char* ws = static_cast<char*>(workspace);
   a.ctl = workspace_ctl(workspace);
@@ -880,15 +922,10 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   a.branch_loss = reinterpret_cast<double*>(ws + L.off_branch);
   const unsigned rows = unsigned(size_t(c.N) * c.W);
   const bool logits = c.t != nullptr;
-  auto halves = c.vec_ok ? (logits ? loss_halves<true, true> : loss_halves<true, false>)
-                         : (logits ? loss_halves<false, true> : loss_halves<false, false>);
-  auto finish = c.vec_ok ? (logits ? loss_finish<true, true> : loss_finish<true, false>)
-                         : (logits ? loss_finish<false, true> : loss_finish<false, false>);
-  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finish, dim3(1), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  const size_t clear_bytes = L.off_branch - L.off_words;
+  return c.dz32 ? launch_all<true>(a, c.vec_ok, logits, rows, clear_bytes, ws + L.off_words, stream)
+                : launch_all<false>(a, c.vec_ok, logits, rows, clear_bytes, ws + L.off_words,
+                                    stream);
 }
 
 }  // namespace lf

@@ -27,6 +27,7 @@ struct LossCall {
   float* loss;
   float* alpha;
   uint16_t* dz;
+  float* dz32;            // debug: fp32 gradient before rounding, or null
 };
 
 bool applicable(int N, int W, int V);

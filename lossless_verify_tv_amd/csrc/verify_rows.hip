@@ -2054,11 +2054,11 @@ Layout make_layout(size_t rows, int V, bool packed, bool trunc = false) {
 }
 
 bool sizes_ok(int32_t B, int32_t Kmax, int32_t V) {
-  return B >= 1 && B <= 65535 && Kmax >= 0 && Kmax <= LVTV_MAX_K && V >= 1 && V <= LVTV_MAX_V;
+  return B >= 1 && B <= LVTV_MAX_B && Kmax >= 0 && Kmax <= LVTV_MAX_K && V >= 1 && V <= LVTV_MAX_V;
 }
 
 bool packed_sizes_ok(int32_t B, int32_t total_rows, int32_t V) {
-  return B >= 1 && B <= 65535 && total_rows >= B && total_rows <= B * (LVTV_MAX_K + 1) &&
+  return B >= 1 && B <= LVTV_MAX_B && total_rows >= B && total_rows <= B * (LVTV_MAX_K + 1) &&
          V >= 1 && V <= LVTV_MAX_V;
 }
 

@@ -140,6 +140,41 @@ def compare_dlogits(gpu_u16, orc_u16, orc_dz64, q64, p64):
     return int(bad.sum()), int(mid.sum()), int(tie.sum()), first
 
 
+# Bounds on the exemptions, as shares of the elements compared.
+#  * Midpoint: the oracle's fp64 value must lie within MIDPOINT_RTOL of a
+#    rounding midpoint. bf16 midpoints are 2^-7 of a value's binade apart,
+#    so at most 2 * 1.5 * MIDPOINT_RTOL / 2^-7 = 3.84e-3 of uniformly spread
+#    values lie that close; 4e-3 bounds the exempted share.
+#  * Tie: |q - p| <= TIE_RTOL max(q, p). With a draft that is the target plus
+#    Gaussian noise of sigma >= 0.3 (in log space), the density of
+#    log(q / p) is at most about 1.4 near 0, so the share of such elements
+#    is about 2 TIE_RTOL * 1.4 < 3e-6; 1e-5 bounds it.
+#    The same bound holds for every element inside the tie window, whether
+#    or not the GPU's element differs.
+#  * Rows matched on the other tie side: at most one per tie-window element
+#    of the rows compared.
+MIDPOINT_SHARE_MAX = 4e-3
+TIE_SHARE_MAX = 1e-5
+
+
+def check_exemption_bounds(n_mid, n_tie, n_alt_rows, n_window, n_elems, tag=""):
+    """n_window: elements of the compared rows inside the tie window."""
+    assert n_mid <= MIDPOINT_SHARE_MAX * n_elems, (tag, "midpoint exemptions", n_mid, n_elems)
+    cap = max(2, TIE_SHARE_MAX * n_elems)
+    assert n_window <= cap, (tag, "elements in the tie window", n_window, n_elems)
+    assert n_tie <= n_window, (tag, "tie exemptions", n_tie, n_window)
+    assert n_alt_rows <= n_window, (tag, "rows on the other tie side", n_alt_rows, n_window)
+
+
+# Verify: an excused mismatch needs an oracle margin below MARGIN, which a
+# uniform accept or draw variate gives with probability about 2 MARGIN per
+# decision; the GPU's rounding must then also carry it across. At most one
+# excused request per call, or 1e-3 of the stochastic requests, is allowed.
+def check_excused_bound(rep, tag=""):
+    excused = rep["excused_accept"] + rep["excused_draw"]
+    assert excused <= max(1, 1e-3 * rep["stochastic"]), (tag, "excused requests", excused, rep)
+
+
 def rel_close(a, b, rtol):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -152,7 +187,8 @@ def compare_branch(gpu_u16, z_u16, p32, n_branches, grad=None):
     ``grad(z64, p64)`` gives the oracle's fp64 gradient of the branch
     ([W, V]); the default is the E2E-TV loss's (the per-step TV loss passes
     its own). Returns (n_bad, n_midpoint, n_tie, n_rows_on_alternative,
-    first_bad)."""
+    first_bad, n_tie_window), the last the number of elements inside the
+    tie window whether or not they differ."""
     from oracle import bf16 as obf16
     from oracle import loss as ol
 
@@ -198,7 +234,7 @@ def _compare_tv_rows(gpu_u16, z64, p64, grad):
         alt_rows += ci > 0
         if first is None and fb is not None:
             first = (k, fb)
-    return tot_bad, tot_mid, tot_tie, alt_rows, first
+    return tot_bad, tot_mid, tot_tie, alt_rows, first, int(tie.sum())
 
 
 XENT_QTOL = 4e-6
@@ -269,5 +305,5 @@ def compare_branch_logits(gpu_u16, z_u16, t_u16, temperature, n_branches, object
 
     def grad(zz, pp):
         return inv * ob.branch(zz, pp, n_branches, objective)[2]
-    bad, mid, tie, _, first = _compare_tv_rows(gpu_u16, s_z, p64, grad)
+    bad, mid, tie, _, first, _ = _compare_tv_rows(gpu_u16, s_z, p64, grad)
     return bad, mid + tie, first

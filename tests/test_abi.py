@@ -40,7 +40,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_strerror(lib):
     assert lib.lvtv_version() >= 1
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert lv.strerror(code)
     assert "unknown" in lv.strerror(-99)
 
@@ -131,6 +131,31 @@ def test_draft_loss_logits_host_errors(lib):
     assert call(dz=NULL) == -1
     assert call(wsb=need - 1) == -4
     assert call(ws=ctypes.c_void_p(0x1010)) == -4
+
+
+def test_debug_loss_host_errors(lib):
+    need = lv.draft_loss_workspace_bytes(4, 3, 100)
+    call = lambda **kw: lib.lvtv_debug_draft_loss(*{**dict(
+        z=FAKE, p=FAKE, t=NULL, T=1.0, N=4, W=3, V=100, obj=0, path=0, spin=0, loss=FAKE,
+        alpha=FAKE, dz=FAKE, dz32=NULL, ws=FAKE, wsb=need, stream=NULL), **kw}.values())
+    assert call(path=1) == -8
+    assert call(path=7) == -8
+    assert call(p=NULL) == -1              # neither target
+    assert call(t=FAKE) == -1              # both targets
+    assert call(p=NULL, t=FAKE, T=0.0) == -7
+    assert call(obj=9) == -6
+    assert call(N=0) == -2
+    assert call(N=65536) == -2
+    assert call(wsb=need - 1) == -4
+
+
+def test_size_limits(lib):
+    # B and N are limited to LVTV_MAX_B / LVTV_MAX_N = 65535
+    assert lv.spec_verify_workspace_bytes(65535, 1, 8, 1) > 0
+    assert lv.spec_verify_workspace_bytes(65536, 1, 8, 1) == 0
+    assert lv.spec_verify_packed_workspace_bytes(65536, 65536, 8, 1) == 0
+    assert lv.e2e_tv_loss_workspace_bytes(65535, 1, 8) > 0
+    assert lv.e2e_tv_loss_workspace_bytes(65536, 1, 8) == 0
 
 
 def test_packed_verify_host_errors(lib):

@@ -1,8 +1,9 @@
 """GPU parity of draft_loss_fwd_bwd (the E2E-TV loss and its per-position
 comparators: per-step TV, CE, KL) against the oracle, through the C ABI.
 
-Small and ragged shapes are compared element by element, the full workload
-(N=512, W=7, V=151936) on sampled branches. The per-step TV loss runs on the
+Small and ragged shapes are compared element by element. At the full
+workload (N=512, W=7, V=151936) the loss and every alpha are compared with
+the oracle run over all 512 branches, the gradient on 32 branches. The per-step TV loss runs on the
 single-read kernel (and, forced, on the multi-pass pipeline); CE and KL on
 the multi-pass pipeline. Gradient rules: tests/parity.py."""
 
@@ -13,8 +14,10 @@ from lossless_verify_tv_amd import synth
 from oracle import bf16 as obf16
 from oracle import objectives as ob
 
-from .gpu_util import announce, run_draft_loss, run_loss
-from .parity import (ALPHA_RTOL, LOSS_RTOL, compare_branch, compare_xent_branch,
+from .gpu_util import (announce, full_loss_case, oracle_loss_all, run_debug_loss,
+                       run_draft_loss, run_loss)
+from .parity import (ALPHA_RTOL, LOSS_RTOL, check_exemption_bounds, compare_branch,
+                     compare_xent_branch,
                      rel_close)
 
 pytestmark = pytest.mark.gpu
@@ -22,25 +25,40 @@ pytestmark = pytest.mark.gpu
 COMPARATORS = ("step_tv", "ce", "kl")
 
 
+# CE and KL: gradient elements that differ from the oracle's rounding but lie
+# within the cancellation bound of compare_xent_branch. The bound is absolute
+# (4e-6 (q sum p + p) / N) on a value q sum p - p that cancels where q is
+# close to p, so its relative width is not small for those elements; this
+# caps their share.
+XENT_WITHIN_SHARE_MAX = 5e-2
+
+
 def _check_branches(gpu, z, p, objective, branches, tag):
     N = z.shape[0]
-    tot = np.zeros(3, dtype=np.int64)
+    tot = np.zeros(5, dtype=np.int64)
     for n in branches:
         if objective in ("ce", "kl"):
             bad, within, first = compare_xent_branch(gpu["dlogits"][n], z[n], p[n], N, objective)
-            tot += (bad, within, 0)
+            tot += (bad, within, 0, 0, 0)
         else:
-            bad, mid, tie, alt, first = compare_branch(
+            bad, mid, tie, alt, first, window = compare_branch(
                 gpu["dlogits"][n], z[n], p[n], N,
                 grad=lambda zz, pp: ob.branch(zz, pp, N, objective)[2])
-            tot += (bad, mid, tie)
+            tot += (bad, mid, tie, alt, window)
         assert bad == 0, (tag, n, first)
-    announce(f"{tag}: bad {tot[0]}, excused (midpoint or bound) {tot[1]}, ties {tot[2]}")
+    elems = len(branches) * z.shape[1] * z.shape[2]
+    announce(f"{tag}: bad {tot[0]}, excused (midpoint or bound) {tot[1]}, ties {tot[2]}, "
+             f"rows on the other tie side {tot[3]}, tie-window elements {tot[4]} of {elems}")
+    if objective in ("ce", "kl"):
+        assert tot[1] <= XENT_WITHIN_SHARE_MAX * elems, (tag, tot[1], elems)
+    else:
+        check_exemption_bounds(tot[1], tot[2], tot[3], tot[4], elems, tag)
 
 
-def _check_small(z, p, objective, tag):
+def _check_small(z, p, objective, tag, path=None):
     announce(f"{tag} shape={z.shape}")
-    gpu = run_draft_loss(z, p, objective)
+    gpu = (run_draft_loss(z, p, objective) if path is None else
+           run_debug_loss(z, p, objective, path=path))
     orc = ob.draft_loss(z, p, objective)
     assert rel_close(gpu["loss"], orc["loss"], LOSS_RTOL), (gpu["loss"], orc["loss"])
     assert np.all(rel_close(gpu["alpha"], orc["alpha"], ALPHA_RTOL))
@@ -55,20 +73,19 @@ def test_comparators_shrunk(objective, vocab):
     _check_small(c.draft_logits, c.target_probs, objective, f"{objective} N=5 W=7 V={vocab}")
 
 
-def test_step_tv_on_both_paths(monkeypatch):
+def test_step_tv_on_both_paths():
     c = synth.loss_case(n_branches=4, width=5, vocab=24000)
     fused = _check_small(c.draft_logits, c.target_probs, "step_tv", "step_tv single-read")
-    monkeypatch.setenv("LVTV_LOSS_PATH", "multi-pass")
-    multi = _check_small(c.draft_logits, c.target_probs, "step_tv", "step_tv multi-pass")
+    multi = _check_small(c.draft_logits, c.target_probs, "step_tv", "step_tv multi-pass",
+                         path="multi-pass")
     assert rel_close(fused["loss"], multi["loss"], 1e-6)
 
 
-def test_step_tv_forced_repair_is_bit_identical(monkeypatch):
+def test_step_tv_forced_repair_is_bit_identical():
     c = synth.loss_case(n_branches=3, width=7, vocab=30000)
     normal = run_draft_loss(c.draft_logits, c.target_probs, "step_tv")
-    monkeypatch.setenv("LVTV_SPIN_LIMIT", "0")
     announce("step_tv forced repair")
-    forced = run_draft_loss(c.draft_logits, c.target_probs, "step_tv")
+    forced = run_debug_loss(c.draft_logits, c.target_probs, "step_tv", spin_limit=0)
     assert normal["loss"] == forced["loss"]
     assert np.array_equal(normal["alpha"], forced["alpha"])
     assert np.array_equal(normal["dlogits"], forced["dlogits"])
@@ -95,28 +112,16 @@ def test_ce_and_kl_differ_by_the_entropy_of_p():
     assert kl["loss"] - ce["loss"] == pytest.approx(plogp, rel=1e-4, abs=1e-5)
 
 
-@pytest.fixture(scope="module")
-def full_case():
-    return synth.loss_case(workers=16)
-
-
 @pytest.mark.parametrize("objective", COMPARATORS)
-def test_comparators_full_workload_sampled(objective, full_case):
-    c = full_case
+def test_comparators_full_workload_against_the_oracle(objective):
+    c = full_loss_case()
     announce(f"{objective} full workload")
     gpu = run_draft_loss(c.draft_logits, c.target_probs, objective)
     N = c.draft_logits.shape[0]
-    sample = (0, 1, 257, N - 1)
-    for n in sample:
-        l_n, alpha, _ = ob.branch(obf16.decode(c.draft_logits[n]), c.target_probs[n], N,
-                                  objective)
-        assert np.all(rel_close(gpu["alpha"][n], alpha, ALPHA_RTOL))
+    loss_o, alpha_o = oracle_loss_all(c.draft_logits, c.target_probs, objective)
+    assert rel_close(gpu["loss"], loss_o, LOSS_RTOL), (objective, gpu["loss"], loss_o)
+    assert np.all(rel_close(gpu["alpha"], alpha_o, ALPHA_RTOL)), objective
+    announce(f"{objective} full workload: loss {gpu['loss']!r} vs {loss_o!r}")
+    sample = list(range(0, N, 16))
     _check_branches(gpu, c.draft_logits, c.target_probs, objective, sample,
-                    f"{objective} full, branches {sample}")
-    # the loss: every branch's value from the oracle would take minutes;
-    # per-step TV follows from the returned alphas exactly
-    if objective == "step_tv":
-        expect = float(np.sum(1.0 - gpu["alpha"].astype(np.float64)) / N)
-        assert rel_close(gpu["loss"], expect, 1e-5)
-    # CE >= 0 (q <= 1) and KL >= 0 (Gibbs)
-    assert np.isfinite(gpu["loss"]) and gpu["loss"] >= 0.0
+                    f"{objective} full, 32 branches")

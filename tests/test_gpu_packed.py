@@ -13,7 +13,7 @@ from lossless_verify_tv_amd import synth
 
 from .gpu_util import announce, device, logits_to_device, run_oracle_verify, run_verify, \
     verify_inputs
-from .parity import compare_verify
+from .parity import check_excused_bound, compare_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +67,7 @@ def test_packed_against_oracle():
         gpu = _unpack(case, acc, toks, alpha, status, off)
         rep = compare_verify(gpu, run_oracle_verify(case), case.k, case.shape[1])
         assert not rep["failures"], (tag, rep["failures"][:5])
+        check_excused_bound(rep, tag)
 
 
 @pytest.mark.parametrize("which", ["workload5_full", "workload3_T0.6"])

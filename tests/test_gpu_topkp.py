@@ -28,7 +28,7 @@ from lossless_verify_tv_amd import synth
 from oracle import verify as ov
 
 from .gpu_util import announce, device, run_verify, verify_inputs
-from .parity import compare_verify
+from .parity import check_excused_bound, compare_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +92,11 @@ def _compare(case, gpu, top_k, top_p, tag, requests=None):
              f"{rep['greedy']} greedy, {rep['faulted']} faulted, truncation near-ties "
              f"excused {excused}, accept {rep['excused_accept']}, draw {rep['excused_draw']}")
     assert not rep["failures"], (tag, [(sel[i], why) for i, why in rep["failures"][:5]])
+    check_excused_bound(rep, tag)
+    # a top-p decision within TRUNC_MARGIN of the kept total: about
+    # 2 TRUNC_MARGIN per truncated row, so at most one such request per call
+    # (or 1e-3 of them)
+    assert excused <= max(1, 1e-3 * len(requests)), (tag, "truncation near-ties", excused)
     return rep, excused
 
 

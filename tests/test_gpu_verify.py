@@ -16,7 +16,7 @@ import lossless_verify_tv_amd as lv
 from lossless_verify_tv_amd import synth
 
 from .gpu_util import announce, device, run_oracle_verify, run_verify, verify_inputs
-from .parity import compare_verify
+from .parity import check_excused_bound, compare_verify
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,7 @@ def _check(case, tag):
              f"{rep['greedy']} greedy, {rep['faulted']} faulted, excused accept "
              f"{rep['excused_accept']}, excused draw {rep['excused_draw']}")
     assert not rep["failures"], rep["failures"][:5]
+    check_excused_bound(rep, tag)
     return rep
 
 
@@ -173,8 +174,7 @@ def test_emitted_law_chi_square_on_gpu():
     announce("chi-square B=30000 V=12")
     gpu = run_verify(case)
     bad = np.flatnonzero(gpu["status"])
-    assert bad.size == 0, (bad.size, bad[:10], np.unique(gpu["status"])[:10],
-                           _cached_workspace_counters())
+    assert bad.size == 0, (bad.size, bad[:10], np.unique(gpu["status"])[:10])
     j, tok = gpu["accepted_len"], gpu["tokens"]
     first = np.bincount(tok[:, 0], minlength=V)
     assert chisquare(first, p[0] * B).pvalue > 1e-3
@@ -270,3 +270,4 @@ def test_workspace_reuse_across_shapes():
                    "alpha": alpha.cpu().numpy(), "status": status.cpu().numpy()}
             rep = compare_verify(gpu, run_oracle_verify(case), case.k, case.shape[1])
             assert not rep["failures"], (rnd, i, rep["failures"][:5])
+            check_excused_bound(rep, f"reuse {rnd} {i}")

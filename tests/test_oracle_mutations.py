@@ -20,6 +20,7 @@ import oracle.verify
 from . import test_oracle_bf16 as t_bf16
 from . import test_oracle_loss as t_loss
 from . import test_oracle_loss_logits as t_logits
+from . import test_oracle_margins as t_margin
 from . import test_oracle_objectives as t_obj
 from . import test_oracle_philox as t_philox
 from . import test_oracle_schedule as t_sched
@@ -143,6 +144,31 @@ CASES = [
     ("uniform from the low bits", oracle.philox,
      "float(int(word) >> 40)", "float(int(word) & 0xFFFFFF)",
      t_philox, "philox", "test_uniforms_are_top_24_bits", ()),
+    ("draw margin not normalised by the total", oracle.verify,
+     "margin = min(float(target) - below, c[v] - float(target)) / total",
+     "margin = min(float(target) - below, c[v] - float(target))",
+     t_margin, "ov", "test_draw_margin_exact", (0.5, 1, 0.25)),
+    ("draw margin measured from the wrong lower bound", oracle.verify,
+     "below = c[v - 1] if v > 0 else 0.0", "below = c[v - 2] if v > 1 else 0.0",
+     t_margin, "ov", "test_draw_margin_exact", (0.75 + 2.0 ** -12, 2, 2.0 ** -12)),
+    ("accept margin measured against p(y) instead of p/q", oracle.verify,
+     "return bool(u < r), abs(u - r)", "return bool(u < r), abs(u - p_y)",
+     t_margin, "ov", "test_accept_margin_exact", (0.25, 0.5, 0.5 - 3 * 2.0 ** -24, True,
+                                                   3 * 2.0 ** -24)),
+    ("top-p margin not normalised", oracle.truncate,
+     "margin = min(abs(c[n - 1] - target), abs(target - below)) / c[-1]",
+     "margin = min(abs(c[n - 1] - target), abs(target - below))",
+     t_margin, "ot", "test_top_p_margin_exact", (0.5 + 2.0 ** -6, 3, 2.0 ** -6)),
+    ("top-p margin normalised by the whole row", oracle.truncate,
+     "margin = min(abs(c[n - 1] - target), abs(target - below)) / c[-1]",
+     "margin = min(abs(c[n - 1] - target), abs(target - below)) / np.sum(np.exp(s - np.max(s)))",
+     t_margin, "ot", "test_top_p_margin_is_normalised_by_the_top_k_total", ()),
+    ("top-p margin taken one token late", oracle.truncate,
+     "below = c[n - 2] if n >= 2 else 0.0", "below = c[n - 1]",
+     t_margin, "ot", "test_top_p_margin_exact", (0.5 + 2.0 ** -6, 3, 2.0 ** -6)),
+    ("schedule lets a NaN throughput win", oracle.schedule,
+     "theta = np.where(np.isnan(theta), -np.inf, theta)", "pass",
+     t_margin, "osch", "test_schedule_never_picks_a_nan_throughput", ()),
     ("bf16 ties rounded away from zero", oracle.bf16,
      "np.rint(scaled)", "np.floor(scaled + 0.5)",
      t_bf16, "bf16", "test_ties_round_to_even", ()),
