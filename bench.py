@@ -14,6 +14,14 @@ last-level cache by the previous one.
 Prints one JSON line: the metric (verified vocab-rows/s over the step), the
 roofline of the dominant kernel (the loss), timed live with HIP events on
 the stream the kernels run on, and the CPU oracle timed on a bounded sample.
+
+Per-call times (the step's components, the variants, the small workloads)
+are medians over many calls, each call bracketed by its own pair of events
+with a 1 GiB write between calls outside the brackets, so that no call is
+served from the 256 MB last-level cache by the one before it.
+
+``python bench.py --trace-summary <kernel_trace.csv>`` prints per-kernel
+launch statistics from a rocprofv3 kernel trace (no GPU needed).
 """
 
 from __future__ import annotations
@@ -54,49 +62,155 @@ def loss_bytes(n, w, vocab):
     return 8 * n * w * vocab
 
 
-def cpu_baseline(verify_cases, loss_case, verify_passes=2, n_branches=LOSS_N):
-    """Time the fp64 oracle, as it stands, on a bounded sample of the same
-    workload (10-15 s of CPU work on the GPU host): every request of each
-    temperature's verify inputs, `verify_passes` times, and the first
-    `n_branches` branches of the loss inputs. Single process, one thread
-    (numpy elementwise work is single-threaded)."""
+_POOL = {}
+
+
+def _verify_task(task):
+    """Worker: the oracle on requests [b0, b1) of verify case ci."""
+    from oracle import verify as ov
+    ci, b0, b1 = task
+    case = _POOL["vcases"][ci]
+    out = []
+    for b in range(b0, b1):
+        r = ov.verify_request(ov.decode_rows(case.target[b], case.dtype),
+                              ov.decode_rows(case.draft[b], case.dtype), case.tokens[b],
+                              case.k[b], case.temperature[b], int(case.seed[b]), b,
+                              case.shape[1])
+        out.append((ci, b, r["accepted_len"], r["tokens"], r["accept_margin"],
+                    r["draw_margin"], r["greedy"]))
+    return out
+
+
+def _loss_task(task):
+    """Worker: the oracle on loss branches [n0, n1)."""
+    from oracle import bf16 as obf16
+    from oracle import loss as ol
+    n0, n1 = task
+    lc = _POOL["lcase"]
+    for n in range(n0, n1):
+        ol.branch(obf16.decode(lc.draft_logits[n]), lc.target_probs[n], LOSS_N)
+    return n1 - n0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(verify_cases, loss_case, gpu_verify, workers):
+    """Time the fp64 oracle, as it stands, on the step's own inputs (every
+    request of each temperature's verify call and every branch of the loss
+    call, about 30 s of single-thread work), in two ways: one process with
+    one thread, and a pool of `workers` processes over requests and branches
+    (the arrays reach the workers by fork). The headline value is the pool's
+    (every core the host gives); the single-thread rate is reported beside
+    it. The pool's verify results are also compared with the GPU outputs of
+    the same calls: differing requests whose oracle decision margin is below
+    1e-6 are counted as excused, any other difference as a mismatch."""
+    from concurrent.futures import ProcessPoolExecutor
+
     sys.path.insert(0, ROOT)
     from oracle import bf16 as obf16
     from oracle import loss as ol
     from oracle import verify as ov
 
-    rows_v = 0
+    rows_v = sum(int(k) + 1 for c in verify_cases for k in c.k)
+    rows_l = LOSS_N * LOSS_W
+    # one process, one thread
     t0 = time.perf_counter()
-    for _ in range(verify_passes):
-        for case in verify_cases:
-            for b in range(case.shape[0]):
-                ov.verify_request(ov.decode_rows(case.target[b], case.dtype),
-                                  ov.decode_rows(case.draft[b], case.dtype), case.tokens[b],
-                                  case.k[b], case.temperature[b], int(case.seed[b]), b,
-                                  case.shape[1])
-                rows_v += int(case.k[b]) + 1
-    t_v = time.perf_counter() - t0
+    for case in verify_cases:
+        for b in range(case.shape[0]):
+            ov.verify_request(ov.decode_rows(case.target[b], case.dtype),
+                              ov.decode_rows(case.draft[b], case.dtype), case.tokens[b],
+                              case.k[b], case.temperature[b], int(case.seed[b]), b,
+                              case.shape[1])
+    t_v1 = time.perf_counter() - t0
     t0 = time.perf_counter()
-    for n in range(n_branches):
+    for n in range(LOSS_N):
         ol.branch(obf16.decode(loss_case.draft_logits[n]), loss_case.target_probs[n], LOSS_N)
-    t_l = time.perf_counter() - t0
-    rows_l = n_branches * LOSS_W
-    step_rows_v = len(verify_cases) * VERIFY_B * (VERIFY_K + 1)
-    step_rows_l = LOSS_N * LOSS_W
-    step_seconds = step_rows_v * t_v / rows_v + step_rows_l * t_l / rows_l
+    t_l1 = time.perf_counter() - t0
+    # a pool of processes
+    _POOL["vcases"], _POOL["lcase"] = verify_cases, loss_case
+    try:
+        with ProcessPoolExecutor(max_workers=workers) as pool:
+            t0 = time.perf_counter()
+            vres = [r for part in pool.map(
+                _verify_task, [(ci, b, b + 1) for ci, c in enumerate(verify_cases)
+                               for b in range(c.shape[0])]) for r in part]
+            t_vp = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            done = sum(pool.map(_loss_task, [(n, min(LOSS_N, n + 4))
+                                             for n in range(0, LOSS_N, 4)]))
+            t_lp = time.perf_counter() - t0
+    finally:
+        _POOL.clear()
+    assert done == LOSS_N
+    # parity of the step's verify outputs against the pool's oracle results
+    par = {"requests": 0, "identical": 0, "excused_accept": 0, "excused_draw": 0,
+           "mismatched": 0}
+    for ci, b, j_o, t_o, am, dm, greedy in vres:
+        acc, toks = gpu_verify[ci]
+        j_g, t_g = int(acc[b]), np.asarray(toks[b])
+        par["requests"] += 1
+        if j_g == j_o and np.array_equal(t_g, t_o):
+            par["identical"] += 1
+        elif not greedy and j_g != j_o and 0 <= min(j_g, j_o) < len(am) \
+                and am[min(j_g, j_o)] < 1e-6:
+            par["excused_accept"] += 1
+        elif not greedy and j_g == j_o and dm < 1e-6:
+            par["excused_draw"] += 1
+        else:
+            par["mismatched"] += 1
+
+    def rate(tv, tl):
+        step_rows_v = len(verify_cases) * VERIFY_B * (VERIFY_K + 1)
+        return (step_rows_v + rows_l) / (step_rows_v * tv / rows_v + rows_l * tl / rows_l)
+
     return {
-        "value": (step_rows_v + step_rows_l) / step_seconds,
+        "value": rate(t_vp, t_lp),
         "unit": "vocab-rows/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"{verify_passes} passes over all requests x {len(verify_cases)} "
-                   f"temperatures of the verify workload ({rows_v} vocab-rows, {t_v:.1f} s) "
-                   f"and {n_branches} branches of the loss workload ({rows_l} vocab-rows, "
-                   f"{t_l:.1f} s), fp64 numpy, one process; scaled to the step's row mix"),
-        "verify_rows_per_s": rows_v / t_v,
-        "loss_rows_per_s": rows_l / t_l,
+        "sample": (f"the step's own inputs: every request of the {len(verify_cases)} verify "
+                   f"calls ({rows_v} vocab-rows) and all {LOSS_N} loss branches ({rows_l} "
+                   f"vocab-rows), fp64 numpy; a pool of {workers} processes took "
+                   f"{t_vp:.1f} s + {t_lp:.1f} s, one process {t_v1:.1f} s + {t_l1:.1f} s; "
+                   f"scaled to the step's row mix"),
+        "single_thread_value": rate(t_v1, t_l1),
+        "verify_rows_per_s": rows_v / t_vp,
+        "loss_rows_per_s": rows_l / t_lp,
+        "cpu_model": _cpu_model(),
         "host_cpus": os.cpu_count(),
+        "numpy": np.__version__,
+        "verify_parity": par,
     }
+
+
+def trace_summary(path):
+    """Per-kernel launch statistics from a rocprofv3 kernel-trace CSV: calls,
+    mean, median, min and max duration in microseconds, and the mean over
+    the last half of the launches (after any warm-up)."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name")
+            t0 = int(r.get("Start_Timestamp") or r.get("BeginNs"))
+            t1 = int(r.get("End_Timestamp") or r.get("EndNs"))
+            rows.setdefault(name, []).append((t0, (t1 - t0) * 1e-3))
+    print("| kernel | calls | mean µs | median µs | min µs | max µs | mean of last half µs |")
+    print("|---|---|---|---|---|---|---|")
+    for name, v in sorted(rows.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        d = np.array([x for _, x in sorted(v)])
+        short = name if len(name) < 90 else name[:87] + "..."
+        print(f"| {short} | {d.size} | {d.mean():.1f} | {np.median(d):.1f} | {d.min():.1f} | "
+              f"{d.max():.1f} | {d[d.size // 2:].mean():.1f} |")
 
 
 def load_traffic(src_hash):
@@ -122,7 +236,14 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three plain 1 GiB device-to-device copies, whose HBM "
                          "bytes are known, so a counter profile of this run can be scaled")
+    ap.add_argument("--calls", type=int, default=100,
+                    help="calls per median for the per-call times (loss calls: a third)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-kernel statistics of a rocprofv3 kernel trace and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this hot path has no "
               "multi-GPU leg to measure", file=sys.stderr)
@@ -182,27 +303,17 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(events=None):
+    def step():
         for i in range(len(TEMPS)):
-            if events is not None:
-                events[2 * i].record(stream)
             lv.spec_verify(**vin[i], workspace=vws, out=vouts[i])
-            if events is not None:
-                events[2 * i + 1].record(stream)
-        if events is not None:
-            events[6].record(stream)
         lv.e2e_tv_loss_fwd_bwd(z, p, workspace=lws, out=lout)
-        if events is not None:
-            events[7].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # The timed region holds the K steps and nothing else: an event recorded
-    # between two calls costs the stream several microseconds, so the
-    # per-call breakdown comes from a second, separate run of K steps.
+    # The timed region holds the K steps and nothing else.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -215,15 +326,39 @@ def main():
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
-    per_step = [[torch.cuda.Event(enable_timing=True) for _ in range(8)]
-                for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(per_step[s])
-    torch.cuda.synchronize()
-    verify_ms = [np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for ev in per_step])
-                 for i in range(len(TEMPS))]
-    loss_ms = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in per_step]))
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.2f} s)")
+    gpu_verify = [(o[0].cpu().numpy(), o[1].cpu().numpy()) for o in vouts]
+
+    # Per-call times: each call between its own two events, a 1 GiB write
+    # between calls (outside the events) so that nothing a call reads is
+    # left in the last-level cache by the previous one; medians over calls.
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def per_call(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for e0, e1 in evs:
+            flush_buf.fill_(1.0)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+        return {"ms": float(np.median(ms)), "ms_mean": float(ms.mean()),
+                "ms_min": float(ms.min()), "calls": n}
+
+    n_v = max(args.calls, 1)
+    n_l = max(args.calls // 3, 1)
+    verify_t = [per_call(lambda i=i: lv.spec_verify(**vin[i], workspace=vws, out=vouts[i]), n_v)
+                for i in range(len(TEMPS))]
+    loss_t = per_call(lambda: lv.e2e_tv_loss_fwd_bwd(z, p, workspace=lws, out=lout), n_l)
+    verify_ms = [t["ms"] for t in verify_t]
+    loss_ms = loss_t["ms"]
+    log("per-call medians: " + ", ".join(f"verify T={t} {m * 1e3:.1f} us"
+                                          for t, m in zip(TEMPS, verify_ms)) +
+        f", loss {loss_ms:.3f} ms")
 
     rows_step = len(TEMPS) * sum(int(k) + 1 for k in base.k) + LOSS_N * LOSS_W
     vb = verify_bytes(base.k, VOCAB)
@@ -253,8 +388,12 @@ def main():
             "algorithmic_bytes_per_step": len(TEMPS) * vb + lb,
         },
         "achieved_hbm_gbs": (len(TEMPS) * vb + lb) / (ms_step * 1e-3) / 1e9,
+        "timing": (f"value and ms_per_step: {args.steps} back-to-back steps between two events; "
+                   f"per-call ms: median of {n_v} calls ({n_l} for the loss) each between its "
+                   f"own two events, a 1 GiB write between calls outside them"),
         "roofline": {
-            "kernel": "loss_halves (e2e_tv_loss_fwd_bwd)",
+            "kernel": "loss_halves (timed as the whole e2e_tv_loss_fwd_bwd call: clear_words "
+                      "+ loss_halves + loss_finish)",
             "bound": "hbm",
             "achieved": loss_gbs,
             "peak": HBM_PEAK_GBS,
@@ -264,7 +403,7 @@ def main():
         },
         "components": {
             f"spec_verify_T{t}": {
-                "ms": verify_ms[i],
+                **verify_t[i],
                 "rows_per_s": VERIFY_B * (VERIFY_K + 1) / (verify_ms[i] * 1e-3),
                 "gbs": vb / (verify_ms[i] * 1e-3) / 1e9,
                 "frac": vb / (verify_ms[i] * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -275,24 +414,17 @@ def main():
         "kernel_source_hash": src_hash,
     }
     result["components"]["e2e_tv_loss_fwd_bwd"] = {
-        "ms": loss_ms, "rows_per_s": LOSS_N * LOSS_W / (loss_ms * 1e-3), "gbs": loss_gbs,
+        **loss_t, "rows_per_s": LOSS_N * LOSS_W / (loss_ms * 1e-3), "gbs": loss_gbs,
         "frac": loss_gbs / HBM_PEAK_GBS, "algorithmic_bytes": lb}
     # The per-position comparators of the loss on the same inputs, outside
-    # the step: each timed over as many calls as the step count.
+    # the step.
     variants = {}
     for name in ("step_tv", "ce", "kl"):
-        lv.draft_loss_fwd_bwd(z, p, name, workspace=lws, out=lout)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            lv.draft_loss_fwd_bwd(z, p, name, workspace=lws, out=lout)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        t = per_call(lambda: lv.draft_loss_fwd_bwd(z, p, name, workspace=lws, out=lout),
+                     max(n_l // 3, 1))
+        ms = t["ms"]
         variants[f"draft_loss_{name}"] = {
-            "ms": ms, "gbs": lb / (ms * 1e-3) / 1e9,
+            **t, "gbs": lb / (ms * 1e-3) / 1e9,
             "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb}
     # The loss with the target given as bf16 logits (target softmax fused;
     # algorithmic bytes 6 per token: z 2 + t 2 read, dz 2 written).
@@ -301,18 +433,11 @@ def main():
     del lgc
     lb6 = 6 * LOSS_N * LOSS_W * VOCAB
     for name, temp in (("e2e_tv", 1.0), ("e2e_tv", 0.7)):
-        lv.draft_loss_logits_fwd_bwd(z, tl, temp, name, workspace=lws, out=lout)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            lv.draft_loss_logits_fwd_bwd(z, tl, temp, name, workspace=lws, out=lout)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        t = per_call(lambda: lv.draft_loss_logits_fwd_bwd(z, tl, temp, name, workspace=lws,
+                                                          out=lout), max(n_l // 3, 1))
+        ms = t["ms"]
         variants[f"draft_loss_logits_{name}_T{temp}"] = {
-            "ms": ms, "gbs": lb6 / (ms * 1e-3) / 1e9,
+            **t, "gbs": lb6 / (ms * 1e-3) / 1e9,
             "frac": lb6 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb6}
     del tl
     result["loss_variants"] = variants
@@ -324,24 +449,16 @@ def main():
     vvar = {}
 
     def time_calls(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        return per_call(fn, n_v)
 
     tk = torch.full((VERIFY_B,), 50, dtype=torch.int32, device=dev)
     tp = torch.full((VERIFY_B,), 0.9, dtype=torch.float32, device=dev)
     tws = lv.new_workspace(lv.spec_verify_topkp_workspace_bytes(VERIFY_B, VERIFY_K, VOCAB), dev)
-    ms = time_calls(lambda: lv.spec_verify_topkp(**vin[2], top_k=tk, top_p=tp, workspace=tws,
-                                                 out=vouts[2]))
+    t = time_calls(lambda: lv.spec_verify_topkp(**vin[2], top_k=tk, top_p=tp, workspace=tws,
+                                                out=vouts[2]))
+    ms = t["ms"]
     vvar["spec_verify_topkp_T1.0_k50_p0.9"] = {
-        "ms": ms, "rows_per_s": VERIFY_B * (VERIFY_K + 1) / (ms * 1e-3),
+        **t, "rows_per_s": VERIFY_B * (VERIFY_K + 1) / (ms * 1e-3),
         "gbs": vb / (ms * 1e-3) / 1e9, "algorithmic_bytes": vb}
     del tws
     rc = synth.verify_case(5)
@@ -353,9 +470,10 @@ def main():
                k_per_req=torch.from_numpy(rc.k).to(dev),
                temperature=torch.from_numpy(rc.temperature).to(dev),
                seed=torch.from_numpy(rc.seed.view(np.int64)).to(dev))
-    ms = time_calls(lambda: lv.spec_verify(**rin))
+    t = time_calls(lambda: lv.spec_verify(**rin))
+    ms = t["ms"]
     vvar["spec_verify_ragged_padded"] = {
-        "ms": ms, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
+        **t, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
         "algorithmic_bytes": rb, "requests": int(rc.k.size), "rows": rrows, "vocab": rvocab}
     kk = np.asarray(rc.k, dtype=np.int64)
     off = np.zeros(kk.size + 1, dtype=np.int32)
@@ -368,9 +486,10 @@ def main():
     offd = torch.from_numpy(off).to(dev)
     rtemp = torch.from_numpy(rc.temperature).to(dev)
     rseed = torch.from_numpy(rc.seed.view(np.int64)).to(dev)
-    ms = time_calls(lambda: lv.spec_verify_packed(pt, pdr, ptok, offd, rtemp, rseed))
+    t = time_calls(lambda: lv.spec_verify_packed(pt, pdr, ptok, offd, rtemp, rseed))
+    ms = t["ms"]
     vvar["spec_verify_ragged_packed"] = {
-        "ms": ms, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
+        **t, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
         "algorithmic_bytes": rb, "requests": int(rc.k.size), "rows": rrows, "vocab": rvocab}
     del pt, pdr, ptok, rc
     result["verify_variants"] = vvar
@@ -397,9 +516,34 @@ def main():
     result["dspark_schedule"] = {"us": e0.elapsed_time(e1) / reps * 1e3, "requests": sR,
                                  "positions": sL}
     log(f"dspark_schedule R={sR} L={sL}: {result['dspark_schedule']['us']:.1f} us")
+    # The two small workloads (latency-bound; reported as time per call):
+    # B=1 K=4 V=4096 fp32 at T = 1 and T = 0, and B=32 K=4 V=32000 bf16.
+    small = {}
+    for tag, sc in (("B1_K4_V4096_f32_T1.0", synth.verify_case(1, temperature=1.0)),
+                    ("B1_K4_V4096_f32_T0.0", synth.verify_case(1, temperature=0.0)),
+                    ("B32_K4_V32000_bf16_T1.0", synth.verify_case(2))):
+        conv = bf16_dev if sc.dtype == "bf16" else (
+            lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev))
+        sin = dict(target_logits=conv(sc.target), draft_logits=conv(sc.draft),
+                   draft_tokens=torch.from_numpy(sc.tokens).to(dev),
+                   k_per_req=torch.from_numpy(sc.k).to(dev),
+                   temperature=torch.from_numpy(sc.temperature).to(dev),
+                   seed=torch.from_numpy(sc.seed.view(np.int64)).to(dev))
+        t = per_call(lambda: lv.spec_verify(**sin), n_v)
+        sb = verify_bytes(sc.k, sc.shape[2], 2 if sc.dtype == "bf16" else 4)
+        rows = int(sum(int(k) + 1 for k in sc.k))
+        small[tag] = {**t, "us": t["ms"] * 1e3, "rows_per_s": rows / (t["ms"] * 1e-3),
+                      "gbs": sb / (t["ms"] * 1e-3) / 1e9, "algorithmic_bytes": sb}
+    result["small_workloads"] = small
+    log("small workloads: " + ", ".join(f"{k} {v['us']:.1f} us" for k, v in small.items()))
+    del flush_buf
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(vcases, lcase)
+        log("timing the CPU oracle on the step's inputs (one process, then a pool)")
+        result["cpu_baseline"] = cpu_baseline(vcases, lcase, gpu_verify,
+                                              workers=min(16, os.cpu_count() or 1))
+        log(f"cpu baseline {result['cpu_baseline']['value']:.0f} vocab-rows/s on "
+            f"{result['cpu_baseline']['cores']} processes; verify parity "
+            f"{result['cpu_baseline']['verify_parity']}")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
