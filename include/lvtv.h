@@ -58,6 +58,7 @@ extern "C" {
 #define LVTV_ERR_OBJECTIVE (-6) /* unknown loss objective                */
 #define LVTV_ERR_TEMPERATURE (-7) /* loss temperature not finite and > 0 */
 #define LVTV_ERR_OPTION (-8)    /* unknown debug option (lvtv_debug_draft_loss) */
+#define LVTV_ERR_SCRATCH (-9)   /* sizes need more than spec_verify_noalloc's scratch */
 
 /* Objectives of draft_loss_fwd_bwd, each summed over a branch's W positions
  * and averaged over the N branches. */
@@ -152,6 +153,32 @@ int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
                 int32_t Kmax, int32_t V, int32_t* accepted_len,
                 int32_t* out_tokens, float* alpha, int32_t* status,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It takes no workspace: the scratch lives in a static
+ * device array of LVTV_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends. The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine); the first call on a device looks
+ * the array's address up once (hipGetSymbolAddress) with that device current.
+ *
+ * Arguments, results and errors as spec_verify, without workspace and
+ * workspace_bytes; sizes whose spec_verify workspace would exceed the scratch
+ * (spec_verify_workspace_bytes(B, Kmax, V, dtype) > LVTV_NOALLOC_SCRATCH_BYTES)
+ * return LVTV_ERR_SCRATCH before enqueueing anything, and LVTV_ERR_LAUNCH is
+ * also returned if the address lookup fails. Every call on one GPU shares
+ * that GPU's array, which keeps the last call's contents (no call depends on
+ * them): calls that overlap on one GPU (on different streams, or from several
+ * threads without ordering) race and give undefined results; order them on
+ * one stream.
+ */
+#define LVTV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, int dtype,
+                        const int32_t* draft_tokens, const int32_t* k_per_req,
+                        const float* temperature, const uint64_t* seed, int32_t B,
+                        int32_t Kmax, int32_t V, int32_t* accepted_len,
+                        int32_t* out_tokens, float* alpha, int32_t* status, void* stream);
 
 /*
  * Workspace bytes spec_verify_packed needs (0 if out of range). Host only.

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     STATUS_NONFINITE,
     OBJECTIVES,
     LvtvError,
+    NOALLOC_SCRATCH_BYTES,
     PATHS,
     debug_draft_loss,
     draft_loss_fwd_bwd,
@@ -35,6 +36,7 @@ from ._binding import (  # noqa: F401
     load_library,
     new_workspace,
     spec_verify,
+    spec_verify_noalloc,
     spec_verify_packed,
     spec_verify_packed_workspace_bytes,
     spec_verify_topkp,

@@ -45,7 +45,10 @@ EXPORTS = (
     "draft_loss_logits_fwd_bwd",
     "dspark_schedule",
     "lvtv_debug_draft_loss",
+    "spec_verify_noalloc",
 )
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # LVTV_NOALLOC_SCRATCH_BYTES
 
 SCHED_MAX_ITEMS = 8192  # LVTV_SCHED_MAX_ITEMS
 
@@ -112,6 +115,9 @@ def load_library(path: str = LIB_PATH):
                                                   ctypes.c_int, vp, vp, vp, vp, sz, vp]
         lib.dspark_schedule.restype = ctypes.c_int
         lib.dspark_schedule.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+        lib.spec_verify_noalloc.restype = ctypes.c_int
+        lib.spec_verify_noalloc.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, i32, i32, i32,
+                                            vp, vp, vp, vp, vp]
         lib.lvtv_debug_draft_loss.restype = ctypes.c_int
         lib.lvtv_debug_draft_loss.argtypes = [vp, vp, vp, ctypes.c_float, i32, i32, i32,
                                               ctypes.c_int, ctypes.c_int, i32, vp, vp, vp, vp,
@@ -248,6 +254,33 @@ def spec_verify(target_logits, draft_logits, draft_tokens, k_per_req, temperatur
                                    _ptr(status), _ptr(ws), ws.numel(), _stream(dev))
     _check(code, "spec_verify_topkp" if trunc else "spec_verify")
     return acc, toks, alpha, status
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, k_per_req, temperature, seed,
+                        out):
+    """spec_verify through the entry point that allocates nothing (its
+    scratch is the library's static per-GPU array). ``out`` = (accepted_len,
+    out_tokens, alpha, status), preallocated by the caller; tensors as
+    spec_verify. Returns ``out``."""
+    lib = load_library()
+    dev = target_logits.device
+    _require(dev.type == "cuda", "spec_verify_noalloc needs GPU tensors")
+    B, K1, V = target_logits.shape
+    Kmax = K1 - 1
+    _require(tuple(draft_logits.shape) == (B, Kmax, V), "draft_logits must be [B, Kmax, V]")
+    _require(target_logits.dtype == draft_logits.dtype, "target and draft dtypes differ")
+    dtype = _dtype_code(target_logits)
+    acc, toks, alpha, status = out
+    for t in (target_logits, draft_logits, draft_tokens, k_per_req, temperature, seed, acc, toks,
+              alpha, status):
+        _require(t.device == dev and t.is_contiguous(), "tensors must be contiguous on one GPU")
+    with torch.cuda.device(dev):
+        code = lib.spec_verify_noalloc(_ptr(target_logits), _ptr(draft_logits), dtype,
+                                       _ptr(draft_tokens), _ptr(k_per_req), _ptr(temperature),
+                                       _ptr(seed), B, Kmax, V, _ptr(acc), _ptr(toks),
+                                       _ptr(alpha), _ptr(status), _stream(dev))
+    _check(code, "spec_verify_noalloc")
+    return out
 
 
 def spec_verify_topkp_workspace_bytes(B, Kmax, V, dtype=LVTV_BF16) -> int:

@@ -47,6 +47,7 @@ extern "C" const char* lvtv_strerror(int code) {
     case LVTV_ERR_OBJECTIVE: return "unknown loss objective";
     case LVTV_ERR_TEMPERATURE: return "temperature not finite and > 0 (or 1/T overflows)";
     case LVTV_ERR_OPTION: return "unknown debug option";
+    case LVTV_ERR_SCRATCH: return "sizes need more than the no-allocation scratch holds";
     default: return "unknown error code";
   }
 }

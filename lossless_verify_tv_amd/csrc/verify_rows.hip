@@ -37,6 +37,7 @@
 #include <climits>
 #include <cstddef>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/lvtv.h"
 #include "device_common.hpp"
@@ -2178,6 +2179,59 @@ int verify_padded(const void* target_logits, const void* draft_logits, int dtype
 }  // namespace
 }  // namespace vr
 }  // namespace lvtv
+
+// ------------------------------------------------------------------ no-allocation entry
+
+namespace lvtv {
+namespace vr {
+namespace {
+
+// The verify step's scratch for callers that cannot allocate: one array per
+// GPU in the library's own device memory, held until the process ends. Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in): each device's address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+constexpr size_t kNoAllocBytes = LVTV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's scratch address (nullptr on a HIP error).
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+}  // namespace vr
+}  // namespace lvtv
+
+extern "C" int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                                   int dtype, const int32_t* draft_tokens,
+                                   const int32_t* k_per_req, const float* temperature,
+                                   const uint64_t* seed, int32_t B, int32_t Kmax, int32_t V,
+                                   int32_t* accepted_len, int32_t* out_tokens, float* alpha,
+                                   int32_t* status, void* stream) {
+  using namespace lvtv::vr;
+  if (dtype != LVTV_F32 && dtype != LVTV_BF16) return LVTV_ERR_DTYPE;
+  if (!sizes_ok(B, Kmax, V)) return LVTV_ERR_SHAPE;
+  if (make_layout(size_t(B) * (Kmax + 1), V, false).total > kNoAllocBytes)
+    return LVTV_ERR_SCRATCH;
+  void* ws = device_scratch();
+  if (!ws) return LVTV_ERR_LAUNCH;
+  return verify_padded(target_logits, draft_logits, dtype, draft_tokens, k_per_req, temperature,
+                       seed, nullptr, nullptr, B, Kmax, V, accepted_len, out_tokens, alpha,
+                       status, ws, kNoAllocBytes, stream);
+}
 
 extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype) {
   if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
