@@ -93,30 +93,6 @@ __device__ __forceinline__ bool keeps(const KeepRow& k, float s, int v) {
   return d < k.key || (d == k.key && v <= k.idx);
 }
 
-// Records of the single-read (stream) kernel: a sampling row's statistics
-// in the row kernel's convention, and one slice's argmaxes of a greedy row.
-struct RowStat {
-  float Rt, Lt, Rd, Ld;
-};
-struct GArg {
-  float vt;
-  int32_t it;
-  float vd;
-  int32_t id;
-  int32_t nan;  // bit 0: the target slice held a NaN, bit 1: the draft slice
-  int32_t pad[3];
-};
-static_assert(sizeof(GArg) == 32, "slice argmax record is 32 bytes");
-
-// A used target row as the stream kernel reads it (one 16-byte scalar load).
-struct RowRec {
-  int32_t r;     // target row
-  int32_t dr;    // draft row (meaningful when k < K_b)
-  int32_t kind;  // stream item kind (see verify_stream.hpp)
-  float T;       // the request's temperature
-};
-static_assert(sizeof(RowRec) == 16, "row record is 16 bytes");
-
 struct Args {
   const void* target;
   const void* draft;
@@ -149,18 +125,6 @@ struct Args {
   // streams the row). Written by trunc_rows for every row it truncates.
   int32_t* klen;   // [target rows]
   int32_t* klist;  // [target rows][kCand]
-  // Single-read (stream) kernel: rows cut into S slices (stream == 0: the
-  // row kernel ran and `rows` holds the records).
-  int stream;
-  int S;
-  uint64_t* words;       // [target rows][S][4] tagged slice statistics
-  float* apart;          // [target rows][S] the slices' parts of alpha
-  GArg* garg;            // [target rows][S] greedy slices' argmaxes
-  RowStat* rstat;        // [target rows] sampling rows' statistics
-  uint32_t* unfinished;  // [target rows] 1: a slice gave up waiting; the finalize redoes the row
-  RowRec* recs;          // [target rows] the used rows, request by request
-  int32_t* n_used;       // how many
-  int spin_limit;
 };
 
 __device__ __forceinline__ KeepRow keep_all() { return KeepRow{0xffffffffu, INT_MAX, 0.f, 0.f}; }

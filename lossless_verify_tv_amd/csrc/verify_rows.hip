@@ -508,7 +508,6 @@ __global__ __launch_bounds__(kThreads) void verify_rows_f32(Args a) {
 }  // namespace lvtv
 
 #include "verify_trunc.hpp"
-#include "verify_stream.hpp"
 
 namespace lvtv {
 namespace vr {
@@ -688,17 +687,14 @@ __device__ __forceinline__ void write_fault(const Args& a, int b, int status, co
 
 struct FinShared {
   Shared red;
-  StreamShared srd;
   double ratio[LVTV_MAX_K];
   double uacc[LVTV_MAX_K];
   int j;
   RowOut rc[LVTV_MAX_K + 1];  // the request's row records, read once
 };
 
-template <int kDtype, bool kVecOk>
+template <int kDtype>
 __device__ __forceinline__ void finalize_body(const Args& a) {
-  // the stream kernel serves aligned bf16 rows only
-  constexpr bool kStreamed = kDtype == 1 && kVecOk;
   __shared__ FinShared fs;
   Shared& sh = fs.red;
   const int b = blockIdx.x;
@@ -724,25 +720,12 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const bool greedy = (T == 0.f);
   const int32_t* y = a.tokens + draft_row(a, b, 0);
   const RowOut* rows = a.rows + target_row(a, b, 0);
-  const bool unit = (T == 1.f);
-  const float inv_t = __fdiv_rn(1.f, T);
-  if constexpr (kStreamed) {
-    if (a.stream && k_ok && t_ok && !greedy) {
-      // rows a slice left unfinished (it gave up waiting for the others)
-      for (int k = 0; k <= kb; ++k)
-        if (a.unfinished[target_row(a, b, k)]) repair_stream_row(a, b, k, kb, T, fs.srd);
-    }
-  }
   int bad = 0, fault = 0;
   if (k_ok) {
     for (int k = threadIdx.x; k <= kb; k += kThreads) {
       if (k < kb) bad |= (y[k] < 0 || y[k] >= a.V);
       if (!t_ok) continue;
-      RowOut r;
-      if constexpr (kStreamed)
-        r = a.stream ? gather_stream_row(a, b, k, kb, greedy, inv_t, unit) : rows[k];
-      else
-        r = rows[k];
+      const RowOut r = rows[k];
       fs.rc[k] = r;
       if (greedy) {
         fault |= (r.nan & 1) || !isfinite(r.Rt);
@@ -768,19 +751,21 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
     if (threadIdx.x == 0) {
       int j = kb;
       for (int k = 0; k < kb; ++k)
-        if (y[k] != fs.rc[k].arg_t) {
+        if (y[k] != rows[k].arg_t) {
           j = k;
           break;
         }
       for (int k = 0; k < o.nalpha; ++k)
-        out_alpha[k] = (k < kb) ? (fs.rc[k].arg_t == fs.rc[k].arg_d ? 1.f : 0.f) : 0.f;
-      for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? y[k] : (k == j ? fs.rc[j].arg_t : -1);
+        out_alpha[k] = (k < kb) ? (rows[k].arg_t == rows[k].arg_d ? 1.f : 0.f) : 0.f;
+      for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? y[k] : (k == j ? rows[j].arg_t : -1);
       a.acc_len[b] = j;
       a.status[b] = 0;
     }
     return;
   }
 
+  const bool unit = (T == 1.f);
+  const float inv_t = __fdiv_rn(1.f, T);
   // accept inputs for every position in parallel: u_k, and p(y_k)/q(y_k)
   // as the row kernel evaluated it (prob64_of with the row's statistics)
   if (int(threadIdx.x) < kb) {
@@ -857,9 +842,9 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   }
 }
 
-template <int kDtype, bool kVecOk>
+template <int kDtype>
 __global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
-  finalize_body<kDtype, kVecOk>(a);
+  finalize_body<kDtype>(a);
 }
 
 // ------------------------------------------------------------------ host side
@@ -867,24 +852,17 @@ __global__ __launch_bounds__(kThreads) void verify_finalize(Args a) {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-  int n_tiles, NC, S;
-  bool stream;
-  size_t off_rows, off_chunk, off_map, off_keep, off_klen, off_klist;
-  size_t off_words, off_unfin, off_clear_end, off_apart, off_garg, off_rstat, off_list, total;
+  int n_tiles, NC;
+  size_t off_rows, off_chunk, off_map, off_keep, off_klen, off_klist, total;
 };
 
 // `rows` target rows (B (Kmax + 1) padded, total_rows packed); the row map
 // and its validity flag only for the packed layout, the keep records only
-// with truncation, the stream kernel's records when it serves the call
-// (bf16 without truncation, at most kMaxSlices slices per row; the arrays
-// are laid out even if the call then takes the row kernel for unaligned
-// rows).
-Layout make_layout(size_t rows, int V, bool packed, bool trunc, int dtype) {
+// with truncation.
+Layout make_layout(size_t rows, int V, bool packed, bool trunc = false) {
   Layout L;
   L.n_tiles = (V + kTile - 1) / kTile;
   L.NC = L.n_tiles * kWaves;
-  L.S = (L.n_tiles + kSTiles - 1) / kSTiles;
-  L.stream = !trunc && dtype == LVTV_BF16 && L.S <= kMaxSlices;
   size_t off = kReservedBytes;
   L.off_rows = off;
   off = align256(off + sizeof(RowOut) * rows);
@@ -898,35 +876,8 @@ Layout make_layout(size_t rows, int V, bool packed, bool trunc, int dtype) {
   if (trunc) off = align256(off + sizeof(int32_t) * rows);
   L.off_klist = off;
   if (trunc) off = align256(off + sizeof(int32_t) * rows * kCand);
-  L.off_words = off;
-  if (L.stream) off = align256(off + sizeof(uint64_t) * 4 * rows * L.S);
-  L.off_unfin = off;
-  if (L.stream) off = align256(off + sizeof(uint32_t) * rows);
-  L.off_clear_end = off;
-  L.off_apart = off;
-  if (L.stream) off = align256(off + sizeof(float) * rows * L.S);
-  L.off_garg = off;
-  if (L.stream) off = align256(off + sizeof(GArg) * rows * L.S);
-  L.off_rstat = off;
-  if (L.stream) off = align256(off + sizeof(RowStat) * rows);
-  L.off_list = off;
-  if (L.stream) off = align256(off + sizeof(RowRec) * rows + sizeof(int32_t));
   L.total = off;
   return L;
-}
-
-// Points the stream kernel's arrays of `a` into the workspace.
-void set_stream(Args& a, const Layout& L, char* ws) {
-  a.stream = L.stream ? 1 : 0;
-  a.S = L.S;
-  a.words = reinterpret_cast<uint64_t*>(ws + L.off_words);
-  a.unfinished = reinterpret_cast<uint32_t*>(ws + L.off_unfin);
-  a.apart = reinterpret_cast<float*>(ws + L.off_apart);
-  a.garg = reinterpret_cast<GArg*>(ws + L.off_garg);
-  a.rstat = reinterpret_cast<RowStat*>(ws + L.off_rstat);
-  a.recs = reinterpret_cast<RowRec*>(ws + L.off_list);
-  a.n_used = reinterpret_cast<int32_t*>(a.recs + a.total_rows);
-  a.spin_limit = 1 << 16;
 }
 
 bool sizes_ok(int32_t B, int32_t Kmax, int32_t V) {
@@ -960,49 +911,8 @@ __global__ __launch_bounds__(1024) void packed_map(const int32_t* toff, int B, i
   if (threadIdx.x == 0) *ok = good ? 1 : 0;
 }
 
-// Workgroups of the stream kernel that are resident at once on the current
-// device (its grid), looked up once per device.
-int stream_grid() {
-  constexpr int kDevices = 64;
-  static std::mutex mu;
-  static int cache[kDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!cache[dev]) {
-    int nb = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(verify_stream), kSThreads, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cache[dev] = (nb < 1 ? 1 : nb) * cus;
-  }
-  return cache[dev];
-}
-
-// The stream path: the preparation kernel, then the stream kernel on every
-// resident workgroup slot (or one per item if there are fewer items).
-hipError_t launch_stream(const Args& a, hipStream_t stream, size_t clear_bytes) {
-  const size_t n16 = clear_bytes / 16;
-  size_t cb = (n16 + 1023) / 1024;
-  if (cb < 1) cb = 1;
-  if (cb > 256) cb = 256;
-  hipLaunchKernelGGL(stream_prep, dim3(unsigned(cb)), dim3(1024), 0, stream, a,
-                     reinterpret_cast<u32x4*>(a.words), n16);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long n_items = long(a.total_rows) * a.S;  // at most: every row used
-  int g = stream_grid();
-  if (g <= 0) return hipErrorInvalidValue;
-  if (long(g) > n_items) g = int(n_items);
-  hipLaunchKernelGGL(verify_stream, dim3(unsigned(g)), dim3(kSThreads), 0, stream, a);
-  return hipGetLastError();
-}
-
-// Unaligned rows (kVecOk false) and fp32 rows always take the row kernel.
 template <int kDtype, bool kVecOk>
-hipError_t launch(Args a, hipStream_t stream, size_t clear_bytes) {
-  if constexpr (!(kDtype == 1 && kVecOk)) a.stream = 0;
+hipError_t launch(const Args& a, hipStream_t stream) {
   if (a.toff) {
     hipLaunchKernelGGL(packed_map, dim3(1), dim3(1024), 0, stream, a.toff, a.B, a.total_rows,
                        const_cast<int32_t*>(a.rowmap), const_cast<int32_t*>(a.packed_ok));
@@ -1011,17 +921,7 @@ hipError_t launch(Args a, hipStream_t stream, size_t clear_bytes) {
   }
   const unsigned grid =
       a.toff ? unsigned(a.total_rows) : unsigned(a.B) * unsigned(a.Kmax + 1);
-  bool streamed = false;
-  if constexpr (kDtype == 1 && kVecOk) {
-    if (a.stream) {
-      const hipError_t e = launch_stream(a, stream, clear_bytes);
-      if (e != hipSuccess) return e;
-      streamed = true;
-    }
-  }
-  if (streamed) {
-    // the stream kernel's records feed the finalize
-  } else if (a.keep) {
+  if (a.keep) {
     hipLaunchKernelGGL((trunc_rows<kDtype, kVecOk>), dim3(2 * grid), dim3(kThreads), 0, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1039,8 +939,7 @@ hipError_t launch(Args a, hipStream_t stream, size_t clear_bytes) {
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_finalize<kDtype, kVecOk>), dim3(unsigned(a.B)), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL(verify_finalize<kDtype>, dim3(unsigned(a.B)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1060,7 +959,7 @@ int verify_padded(const void* target_logits, const void* draft_logits, int dtype
   if (Kmax > 0 && (!draft_logits || !draft_tokens || !alpha)) return LVTV_ERR_NULL;
   const bool trunc = top_k || top_p;
   if (trunc && !(top_k && top_p)) return LVTV_ERR_NULL;
-  const Layout L = make_layout(size_t(B) * (Kmax + 1), V, false, trunc, dtype);
+  const Layout L = make_layout(size_t(B) * (Kmax + 1), V, false, trunc);
   if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
   Args a;
@@ -1091,17 +990,15 @@ int verify_padded(const void* target_logits, const void* draft_logits, int dtype
   a.keep = trunc ? reinterpret_cast<KeepPair*>(ws + L.off_keep) : nullptr;
   a.klen = trunc ? reinterpret_cast<int32_t*>(ws + L.off_klen) : nullptr;
   a.klist = trunc ? reinterpret_cast<int32_t*>(ws + L.off_klist) : nullptr;
-  set_stream(a, L, ws);
-  const size_t clear = L.off_clear_end - L.off_words;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
                         reinterpret_cast<uintptr_t>(draft_logits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == LVTV_BF16)
-    e = vec_ok ? launch<1, true>(a, s, clear) : launch<1, false>(a, s, clear);
+    e = vec_ok ? launch<1, true>(a, s) : launch<1, false>(a, s);
   else
-    e = vec_ok ? launch<0, true>(a, s, clear) : launch<0, false>(a, s, clear);
+    e = vec_ok ? launch<0, true>(a, s) : launch<0, false>(a, s);
   return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
 }
 
@@ -1153,7 +1050,7 @@ extern "C" int spec_verify_noalloc(const void* target_logits, const void* draft_
   using namespace lvtv::vr;
   if (dtype != LVTV_F32 && dtype != LVTV_BF16) return LVTV_ERR_DTYPE;
   if (!sizes_ok(B, Kmax, V)) return LVTV_ERR_SHAPE;
-  if (make_layout(size_t(B) * (Kmax + 1), V, false, false, dtype).total > kNoAllocBytes)
+  if (make_layout(size_t(B) * (Kmax + 1), V, false).total > kNoAllocBytes)
     return LVTV_ERR_SCRATCH;
   void* ws = device_scratch();
   if (!ws) return LVTV_ERR_LAUNCH;
@@ -1164,14 +1061,14 @@ extern "C" int spec_verify_noalloc(const void* target_logits, const void* draft_
 
 extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t Kmax, int32_t V, int dtype) {
   if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
-  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false, false, dtype).total;
+  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false).total;
 }
 
 extern "C" size_t spec_verify_packed_workspace_bytes(int32_t B, int32_t total_rows, int32_t V,
                                                       int dtype) {
   if (!lvtv::vr::packed_sizes_ok(B, total_rows, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16))
     return 0;
-  return lvtv::vr::make_layout(size_t(total_rows), V, true, false, dtype).total;
+  return lvtv::vr::make_layout(size_t(total_rows), V, true).total;
 }
 
 extern "C" int spec_verify(const void* target_logits, const void* draft_logits, int dtype,
@@ -1188,7 +1085,7 @@ extern "C" int spec_verify(const void* target_logits, const void* draft_logits, 
 extern "C" size_t spec_verify_topkp_workspace_bytes(int32_t B, int32_t Kmax, int32_t V,
                                                      int dtype) {
   if (!lvtv::vr::sizes_ok(B, Kmax, V) || (dtype != LVTV_F32 && dtype != LVTV_BF16)) return 0;
-  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false, true, dtype).total;
+  return lvtv::vr::make_layout(size_t(B) * (Kmax + 1), V, false, true).total;
 }
 
 extern "C" int spec_verify_topkp(const void* target_logits, const void* draft_logits, int dtype,
@@ -1218,7 +1115,7 @@ extern "C" int spec_verify_packed(const void* target_logits, const void* draft_l
       !status)
     return LVTV_ERR_NULL;
   if (total_rows > B && (!draft_logits || !draft_tokens || !alpha)) return LVTV_ERR_NULL;
-  const Layout L = make_layout(size_t(total_rows), V, true, false, dtype);
+  const Layout L = make_layout(size_t(total_rows), V, true);
   if (!workspace || workspace_bytes < L.total || (reinterpret_cast<uintptr_t>(workspace) & 255))
     return LVTV_ERR_WORKSPACE;
   Args a;
@@ -1249,16 +1146,14 @@ extern "C" int spec_verify_packed(const void* target_logits, const void* draft_l
   a.keep = nullptr;
   a.klen = nullptr;
   a.klist = nullptr;
-  set_stream(a, L, ws);
-  const size_t clear = L.off_clear_end - L.off_words;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(target_logits) |
                         reinterpret_cast<uintptr_t>(draft_logits);
   const bool vec_ok = (V % kVec == 0) && ((mis & 15) == 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == LVTV_BF16)
-    e = vec_ok ? launch<1, true>(a, s, clear) : launch<1, false>(a, s, clear);
+    e = vec_ok ? launch<1, true>(a, s) : launch<1, false>(a, s);
   else
-    e = vec_ok ? launch<0, true>(a, s, clear) : launch<0, false>(a, s, clear);
+    e = vec_ok ? launch<0, true>(a, s) : launch<0, false>(a, s);
   return e == hipSuccess ? LVTV_OK : LVTV_ERR_LAUNCH;
 }

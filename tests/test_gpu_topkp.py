@@ -27,7 +27,7 @@ import lossless_verify_tv_amd as lv
 from lossless_verify_tv_amd import synth
 from oracle import verify as ov
 
-from .gpu_util import run_oracle_verify, announce, device, run_verify, verify_inputs
+from .gpu_util import announce, device, run_verify, verify_inputs
 from .parity import check_excused_bound, compare_verify
 
 pytestmark = pytest.mark.gpu
@@ -299,10 +299,8 @@ def test_topkp_workspace_contents_do_not_matter():
 
 
 def test_truncation_off_equals_plain_verify():
-    """top_k <= 0 or >= V and top_p >= 1 keep every token: the outputs match
-    spec_verify's on the full-vocabulary workload (the two calls run
-    different kernels, so alpha agrees to rounding and each decision to the
-    oracle's margin rule)."""
+    """top_k <= 0 or >= V and top_p >= 1 keep every token: the outputs are
+    bit-identical to spec_verify's on the full-vocabulary workload."""
     dev = device()
     case = synth.verify_case(3, temperature=0.6, batch=16)
     B, _, V = case.shape
@@ -311,13 +309,8 @@ def test_truncation_off_equals_plain_verify():
     announce(f"topkp off vs plain shape={case.shape}")
     plain = run_verify(case, dev)
     trunc = _run_gpu(case, top_k, top_p, dev)
-    assert np.array_equal(plain["status"], trunc["status"])
-    assert np.allclose(plain["alpha"], trunc["alpha"], rtol=2e-6, atol=0)
-    orc = run_oracle_verify(case)
-    for tag, g in (("plain", plain), ("truncation off", trunc)):
-        rep = compare_verify(g, orc, case.k, case.shape[1])
-        assert not rep["failures"], (tag, rep["failures"][:5])
-        check_excused_bound(rep, tag)
+    for key in ("accepted_len", "status", "tokens", "alpha"):
+        assert np.array_equal(plain[key], trunc[key]), key
 
 
 def test_topkp_full_vocabulary_workload():

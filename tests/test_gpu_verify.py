@@ -210,11 +210,8 @@ def _offset_copy(t, offset):
 
 
 def test_vector_and_element_load_paths_agree():
-    """Rows whose base is not 16-byte aligned take the row kernel with
-    per-element loads, aligned rows the single-read stream kernel. Greedy
-    outputs are bit-identical; sampling outputs have the same status, alpha
-    equal to rounding (the kernels sum in different orders), and both agree
-    with the oracle under the margin rule."""
+    """Rows whose base is not 16-byte aligned take the per-element loads;
+    the results must be bit-identical to the 16-byte vector loads."""
     dev = device()
     for case in (synth.verify_case(3, temperature=1.0, batch=5, vocab=30000),
                  synth.verify_case(3, temperature=0.0, batch=4, vocab=30000),
@@ -226,17 +223,8 @@ def test_vector_and_element_load_paths_agree():
         shifted["draft_logits"] = _offset_copy(inputs["draft_logits"], 3)
         announce(f"element-load path shape={case.shape}")
         other = run_verify(case, dev, shifted)
-        if np.all(case.temperature == 0):
-            for key in aligned:
-                assert np.array_equal(aligned[key], other[key]), key
-            continue
-        assert np.array_equal(aligned["status"], other["status"])
-        assert np.allclose(aligned["alpha"], other["alpha"], rtol=2e-6, atol=0)
-        orc = run_oracle_verify(case)
-        for tag, g in (("stream kernel", aligned), ("row kernel", other)):
-            rep = compare_verify(g, orc, case.k, case.shape[1])
-            assert not rep["failures"], (tag, rep["failures"][:5])
-            check_excused_bound(rep, tag)
+        for key in aligned:
+            assert np.array_equal(aligned[key], other[key]), key
 
 
 def test_workspace_contents_do_not_matter():
