@@ -12,8 +12,9 @@ region. Each temperature's call reads its own copy of the logits, and the
 last-level cache by the previous one.
 
 Prints one JSON line: the metric (verified vocab-rows/s over the step), the
-roofline of the dominant kernel (the loss), timed live with HIP events on
-the stream the kernels run on, and the CPU oracle timed on a bounded sample.
+roofline of the dominant kernel (the loss), timed live inside the timed steps
+with a pair of HIP events around the loss call on the stream the kernels run
+on, and the CPU oracle timed on the step's own inputs.
 
 Per-call times (the step's components, the variants, the small workloads)
 are medians over many calls, each call bracketed by its own pair of events
@@ -21,7 +22,11 @@ with a 1 GiB write between calls outside the brackets, so that no call is
 served from the 256 MB last-level cache by the one before it.
 
 ``python bench.py --trace-summary <kernel_trace.csv>`` prints per-kernel
-launch statistics from a rocprofv3 kernel trace (no GPU needed).
+launch statistics from a rocprofv3 kernel trace, and the per-launch medians
+of the bench steps found in it (no GPU needed).
+``python bench.py --traffic <fetch.csv> <write.csv>`` writes
+profiles/traffic.json from two rocprofv3 --pmc runs of this script
+(FETCH_SIZE, then WRITE_SIZE, with --copy-calibration; no GPU needed).
 """
 
 from __future__ import annotations
@@ -192,18 +197,23 @@ def cpu_baseline(verify_cases, loss_case, gpu_verify, workers):
     }
 
 
-def trace_summary(path):
+def trace_summary(path, timed_steps=None):
     """Per-kernel launch statistics from a rocprofv3 kernel-trace CSV: calls,
     mean, median, min and max duration in microseconds, and the mean over
-    the last half of the launches (after any warm-up)."""
+    the last half of the launches (after any warm-up). Then the bench steps
+    found in the trace (the verify row kernel and finalize at T = 0, 0.6,
+    1.0, then clear_words, loss_halves and loss_finish, with no other launch
+    in between): per-launch medians over the steps."""
     import csv
     rows = {}
+    seq = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name")
             t0 = int(r.get("Start_Timestamp") or r.get("BeginNs"))
             t1 = int(r.get("End_Timestamp") or r.get("EndNs"))
             rows.setdefault(name, []).append((t0, (t1 - t0) * 1e-3))
+            seq.append((t0, t1, name))
     print("| kernel | calls | mean µs | median µs | min µs | max µs | mean of last half µs |")
     print("|---|---|---|---|---|---|---|")
     for name, v in sorted(rows.items(), key=lambda kv: -sum(d for _, d in kv[1])):
@@ -211,6 +221,108 @@ def trace_summary(path):
         short = name if len(name) < 90 else name[:87] + "..."
         print(f"| {short} | {d.size} | {d.mean():.1f} | {np.median(d):.1f} | {d.min():.1f} | "
               f"{d.max():.1f} | {d[d.size // 2:].mean():.1f} |")
+    seq.sort()
+    pattern = ["rows", "finalize"] * 3 + ["clear", "loss", "loss_finish"]
+    steps = []
+    for i in range(len(seq) - len(pattern) + 1):
+        win = seq[i:i + len(pattern)]
+        if all(_TRAFFIC_KERNELS[k] in n for k, (_, _, n) in zip(pattern, win)):
+            steps.append([(t1 - t0) * 1e-3 for t0, t1, _ in win] +
+                         [(win[-1][1] - win[-3][0]) * 1e-3])
+    if steps:
+        st = np.array(steps)
+        head = ("| steps | T=0 rows | T=0 finalize | T=0.6 rows | T=0.6 finalize | T=1.0 rows | "
+                "T=1.0 finalize | clear_words | loss_halves | loss_finish | loss call span |")
+        print()
+        print(f"Bench steps found in the trace: {len(steps)} (warm-up and timed); µs per launch:")
+        print()
+        print(head)
+        print("|---|---|---|---|---|---|---|---|---|---|---|")
+        print(f"| median of all {len(steps)} | " +
+              " | ".join(f"{x:.1f}" for x in np.median(st, axis=0)) + " |")
+        if timed_steps and timed_steps <= len(steps):
+            print(f"| mean of the last {timed_steps} (the timed steps) | " +
+                  " | ".join(f"{x:.1f}" for x in st[-timed_steps:].mean(axis=0)) + " |")
+
+
+# Kernels whose per-launch HBM bytes traffic.json records, by the part of
+# the demangled name that identifies them.
+_TRAFFIC_KERNELS = {
+    "rows": "verify_rows_bf16<true, false>",
+    "finalize": "verify_finalize<1>",
+    "clear": "clear_words",
+    "loss": "loss_halves<true, false, false>",
+    "loss_finish": "loss_finish<true, false, false>",
+    "loss_logits": "loss_halves<true, true, false>",
+    "trunc": "trunc_rows<1, true>",
+    "rows_trunc": "verify_rows_bf16<true, true>",
+}
+
+
+def _counter_dispatches(path, counter):
+    """[(kernel name, value)] per dispatch, in dispatch order, of one counter
+    of a rocprofv3 --pmc CSV (values summed over the CSV's rows of a
+    dispatch)."""
+    import csv
+    disp = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            if d not in disp:
+                disp[d] = [r["Kernel_Name"], 0.0]
+            disp[d][1] += float(r["Counter_Value"])
+    return [tuple(disp[d]) for d in sorted(disp)]
+
+
+def traffic_from_counters(fetch_csv, write_csv):
+    """HBM bytes per launch of the step's kernels from two rocprofv3 --pmc
+    runs of `bench.py --steps 1 --warmup 0 --calls 3 --no-cpu-baseline
+    --copy-calibration`: FETCH_SIZE in one, WRITE_SIZE in the other (KiB per
+    dispatch). Each counter is scaled by 1 GiB over its median reading for
+    the three plain 1 GiB device copies the calibration runs first. The
+    step's kernels are the first launches after the calibration: the
+    verify row kernel and finalize of T = 0, 0.6, 1.0 in that order, then
+    the loss call; the logits-target loss and the top-k/top-p kernels are
+    the first launches of theirs."""
+    out = {"kernel_source_hash": kernel_source_hash(),
+           "method": ("rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (separate runs) of "
+                      "bench.py --steps 1 --warmup 0 --calls 3 --no-cpu-baseline "
+                      "--copy-calibration; each counter scaled by (1 GiB / the counter's "
+                      "median reading for the plain 1 GiB device copies in the same run); "
+                      "derived by bench.py --traffic")}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
+                               ("write", write_csv, "WRITE_SIZE")):
+        disp = _counter_dispatches(path, counter)
+        first = next(i for i, (n, _) in enumerate(disp) if _TRAFFIC_KERNELS["rows"] in n)
+        copies = sorted((v for n, v in disp[:first] if "copy" in n.lower()), reverse=True)[:3]
+        if len(copies) < 3 or copies[-1] <= 0:
+            raise SystemExit(f"{path}: no 1 GiB copy calibration before the step")
+        scale = float(1 << 30) / (float(np.median(copies)) * 1024.0)
+        out[f"{key}_scale"] = scale
+        after = disp[first:]
+
+        def nth(tag, k=0):
+            hits = [v for n, v in after if _TRAFFIC_KERNELS[tag] in n]
+            return hits[k] * 1024.0 * scale if len(hits) > k else None
+
+        for i, t in enumerate(TEMPS):
+            out[f"verify_T{t}_rows_{key}"] = nth("rows", i)
+            out[f"verify_T{t}_finalize_{key}"] = nth("finalize", i)
+        out[f"loss_{key}_bytes"] = nth("loss")
+        out[f"loss_finish_{key}_bytes"] = nth("loss_finish")
+        out[f"clear_words_{key}_bytes"] = nth("clear")
+        out[f"loss_logits_T1.0_{key}_bytes"] = nth("loss_logits")
+        out[f"trunc_topk50_{key}_bytes"] = nth("trunc")
+        out[f"rows_topk50_{key}_bytes"] = nth("rows_trunc")
+    out["loss_bytes_per_launch"] = out["loss_fetch_bytes"] + out["loss_write_bytes"]
+    for t in TEMPS:
+        rows = out[f"verify_T{t}_rows_fetch"] + out[f"verify_T{t}_rows_write"]
+        fin = out[f"verify_T{t}_finalize_fetch"] + out[f"verify_T{t}_finalize_write"]
+        out[f"verify_T{t}_rows_kernel_bytes"] = rows
+        out[f"verify_T{t}_bytes_per_launch"] = rows + fin
+    return out
 
 
 def load_traffic(src_hash):
@@ -240,9 +352,19 @@ def main():
                     help="calls per median for the per-call times (loss calls: a third)")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-kernel statistics of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs "
+                         "(FETCH_SIZE, WRITE_SIZE) of this script and exit")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(args.trace_summary)
+        trace_summary(args.trace_summary, args.steps)
+        return
+    if args.traffic:
+        data = traffic_from_counters(*args.traffic)
+        with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+            json.dump(data, f, indent=1)
+            f.write("\n")
+        print(json.dumps(data, indent=1))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this hot path has no "
@@ -303,29 +425,37 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(loss_events=None):
         for i in range(len(TEMPS)):
             lv.spec_verify(**vin[i], workspace=vws, out=vouts[i])
+        if loss_events:
+            loss_events[0].record(stream)
         lv.e2e_tv_loss_fwd_bwd(z, p, workspace=lws, out=lout)
+        if loss_events:
+            loss_events[1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    # The timed region holds the K steps and nothing else.
+    # The timed region holds the K steps and nothing else; inside each step
+    # a pair of events brackets the loss call (the roofline's kernel).
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    loss_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for s in range(args.steps):
-        step()
+        step(loss_evs[s])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / args.steps
+    loss_step_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in loss_evs]))
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall:.2f} s)")
     gpu_verify = [(o[0].cpu().numpy(), o[1].cpu().numpy()) for o in vouts]
 
@@ -364,6 +494,7 @@ def main():
     vb = verify_bytes(base.k, VOCAB)
     lb = loss_bytes(LOSS_N, LOSS_W, VOCAB)
     loss_gbs = lb / (loss_ms * 1e-3) / 1e9
+    roof_gbs = lb / (loss_step_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = load_traffic(src_hash)
     result = {
@@ -389,17 +520,21 @@ def main():
         },
         "achieved_hbm_gbs": (len(TEMPS) * vb + lb) / (ms_step * 1e-3) / 1e9,
         "timing": (f"value and ms_per_step: {args.steps} back-to-back steps between two events; "
-                   f"per-call ms: median of {n_v} calls ({n_l} for the loss) each between its "
-                   f"own two events, a 1 GiB write between calls outside them"),
+                   f"roofline: mean over those steps of the loss call between its own two "
+                   f"events; per-call ms: median of {n_v} calls ({n_l} for the loss) each "
+                   f"between its own two events, a 1 GiB write between calls outside them"),
         "roofline": {
-            "kernel": "loss_halves (timed as the whole e2e_tv_loss_fwd_bwd call: clear_words "
-                      "+ loss_halves + loss_finish)",
+            "kernel": ("loss_halves, timed as the e2e_tv_loss_fwd_bwd call inside each timed "
+                       "step (one pair of events on the call's stream: clear_words + "
+                       "loss_halves + loss_finish, the two small kernels about 11 us)"),
             "bound": "hbm",
-            "achieved": loss_gbs,
+            "achieved": roof_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": loss_gbs / HBM_PEAK_GBS,
+            "frac": roof_gbs / HBM_PEAK_GBS,
             "traffic": (traffic or {}).get("loss_bytes_per_launch"),
+            "ms_per_launch": loss_step_ms,
+            "algorithmic_bytes_per_launch": lb,
         },
         "components": {
             f"spec_verify_T{t}": {
