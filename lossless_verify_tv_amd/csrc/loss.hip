@@ -529,9 +529,11 @@ int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t 
   const float inv_t = unit ? 1.f : 1.f / tg.temperature;
   const float c = unit ? kLog2e : kLog2e * inv_t;
   // the single-read kernel serves the TV objectives (their gradients need
-  // only the held z, the mask and per-row scalars)
-  if ((objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV) && use_fused(opt, N, W, V) &&
-      (!logits || lf::logits_supported())) {
+  // only the held z, the mask and per-row scalars) and, for a probability
+  // target, CE and KL (their gradient streams p a second time)
+  const bool tv = objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV;
+  const bool fused_ok = tv ? (!logits || lf::logits_supported()) : lf::xent_supported(logits);
+  if (fused_ok && use_fused(opt, N, W, V)) {
     lf::LossCall lc;
     lc.z = draft_logits;
     lc.p = logits ? nullptr : tg.probs;

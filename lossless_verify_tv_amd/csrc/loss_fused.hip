@@ -286,6 +286,37 @@ __device__ __forceinline__ uint32_t grp_overlap(const u32x4& g, const u32x4& pa,
   return bits;
 }
 
+// Cross-entropy and KL parts of a group (probability target): alpha's part
+// sum min(q, p), sum p, and the loss part sum p (M + ln L - z) = -sum p ln q
+// (KL adds p ln p per token), each in fp32 over the group and fp64 across
+// groups; mlnl = fl32(M + ln L) of the row. Tokens at or past V (z = -inf,
+// p = 0) add nothing (with kVecOk a group lies wholly inside or past the
+// row).
+constexpr float kLn2f = 0.693147180559945309f;
+
+template <bool kVecOk>
+__device__ __forceinline__ void grp_xent(const u32x4& g, const u32x4& pa, const u32x4& pb, int e,
+                                         int V, float cz, const RowStats& rs, float mlnl, bool kl,
+                                         double& al, double& sp, double& sl) {
+  float a = 0.f, b = 0.f, c = 0.f;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const bool in = kVecOk ? (e < V) : (e + j < V);
+    const float x = zelem(g, j);
+    const float p = pelem(pa, pb, j);
+    a += fminf(qval(x, cz, rs.nm, rs.inv_l), p);
+    b += p;
+    // -ln q, plus ln p for KL (from the hardware base-2 logarithm; p below
+    // the smallest normal float takes ln p as 0: its term is below 1e-36)
+    float t = mlnl - x;
+    if (kl) t += (p >= 1.17549435e-38f) ? __builtin_amdgcn_logf(p) * kLn2f : 0.f;
+    c += in ? p * t : 0.f;
+  }
+  al += (double)a;
+  sp += (double)b;
+  sl += (double)c;
+}
+
 // Half statistics from per-thread partials: every thread's m is already the
 // block maximum; l is summed over the block.
 struct HalfStats {
@@ -329,6 +360,20 @@ __device__ __forceinline__ RowStats row_stats_from(const uint32_t* w, int first,
                         c);
 }
 
+
+// M + ln L of a row in fp64 (natural log; the row's maximum raw logit and
+// sum of e^(z - M), from the words [first, first + 3) of its two half slots
+// in the same arithmetic as combine_halves): -ln q(v) = M + ln L - z(v).
+__device__ __forceinline__ double row_mlnl_from(const uint32_t* w, int first, float c) {
+  const float m0 = __uint_as_float(w[first]), m1 = __uint_as_float(w[kSlotWords + first]);
+  const double l0 = word_f64(w, first + 1), l1 = word_f64(w, kSlotWords + first + 1);
+  const float M = fmaxf(m0, m1);
+  const double w0 = (m0 == -INFINITY) ? l0 * 0.0
+                                      : l0 * (double)__builtin_amdgcn_exp2f((m0 - M) * c);
+  const double w1 = (m1 == -INFINITY) ? l1 * 0.0
+                                      : l1 * (double)__builtin_amdgcn_exp2f((m1 - M) * c);
+  return (double)M + log(w0 + w1);
+}
 
 __device__ __forceinline__ void f64_words(double v, uint32_t& lo, uint32_t& hi) {
   const uint64_t bits = uint64_t(__double_as_longlong(v));
@@ -381,8 +426,16 @@ __device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size
       const int b1 = (k * 2 + 1) * kSlotWords + 4 + 2 * which;
       return word_f64(sh.words, b0) + word_f64(sh.words, b1);
     };
-    double loss_n = 0.0, g;
-    if (a.objective == LVTV_OBJ_STEP_TV) {
+    double loss_n = 0.0, g = 0.0;
+    if (a.objective == LVTV_OBJ_CE || a.objective == LVTV_OBJ_KL) {
+      // parts (alpha, sum p, the half's loss part): the branch loss is the
+      // sum of the rows' parts; dz = q (sum p)/N - p/N
+      for (int k = 0; k < W; ++k) loss_n += part(k, 2);
+      sh.coef[0] = part(j, 1) / double(a.N) * a.inv_t;
+      sh.coef[1] = 1.0 / double(a.N) * a.inv_t;
+      a.alpha[row] = float(part(j, 0));
+      if (j == 0) a.branch_loss[n] = loss_n;
+    } else if (a.objective == LVTV_OBJ_STEP_TV) {
       // sum_k (1 - alpha_k); d/dalpha_j = -1
       for (int k = 0; k < W; ++k) loss_n += 1.0 - part(k, 0);
       g = -1.0 / double(a.N);
@@ -397,10 +450,12 @@ __device__ __forceinline__ void branch_scalars(const Args& a, int n, int j, size
       for (int k = W - 2; k >= j; --k) suffix = 1.0 + part(k + 1, 0) * suffix;
       g = -before * suffix / double(a.N);
     }
-    sh.coef[0] = g * part(j, 2) * a.inv_t;   // S'_j
-    sh.coef[1] = -g * part(j, 1) * a.inv_t;  // S_j
-    a.alpha[row] = float(part(j, 0));
-    if (j == 0) a.branch_loss[n] = loss_n;
+    if (a.objective == LVTV_OBJ_E2E_TV || a.objective == LVTV_OBJ_STEP_TV) {
+      sh.coef[0] = g * part(j, 2) * a.inv_t;   // S'_j
+      sh.coef[1] = -g * part(j, 1) * a.inv_t;  // S_j
+      a.alpha[row] = float(part(j, 0));
+      if (j == 0) a.branch_loss[n] = loss_n;
+    }
   }
   __syncthreads();
 }
@@ -424,6 +479,43 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e,
       const int jj = 2 * h + t;
       const bool below = (bits8 >> jj) & 1u;
       v2[t] = qval(zelem(zv, jj), cz, rs.nm, rs.inv_l) * (below ? c_below : c_above);
+      g32[jj] = v2[t];
+    }
+    const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
+    out[h] = __builtin_bit_cast(uint32_t, b);
+  }
+  if (kVecOk) {
+    if (e < V) st_nt16(dz + e, out);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kVec; ++t)
+      if (e + t < V) dz[e + t] = uint16_t(out[t >> 1] >> (16 * (t & 1)));
+  }
+  if constexpr (kDbg) {
+#pragma unroll
+    for (int t = 0; t < kVec; ++t)
+      if (e + t < V) dz32[e + t] = g32[t];
+  }
+}
+
+// CE / KL dz of one group, bf16 (nearest even): fma(q, c_q, -(p c_p)) with
+// c_q = (sum p)/N and c_p = 1/N (each times the chain factor fl32(1/T)).
+template <bool kVecOk, bool kDbg>
+__device__ __forceinline__ void dz_xent_group(const u32x4& zv, const u32x4& pa, const u32x4& pb,
+                                              int e, int V, float cz, const RowStats& rs,
+                                              float c_q, float c_p, uint16_t* dz, float* dz32) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  u32x4 out;
+  float g32[kVec];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float v2[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int jj = 2 * h + t;
+      const float q = qval(zelem(zv, jj), cz, rs.nm, rs.inv_l);
+      v2[t] = __builtin_fmaf(q, c_q, -(pelem(pa, pb, jj) * c_p));
       g32[jj] = v2[t];
     }
     const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
@@ -496,8 +588,9 @@ __device__ __forceinline__ void publish_stats(uint64_t* slot, int first, uint32_
 
 // ------------------------------------------------------------------ half-row kernel
 
-template <bool kVecOk, bool kLogits, bool kDbg>
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent>
 __device__ __forceinline__ void half_body(const Args& a) {
+  static_assert(!(kLogits && kXent), "CE and KL take a probability target here");
   __shared__ Shared sh;
   __shared__ u32x4 zl[kZL][kThreads];
   const int W = a.W, V = a.V;
@@ -561,11 +654,14 @@ __device__ __forceinline__ void half_body(const Args& a) {
 #pragma unroll
   for (int w = 0; w < kMaskWords; ++w) mask[w] = 0u;
   const int tbp = opaque(group_elem(h, 0));
+  const bool kl = a.objective == LVTV_OBJ_KL;
+  const float mlnl = kXent ? float(row_mlnl_from(sh.words, 0, c)) : 0.f;
+  constexpr int kB = kPBatch;
 #pragma unroll
-  for (int g0 = 0; g0 < kZG; g0 += kPBatch) {
-    u32x4 pa[kPBatch], pb[kPBatch];
+  for (int g0 = 0; g0 < kZG; g0 += kB) {
+    u32x4 pa[kB], pb[kB];
 #pragma unroll
-    for (int i = 0; i < kPBatch; ++i)
+    for (int i = 0; i < kB; ++i)
       if (g0 + i < kZG) {
         if constexpr (kLogits)
           pa[i] = load_z<kVecOk>(t, V, opaque(tbp) + (g0 + i) * kTile);
@@ -573,12 +669,18 @@ __device__ __forceinline__ void half_body(const Args& a) {
           load_p<kVecOk>(p, V, opaque(tbp) + (g0 + i) * kTile, pa[i], pb[i]);
       }
 #pragma unroll
-    for (int i = 0; i < kPBatch; ++i)
+    for (int i = 0; i < kB; ++i)
       if (g0 + i < kZG) {
         const int g = g0 + i;
-        const uint32_t bits =
-            grp_overlap<kLogits>(zg.get(g), pa[i], pb[i], c, rs, ts, al, sb, sa);
-        mask[(g * kVec) / 32] |= bits << ((g * kVec) % 32);
+        if constexpr (kXent) {
+          // al, sum p (in sb), the loss part (in sa)
+          grp_xent<kVecOk>(zg.get(g), pa[i], pb[i], opaque(tbp) + g * kTile, V, c, rs, mlnl, kl,
+                           al, sb, sa);
+        } else {
+          const uint32_t bits =
+              grp_overlap<kLogits>(zg.get(g), pa[i], pb[i], c, rs, ts, al, sb, sa);
+          mask[(g * kVec) / 32] |= bits << ((g * kVec) % 32);
+        }
       }
     // keep the next batch's loads behind this batch's arithmetic
     __builtin_amdgcn_sched_barrier(0);
@@ -606,14 +708,32 @@ __device__ __forceinline__ void half_body(const Args& a) {
   const float c_below = float(sh.coef[0]);
   const float c_above = float(sh.coef[1]);
 
-  // 5. dz of this half from the held copy and the mask
+  // 5. dz of this half from the held copy and the mask (CE / KL: and p,
+  //    streamed again)
   uint16_t* dz = a.dz + row * V;
   const int tbd = opaque(group_elem(h, 0));
+  if constexpr (kXent) {
 #pragma unroll
-  for (int g = 0; g < kZG; ++g) {
-    dz_group<kVecOk, kDbg>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, c, rs,
-                           c_below, c_above, dz, kDbg ? a.dz32 + row * V : nullptr);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int g0 = 0; g0 < kZG; g0 += kB) {
+      u32x4 pa[kB], pb[kB];
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+        if (g0 + i < kZG) load_p<kVecOk>(p, V, opaque(tbd) + (g0 + i) * kTile, pa[i], pb[i]);
+#pragma unroll
+      for (int i = 0; i < kB; ++i)
+        if (g0 + i < kZG)
+          dz_xent_group<kVecOk, kDbg>(zg.get(g0 + i), pa[i], pb[i], opaque(tbd) + (g0 + i) * kTile,
+                                      V, c, rs, c_below, c_above, dz,
+                                      kDbg ? a.dz32 + row * V : nullptr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kZG; ++g) {
+      dz_group<kVecOk, kDbg>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, c, rs,
+                             c_below, c_above, dz, kDbg ? a.dz32 + row * V : nullptr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -667,6 +787,26 @@ __device__ __forceinline__ void stream_half_parts(const Args& a, size_t row, int
   block_sum3(al, sb, sa, sh);
 }
 
+// CE / KL parts of half h of a row, streamed from memory (same per-group
+// steps, order and reductions as a half workgroup): alpha's part, sum p and
+// the half's part of the row's loss.
+template <bool kVecOk>
+__device__ __forceinline__ void stream_half_xent(const Args& a, size_t row, int h,
+                                                 const RowStats& rs, float mlnl, double& al,
+                                                 double& sp, double& part, Shared& sh) {
+  const bool kl = a.objective == LVTV_OBJ_KL;
+  al = sp = part = 0.0;
+  const uint16_t* z = a.z + row * a.V;
+#pragma unroll 1
+  for (int g = 0; g < kZG; ++g) {
+    const int e = group_elem(h, g);
+    u32x4 pa, pb;
+    load_target<kVecOk, false>(a, row, e, pa, pb);
+    grp_xent<kVecOk>(load_z<kVecOk>(z, a.V, e), pa, pb, e, a.V, a.c, rs, mlnl, kl, al, sp, part);
+  }
+  block_sum3(al, sp, part, sh);
+}
+
 // Writes half statistics into words [first, first + 3) of slot s of a
 // branch's word copy.
 __device__ __forceinline__ void put_stats(uint32_t* bw, int s, int first, const HalfStats& hs) {
@@ -682,7 +822,7 @@ __device__ __forceinline__ void put_stats(uint32_t* bw, int s, int first, const 
 // missing is recomputed from the inputs with the same steps and reductions.
 // Then both halves' dz are written (the mask recomputed from z and p). Every
 // thread of the block calls it.
-template <bool kVecOk, bool kLogits, bool kDbg>
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent>
 __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag, Shared& sh,
                                            uint32_t* bw) {
   const int W = a.W, V = a.V;
@@ -733,7 +873,12 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
         const int s = 2 * k + hh;
         if (!(sh.have[s] & 2)) {
           double x, y, w;
-          stream_half_parts<kVecOk, kLogits>(a, rk, hh, rs, ts, x, y, w, sh);
+          if constexpr (kXent)
+            stream_half_xent<kVecOk>(a, rk, hh, rs,
+                                     float(row_mlnl_from(bw + 2 * k * kSlotWords, 0, c)), x, y,
+                                     w, sh);
+          else
+            stream_half_parts<kVecOk, kLogits>(a, rk, hh, rs, ts, x, y, w, sh);
           __syncthreads();
           if (threadIdx.x == 0) {
             const double v[3] = {x, y, w};
@@ -765,20 +910,25 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
         const u32x4 zv = load_z<kVecOk>(z, V, e);
         u32x4 pa, pb;
         load_target<kVecOk, kLogits>(a, size_t(row), e, pa, pb);
-        double x = 0.0, y = 0.0, w = 0.0;
-        const uint32_t bits = grp_overlap<kLogits>(zv, pa, pb, c, rs, ts, x, y, w);
-        dz_group<kVecOk, kDbg>(zv, bits, e, V, c, rs, c_below, c_above, dz,
-                               kDbg ? a.dz32 + size_t(row) * V : nullptr);
+        if constexpr (kXent) {
+          dz_xent_group<kVecOk, kDbg>(zv, pa, pb, e, V, c, rs, c_below, c_above, dz,
+                                      kDbg ? a.dz32 + size_t(row) * V : nullptr);
+        } else {
+          double x = 0.0, y = 0.0, w = 0.0;
+          const uint32_t bits = grp_overlap<kLogits>(zv, pa, pb, c, rs, ts, x, y, w);
+          dz_group<kVecOk, kDbg>(zv, bits, e, V, c, rs, c_below, c_above, dz,
+                                 kDbg ? a.dz32 + size_t(row) * V : nullptr);
+        }
       }
     }
     __syncthreads();
   }
 }
 
-template <bool kVecOk, bool kLogits, bool kDbg>
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 loss_halves(Args a) {
-  half_body<kVecOk, kLogits, kDbg>(a);
+  half_body<kVecOk, kLogits, kDbg, kXent>(a);
 }
 
 __device__ __forceinline__ int block_min(int v, Shared& sh) {
@@ -797,7 +947,7 @@ __device__ __forceinline__ int block_min(int v, Shared& sh) {
 // up to 32 rows per thread are read at once, so the usual case (no flag) costs
 // one round of loads. (2) The loss is the mean of the branch losses, summed
 // in a fixed order. (3) The call epoch advances.
-template <bool kVecOk, bool kLogits, bool kDbg>
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent>
 __global__ __launch_bounds__(kThreads) void loss_finish(Args a) {
   __shared__ Shared sh;
   __shared__ uint32_t bw[LVTV_MAX_W * 2 * kSlotWords];  // a branch's words
@@ -815,7 +965,7 @@ __global__ __launch_bounds__(kThreads) void loss_finish(Args a) {
       const int cand = mine ? r0 + int(threadIdx.x) + __builtin_ctz(mine) * kThreads : INT_MAX;
       const int row = block_min(cand, sh);
       if (cand == row) mine &= mine - 1u;
-      repair_row<kVecOk, kLogits, kDbg>(a, row, tag, sh, bw);
+      repair_row<kVecOk, kLogits, kDbg, kXent>(a, row, tag, sh, bw);
     }
   }
   const int per = (a.N + kThreads - 1) / kThreads;
@@ -864,6 +1014,24 @@ __global__ __launch_bounds__(256) void clear_words(u32x4* w, size_t n16) {
     w[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+template <bool kDbg, bool kXent>
+hipError_t launch_kernels(const Args& a, bool vec_ok, bool logits, unsigned rows,
+                          hipStream_t stream) {
+  auto halves = vec_ok ? (logits ? loss_halves<true, true, kDbg, false>
+                                 : loss_halves<true, false, kDbg, kXent>)
+                       : (logits ? loss_halves<false, true, kDbg, false>
+                                 : loss_halves<false, false, kDbg, kXent>);
+  auto finish = vec_ok ? (logits ? loss_finish<true, true, kDbg, false>
+                                 : loss_finish<true, false, kDbg, kXent>)
+                       : (logits ? loss_finish<false, true, kDbg, false>
+                                 : loss_finish<false, false, kDbg, kXent>);
+  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(finish, dim3(1), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <bool kDbg>
 hipError_t launch_all(const Args& a, bool vec_ok, bool logits, unsigned rows, size_t clear_bytes,
                       void* clear_base, hipStream_t stream) {
@@ -872,22 +1040,18 @@ hipError_t launch_all(const Args& a, bool vec_ok, bool logits, unsigned rows, si
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(clear_words, dim3(unsigned(blocks)), dim3(256), 0, stream,
                      static_cast<u32x4*>(clear_base), n16);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  auto halves = vec_ok ? (logits ? loss_halves<true, true, kDbg> : loss_halves<true, false, kDbg>)
-                       : (logits ? loss_halves<false, true, kDbg> : loss_halves<false, false, kDbg>);
-  auto finish = vec_ok ? (logits ? loss_finish<true, true, kDbg> : loss_finish<true, false, kDbg>)
-                       : (logits ? loss_finish<false, true, kDbg> : loss_finish<false, false, kDbg>);
-  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(finish, dim3(1), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  const bool xent = a.objective == LVTV_OBJ_CE || a.objective == LVTV_OBJ_KL;
+  return xent ? launch_kernels<kDbg, true>(a, vec_ok, false, rows, stream)
+              : launch_kernels<kDbg, false>(a, vec_ok, logits, rows, stream);
 }
 
 }  // namespace
 
 bool logits_supported() { return true; }
+
+bool xent_supported(bool logits) { return !logits; }
 
 bool applicable(int N, int W, int V) {
   return V <= kMaxV && size_t(N) * W * 2 < (size_t(1) << 31);
@@ -899,6 +1063,8 @@ size_t workspace_bytes(int N, int W, int V) {
 }
 
 hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
+  const bool xent = c.objective == LVTV_OBJ_CE || c.objective == LVTV_OBJ_KL;
+  if (xent && !xent_supported(c.t != nullptr)) return hipErrorInvalidValue;
   const Layout L = make_layout(c.N, c.W);
   Args a;
   a.z = c.z;

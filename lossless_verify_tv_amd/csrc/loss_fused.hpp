@@ -33,6 +33,8 @@ struct LossCall {
 bool applicable(int N, int W, int V);
 // Whether the single-read kernel takes a logits target.
 bool logits_supported();
+// Whether the single-read kernel takes CE and KL (probability target only).
+bool xent_supported(bool logits);
 size_t workspace_bytes(int N, int W, int V);
 hipError_t run(const LossCall& c, void* workspace, hipStream_t stream);
 

@@ -176,3 +176,29 @@ def test_verify_and_loss_share_one_workspace():
         got = _loss_of(z, p, ws)
         assert got[0] == ref[0]
         assert np.array_equal(got[1], ref[1]) and np.array_equal(got[2], ref[2])
+
+
+@pytest.mark.parametrize("objective", ["ce", "kl"])
+@pytest.mark.parametrize("shape", [(4, 7, 20000), (3, 5, 20001)])
+@pytest.mark.parametrize("path", ["auto", "multi-pass"])
+def test_fp32_xent_gradient_against_the_oracle(objective, shape, path):
+    """CE / KL: the fp32 gradient q sum p - p (over N) against the oracle's
+    fp64 one, within 4e-6 (q sum p + p) / N: q carries about 1e-6 relative
+    error from the fp32 exponent reference, and q sum p - p cancels where q
+    is close to p, so the bound is absolute in the size of the two terms."""
+    c = synth.loss_case(n_branches=shape[0], width=shape[1], vocab=shape[2])
+    announce(f"fp32 gradient {objective} {path} shape={shape}")
+    dbg = run_debug_loss(c.draft_logits, c.target_probs, objective, path=path, want_f32=True)
+    N = shape[0]
+    worst = 0.0
+    for n in range(N):
+        z64 = obf16.decode(c.draft_logits[n])
+        p64 = np.asarray(c.target_probs[n], dtype=np.float64)
+        dz = ob.branch(z64, p64, N, objective)[2]
+        q = np.exp(z64 - z64.max(-1, keepdims=True))
+        q /= q.sum(-1, keepdims=True)
+        bound = 4e-6 * (q * p64.sum(-1, keepdims=True) + p64) / N
+        err = np.abs(dbg["dlogits_f32"][n] - dz)
+        worst = max(worst, float(np.max(err / np.maximum(bound, 1e-300))))
+        assert np.all(err <= bound + FP32_MIN_NORMAL), (n, float(err.max()))
+    announce(f"fp32 gradient {objective} {path}: largest error / bound {worst:.3g}")

@@ -3,9 +3,11 @@ comparators: per-step TV, CE, KL) against the oracle, through the C ABI.
 
 Small and ragged shapes are compared element by element. At the full
 workload (N=512, W=7, V=151936) the loss and every alpha are compared with
-the oracle run over all 512 branches, the gradient on 32 branches. The per-step TV loss runs on the
-single-read kernel (and, forced, on the multi-pass pipeline); CE and KL on
-the multi-pass pipeline. Gradient rules: tests/parity.py."""
+the oracle run over all 512 branches, the gradient on 32 branches. Every
+comparator runs on the single-read kernel (CE and KL streaming p a second
+time for the gradient) and, forced through the debug entry point, on the
+multi-pass pipeline; the single-read kernel's repair launch gives the same
+bits. Gradient rules: tests/parity.py."""
 
 import numpy as np
 import pytest
@@ -73,19 +75,24 @@ def test_comparators_shrunk(objective, vocab):
     _check_small(c.draft_logits, c.target_probs, objective, f"{objective} N=5 W=7 V={vocab}")
 
 
-def test_step_tv_on_both_paths():
+@pytest.mark.parametrize("objective", COMPARATORS)
+def test_comparators_on_both_paths(objective):
     c = synth.loss_case(n_branches=4, width=5, vocab=24000)
-    fused = _check_small(c.draft_logits, c.target_probs, "step_tv", "step_tv single-read")
-    multi = _check_small(c.draft_logits, c.target_probs, "step_tv", "step_tv multi-pass",
+    fused = _check_small(c.draft_logits, c.target_probs, objective, f"{objective} single-read",
+                         path="auto")
+    multi = _check_small(c.draft_logits, c.target_probs, objective, f"{objective} multi-pass",
                          path="multi-pass")
     assert rel_close(fused["loss"], multi["loss"], 1e-6)
+    assert np.all(rel_close(fused["alpha"], multi["alpha"], 1e-6))
 
 
-def test_step_tv_forced_repair_is_bit_identical():
-    c = synth.loss_case(n_branches=3, width=7, vocab=30000)
-    normal = run_draft_loss(c.draft_logits, c.target_probs, "step_tv")
-    announce("step_tv forced repair")
-    forced = run_debug_loss(c.draft_logits, c.target_probs, "step_tv", spin_limit=0)
+@pytest.mark.parametrize("objective", COMPARATORS)
+@pytest.mark.parametrize("vocab", [30000, 20001])
+def test_comparators_forced_repair_is_bit_identical(objective, vocab):
+    c = synth.loss_case(n_branches=3, width=7, vocab=vocab)
+    normal = run_draft_loss(c.draft_logits, c.target_probs, objective)
+    announce(f"{objective} forced repair V={vocab}")
+    forced = run_debug_loss(c.draft_logits, c.target_probs, objective, spin_limit=0)
     assert normal["loss"] == forced["loss"]
     assert np.array_equal(normal["alpha"], forced["alpha"])
     assert np.array_equal(normal["dlogits"], forced["dlogits"])
