@@ -251,9 +251,10 @@ _TRAFFIC_KERNELS = {
     "rows": "verify_rows_bf16<true, false>",
     "finalize": "verify_finalize<1>",
     "clear": "clear_words",
-    "loss": "loss_halves<true, false, false>",
-    "loss_finish": "loss_finish<true, false, false>",
-    "loss_logits": "loss_halves<true, true, false>",
+    "loss": "loss_halves<true, false, false, false>",
+    "loss_finish": "loss_finish<true, false, false, false>",
+    "loss_logits": "loss_halves<true, true, false, false>",
+    "loss_xent": "loss_halves<true, false, false, true>",
     "trunc": "trunc_rows<1, true>",
     "rows_trunc": "verify_rows_bf16<true, true>",
 }
@@ -314,6 +315,7 @@ def traffic_from_counters(fetch_csv, write_csv):
         out[f"loss_finish_{key}_bytes"] = nth("loss_finish")
         out[f"clear_words_{key}_bytes"] = nth("clear")
         out[f"loss_logits_T1.0_{key}_bytes"] = nth("loss_logits")
+        out[f"loss_ce_{key}_bytes"] = nth("loss_xent")
         out[f"trunc_topk50_{key}_bytes"] = nth("trunc")
         out[f"rows_topk50_{key}_bytes"] = nth("rows_trunc")
     out["loss_bytes_per_launch"] = out["loss_fetch_bytes"] + out["loss_write_bytes"]
