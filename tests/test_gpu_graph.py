@@ -1,8 +1,9 @@
 """The hot path captured in a HIP graph and replayed.
 
-One verify call per temperature, one verify call with top-k / top-p and one
-loss call (probability target and logits target) are captured once into a
-graph on torch's capture stream,
+One verify call per temperature, one verify call with top-k / top-p and the
+loss calls (E2E-TV with a probability target and with a logits target, and
+the cross-entropy and KL comparators) are captured once into a graph on
+torch's capture stream,
 then replayed several times with eager work and synchronisations between the
 replays; every replay must reproduce the eager outputs bit for bit. The
 library enqueues kernels only (no memset nodes, no allocation, no host
@@ -42,9 +43,11 @@ def test_hot_path_replays_match_eager():
     N, W, V = lc.draft_logits.shape
     louts = [(torch.empty(1, dtype=torch.float32, device=dev),
               torch.empty(N, W, dtype=torch.float32, device=dev),
-              torch.empty(N, W, V, dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+              torch.empty(N, W, V, dtype=torch.bfloat16, device=dev)) for _ in range(4)]
     vws = lv.new_workspace(lv.spec_verify_workspace_bytes(B, K, vcases[0].shape[2]), dev)
-    lws = lv.new_workspace(lv.e2e_tv_loss_workspace_bytes(N, W, V), dev)
+    lws = lv.new_workspace(max(lv.e2e_tv_loss_workspace_bytes(N, W, V),
+                               lv.draft_loss_workspace_bytes(N, W, V),
+                               lv.draft_loss_logits_workspace_bytes(N, W, V)), dev)
     tws = lv.new_workspace(lv.spec_verify_topkp_workspace_bytes(B, K, vcases[0].shape[2]), dev)
     top_k = torch.tensor([50, 3, 0, 200, 1, 40000, 7, 50][:B], dtype=torch.int32, device=dev)
     top_p = torch.tensor([0.9, 1.0, 0.8, 0.95, 1.0, 0.5, 0.99, 1.0][:B], dtype=torch.float32,
@@ -60,6 +63,8 @@ def test_hot_path_replays_match_eager():
         lv.spec_verify_topkp(**vins[1], top_k=top_k, top_p=top_p, workspace=tws, out=touts)
         lv.e2e_tv_loss_fwd_bwd(z, p, workspace=lws, out=louts[0])
         lv.draft_loss_logits_fwd_bwd(z, t, 0.8, "e2e_tv", workspace=lws, out=louts[1])
+        lv.draft_loss_fwd_bwd(z, p, "ce", workspace=lws, out=louts[2])
+        lv.draft_loss_fwd_bwd(z, p, "kl", workspace=lws, out=louts[3])
 
     all_outs = [x for o in vouts for x in o] + list(touts) + [x for o in louts for x in o]
     # eager reference (on a side stream, as graph warm-up is done)
