@@ -149,6 +149,104 @@ __device__ __forceinline__ void apply_keep(Grp<kDtype>& g, int e, float sk, int 
   }
 }
 
+// A truncated row's keep rule on the raw logits. The scaled logit
+// s(x) = scale_logit(x) never decreases as x grows, so "s > sk" is "x > xa"
+// with xa the largest input value whose s is at most sk, and "s == sk" is
+// "xe <= x <= xa" with xe the smallest whose s is at least sk: a token is
+// kept iff x > xa, or x >= xe and its id is at most idx. The bounds are
+// found by bisection over the input format's values in order (16 steps for
+// bf16, 32 for fp32; s itself at T = 1).
+struct KeepCut {
+  float xa, xe;
+  int idx;
+};
+
+__device__ __forceinline__ uint32_t asc_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float asc_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// The input format's values in ascending order, by position.
+template <int kDtype>
+__device__ __forceinline__ uint32_t fmt_pos(float x) {
+  return kDtype == 1 ? asc_key(x) >> 16 : asc_key(x);
+}
+
+template <int kDtype>
+__device__ __forceinline__ float fmt_at(uint32_t i) {
+  if constexpr (kDtype == 1)
+    return asc_value((i << 16) | ((i & 0x8000u) ? 0u : 0xffffu));
+  else
+    return asc_value(i);
+}
+
+template <int kDtype>
+__device__ __forceinline__ KeepCut keep_cut(const KeepRow& kr, float inv_t, bool unit) {
+  const float sk = key_value(kr.key);
+  KeepCut k{sk, sk, kr.idx};
+  if (unit) return k;
+  // largest position with s <= sk: s(-inf) = -inf <= sk, s(+inf) = +inf > sk
+  uint32_t lo = fmt_pos<kDtype>(-INFINITY), hi = fmt_pos<kDtype>(INFINITY);
+  while (hi - lo > 1) {
+    const uint32_t mid = lo + (hi - lo) / 2;
+    if (scale_logit(fmt_at<kDtype>(mid), inv_t, false) <= sk)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  k.xa = fmt_at<kDtype>(lo);
+  // smallest position with s >= sk
+  if (sk == -INFINITY) {
+    k.xe = -INFINITY;
+  } else {
+    lo = fmt_pos<kDtype>(-INFINITY);
+    hi = fmt_pos<kDtype>(INFINITY);
+    while (hi - lo > 1) {
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (scale_logit(fmt_at<kDtype>(mid), inv_t, false) >= sk)
+        hi = mid;
+      else
+        lo = mid;
+    }
+    k.xe = fmt_at<kDtype>(hi);
+  }
+  return k;
+}
+
+// overlap_tile over a pair whose rows are both truncated: a dropped token
+// has p (q) = 0, the value its -inf logit would give.
+template <int kDtype, bool kPair>
+__device__ __forceinline__ void overlap_tile_cut(const Grp<kDtype>& gt, const Grp<kDtype>& gd,
+                                                 int e, float c, float nrt, float nrd,
+                                                 const KeepCut& kt, const KeepCut& kd, float& sa,
+                                                 float* chunk_row, int t) {
+  float r = 0.f;
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    const float xt = gelem(gt, j);
+    const bool keep_t = (xt > kt.xa) | ((xt >= kt.xe) & (e + j <= kt.idx));
+    const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(xt, c, nrt));
+    const float p = keep_t ? pe : 0.f;
+    if constexpr (kPair) {
+      const float xd = gelem(gd, j);
+      const bool keep_d = (xd > kd.xa) | ((xd >= kd.xe) & (e + j <= kd.idx));
+      const float qe = __builtin_amdgcn_exp2f(__builtin_fmaf(xd, c, nrd));
+      const float q = keep_d ? qe : 0.f;
+      const float mn = fminf(p, q);
+      sa += mn;
+      r += p - mn;
+    } else {
+      r += p;
+    }
+  }
+  const float cm = wsum(r);
+  if ((threadIdx.x & (kWave - 1)) == 0) chunk_row[t * kWaves + threadIdx.x / kWave] = cm;
+}
+
 template <int kDtype, bool kVecOk, bool kPair, bool kTrunc>
 __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float T, Shared& sh) {
   constexpr int kHold = hold_tiles<kDtype>();
@@ -254,6 +352,9 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
         write_row(Rt, Lt, Rd, Ld, alpha);
         return;
       }
+      // one pass, the keep rule applied on the raw logits
+      const KeepCut ct = keep_cut<kDtype>(kp.t, inv_t, unit);
+      const KeepCut cd = kPair ? keep_cut<kDtype>(kp.d, inv_t, unit) : ct;
       float sa = 0.f;
       int t = 0;
       for (; t + kBatch <= nfull; t += kBatch) {
@@ -264,24 +365,23 @@ __device__ __forceinline__ void sampling_row(const Args& a, int b, int k, float 
           if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t + n), gd[n]);
         }
 #pragma unroll
-        for (int n = 0; n < kBatch; ++n) {
-          mk(gt[n], gd[n], t + n);
-          overlap_tile<kDtype, kPair>(gt[n], gd[n], c, nrt, nrd, sa, chunk_row, t + n);
-        }
+        for (int n = 0; n < kBatch; ++n)
+          overlap_tile_cut<kDtype, kPair>(gt[n], gd[n], tile_elem(t + n), c, nrt, nrd, ct, cd, sa,
+                                          chunk_row, t + n);
       }
       for (; t < nfull; ++t) {
         Grp<kDtype> gt, gd;
         load_grp<kDtype, kVecOk, true>(trow, V, tile_elem(t), gt);
         if constexpr (kPair) load_grp<kDtype, kVecOk, true>(drow, V, tile_elem(t), gd);
-        mk(gt, gd, t);
-        overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, t);
+        overlap_tile_cut<kDtype, kPair>(gt, gd, tile_elem(t), c, nrt, nrd, ct, cd, sa, chunk_row,
+                                        t);
       }
       if (tail) {
         Grp<kDtype> gt, gd;
         load_tail<kDtype, kVecOk>(trow, V, nfull, gt);
         if constexpr (kPair) load_tail<kDtype, kVecOk>(drow, V, nfull, gd);
-        mk(gt, gd, nfull);
-        overlap_tile<kDtype, kPair>(gt, gd, c, nrt, nrd, sa, chunk_row, nfull);
+        overlap_tile_cut<kDtype, kPair>(gt, gd, tile_elem(nfull), c, nrt, nrd, ct, cd, sa,
+                                        chunk_row, nfull);
       }
       const float alpha = kPair ? block_sum1(sa, sh) : 0.f;
       write_row(Rt, Lt, Rd, Ld, alpha);
