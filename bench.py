@@ -286,7 +286,7 @@ def traffic_from_counters(fetch_csv, write_csv):
     step's kernels are the first launches after the calibration: the
     verify row kernel and finalize of T = 0, 0.6, 1.0 in that order, then
     the loss call; the logits-target loss and the top-k/top-p kernels are
-    the first launches of theirs."""
+    the first launches of theirs (top-p alone: the fifth)."""
     out = {"kernel_source_hash": kernel_source_hash(),
            "method": ("rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (separate runs) of "
                       "bench.py --steps 1 --warmup 0 --calls 3 --no-cpu-baseline "
@@ -318,6 +318,9 @@ def traffic_from_counters(fetch_csv, write_csv):
         out[f"loss_ce_{key}_bytes"] = nth("loss_xent")
         out[f"trunc_topk50_{key}_bytes"] = nth("trunc")
         out[f"rows_topk50_{key}_bytes"] = nth("rows_trunc")
+        # top-p alone follows the top-k 50 calls (one untimed and 3 timed)
+        out[f"trunc_topp_{key}_bytes"] = nth("trunc", 4)
+        out[f"rows_topp_{key}_bytes"] = nth("rows_trunc", 4)
     out["loss_bytes_per_launch"] = out["loss_fetch_bytes"] + out["loss_write_bytes"]
     for t in TEMPS:
         rows = out[f"verify_T{t}_rows_fetch"] + out[f"verify_T{t}_rows_write"]
@@ -550,6 +553,19 @@ def main():
         },
         "kernel_source_hash": src_hash,
     }
+    def traffic_of(*prefixes):
+        """Counter bytes (FETCH_SIZE + WRITE_SIZE, scaled) of one launch of
+        each named kernel, summed; None without counters for this build."""
+        if not traffic:
+            return None
+        tot = 0.0
+        for pre in prefixes:
+            f, w = traffic.get(f"{pre}_fetch_bytes"), traffic.get(f"{pre}_write_bytes")
+            if f is None or w is None:
+                return None
+            tot += f + w
+        return tot
+
     result["components"]["e2e_tv_loss_fwd_bwd"] = {
         **loss_t, "rows_per_s": LOSS_N * LOSS_W / (loss_ms * 1e-3), "gbs": loss_gbs,
         "frac": loss_gbs / HBM_PEAK_GBS, "algorithmic_bytes": lb}
@@ -562,7 +578,8 @@ def main():
         ms = t["ms"]
         variants[f"draft_loss_{name}"] = {
             **t, "gbs": lb / (ms * 1e-3) / 1e9,
-            "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb}
+            "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb,
+            "traffic": traffic_of("loss_ce") if name == "ce" else None}
     # The loss with the target given as bf16 logits (target softmax fused;
     # algorithmic bytes 6 per token: z 2 + t 2 read, dz 2 written).
     lgc = synth.loss_logits_case(workers=min(16, os.cpu_count() or 1))
@@ -575,7 +592,8 @@ def main():
         ms = t["ms"]
         variants[f"draft_loss_logits_{name}_T{temp}"] = {
             **t, "gbs": lb6 / (ms * 1e-3) / 1e9,
-            "frac": lb6 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb6}
+            "frac": lb6 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": lb6,
+            "traffic": traffic_of("loss_logits_T1.0") if temp == 1.0 else None}
     del tl
     result["loss_variants"] = variants
     log("loss variants: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in variants.items()))
@@ -596,7 +614,16 @@ def main():
     ms = t["ms"]
     vvar["spec_verify_topkp_T1.0_k50_p0.9"] = {
         **t, "rows_per_s": VERIFY_B * (VERIFY_K + 1) / (ms * 1e-3),
-        "gbs": vb / (ms * 1e-3) / 1e9, "algorithmic_bytes": vb}
+        "gbs": vb / (ms * 1e-3) / 1e9, "frac": vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": vb, "traffic": traffic_of("trunc_topk50", "rows_topk50")}
+    tk0 = torch.zeros((VERIFY_B,), dtype=torch.int32, device=dev)
+    t = time_calls(lambda: lv.spec_verify_topkp(**vin[2], top_k=tk0, top_p=tp, workspace=tws,
+                                                out=vouts[2]))
+    ms = t["ms"]
+    vvar["spec_verify_topkp_T1.0_p0.9"] = {
+        **t, "rows_per_s": VERIFY_B * (VERIFY_K + 1) / (ms * 1e-3),
+        "gbs": vb / (ms * 1e-3) / 1e9, "frac": vb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_bytes": vb, "traffic": traffic_of("trunc_topp", "rows_topp")}
     del tws
     rc = synth.verify_case(5)
     rvocab = rc.target.shape[2]
@@ -611,6 +638,7 @@ def main():
     ms = t["ms"]
     vvar["spec_verify_ragged_padded"] = {
         **t, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
+        "frac": rb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes": rb, "requests": int(rc.k.size), "rows": rrows, "vocab": rvocab}
     kk = np.asarray(rc.k, dtype=np.int64)
     off = np.zeros(kk.size + 1, dtype=np.int32)
@@ -627,6 +655,7 @@ def main():
     ms = t["ms"]
     vvar["spec_verify_ragged_packed"] = {
         **t, "rows_per_s": rrows / (ms * 1e-3), "gbs": rb / (ms * 1e-3) / 1e9,
+        "frac": rb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "algorithmic_bytes": rb, "requests": int(rc.k.size), "rows": rrows, "vocab": rvocab}
     del pt, pdr, ptok, rc
     result["verify_variants"] = vvar
