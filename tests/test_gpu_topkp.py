@@ -298,11 +298,13 @@ def test_topkp_workspace_contents_do_not_matter():
             assert np.array_equal(x, y)
 
 
-def test_truncation_off_equals_plain_verify():
+@pytest.mark.parametrize("vocab", [None, 30000])
+def test_truncation_off_equals_plain_verify(vocab):
     """top_k <= 0 or >= V and top_p >= 1 keep every token: the outputs are
-    bit-identical to spec_verify's on the full-vocabulary workload."""
+    bit-identical to spec_verify's, on the full-vocabulary workload and on
+    short rows (7 tiles and a partial one)."""
     dev = device()
-    case = synth.verify_case(3, temperature=0.6, batch=16)
+    case = synth.verify_case(3, temperature=0.6, batch=16, vocab=vocab)
     B, _, V = case.shape
     top_k = np.where(np.arange(B) % 2 == 0, 0, V).astype(np.int32)
     top_p = np.where(np.arange(B) % 3 == 0, 1.0, 2.5).astype(np.float32)

@@ -227,6 +227,26 @@ def test_vector_and_element_load_paths_agree():
             assert np.array_equal(aligned[key], other[key]), key
 
 
+@pytest.mark.parametrize("vocab", [4096, 9000, 12288, 16400, 24576, 30000, 32768])
+def test_vector_and_element_loads_agree_for_every_tile_count(vocab):
+    """The vector and element load paths (aligned and unaligned copies of
+    the same inputs) give bit-identical outputs for every tile count from 1
+    to 8, with and without a partial last tile: the row statistics' batches
+    (streamed tiles, the held tiles, the tail) take every shape there."""
+    dev = device()
+    for temperature in (0.7, 1.0):
+        case = synth.verify_case(3, temperature=temperature, batch=3, vocab=vocab)
+        inputs = verify_inputs(case, dev)
+        announce(f"load paths V={vocab} T={temperature}")
+        vec = run_verify(case, dev, inputs)
+        shifted = dict(inputs)
+        shifted["target_logits"] = _offset_copy(inputs["target_logits"], 1)
+        shifted["draft_logits"] = _offset_copy(inputs["draft_logits"], 3)
+        elem = run_verify(case, dev, shifted)
+        for key in vec:
+            assert np.array_equal(vec[key], elem[key]), (key, vocab, temperature)
+
+
 def test_workspace_contents_do_not_matter():
     """A call depends on nothing a previous call left in the workspace: a
     workspace full of garbage gives the same outputs as a fresh one."""
