@@ -118,6 +118,32 @@ def test_topkp_ragged_against_oracle(dtype_case, temperature):
              f"ragged case={dtype_case} T={temperature}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("temperature", [0.7, 1.3])
+def test_topp_wide_cuts_against_oracle(dtype, temperature):
+    """Top-p cuts in the body of Zipf-shaped rows, aligned rows of both
+    dtypes, against the oracle. At T = 1.3 the rows are flat enough that the
+    cuts keep more tokens than the selection list holds, so the row kernel
+    makes its one pass with the keep rule on the raw logits (bounds found by
+    bisection over the input format, T != 1); at T = 0.7 they keep a few
+    hundred and take the list path."""
+    dev = device()
+    case = synth.verify_case(3, temperature=temperature, batch=12, vocab=24576,
+                             k_values=[(b * 3) % 8 for b in range(12)])
+    if dtype == "f32":
+        case.dtype = "f32"
+        case.target = synth.from_bf16(case.target)
+        case.draft = synth.from_bf16(case.draft)
+    B = case.shape[0]
+    top_k = np.zeros(B, np.int32)
+    # cuts in the body of the distribution, where the boundary token's own
+    # weight keeps the truncation margin above the excusal threshold
+    top_p = np.array([0.9, 0.95, 0.8, 0.97, 0.85, 0.93] * 2, np.float32)[:B]
+    announce(f"topp wide cuts {dtype} T={temperature} shape={case.shape}")
+    _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p,
+             f"wide cuts {dtype} T={temperature}")
+
+
 def test_topkp_greedy_and_mixed_temperatures():
     dev = device()
     case = synth.verify_case(3, batch=17, vocab=5000, kmax=5)
