@@ -568,7 +568,8 @@ def main():
 
     result["components"]["e2e_tv_loss_fwd_bwd"] = {
         **loss_t, "rows_per_s": LOSS_N * LOSS_W / (loss_ms * 1e-3), "gbs": loss_gbs,
-        "frac": loss_gbs / HBM_PEAK_GBS, "algorithmic_bytes": lb}
+        "frac": loss_gbs / HBM_PEAK_GBS, "algorithmic_bytes": lb,
+        "traffic": traffic_of("loss", "clear_words", "loss_finish")}
     # The per-position comparators of the loss on the same inputs, outside
     # the step.
     variants = {}
