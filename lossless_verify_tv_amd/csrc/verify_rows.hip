@@ -615,15 +615,31 @@ namespace {
 
 // ------------------------------------------------------------------ finalize
 
+// One DPP move of an fp64 value (both halves with the same control); lanes
+// without a source, or in rows the row mask leaves out, read 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b)), kCtrl, kRowMask,
+                                                           0xf, true));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), kCtrl,
+                                                           kRowMask, 0xf, true));
+  return __longlong_as_double((long long)((uint64_t(hi) << 32) | lo));
+}
+
 // Block-wide exclusive scan in fp64 (fixed order); `total` gets the sum.
+// Within a wave: an inclusive scan of each 16-lane row by row shifts of 1,
+// 2, 4 and 8 lanes, then rows 1 and 3 add the last lane of the row before
+// them and rows 2 and 3 the last lane of row 1 (row broadcasts 15 and 31).
 __device__ __forceinline__ double block_exscan(double v, Shared& sh, double& total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   double inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double n = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += n;
-  }
+  inc += dpp_f64<0x111, 0xf>(inc);  // row_shr:1
+  inc += dpp_f64<0x112, 0xf>(inc);  // row_shr:2
+  inc += dpp_f64<0x114, 0xf>(inc);  // row_shr:4
+  inc += dpp_f64<0x118, 0xf>(inc);  // row_shr:8
+  inc += dpp_f64<0x142, 0xa>(inc);  // row_bcast:15 into rows 1 and 3
+  inc += dpp_f64<0x143, 0xc>(inc);  // row_bcast:31 into rows 2 and 3
   __syncthreads();
   if (lane == kWave - 1) sh.d[wave] = inc;
   __syncthreads();
@@ -789,6 +805,7 @@ struct FinShared {
   Shared red;
   double ratio[LVTV_MAX_K];
   double uacc[LVTV_MAX_K];
+  double udraw[LVTV_MAX_K + 1];  // word 1 of each position's Philox block
   int j;
   RowOut rc[LVTV_MAX_K + 1];  // the request's row records, read once
 };
@@ -868,12 +885,15 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const float inv_t = __fdiv_rn(1.f, T);
   // accept inputs for every position in parallel: u_k, and p(y_k)/q(y_k)
   // as the row kernel evaluated it (prob64_of with the row's statistics)
-  if (int(threadIdx.x) < kb) {
+  if (int(threadIdx.x) <= kb) {
     const int k = threadIdx.x;
     double u, u2;
     verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
-    fs.uacc[k] = u;
-    fs.ratio[k] = get_ratio(fs.rc[k]);
+    fs.udraw[k] = u2;
+    if (k < kb) {
+      fs.uacc[k] = u;
+      fs.ratio[k] = get_ratio(fs.rc[k]);
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -890,8 +910,7 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const int j = fs.j;
 
   // the draw at position j
-  double u_acc, u_draw;
-  verify_uniforms(a.seed[b], uint64_t(b), uint64_t(j), u_acc, u_draw);
+  const double u_draw = fs.udraw[j];
   const bool residual = j < kb;
   const RowOut r = fs.rc[j];
   const void* trow = row_ptr<kDtype>(a, b, true, j);
