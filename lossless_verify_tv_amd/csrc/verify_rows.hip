@@ -713,11 +713,11 @@ __device__ __forceinline__ int pick_chunk(const float* m, int NC, double u, Shar
 }
 
 // pick_chunk for NC <= kThreads chunks in one block scan: thread c holds
-// chunk c's mass. Returns -1 (every thread) when no chunk has positive mass.
-__device__ __forceinline__ int pick_chunk_small(const float* m, int NC, double u, Shared& sh,
+// chunk c's mass mc (0 past NC). Returns -1 (every thread) when no chunk has
+// positive mass.
+__device__ __forceinline__ int pick_chunk_small(double mc, int NC, double u, Shared& sh,
                                                 double& rem) {
   const int c = threadIdx.x;
-  const double mc = c < NC ? (double)m[c] : 0.0;
   double total;
   const double exc = block_exscan(mc, sh, total);
   const double target = u * total;
@@ -733,6 +733,12 @@ __device__ __forceinline__ int pick_chunk_small(const float* m, int NC, double u
   const int last = -block_min((c < NC && mc > 0.0) ? -c : INT_MAX, sh);
   rem = INFINITY;
   return last == -INT_MAX ? -1 : last;
+}
+
+__device__ __forceinline__ int pick_chunk_small(const float* m, int NC, double u, Shared& sh,
+                                                double& rem) {
+  const int c = threadIdx.x;
+  return pick_chunk_small(c < NC ? (double)m[c] : 0.0, NC, u, sh, rem);
 }
 
 // Token of chunk c at remaining mass `rem`: fp64 weights of the chunk's 512
@@ -806,8 +812,10 @@ struct FinShared {
   double ratio[LVTV_MAX_K];
   double uacc[LVTV_MAX_K];
   double udraw[LVTV_MAX_K + 1];  // word 1 of each position's Philox block
+  double cmass;                  // the chosen chunk's mass
   int j;
   RowOut rc[LVTV_MAX_K + 1];  // the request's row records, read once
+  int32_t y[LVTV_MAX_K];      // its draft tokens, read once
 };
 
 template <int kDtype>
@@ -815,8 +823,10 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   __shared__ FinShared fs;
   Shared& sh = fs.red;
   const int b = blockIdx.x;
+  const int tid = threadIdx.x;
   const float T = a.temp[b];
   const int Kmax = a.Kmax;
+  const int NC = a.NC;
   int kb;
   Slots o;
   if (a.toff) {
@@ -838,10 +848,16 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const int32_t* y = a.tokens + draft_row(a, b, 0);
   const RowOut* rows = a.rows + target_row(a, b, 0);
   int bad = 0, fault = 0;
-  if (k_ok) {
-    for (int k = threadIdx.x; k <= kb; k += kThreads) {
-      if (k < kb) bad |= (y[k] < 0 || y[k] >= a.V);
-      if (!t_ok) continue;
+  // kb <= LVTV_MAX_K < kThreads: thread k takes position k, and the draft
+  // tokens and row records go to LDS for the serial steps below
+  if (k_ok && tid <= kb) {
+    const int k = tid;
+    if (k < kb) {
+      const int32_t yv = y[k];
+      fs.y[k] = yv;
+      bad |= (yv < 0 || yv >= a.V);
+    }
+    if (t_ok) {
       const RowOut r = rows[k];
       fs.rc[k] = r;
       if (greedy) {
@@ -868,13 +884,14 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
     if (threadIdx.x == 0) {
       int j = kb;
       for (int k = 0; k < kb; ++k)
-        if (y[k] != rows[k].arg_t) {
+        if (fs.y[k] != fs.rc[k].arg_t) {
           j = k;
           break;
         }
       for (int k = 0; k < o.nalpha; ++k)
-        out_alpha[k] = (k < kb) ? (rows[k].arg_t == rows[k].arg_d ? 1.f : 0.f) : 0.f;
-      for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? y[k] : (k == j ? rows[j].arg_t : -1);
+        out_alpha[k] = (k < kb) ? (fs.rc[k].arg_t == fs.rc[k].arg_d ? 1.f : 0.f) : 0.f;
+      for (int k = 0; k < o.ntok; ++k)
+        out_tok[k] = k < j ? fs.y[k] : (k == j ? fs.rc[j].arg_t : -1);
       a.acc_len[b] = j;
       a.status[b] = 0;
     }
@@ -885,8 +902,8 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const float inv_t = __fdiv_rn(1.f, T);
   // accept inputs for every position in parallel: u_k, and p(y_k)/q(y_k)
   // as the row kernel evaluated it (prob64_of with the row's statistics)
-  if (int(threadIdx.x) <= kb) {
-    const int k = threadIdx.x;
+  if (tid <= kb) {
+    const int k = tid;
     double u, u2;
     verify_uniforms(a.seed[b], uint64_t(b), uint64_t(k), u, u2);
     fs.udraw[k] = u2;
@@ -915,22 +932,27 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   const RowOut r = fs.rc[j];
   const void* trow = row_ptr<kDtype>(a, b, true, j);
   const void* drow = residual ? row_ptr<kDtype>(a, b, false, j) : nullptr;
-  float* m = a.chunk + size_t(target_row(a, b, j)) * a.NC;
-  const int NC = a.NC;
+  float* m = a.chunk + size_t(target_row(a, b, j)) * NC;
   const KeepPair kp = a.keep ? a.keep[target_row(a, b, j)] : KeepPair{keep_all(), keep_all()};
   double rem;
   int c;
+  double cmass;
   if (NC <= kThreads) {
     // one block scan of the chunk masses gives the total and every chunk's
     // running mass
-    c = pick_chunk_small(m, NC, u_draw, sh, rem);
+    double mc = tid < NC ? (double)m[tid] : 0.0;
+    c = pick_chunk_small(mc, NC, u_draw, sh, rem);
     if (c < 0 && residual) {
       // residual zero everywhere: draw from p_j
       p_chunk_masses<kDtype>(trow, a.V, NC, inv_t, unit, r.Rt, r.Lt, kp.t, m);
       drow = nullptr;
-      c = pick_chunk_small(m, NC, u_draw, sh, rem);
+      mc = tid < NC ? (double)m[tid] : 0.0;
+      c = pick_chunk_small(mc, NC, u_draw, sh, rem);
     }
     if (c < 0) c = 0;
+    if (tid == c) fs.cmass = mc;
+    __syncthreads();
+    cmass = fs.cmass;
   } else {
     int any = 0;
     for (int cc = threadIdx.x; cc < NC; cc += kThreads) any |= m[cc] > 0.f;
@@ -940,8 +962,8 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
       drow = nullptr;
     }
     c = pick_chunk(m, NC, u_draw, sh, rem);
+    cmass = (double)m[c];
   }
-  const double cmass = (double)m[c];
   int v = search_chunk<kDtype>(trow, drow, a.V, c, rem, cmass, inv_t, unit, r.Rt, r.Lt, r.Rd,
                                r.Ld, kp, sh);
   if (v < 0 && drow) {
@@ -955,7 +977,7 @@ __device__ __forceinline__ void finalize_body(const Args& a) {
   }
   if (v < 0 || v >= a.V) v = a.V - 1;  // unreachable: the chosen chunk has positive mass
   if (threadIdx.x == 0) {
-    for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? y[k] : (k == j ? v : -1);
+    for (int k = 0; k < o.ntok; ++k) out_tok[k] = k < j ? fs.y[k] : (k == j ? v : -1);
     a.acc_len[b] = j;
     a.status[b] = 0;
   }
