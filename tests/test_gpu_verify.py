@@ -15,7 +15,7 @@ from scipy.stats import chisquare
 import lossless_verify_tv_amd as lv
 from lossless_verify_tv_amd import synth
 
-from .gpu_util import announce, device, run_oracle_verify, run_verify, verify_inputs
+from .gpu_util import announce, device, logits_to_device, run_oracle_verify, run_verify, verify_inputs
 from .parity import check_excused_bound, compare_verify
 
 pytestmark = pytest.mark.gpu
@@ -82,6 +82,38 @@ def test_tiny_vocab():
         _check(case, f"V={V} T=1")
         case.temperature[:] = 0.0
         _check(case, f"V={V} T=0")
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.8])
+def test_max_draft_positions(temperature):
+    """Kmax at its limit (16 draft positions), K_b from 0 to 16 across the
+    batch, padded and packed layouts, against the oracle."""
+    dev = device()
+    ks = [16, 0, 7, 16, 1, 12, 16, 3]
+    case = synth.verify_case(3, temperature=temperature, batch=len(ks), kmax=16, vocab=6000,
+                             k_values=ks)
+    _check(case, f"Kmax=16 T={temperature}")
+    # the packed layout of the same requests gives the same outputs
+    inputs = verify_inputs(case, dev)
+    padded = run_verify(case, dev, inputs)
+    kk = np.asarray(ks)
+    off = np.zeros(len(ks) + 1, np.int32)
+    off[1:] = np.cumsum(kk + 1)
+    pt = logits_to_device(np.concatenate([case.target[b, :kk[b] + 1] for b in range(len(ks))]),
+                          case.dtype, dev)
+    pd = logits_to_device(np.concatenate([case.draft[b, :kk[b]] for b in range(len(ks))]),
+                          case.dtype, dev)
+    ptok = torch.from_numpy(np.concatenate([case.tokens[b, :kk[b]] for b in range(len(ks))])
+                            .astype(np.int32)).to(dev)
+    acc, toks, alpha, status = lv.spec_verify_packed(pt, pd, ptok, torch.from_numpy(off).to(dev),
+                                                     inputs["temperature"], inputs["seed"])
+    torch.cuda.synchronize(dev)
+    acc, toks, alpha, status = (x.cpu().numpy() for x in (acc, toks, alpha, status))
+    assert np.array_equal(acc, padded["accepted_len"]) and np.array_equal(status, padded["status"])
+    for b in range(len(ks)):
+        assert np.array_equal(toks[off[b]:off[b + 1]], padded["tokens"][b, :kk[b] + 1]), b
+        assert np.array_equal(alpha[off[b] - b:off[b + 1] - b - 1].view(np.uint32),
+                              padded["alpha"][b, :kk[b]].view(np.uint32)), b
 
 
 def test_faulted_requests():
