@@ -19,7 +19,10 @@ on, and the CPU oracle timed on the step's own inputs.
 Per-call times (the step's components, the variants, the small workloads)
 are medians over many calls, each call bracketed by its own pair of events
 with a 1 GiB write between calls outside the brackets, so that no call is
-served from the 256 MB last-level cache by the one before it.
+served from the 256 MB last-level cache by the one before it. The step's
+components also carry batched times: the median over 5 batches of
+back-to-back calls of the batch time per call, the verify inputs rotated
+over 4 copies (4 x 292 MB) for the same reason.
 
 ``python bench.py --trace-summary <kernel_trace.csv>`` prints per-kernel
 launch statistics from a rocprofv3 kernel trace, and the per-launch medians
@@ -495,6 +498,41 @@ def main():
                                           for t, m in zip(TEMPS, verify_ms)) +
         f", loss {loss_ms:.3f} ms")
 
+    # Batched per-call times: 5 batches of back-to-back calls, each batch
+    # between two events (a 1 GiB write before each batch, outside them);
+    # the verify calls rotate over 4 copies of their inputs (4 x 292 MB,
+    # beyond the 256 MB last-level cache), the loss reads 4.4 GB per call.
+    # Median over the batches of the batch time per call.
+    def batched(fns, n, nb=5):
+        flush_buf.fill_(1.0)  # also keeps these calls from reading as a bench step in a trace
+        for fn in fns:
+            fn()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(nb):
+            flush_buf.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for c in range(n):
+                fns[c % len(fns)]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n)
+        return {"ms": float(np.median(per)), "batches": nb, "calls_per_batch": n,
+                "ms_per_batch": [float(x) for x in per]}
+
+    verify_b = []
+    for i in range(len(TEMPS)):
+        copies = [vin[i]] + [dict(vin[i], target_logits=vin[i]["target_logits"].clone(),
+                                  draft_logits=vin[i]["draft_logits"].clone()) for _ in range(3)]
+        verify_b.append(batched([lambda v=v, i=i: lv.spec_verify(**v, workspace=vws, out=vouts[i])
+                                 for v in copies], n_v))
+        del copies
+    loss_b = batched([lambda: lv.e2e_tv_loss_fwd_bwd(z, p, workspace=lws, out=lout)], n_l)
+    log("batched per-call times: " + ", ".join(f"verify T={t} {b['ms'] * 1e3:.1f} us"
+                                               for t, b in zip(TEMPS, verify_b)) +
+        f", loss {loss_b['ms']:.3f} ms")
+
     rows_step = len(TEMPS) * sum(int(k) + 1 for k in base.k) + LOSS_N * LOSS_W
     vb = verify_bytes(base.k, VOCAB)
     lb = loss_bytes(LOSS_N, LOSS_W, VOCAB)
@@ -527,7 +565,10 @@ def main():
         "timing": (f"value and ms_per_step: {args.steps} back-to-back steps between two events; "
                    f"roofline: mean over those steps of the loss call between its own two "
                    f"events; per-call ms: median of {n_v} calls ({n_l} for the loss) each "
-                   f"between its own two events, a 1 GiB write between calls outside them"),
+                   f"between its own two events, a 1 GiB write between calls outside them; "
+                   f"'batched': median over 5 batches of {n_v} back-to-back calls ({n_l} "
+                   f"for the loss) of the batch time per call, verify inputs rotated over 4 "
+                   f"copies"),
         "roofline": {
             "kernel": ("loss_halves, timed as the e2e_tv_loss_fwd_bwd call inside each timed "
                        "step (one pair of events on the call's stream: clear_words + "
@@ -549,6 +590,7 @@ def main():
                 "frac": vb / (verify_ms[i] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "algorithmic_bytes": vb,
                 "traffic": (traffic or {}).get(f"verify_T{t}_bytes_per_launch"),
+                "batched": verify_b[i],
             } for i, t in enumerate(TEMPS)
         },
         "kernel_source_hash": src_hash,
@@ -569,7 +611,7 @@ def main():
     result["components"]["e2e_tv_loss_fwd_bwd"] = {
         **loss_t, "rows_per_s": LOSS_N * LOSS_W / (loss_ms * 1e-3), "gbs": loss_gbs,
         "frac": loss_gbs / HBM_PEAK_GBS, "algorithmic_bytes": lb,
-        "traffic": traffic_of("loss", "clear_words", "loss_finish")}
+        "traffic": traffic_of("loss", "clear_words", "loss_finish"), "batched": loss_b}
     # The per-position comparators of the loss on the same inputs, outside
     # the step.
     variants = {}
