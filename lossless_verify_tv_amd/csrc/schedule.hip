@@ -16,12 +16,12 @@
 // B - R largest survivals, which form a prefix of every request. The kernel:
 //   1. survivals in binary32, left to right (confidences clamped to [0, 1],
 //      NaN read as 0), as 64-bit keys: the complement of the value's bits
-//      above the flat index r L + j, so that one ascending sort orders them
-//      largest first and equal values by index;
-//   2. a bitonic sort of the keys, held E = 1, 2, 4 or 8 per thread: stages
-//      whose partners share a thread swap in registers, partners in the
-//      same wave exchange through lane shuffles, and only the stages that
-//      cross waves go through LDS and a barrier (10 of 78 at R L = 4096);
+//      above the flat index r L + j, so that ascending order is largest
+//      first and equal values by index; a request's keys, survivals that
+//      never grow, form an ascending run already;
+//   2. a merge sort that starts from those R runs: ceil(log2 R) rounds
+//      between two LDS buffers, each thread placing E consecutive outputs
+//      of a round after one binary search for where they start;
 //   3. an fp64 block scan of the sorted survivals; Theta(B) for every B from
 //      R to R (1 + L), the largest kept (the smallest B among equals; a NaN
 //      Theta never wins);
@@ -44,9 +44,14 @@ constexpr int kWave = 64;
 constexpr int kWaves = kThreads / kWave;
 
 struct Shared {
-  uint64_t key[kMaxItems];  // survival keys, then (cross-wave stages) the sort's exchange
-  float conf[kMaxItems];
-  int32_t len[kMaxItems];   // per request (R <= R L)
+  uint64_t key[kMaxItems];  // survival keys, then the merge rounds' buffers
+  union {
+    uint64_t other[kMaxItems];  // the second merge buffer
+    struct {
+      float conf[kMaxItems];    // confidences (before the sort)
+      int32_t len[kMaxItems];   // lengths per request (R <= R L; after the sort)
+    } io;
+  } u;
   double wsum[kWaves];
   double wbest[kWaves];
   int32_t wt[kWaves];
@@ -63,56 +68,69 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(0xffffffffu - uint32_t(key >> 32));
 }
 
-// One compare-exchange step of the bitonic network for the key at index i
-// with partner value b (index i ^ j): the lower index of an ascending pair
-// (i & k == 0) keeps the smaller key, of a descending pair the larger.
-__device__ __forceinline__ uint64_t bitonic_pick(uint64_t a, uint64_t b, int i, int j, int k) {
-  const bool asc = (i & k) == 0, lower = (i & j) == 0;
-  return (asc == lower) ? (a < b ? a : b) : (a < b ? b : a);
-}
-
-// Sorts the P = 1024 E keys held E per thread (thread t holds indices
-// t E .. t E + E - 1) ascending with the bitonic network: partners in the
-// same thread swap in registers, partners in the same wave through lane
-// shuffles, partners in other waves through LDS.
+// Merges the n keys of sh.key, ascending runs of w keys each (the last one
+// possibly shorter), pairwise until one run holds them all; keys are
+// distinct. Thread t writes outputs [t E, t E + E) of a round: a binary
+// search finds how many of the pair's first run precede its first output,
+// then it merges on from there (starting again where the next pair begins).
+// Returns the buffer holding the result.
 template <int E>
-__device__ __forceinline__ void bitonic_sort(uint64_t (&x)[E], int P, Shared& sh) {
-  const int tid = threadIdx.x;
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < E) {
-        uint64_t y[E];
+__device__ __forceinline__ const uint64_t* merge_runs(Shared& sh, int n, int w) {
+  const int o0 = threadIdx.x * E;
+  uint64_t* src = sh.key;
+  uint64_t* dst = sh.u.other;
+  for (; w < n; w *= 2) {
+    if (o0 < n) {
+      int a0 = o0 - o0 % (2 * w);
+      int a1 = min(a0 + w, n), b1 = min(a0 + 2 * w, n);
+      const int k = o0 - a0;
+      // smallest i with A[i] > B[k - 1 - i]: the first k outputs hold i of A
+      int lo = max(0, k - (b1 - a1)), hi = min(k, a1 - a0);
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (src[a0 + mid] < src[a1 + k - 1 - mid])
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      int i = a0 + lo, j = a1 + k - lo;  // next unmerged key of each run
+      uint64_t va = i < a1 ? src[i] : ~uint64_t(0);
+      uint64_t vb = j < b1 ? src[j] : ~uint64_t(0);
 #pragma unroll
-        for (int e = 0; e < E; ++e) y[e] = bitonic_pick(x[e], x[e ^ j], tid * E + e, j, k);
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = y[e];
-      } else if (j < kWave * E) {
-        const int m = j / E;  // partner lane = lane ^ m
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const uint64_t b = (uint64_t)__shfl_xor((long long)x[e], m, kWave);
-          x[e] = bitonic_pick(x[e], b, tid * E + e, j, k);
+      for (int e = 0; e < E; ++e) {
+        const int o = o0 + e;
+        if (o >= n) break;
+        if (o == b1) {  // the next pair of runs starts here
+          a0 = o;
+          a1 = min(a0 + w, n);
+          b1 = min(a0 + 2 * w, n);
+          i = a0;
+          j = a1;
+          va = src[i];
+          vb = j < b1 ? src[j] : ~uint64_t(0);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) sh.key[tid * E + e] = x[e];
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = tid * E + e;
-          x[e] = bitonic_pick(x[e], sh.key[i ^ j], i, j, k);
-        }
-        __syncthreads();
+        const bool ta = va < vb;
+        dst[o] = ta ? va : vb;
+        i += ta;
+        j += !ta;
+        const int p = ta ? i : j;
+        const uint64_t nv = p < (ta ? a1 : b1) ? src[p] : ~uint64_t(0);
+        va = ta ? nv : va;
+        vb = ta ? vb : nv;
       }
     }
+    __syncthreads();
+    uint64_t* t = src;
+    src = dst;
+    dst = t;
   }
+  return src;
 }
 
 template <int E>
 __device__ __forceinline__ void schedule_body(const float* conf, const float* sps, int R, int L,
                                               int32_t* verify_len, double* best, Shared& sh) {
   const int n = R * L;
-  const int P = kThreads * E;
   const int tid = threadIdx.x;
   // the throughputs this thread's sorted items price (B = R + i + 1), loaded
   // now so their latency hides behind the sort
@@ -124,29 +142,45 @@ __device__ __forceinline__ void schedule_body(const float* conf, const float* sp
   }
   const float sps0 = sps[R];
 
-  // 1. confidences into LDS (coalesced), survivals as sort keys
-  for (int i = tid; i < n; i += kThreads) sh.conf[i] = conf[i];
+  // 1. confidences into LDS (coalesced), survivals as sort keys: request
+  //    r's keys form the ascending run [r L, r L + L)
+  for (int i = tid; i < n; i += kThreads) sh.u.io.conf[i] = conf[i];
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
     float run = 1.f;
-    for (int j = 0; j < L; ++j) {
-      run = __fmul_rn(run, clamp_conf(sh.conf[r * L + j]));
+    int j = 0;
+    // 8 confidences read ahead of their products, so that a long request
+    // waits on LDS once per 8 positions
+    for (; j + 8 <= L; j += 8) {
+      float c[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) c[q] = sh.u.io.conf[r * L + j + q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        run = __fmul_rn(run, clamp_conf(c[q]));
+        const uint32_t idx = uint32_t(r * L + j + q);
+        sh.key[idx] = (uint64_t(0xffffffffu - __float_as_uint(run)) << 32) | idx;
+      }
+    }
+    for (; j < L; ++j) {
+      run = __fmul_rn(run, clamp_conf(sh.u.io.conf[r * L + j]));
       const uint32_t idx = uint32_t(r * L + j);
       sh.key[idx] = (uint64_t(0xffffffffu - __float_as_uint(run)) << 32) | idx;
     }
-    sh.len[r] = 0;
   }
   __syncthreads();
+
+  // 2. sort, ascending: the largest survivals first, equal ones by index;
+  //    thread t then takes sorted items [t E, t E + E)
+  const uint64_t* sorted = merge_runs<E>(sh, n, L);
   uint64_t x[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = tid * E + e;
-    x[e] = i < n ? sh.key[i] : ~uint64_t(0);
+    x[e] = i < n ? sorted[i] : ~uint64_t(0);
   }
   __syncthreads();
-
-  // 2. sort, ascending: the largest survivals first, equal ones by index
-  bitonic_sort<E>(x, P, sh);
+  for (int r = tid; r < R; r += kThreads) sh.u.io.len[r] = 0;
 
   // 3. scan of the sorted survivals: thread t owns items [t E, t E + E)
   double local = 0.0;
@@ -225,11 +259,11 @@ __device__ __forceinline__ void schedule_body(const float* conf, const float* sp
     if (i < t) {
       const uint32_t idx = uint32_t(x[e]);
       const int r = int(idx) / L, j = int(idx) - r * L;
-      atomicMax(&sh.len[r], j + 1);
+      atomicMax(&sh.u.io.len[r], j + 1);
     }
   }
   __syncthreads();
-  for (int r = tid; r < R; r += kThreads) verify_len[r] = sh.len[r];
+  for (int r = tid; r < R; r += kThreads) verify_len[r] = sh.u.io.len[r];
   if (tid == 0) {
     best[0] = sh.best_theta;
     best[1] = double(R + t);
