@@ -61,7 +61,7 @@ def _check(conf, sps, tag):
 
 @pytest.mark.parametrize("kind", ["steps", "random", "linear"])
 @pytest.mark.parametrize("R,L", [(1, 1), (1, 16), (7, 5), (64, 8), (256, 16), (512, 16),
-                                 (8192, 1), (1000, 8)])
+                                 (8192, 1), (1000, 8), (33, 31), (3, 2730), (1, 8192)])
 def test_schedule_against_oracle(kind, R, L):
     rng = np.random.default_rng(R * 100 + L + {"steps": 0, "random": 1, "linear": 2}[kind])
     excused = 0
