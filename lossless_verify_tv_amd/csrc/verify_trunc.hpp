@@ -358,12 +358,14 @@ __device__ __forceinline__ Sel select_value(Src&& src, Adm&& adm, bool by_idx, b
 template <int kDtype, bool kVecOk>
 __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t, uint32_t key,
                                             uint64_t n, TruncShared& ts) {
+  static_assert(kVec <= 8, "a tile's tokens of one thread fit 8 mask bits");
   if (threadIdx.x == 0) ts.r32 = INT_MAX;
   const int nt = (V + kTile - 1) / kTile;
   uint64_t run = 0;  // matches in the tiles before t
   for (int t = 0; t < nt && run < n; t += 4) {
     Grp<kDtype> g[4];
-    uint64_t mine = 0;  // this thread's matches per tile, 16 bits each
+    uint64_t mine = 0;   // this thread's matches per tile, 16 bits each
+    uint32_t masks = 0;  // which of its kVec tokens match, 8 bits a tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (t + i < nt)
@@ -373,13 +375,15 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint64_t c = 0;
+      uint32_t mk = 0;
 #pragma unroll
       for (int j = 0; j < kVec; ++j) {
         const int v = tile_elem(t + i) + j;
-        c += (t + i < nt && v < V && desc_key(__fmul_rn(gelem(g[i], j), inv_t)) == key);
+        mk |= uint32_t(t + i < nt && v < V &&
+                       desc_key(__fmul_rn(gelem(g[i], j), inv_t)) == key) << j;
       }
-      mine |= c << (16 * i);
+      masks |= mk << (8 * i);
+      mine |= uint64_t(__popc(mk)) << (16 * i);
     }
     uint64_t exc, e1, total, t1;
     block_exscan2_u64(mine, 0, exc, e1, total, t1, ts);
@@ -388,14 +392,17 @@ __device__ __forceinline__ int nth_with_key(const void* row, int V, float inv_t,
       const uint64_t before = run + ((exc >> (16 * i)) & 0xffff);
       const uint64_t c = (mine >> (16 * i)) & 0xffff;
       if (before < n && n <= before + c) {
-        uint64_t seen = before;
+        // the (n - before)-th set bit of the tile's mask
+        const uint32_t mk = (masks >> (8 * i)) & 0xffu;
+        uint32_t left = uint32_t(n - before);
+        int hit = 0;
         for (int j = 0; j < kVec; ++j) {
-          const int v = tile_elem(t + i) + j;
-          if (v < V && desc_key(__fmul_rn(gelem(g[i], j), inv_t)) == key && ++seen == n) {
-            ts.r32 = v;
+          if (((mk >> j) & 1u) && --left == 0) {
+            hit = j;
             break;
           }
         }
+        ts.r32 = tile_elem(t + i) + hit;
       }
       run += (total >> (16 * i)) & 0xffff;
     }
