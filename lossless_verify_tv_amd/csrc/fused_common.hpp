@@ -73,46 +73,22 @@ __device__ __forceinline__ u32x4 ld_nt16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-__device__ __forceinline__ void st_nt16(void* p, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+// The same from an address that is only 2-byte aligned. Code objects for
+// this target run in unaligned access mode (the compiler emits one 16-byte
+// load for such a type), so this stays a single vector load; the caller makes
+// sure that all 16 bytes lie inside the row.
+typedef u32x4 u32x4_u __attribute__((aligned(2)));
+
+__device__ __forceinline__ u32x4 ld_nt16_u(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_u*>(p));
 }
 
-// Eight consecutive elements [e, e+8) of a row as fp32 (streaming loads);
-// elements at or beyond V read as -inf. kVecOk: the row base is 16-byte
-// aligned and V % 8 == 0, so an in-range group is one or two 16-byte loads.
-template <int kDtype, bool kVecOk>
-__device__ __forceinline__ void load8_nt(const void* row, int64_t e, int64_t V, float (&x)[kVec]) {
-  if (kVecOk && e + kVec <= V) {
-    if constexpr (kDtype == 1) {
-      const u32x4 w = ld_nt16(static_cast<const uint16_t*>(row) + e);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-      }
-    } else {
-      const u32x4 a = ld_nt16(static_cast<const float*>(row) + e);
-      const u32x4 b = ld_nt16(static_cast<const float*>(row) + e + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = __uint_as_float(a[i]);
-        x[4 + i] = __uint_as_float(b[i]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kVec; ++i) {
-      const int64_t idx = e + i;
-      if (idx < V) {
-        if constexpr (kDtype == 1)
-          x[i] = bf16_bits_to_f32(static_cast<const uint16_t*>(row)[idx]);
-        else
-          x[i] = static_cast<const float*>(row)[idx];
-      } else {
-        x[i] = -INFINITY;
-      }
-    }
-  }
+__device__ __forceinline__ u32x4 ld16_u(const void* p) {
+  return *reinterpret_cast<const u32x4_u*>(p);
+}
+
+__device__ __forceinline__ void st_nt16(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 }  // namespace lvtv

@@ -125,6 +125,9 @@ __device__ __forceinline__ u32x4 load_z(const uint16_t* row, int V, int e) {
     const uint32_t f = 0xff80ff80u;
     return u32x4{in ? v[0] : f, in ? v[1] : f, in ? v[2] : f, in ? v[3] : f};
   } else {
+    // rows that are not 16-byte aligned: an unaligned vector load for a
+    // group wholly inside the row, the row's last group token by token
+    if (e + kVec <= V) return ld_nt16_u(row + e);
     u32x4 r;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -145,6 +148,10 @@ __device__ __forceinline__ void load_p(const float* row, int V, int e, u32x4& a,
     const u32x4 x = ld_nt16(q), y = ld_nt16(q + 4);
     a = u32x4{in ? x[0] : 0u, in ? x[1] : 0u, in ? x[2] : 0u, in ? x[3] : 0u};
     b = u32x4{in ? y[0] : 0u, in ? y[1] : 0u, in ? y[2] : 0u, in ? y[3] : 0u};
+  } else if (e + kVec <= V) {
+    // a group wholly inside a row that is not 16-byte aligned
+    a = ld_nt16_u(row + e);
+    b = ld_nt16_u(row + e + 4);
   } else {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {

@@ -194,7 +194,14 @@ __device__ __forceinline__ void load_grp(const void* row, int V, int e, Grp<kDty
       g.q[0] = p[0];
       if constexpr (kDtype == 0) g.q[1] = p[1];
     }
+  } else if (e + kVec <= V) {
+    // a group wholly inside a row that is not 16-byte aligned: unaligned
+    // vector loads
+    const char* p = static_cast<const char*>(row) + int64_t(e) * (kDtype == 1 ? 2 : 4);
+    g.q[0] = kNt ? ld_nt16_u(p) : ld16_u(p);
+    if constexpr (kDtype == 0) g.q[1] = kNt ? ld_nt16_u(p + 16) : ld16_u(p + 16);
   } else if constexpr (kDtype == 1) {
+    // the row's last group: token by token
     const uint16_t* p = static_cast<const uint16_t*>(row);
 #pragma unroll
     for (int h = 0; h < 4; ++h) {

@@ -8,12 +8,15 @@ exemptions the parity rules allow are counted and bounded."""
 
 import numpy as np
 import pytest
+import torch
 
+import lossless_verify_tv_amd as lv
 from lossless_verify_tv_amd import synth
 from oracle import bf16 as obf16
 from oracle import loss as ol
 
-from .gpu_util import announce, full_loss_case, oracle_loss_all, run_debug_loss, run_loss
+from .gpu_util import (announce, device, full_loss_case, loss_to_device, oracle_loss_all,
+                       run_debug_loss, run_loss)
 from .parity import (ALPHA_RTOL, LOSS_RTOL, check_exemption_bounds, compare_branch,
                      rel_close)
 
@@ -48,6 +51,33 @@ def _check_small(z, p, tag, path=None):
 def test_loss_shrunk(vocab):
     c = synth.loss_case(n_branches=5, width=7, vocab=vocab)
     _check_small(c.draft_logits, c.target_probs, f"N=5 W=7 V={vocab}")
+
+
+def _offset_copy(t, offset):
+    """The values of `t` stored `offset` elements past a fresh allocation's
+    start: rows whose base is not 16-byte aligned."""
+    flat = torch.empty(t.numel() + offset, dtype=t.dtype, device=t.device)
+    view = flat[offset:].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+@pytest.mark.parametrize("objective", ["e2e_tv", "step_tv", "ce", "kl"])
+def test_unaligned_bases_match_aligned(objective):
+    """Inputs whose rows are not 16-byte aligned take the unaligned loads
+    (one unaligned vector load per group inside a row, the row's last group
+    token by token); outputs must be bit-identical to those from aligned
+    copies, whose rows take 16-byte loads."""
+    dev = device()
+    c = synth.loss_case(n_branches=3, width=7, vocab=30000)
+    z, p = loss_to_device(c.draft_logits, c.target_probs, dev)
+    announce(f"loss unaligned bases objective={objective}")
+    ref = lv.draft_loss_fwd_bwd(z, p, objective)
+    got = lv.draft_loss_fwd_bwd(_offset_copy(z, 1), _offset_copy(p, 3), objective)
+    torch.cuda.synchronize(dev)
+    assert ref[0].item() == got[0].item()
+    assert torch.equal(ref[1], got[1])
+    assert torch.equal(ref[2].view(torch.int16), got[2].view(torch.int16))
 
 
 def test_loss_single_position_and_branch():
