@@ -87,6 +87,39 @@ __device__ __forceinline__ u32x4 ld16_u(const void* p) {
   return *reinterpret_cast<const u32x4_u*>(p);
 }
 
+__device__ __forceinline__ void st_nt16_u(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_u*>(p));
+}
+
+// A group's tokens moved down by s places (token j takes token j + s), the
+// top places taking `fill`: s >= 8 leaves only fill. bf16 tokens, two a word.
+__device__ __forceinline__ u32x4 shift_bf16(u32x4 w, uint32_t s, uint32_t fill) {
+  if (s & 4) w = u32x4{w[2], w[3], fill, fill};
+  if (s & 2) w = u32x4{w[1], w[2], w[3], fill};
+  if (s & 1)
+    w = u32x4{__builtin_amdgcn_alignbyte(w[1], w[0], 2), __builtin_amdgcn_alignbyte(w[2], w[1], 2),
+              __builtin_amdgcn_alignbyte(w[3], w[2], 2), __builtin_amdgcn_alignbyte(fill, w[3], 2)};
+  return s >= 8 ? u32x4{fill, fill, fill, fill} : w;
+}
+
+// The same for 8 fp32 tokens, one a word, in a (tokens 0-3) and b (4-7).
+__device__ __forceinline__ void shift_f32(u32x4& a, u32x4& b, uint32_t s, uint32_t fill) {
+  const u32x4 f = u32x4{fill, fill, fill, fill};
+  if (s & 4) {
+    a = b;
+    b = f;
+  }
+  if (s & 2) {
+    a = u32x4{a[2], a[3], b[0], b[1]};
+    b = u32x4{b[2], b[3], fill, fill};
+  }
+  if (s & 1) {
+    a = u32x4{a[1], a[2], a[3], b[0]};
+    b = u32x4{b[1], b[2], b[3], fill};
+  }
+  if (s >= 8) a = b = f;
+}
+
 __device__ __forceinline__ void st_nt16(void* p, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }

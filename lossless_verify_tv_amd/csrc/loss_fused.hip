@@ -125,17 +125,13 @@ __device__ __forceinline__ u32x4 load_z(const uint16_t* row, int V, int e) {
     const uint32_t f = 0xff80ff80u;
     return u32x4{in ? v[0] : f, in ? v[1] : f, in ? v[2] : f, in ? v[3] : f};
   } else {
-    // rows that are not 16-byte aligned: an unaligned vector load for a
-    // group wholly inside the row, the row's last group token by token
-    if (e + kVec <= V) return ld_nt16_u(row + e);
-    u32x4 r;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const uint32_t lo = (e + 2 * h < V) ? row[e + 2 * h] : 0xff80u;
-      const uint32_t hi = (e + 2 * h + 1 < V) ? row[e + 2 * h + 1] : 0xff80u;
-      r[h] = lo | (hi << 16);
-    }
-    return r;
+    // rows that are not 16-byte aligned (V >= 8 on this kernel): one
+    // unaligned vector load of the 16 bytes that end at the group's end or
+    // at the row's end, whichever comes first (always inside the row), and
+    // the tokens moved into place (no move inside the row). No branch, so
+    // nothing splits a batch of loads.
+    const int es = min(e, V - kVec);
+    return shift_bf16(ld_nt16_u(row + es), uint32_t(e - es), 0xff80ff80u);
   }
 }
 
@@ -148,16 +144,12 @@ __device__ __forceinline__ void load_p(const float* row, int V, int e, u32x4& a,
     const u32x4 x = ld_nt16(q), y = ld_nt16(q + 4);
     a = u32x4{in ? x[0] : 0u, in ? x[1] : 0u, in ? x[2] : 0u, in ? x[3] : 0u};
     b = u32x4{in ? y[0] : 0u, in ? y[1] : 0u, in ? y[2] : 0u, in ? y[3] : 0u};
-  } else if (e + kVec <= V) {
-    // a group wholly inside a row that is not 16-byte aligned
-    a = ld_nt16_u(row + e);
-    b = ld_nt16_u(row + e + 4);
   } else {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      a[h] = (e + h < V) ? __float_as_uint(row[e + h]) : 0u;
-      b[h] = (e + 4 + h < V) ? __float_as_uint(row[e + 4 + h]) : 0u;
-    }
+    // rows that are not 16-byte aligned, as for z
+    const int es = min(e, V - kVec);
+    a = ld_nt16_u(row + es);
+    b = ld_nt16_u(row + es + 4);
+    shift_f32(a, b, uint32_t(e - es), 0u);
   }
 }
 
@@ -493,6 +485,8 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e,
   }
   if (kVecOk) {
     if (e < V) st_nt16(dz + e, out);
+  } else if (e + kVec <= V) {
+    st_nt16_u(dz + e, out);
   } else {
 #pragma unroll
     for (int t = 0; t < kVec; ++t)
@@ -530,6 +524,8 @@ __device__ __forceinline__ void dz_xent_group(const u32x4& zv, const u32x4& pa, 
   }
   if (kVecOk) {
     if (e < V) st_nt16(dz + e, out);
+  } else if (e + kVec <= V) {
+    st_nt16_u(dz + e, out);
   } else {
 #pragma unroll
     for (int t = 0; t < kVec; ++t)
@@ -1061,7 +1057,9 @@ bool logits_supported() { return true; }
 bool xent_supported(bool logits) { return !logits; }
 
 bool applicable(int N, int W, int V) {
-  return V <= kMaxV && size_t(N) * W * 2 < (size_t(1) << 31);
+  // rows of at least one group: a row that is not 16-byte aligned is read
+  // 16 bytes at a time, always inside the row
+  return V >= kVec && V <= kMaxV && size_t(N) * W * 2 < (size_t(1) << 31);
 }
 
 size_t workspace_bytes(int N, int W, int V) {
