@@ -107,9 +107,29 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// A row's halves: [0, hv) and [hv, V), hv = ceil(V / 2) rounded up to a
+// whole group (at most kHalf), so that both workgroups of a row get about
+// the same work whatever V is.
+__host__ __device__ __forceinline__ int half_len(int V) {
+  const int hv = ((V + 1) / 2 + kVec - 1) / kVec * kVec;
+  return hv < kHalf ? hv : kHalf;
+}
+
+// End of half h: its tokens are read up to here (the rest as past the end).
+__host__ __device__ __forceinline__ int half_end(int V, int h) {
+  const int e = (h + 1) * half_len(V);
+  return e < V ? e : V;
+}
+
+// Groups (a thread's kVec tokens in each of kTile) that half h reaches;
+// the rest hold no token of it and are skipped (they would add only zeros).
+__host__ __device__ __forceinline__ int half_groups(int V, int h) {
+  return (half_end(V, h) - h * half_len(V) + kTile - 1) / kTile;
+}
+
 // First token of this thread's group g in half h.
-__device__ __forceinline__ int group_elem(int h, int g) {
-  return h * kHalf + g * kTile + int(threadIdx.x) * kVec;
+__device__ __forceinline__ int group_elem(int V, int h, int g) {
+  return h * half_len(V) + g * kTile + int(threadIdx.x) * kVec;
 }
 
 // z group of a row: 8 bf16 tokens packed in 4 registers; tokens at or beyond
@@ -553,13 +573,15 @@ __device__ __forceinline__ HalfStats target_half_stats(const uint16_t* t, int V,
                                                        Shared& sh) {
   float m = -INFINITY;
   double l = 0.0;
-  const int tb = opaque(group_elem(h, 0));
+  const int tb = opaque(group_elem(V, h, 0));
+  const int ve = half_end(V, h);
+  const int ng = half_groups(V, h);
 #pragma unroll 1
-  for (int g0 = 0; g0 < kZG; g0 += kPBatch) {
+  for (int g0 = 0; g0 < ng; g0 += kPBatch) {
     u32x4 x[kPBatch];
 #pragma unroll
     for (int i = 0; i < kPBatch; ++i)
-      if (g0 + i < kZG) x[i] = load_z<kVecOk>(t, V, opaque(tb) + (g0 + i) * kTile);
+      if (g0 + i < kZG) x[i] = load_z<kVecOk>(t, ve, opaque(tb) + (g0 + i) * kTile);
     float bm = m;
 #pragma unroll
     for (int i = 0; i < kPBatch; ++i)
@@ -591,7 +613,9 @@ __device__ __forceinline__ void publish_stats(uint64_t* slot, int first, uint32_
 
 // ------------------------------------------------------------------ half-row kernel
 
-template <bool kVecOk, bool kLogits, bool kDbg, bool kXent>
+// kAll: both halves of a row reach every group (V near the largest), so the
+// tests of the group count fold away.
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent, bool kAll>
 __device__ __forceinline__ void half_body(const Args& a) {
   static_assert(!(kLogits && kXent), "CE and KL take a probability target here");
   __shared__ Shared sh;
@@ -613,27 +637,34 @@ __device__ __forceinline__ void half_body(const Args& a) {
   // 1. this half of z into the held copy
   Held zg;
   zg.lds = zl;
+  const int ve = half_end(V, h);    // this half's tokens end here
+  const int ng = kAll ? kZG : half_groups(V, h);  // groups past ng are skipped (uniform tests)
   {
-    const int tb = opaque(group_elem(h, 0));
+    const int tb = opaque(group_elem(V, h, 0));
     u32x4 tmp[kZL];
 #pragma unroll
-    for (int g = 0; g < kZL; ++g) tmp[g] = load_z<kVecOk>(z, V, tb + g * kTile);
+    for (int g = 0; g < kZL; ++g)
+      if (g < ng) tmp[g] = load_z<kVecOk>(z, ve, tb + g * kTile);
 #pragma unroll
-    for (int g = kZL; g < kZG; ++g) zg.r[g - kZL] = load_z<kVecOk>(z, V, tb + g * kTile);
+    for (int g = kZL; g < kZG; ++g)
+      if (g < ng) zg.r[g - kZL] = load_z<kVecOk>(z, ve, tb + g * kTile);
 #pragma unroll
-    for (int g = 0; g < kZL; ++g) zl[g][threadIdx.x] = tmp[g];
+    for (int g = 0; g < kZL; ++g)
+      if (g < ng) zl[g][threadIdx.x] = tmp[g];
   }
 
   // 2. half statistics, swapped with the other half
   float m = -INFINITY;
 #pragma unroll
-  for (int g = 0; g < kZG; ++g) m = grp_max(zg.get(g), m);
+  for (int g = 0; g < kZG; ++g)
+    if (g < ng) m = grp_max(zg.get(g), m);
   launder(zg);
   m = block_max(m, sh);
   const float nm0 = (m == -INFINITY) ? 0.f : -(m * c);
   double l = 0.0;
 #pragma unroll
-  for (int g = 0; g < kZG; ++g) l += (double)grp_expsum(zg.get(g), c, nm0);
+  for (int g = 0; g < kZG; ++g)
+    if (g < ng) l += (double)grp_expsum(zg.get(g), c, nm0);
   launder(zg);
   l = block_sum1(l, sh);
   if (threadIdx.x == 0) publish_stats(slot, 0, tag, HalfStats{m, l});
@@ -656,7 +687,7 @@ __device__ __forceinline__ void half_body(const Args& a) {
   uint32_t mask[kMaskWords];
 #pragma unroll
   for (int w = 0; w < kMaskWords; ++w) mask[w] = 0u;
-  const int tbp = opaque(group_elem(h, 0));
+  const int tbp = opaque(group_elem(V, h, 0));
   const bool kl = a.objective == LVTV_OBJ_KL;
   const float mlnl = kXent ? float(row_mlnl_from(sh.words, 0, c)) : 0.f;
   constexpr int kB = kPBatch;
@@ -665,19 +696,19 @@ __device__ __forceinline__ void half_body(const Args& a) {
     u32x4 pa[kB], pb[kB];
 #pragma unroll
     for (int i = 0; i < kB; ++i)
-      if (g0 + i < kZG) {
+      if (g0 + i < kZG && g0 + i < ng) {
         if constexpr (kLogits)
-          pa[i] = load_z<kVecOk>(t, V, opaque(tbp) + (g0 + i) * kTile);
+          pa[i] = load_z<kVecOk>(t, ve, opaque(tbp) + (g0 + i) * kTile);
         else
-          load_p<kVecOk>(p, V, opaque(tbp) + (g0 + i) * kTile, pa[i], pb[i]);
+          load_p<kVecOk>(p, ve, opaque(tbp) + (g0 + i) * kTile, pa[i], pb[i]);
       }
 #pragma unroll
     for (int i = 0; i < kB; ++i)
-      if (g0 + i < kZG) {
+      if (g0 + i < kZG && g0 + i < ng) {
         const int g = g0 + i;
         if constexpr (kXent) {
           // al, sum p (in sb), the loss part (in sa)
-          grp_xent<kVecOk>(zg.get(g), pa[i], pb[i], opaque(tbp) + g * kTile, V, c, rs, mlnl, kl,
+          grp_xent<kVecOk>(zg.get(g), pa[i], pb[i], opaque(tbp) + g * kTile, ve, c, rs, mlnl, kl,
                            al, sb, sa);
         } else {
           const uint32_t bits =
@@ -714,27 +745,29 @@ __device__ __forceinline__ void half_body(const Args& a) {
   // 5. dz of this half from the held copy and the mask (CE / KL: and p,
   //    streamed again)
   uint16_t* dz = a.dz + row * V;
-  const int tbd = opaque(group_elem(h, 0));
+  const int tbd = opaque(group_elem(V, h, 0));
   if constexpr (kXent) {
 #pragma unroll
     for (int g0 = 0; g0 < kZG; g0 += kB) {
       u32x4 pa[kB], pb[kB];
 #pragma unroll
       for (int i = 0; i < kB; ++i)
-        if (g0 + i < kZG) load_p<kVecOk>(p, V, opaque(tbd) + (g0 + i) * kTile, pa[i], pb[i]);
+        if (g0 + i < kZG && g0 + i < ng)
+          load_p<kVecOk>(p, ve, opaque(tbd) + (g0 + i) * kTile, pa[i], pb[i]);
 #pragma unroll
       for (int i = 0; i < kB; ++i)
-        if (g0 + i < kZG)
+        if (g0 + i < kZG && g0 + i < ng)
           dz_xent_group<kVecOk, kDbg>(zg.get(g0 + i), pa[i], pb[i], opaque(tbd) + (g0 + i) * kTile,
-                                      V, c, rs, c_below, c_above, dz,
+                                      ve, c, rs, c_below, c_above, dz,
                                       kDbg ? a.dz32 + row * V : nullptr);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
     for (int g = 0; g < kZG; ++g) {
-      dz_group<kVecOk, kDbg>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, V, c, rs,
-                             c_below, c_above, dz, kDbg ? a.dz32 + row * V : nullptr);
+      if (g < ng)
+        dz_group<kVecOk, kDbg>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, ve, c, rs,
+                               c_below, c_above, dz, kDbg ? a.dz32 + row * V : nullptr);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -748,14 +781,16 @@ template <bool kVecOk>
 __device__ __forceinline__ HalfStats stream_half_stats(const uint16_t* z, int V, int h, float c,
                                                        Shared& sh) {
   float m = -INFINITY;
+  const int ve = half_end(V, h);
+  const int ng = half_groups(V, h);
 #pragma unroll 1
-  for (int g = 0; g < kZG; ++g) m = grp_max(load_z<kVecOk>(z, V, group_elem(h, g)), m);
+  for (int g = 0; g < ng; ++g) m = grp_max(load_z<kVecOk>(z, ve, group_elem(V, h, g)), m);
   m = block_max(m, sh);
   const float nm0 = (m == -INFINITY) ? 0.f : -(m * c);
   double l = 0.0;
 #pragma unroll 1
-  for (int g = 0; g < kZG; ++g)
-    l += (double)grp_expsum(load_z<kVecOk>(z, V, group_elem(h, g)), c, nm0);
+  for (int g = 0; g < ng; ++g)
+    l += (double)grp_expsum(load_z<kVecOk>(z, ve, group_elem(V, h, g)), c, nm0);
   l = block_sum1(l, sh);
   return HalfStats{m, l};
 }
@@ -763,13 +798,13 @@ __device__ __forceinline__ HalfStats stream_half_stats(const uint16_t* z, int V,
 // The target's group at token e: 8 probabilities in (pa, pb), or (kLogits)
 // 8 bf16 logits in pa.
 template <bool kVecOk, bool kLogits>
-__device__ __forceinline__ void load_target(const Args& a, size_t row, int e, u32x4& pa,
+__device__ __forceinline__ void load_target(const Args& a, size_t row, int e, int ve, u32x4& pa,
                                             u32x4& pb) {
   if constexpr (kLogits) {
-    pa = load_z<kVecOk>(a.t + row * a.V, a.V, e);
+    pa = load_z<kVecOk>(a.t + row * a.V, ve, e);
     pb = pa;
   } else {
-    load_p<kVecOk>(a.p + row * a.V, a.V, e, pa, pb);
+    load_p<kVecOk>(a.p + row * a.V, ve, e, pa, pb);
   }
 }
 
@@ -780,12 +815,14 @@ __device__ __forceinline__ void stream_half_parts(const Args& a, size_t row, int
                                                   double& al, double& sb, double& sa, Shared& sh) {
   al = sb = sa = 0.0;
   const uint16_t* z = a.z + row * a.V;
+  const int ve = half_end(a.V, h);
+  const int ng = half_groups(a.V, h);
 #pragma unroll 1
-  for (int g = 0; g < kZG; ++g) {
-    const int e = group_elem(h, g);
+  for (int g = 0; g < ng; ++g) {
+    const int e = group_elem(a.V, h, g);
     u32x4 pa, pb;
-    load_target<kVecOk, kLogits>(a, row, e, pa, pb);
-    (void)grp_overlap<kLogits>(load_z<kVecOk>(z, a.V, e), pa, pb, a.c, rs, ts, al, sb, sa);
+    load_target<kVecOk, kLogits>(a, row, e, ve, pa, pb);
+    (void)grp_overlap<kLogits>(load_z<kVecOk>(z, ve, e), pa, pb, a.c, rs, ts, al, sb, sa);
   }
   block_sum3(al, sb, sa, sh);
 }
@@ -800,12 +837,14 @@ __device__ __forceinline__ void stream_half_xent(const Args& a, size_t row, int 
   const bool kl = a.objective == LVTV_OBJ_KL;
   al = sp = part = 0.0;
   const uint16_t* z = a.z + row * a.V;
+  const int ve = half_end(a.V, h);
+  const int ng = half_groups(a.V, h);
 #pragma unroll 1
-  for (int g = 0; g < kZG; ++g) {
-    const int e = group_elem(h, g);
+  for (int g = 0; g < ng; ++g) {
+    const int e = group_elem(a.V, h, g);
     u32x4 pa, pb;
-    load_target<kVecOk, false>(a, row, e, pa, pb);
-    grp_xent<kVecOk>(load_z<kVecOk>(z, a.V, e), pa, pb, e, a.V, a.c, rs, mlnl, kl, al, sp, part);
+    load_target<kVecOk, false>(a, row, e, ve, pa, pb);
+    grp_xent<kVecOk>(load_z<kVecOk>(z, ve, e), pa, pb, e, ve, a.c, rs, mlnl, kl, al, sp, part);
   }
   block_sum3(al, sp, part, sh);
 }
@@ -907,19 +946,21 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
     const uint16_t* z = a.z + size_t(row) * V;
     uint16_t* dz = a.dz + size_t(row) * V;
     for (int hh = 0; hh < 2; ++hh) {
+      const int ve = half_end(V, hh);
+      const int ng = half_groups(V, hh);
 #pragma unroll 1
-      for (int g = 0; g < kZG; ++g) {
-        const int e = group_elem(hh, g);
-        const u32x4 zv = load_z<kVecOk>(z, V, e);
+      for (int g = 0; g < ng; ++g) {
+        const int e = group_elem(V, hh, g);
+        const u32x4 zv = load_z<kVecOk>(z, ve, e);
         u32x4 pa, pb;
-        load_target<kVecOk, kLogits>(a, size_t(row), e, pa, pb);
+        load_target<kVecOk, kLogits>(a, size_t(row), e, ve, pa, pb);
         if constexpr (kXent) {
-          dz_xent_group<kVecOk, kDbg>(zv, pa, pb, e, V, c, rs, c_below, c_above, dz,
+          dz_xent_group<kVecOk, kDbg>(zv, pa, pb, e, ve, c, rs, c_below, c_above, dz,
                                       kDbg ? a.dz32 + size_t(row) * V : nullptr);
         } else {
           double x = 0.0, y = 0.0, w = 0.0;
           const uint32_t bits = grp_overlap<kLogits>(zv, pa, pb, c, rs, ts, x, y, w);
-          dz_group<kVecOk, kDbg>(zv, bits, e, V, c, rs, c_below, c_above, dz,
+          dz_group<kVecOk, kDbg>(zv, bits, e, ve, c, rs, c_below, c_above, dz,
                                  kDbg ? a.dz32 + size_t(row) * V : nullptr);
         }
       }
@@ -928,10 +969,10 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
   }
 }
 
-template <bool kVecOk, bool kLogits, bool kDbg, bool kXent>
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent, bool kAll>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 loss_halves(Args a) {
-  half_body<kVecOk, kLogits, kDbg, kXent>(a);
+  half_body<kVecOk, kLogits, kDbg, kXent, kAll>(a);
 }
 
 __device__ __forceinline__ int block_min(int v, Shared& sh) {
@@ -1017,18 +1058,26 @@ __global__ __launch_bounds__(256) void clear_words(u32x4* w, size_t n16) {
     w[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+template <bool kDbg, bool kXent, bool kAll>
+void launch_halves(const Args& a, bool vec_ok, bool logits, unsigned rows, hipStream_t stream) {
+  auto halves = vec_ok ? (logits ? loss_halves<true, true, kDbg, false, kAll>
+                                 : loss_halves<true, false, kDbg, kXent, kAll>)
+                       : (logits ? loss_halves<false, true, kDbg, false, kAll>
+                                 : loss_halves<false, false, kDbg, kXent, kAll>);
+  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
+}
+
 template <bool kDbg, bool kXent>
 hipError_t launch_kernels(const Args& a, bool vec_ok, bool logits, unsigned rows,
                           hipStream_t stream) {
-  auto halves = vec_ok ? (logits ? loss_halves<true, true, kDbg, false>
-                                 : loss_halves<true, false, kDbg, kXent>)
-                       : (logits ? loss_halves<false, true, kDbg, false>
-                                 : loss_halves<false, false, kDbg, kXent>);
   auto finish = vec_ok ? (logits ? loss_finish<true, true, kDbg, false>
                                  : loss_finish<true, false, kDbg, kXent>)
                        : (logits ? loss_finish<false, true, kDbg, false>
                                  : loss_finish<false, false, kDbg, kXent>);
-  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
+  if (half_groups(a.V, 0) == kZG && half_groups(a.V, 1) == kZG)
+    launch_halves<kDbg, kXent, true>(a, vec_ok, logits, rows, stream);
+  else
+    launch_halves<kDbg, kXent, false>(a, vec_ok, logits, rows, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(finish, dim3(1), dim3(kThreads), 0, stream, a);
