@@ -53,6 +53,17 @@ def test_loss_shrunk(vocab):
     _check_small(c.draft_logits, c.target_probs, f"N=5 W=7 V={vocab}")
 
 
+@pytest.mark.parametrize("vocab", [8, 9, 15, 16, 17, 4104, 8200, 77825, 155647])
+def test_loss_half_split_edges(vocab):
+    """A row's halves meet at ceil(V/2) rounded up to a group of 8: rows of
+    one group (the second half empty), a second half of one token, halves
+    whose last group holds a single group's tokens for one thread, V just
+    past the largest half, and V near the largest (every group used, the
+    last one partial)."""
+    c = synth.loss_case(n_branches=3, width=4, vocab=vocab)
+    _check_small(c.draft_logits, c.target_probs, f"N=3 W=4 V={vocab}")
+
+
 def _offset_copy(t, offset):
     """The values of `t` stored `offset` elements past a fresh allocation's
     start: rows whose base is not 16-byte aligned."""

@@ -41,7 +41,8 @@ def _check(z, t, T, objective, tag, branches=None, path=None):
 
 
 @pytest.mark.parametrize("objective", OBJECTIVES)
-@pytest.mark.parametrize("vocab,T", [(20000, 0.6), (1001, 1.0), (3, 1.5), (8192, 0.35)])
+@pytest.mark.parametrize("vocab,T", [(20000, 0.6), (1001, 1.0), (3, 1.5), (8192, 0.35),
+                                     (9, 0.8), (8200, 1.2)])
 def test_logits_target_shrunk(objective, vocab, T):
     c = synth.loss_logits_case(n_branches=5, width=7, vocab=vocab)
     _check(c.draft_logits, c.target_logits, T, objective, f"{objective} V={vocab}")
