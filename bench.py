@@ -16,8 +16,9 @@ roofline of the dominant kernel (the loss), timed live inside the timed steps
 with a pair of HIP events around the loss call on the stream the kernels run
 on, and the CPU oracle timed on the step's own inputs.
 
-Per-call times (the step's components, the variants, the small workloads)
-are medians over many calls, each call bracketed by its own pair of events
+Per-call times (the step's components, the variants, the small workloads,
+and a sweep of the loss and the sampling verify over three other
+vocabularies, one of them not a multiple of 8) are medians over many calls, each call bracketed by its own pair of events
 with a 1 GiB write between calls outside the brackets, so that no call is
 served from the 256 MB last-level cache by the one before it. The step's
 components also carry batched times: the median over 5 batches of
@@ -746,6 +747,38 @@ def main():
                       "gbs": sb / (t["ms"] * 1e-3) / 1e9, "algorithmic_bytes": sb}
     result["small_workloads"] = small
     log("small workloads: " + ", ".join(f"{k} {v['us']:.1f} us" for k, v in small.items()))
+    # Other vocabularies (seeded random logits drawn on the device; one V not
+    # a multiple of 8, so its rows are not 16-byte aligned): the loss at
+    # N=512 W=7 and the sampling verify at B=64 K=7 T=1, time per call.
+    sweep = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    for sv in (32000, 50257, 128256):
+        zs = (torch.randn(LOSS_N, LOSS_W, sv, device=dev, generator=gen) * 2).to(torch.bfloat16)
+        ps = torch.softmax(torch.randn(LOSS_N, LOSS_W, sv, device=dev, generator=gen) * 2, dim=-1)
+        t = per_call(lambda: lv.e2e_tv_loss_fwd_bwd(zs, ps), max(n_l // 3, 3))
+        lbs = LOSS_N * LOSS_W * sv * 8
+        sweep[f"loss_N{LOSS_N}_W{LOSS_W}_V{sv}"] = {
+            **t, "us": t["ms"] * 1e3, "gbs": lbs / (t["ms"] * 1e-3) / 1e9,
+            "algorithmic_bytes": lbs}
+        del zs, ps
+        vt = (torch.randn(VERIFY_B, VERIFY_K + 1, sv, device=dev, generator=gen) * 2).to(
+            torch.bfloat16)
+        vd = (torch.randn(VERIFY_B, VERIFY_K, sv, device=dev, generator=gen) * 2).to(
+            torch.bfloat16)
+        tok = torch.randint(0, sv, (VERIFY_B, VERIFY_K), device=dev, dtype=torch.int32,
+                            generator=gen)
+        kk = torch.full((VERIFY_B,), VERIFY_K, device=dev, dtype=torch.int32)
+        temp = torch.ones(VERIFY_B, device=dev, dtype=torch.float32)
+        seed = torch.arange(VERIFY_B, device=dev, dtype=torch.int64)
+        t = per_call(lambda: lv.spec_verify(vt, vd, tok, kk, temp, seed), max(n_v // 5, 5))
+        vbs = VERIFY_B * (2 * VERIFY_K + 1) * sv * 2
+        sweep[f"verify_B{VERIFY_B}_K{VERIFY_K}_V{sv}_T1.0"] = {
+            **t, "us": t["ms"] * 1e3, "gbs": vbs / (t["ms"] * 1e-3) / 1e9,
+            "algorithmic_bytes": vbs}
+        del vt, vd
+    result["vocab_sweep"] = sweep
+    log("vocabulary sweep: " + ", ".join(f"{k} {v['us']:.1f} us" for k, v in sweep.items()))
     del flush_buf
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the step's inputs (one process, then a pool)")
