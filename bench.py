@@ -255,11 +255,12 @@ _TRAFFIC_KERNELS = {
     "rows": "verify_rows_bf16<true, false>",
     "finalize": "verify_finalize<1>",
     "clear": "clear_words",
-    # loss_halves<vector loads, logits target, debug, CE/KL, every group>
-    "loss": "loss_halves<true, false, false, false, true>",
+    # loss_halves<vector loads, logits target, debug, CE/KL, row mode (1: two
+    # workgroups a row, every group used)>
+    "loss": "loss_halves<true, false, false, false, 1>",
     "loss_finish": "loss_finish<true, false, false, false>",
-    "loss_logits": "loss_halves<true, true, false, false, true>",
-    "loss_xent": "loss_halves<true, false, false, true, true>",
+    "loss_logits": "loss_halves<true, true, false, false, 1>",
+    "loss_xent": "loss_halves<true, false, false, true, 1>",
     "trunc": "trunc_rows<1, true>",
     "rows_trunc": "verify_rows_bf16<true, true>",
 }

@@ -67,6 +67,7 @@ constexpr int kZG = kMaxGroups;                  // groups of z held per thread 
 constexpr int kHalf = kZG * kTile;               // tokens per half row
 constexpr int kZL = 8;                           // ... of which in LDS (64 KB per workgroup)
 constexpr int kZR = kZG - kZL;                   // ... and in registers
+constexpr int kWholeMaxV = kHalf;                 // rows up to this take one workgroup
 constexpr int kMaskWords = (kZG * kVec + 31) / 32;
 constexpr int kPBatch = 4;                       // groups of p in flight together
 static_assert(2 * kHalf >= kMaxV, "two halves cover the largest V");
@@ -87,6 +88,7 @@ struct Args {
   int N, W, V;
   int objective;  // LVTV_OBJ_E2E_TV or LVTV_OBJ_STEP_TV
   int spin_limit;
+  int whole;      // 1: one workgroup takes a whole row (its second half is empty)
   float* alpha;
   uint16_t* dz;
   float* dz32;           // debug output: the fp32 gradient before rounding (kDbg only)
@@ -107,29 +109,31 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// A row's halves: [0, hv) and [hv, V), hv = ceil(V / 2) rounded up to a
-// whole group (at most kHalf), so that both workgroups of a row get about
-// the same work whatever V is.
-__host__ __device__ __forceinline__ int half_len(int V) {
-  const int hv = ((V + 1) / 2 + kVec - 1) / kVec * kVec;
+// A row's halves: [0, hv) and [hv, V). With two workgroups a row, hv =
+// ceil(V / 2) rounded up to a whole group (at most kHalf), so that both get
+// about the same work whatever V is; with one (whole, V <= kHalf), hv is V
+// rounded up to a group and the second half is empty.
+__host__ __device__ __forceinline__ int half_len(int V, int whole) {
+  const int hv = ((whole ? V : (V + 1) / 2) + kVec - 1) / kVec * kVec;
   return hv < kHalf ? hv : kHalf;
 }
 
 // End of half h: its tokens are read up to here (the rest as past the end).
-__host__ __device__ __forceinline__ int half_end(int V, int h) {
-  const int e = (h + 1) * half_len(V);
+__host__ __device__ __forceinline__ int half_end(int V, int hv, int h) {
+  const int e = (h + 1) * hv;
   return e < V ? e : V;
 }
 
 // Groups (a thread's kVec tokens in each of kTile) that half h reaches;
 // the rest hold no token of it and are skipped (they would add only zeros).
-__host__ __device__ __forceinline__ int half_groups(int V, int h) {
-  return (half_end(V, h) - h * half_len(V) + kTile - 1) / kTile;
+__host__ __device__ __forceinline__ int half_groups(int V, int hv, int h) {
+  const int n = half_end(V, hv, h) - h * hv;
+  return n > 0 ? (n + kTile - 1) / kTile : 0;
 }
 
 // First token of this thread's group g in half h.
-__device__ __forceinline__ int group_elem(int V, int h, int g) {
-  return h * half_len(V) + g * kTile + int(threadIdx.x) * kVec;
+__device__ __forceinline__ int group_elem(int hv, int h, int g) {
+  return h * hv + g * kTile + int(threadIdx.x) * kVec;
 }
 
 // z group of a row: 8 bf16 tokens packed in 4 registers; tokens at or beyond
@@ -569,13 +573,13 @@ __device__ __forceinline__ uint32_t mask_bits(const uint32_t (&mask)[kMaskWords]
 // and the last launch call this with the same thread layout, so they agree
 // bit for bit.
 template <bool kVecOk>
-__device__ __forceinline__ HalfStats target_half_stats(const uint16_t* t, int V, int h, float c,
-                                                       Shared& sh) {
+__device__ __forceinline__ HalfStats target_half_stats(const uint16_t* t, int V, int hv, int h,
+                                                       float c, Shared& sh) {
   float m = -INFINITY;
   double l = 0.0;
-  const int tb = opaque(group_elem(V, h, 0));
-  const int ve = half_end(V, h);
-  const int ng = half_groups(V, h);
+  const int tb = opaque(group_elem(hv, h, 0));
+  const int ve = half_end(V, hv, h);
+  const int ng = half_groups(V, hv, h);
 #pragma unroll 1
   for (int g0 = 0; g0 < ng; g0 += kPBatch) {
     u32x4 x[kPBatch];
@@ -613,17 +617,23 @@ __device__ __forceinline__ void publish_stats(uint64_t* slot, int first, uint32_
 
 // ------------------------------------------------------------------ half-row kernel
 
-// kAll: both halves of a row reach every group (V near the largest), so the
-// tests of the group count fold away.
-template <bool kVecOk, bool kLogits, bool kDbg, bool kXent, bool kAll>
+// Row modes: two workgroups a row, groups past a half's end skipped
+// (kSplit); the same when both halves reach every group, V near the
+// largest, so the tests of the group count fold away (kSplitAll); one
+// workgroup a row, V <= kWholeMaxV (kWhole).
+constexpr int kSplit = 0, kSplitAll = 1, kWhole = 2;
+
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent, int kMode>
 __device__ __forceinline__ void half_body(const Args& a) {
   static_assert(!(kLogits && kXent), "CE and KL take a probability target here");
   __shared__ Shared sh;
   __shared__ u32x4 zl[kZL][kThreads];
   const int W = a.W, V = a.V;
   // uniform coordinates, kept in scalar registers
-  const int r = __builtin_amdgcn_readfirstlane(int(blockIdx.x) >> 1);
-  const int h = __builtin_amdgcn_readfirstlane(int(blockIdx.x) & 1);
+  constexpr bool whole = kMode == kWhole;
+  const int r = __builtin_amdgcn_readfirstlane(whole ? int(blockIdx.x) : int(blockIdx.x) >> 1);
+  const int h = __builtin_amdgcn_readfirstlane(whole ? 0 : int(blockIdx.x) & 1);
+  const int hv = half_len(V, whole);
   const int n = __builtin_amdgcn_readfirstlane(r / W);
   const int j = __builtin_amdgcn_readfirstlane(r - n * W);
   const size_t row = size_t(r);
@@ -637,10 +647,11 @@ __device__ __forceinline__ void half_body(const Args& a) {
   // 1. this half of z into the held copy
   Held zg;
   zg.lds = zl;
-  const int ve = half_end(V, h);    // this half's tokens end here
-  const int ng = kAll ? kZG : half_groups(V, h);  // groups past ng are skipped (uniform tests)
+  const int ve = half_end(V, hv, h);  // this half's tokens end here
+  // groups past ng are skipped (uniform tests)
+  const int ng = kMode == kSplitAll ? kZG : half_groups(V, hv, h);
   {
-    const int tb = opaque(group_elem(V, h, 0));
+    const int tb = opaque(group_elem(hv, h, 0));
     u32x4 tmp[kZL];
 #pragma unroll
     for (int g = 0; g < kZL; ++g)
@@ -667,11 +678,20 @@ __device__ __forceinline__ void half_body(const Args& a) {
     if (g < ng) l += (double)grp_expsum(zg.get(g), c, nm0);
   launder(zg);
   l = block_sum1(l, sh);
-  if (threadIdx.x == 0) publish_stats(slot, 0, tag, HalfStats{m, l});
+  if (threadIdx.x == 0) {
+    publish_stats(slot, 0, tag, HalfStats{m, l});
+    // a whole row: the empty second half's words, as its workgroup would
+    // have published them
+    if constexpr (whole) publish_stats(slot + kSlotWords, 0, tag, HalfStats{-INFINITY, 0.0});
+  }
   if constexpr (kLogits) {
-    const HalfStats ht = target_half_stats<kVecOk>(t, V, h, c, sh);
+    const HalfStats ht = target_half_stats<kVecOk>(t, V, hv, h, c, sh);
     launder(zg);
-    if (threadIdx.x == 0) publish_stats(slot, kTStatWord, tag, ht);
+    if (threadIdx.x == 0) {
+      publish_stats(slot, kTStatWord, tag, ht);
+      if constexpr (whole)
+        publish_stats(slot + kSlotWords, kTStatWord, tag, HalfStats{-INFINITY, 0.0});
+    }
   }
   uint64_t* rslots = a.words + row * 2 * kSlotWords;
   if (!poll_slots(rslots, 2, 0, kStatWords, tag, a.spin_limit, sh) ||
@@ -687,7 +707,7 @@ __device__ __forceinline__ void half_body(const Args& a) {
   uint32_t mask[kMaskWords];
 #pragma unroll
   for (int w = 0; w < kMaskWords; ++w) mask[w] = 0u;
-  const int tbp = opaque(group_elem(V, h, 0));
+  const int tbp = opaque(group_elem(hv, h, 0));
   const bool kl = a.objective == LVTV_OBJ_KL;
   const float mlnl = kXent ? float(row_mlnl_from(sh.words, 0, c)) : 0.f;
   constexpr int kB = kPBatch;
@@ -731,6 +751,10 @@ __device__ __forceinline__ void half_body(const Args& a) {
       f64_words(v[i], lo, hi);
       tag_store(slot + 4 + 2 * i, tag, lo);
       tag_store(slot + 5 + 2 * i, tag, hi);
+      if constexpr (whole) {  // the empty second half's parts: 0.0
+        tag_store(slot + kSlotWords + 4 + 2 * i, tag, 0u);
+        tag_store(slot + kSlotWords + 5 + 2 * i, tag, 0u);
+      }
     }
   }
   if (!poll_slots(a.words + size_t(n) * W * 2 * kSlotWords, 2 * W, 4, kPartWords, tag,
@@ -745,7 +769,7 @@ __device__ __forceinline__ void half_body(const Args& a) {
   // 5. dz of this half from the held copy and the mask (CE / KL: and p,
   //    streamed again)
   uint16_t* dz = a.dz + row * V;
-  const int tbd = opaque(group_elem(V, h, 0));
+  const int tbd = opaque(group_elem(hv, h, 0));
   if constexpr (kXent) {
 #pragma unroll
     for (int g0 = 0; g0 < kZG; g0 += kB) {
@@ -778,19 +802,19 @@ __device__ __forceinline__ void half_body(const Args& a) {
 // Statistics of half h of a row, streamed from memory (same steps and
 // reductions as a half workgroup).
 template <bool kVecOk>
-__device__ __forceinline__ HalfStats stream_half_stats(const uint16_t* z, int V, int h, float c,
-                                                       Shared& sh) {
+__device__ __forceinline__ HalfStats stream_half_stats(const uint16_t* z, int V, int hv, int h,
+                                                       float c, Shared& sh) {
   float m = -INFINITY;
-  const int ve = half_end(V, h);
-  const int ng = half_groups(V, h);
+  const int ve = half_end(V, hv, h);
+  const int ng = half_groups(V, hv, h);
 #pragma unroll 1
-  for (int g = 0; g < ng; ++g) m = grp_max(load_z<kVecOk>(z, ve, group_elem(V, h, g)), m);
+  for (int g = 0; g < ng; ++g) m = grp_max(load_z<kVecOk>(z, ve, group_elem(hv, h, g)), m);
   m = block_max(m, sh);
   const float nm0 = (m == -INFINITY) ? 0.f : -(m * c);
   double l = 0.0;
 #pragma unroll 1
   for (int g = 0; g < ng; ++g)
-    l += (double)grp_expsum(load_z<kVecOk>(z, ve, group_elem(V, h, g)), c, nm0);
+    l += (double)grp_expsum(load_z<kVecOk>(z, ve, group_elem(hv, h, g)), c, nm0);
   l = block_sum1(l, sh);
   return HalfStats{m, l};
 }
@@ -815,11 +839,12 @@ __device__ __forceinline__ void stream_half_parts(const Args& a, size_t row, int
                                                   double& al, double& sb, double& sa, Shared& sh) {
   al = sb = sa = 0.0;
   const uint16_t* z = a.z + row * a.V;
-  const int ve = half_end(a.V, h);
-  const int ng = half_groups(a.V, h);
+  const int hv = half_len(a.V, a.whole);
+  const int ve = half_end(a.V, hv, h);
+  const int ng = half_groups(a.V, hv, h);
 #pragma unroll 1
   for (int g = 0; g < ng; ++g) {
-    const int e = group_elem(a.V, h, g);
+    const int e = group_elem(hv, h, g);
     u32x4 pa, pb;
     load_target<kVecOk, kLogits>(a, row, e, ve, pa, pb);
     (void)grp_overlap<kLogits>(load_z<kVecOk>(z, ve, e), pa, pb, a.c, rs, ts, al, sb, sa);
@@ -837,11 +862,12 @@ __device__ __forceinline__ void stream_half_xent(const Args& a, size_t row, int 
   const bool kl = a.objective == LVTV_OBJ_KL;
   al = sp = part = 0.0;
   const uint16_t* z = a.z + row * a.V;
-  const int ve = half_end(a.V, h);
-  const int ng = half_groups(a.V, h);
+  const int hv = half_len(a.V, a.whole);
+  const int ve = half_end(a.V, hv, h);
+  const int ng = half_groups(a.V, hv, h);
 #pragma unroll 1
   for (int g = 0; g < ng; ++g) {
-    const int e = group_elem(a.V, h, g);
+    const int e = group_elem(hv, h, g);
     u32x4 pa, pb;
     load_target<kVecOk, false>(a, row, e, ve, pa, pb);
     grp_xent<kVecOk>(load_z<kVecOk>(z, ve, e), pa, pb, e, ve, a.c, rs, mlnl, kl, al, sp, part);
@@ -896,13 +922,14 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
       for (int hh = 0; hh < 2; ++hh) {
         const int s = 2 * k + hh;
         if (!(sh.have[s] & 1)) {
-          const HalfStats hs = stream_half_stats<kVecOk>(zk, V, hh, c, sh);
+          const HalfStats hs = stream_half_stats<kVecOk>(zk, V, half_len(V, a.whole), hh, c, sh);
           __syncthreads();
           if (threadIdx.x == 0) put_stats(bw, s, 0, hs);
           __syncthreads();
         }
         if (!(sh.have[s] & 4)) {
-          const HalfStats hs = target_half_stats<kVecOk>(a.t + rk * V, V, hh, c, sh);
+          const HalfStats hs =
+              target_half_stats<kVecOk>(a.t + rk * V, V, half_len(V, a.whole), hh, c, sh);
           __syncthreads();
           if (threadIdx.x == 0) put_stats(bw, s, kTStatWord, hs);
           __syncthreads();
@@ -946,11 +973,12 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
     const uint16_t* z = a.z + size_t(row) * V;
     uint16_t* dz = a.dz + size_t(row) * V;
     for (int hh = 0; hh < 2; ++hh) {
-      const int ve = half_end(V, hh);
-      const int ng = half_groups(V, hh);
+      const int hv = half_len(V, a.whole);
+      const int ve = half_end(V, hv, hh);
+      const int ng = half_groups(V, hv, hh);
 #pragma unroll 1
       for (int g = 0; g < ng; ++g) {
-        const int e = group_elem(V, hh, g);
+        const int e = group_elem(hv, hh, g);
         const u32x4 zv = load_z<kVecOk>(z, ve, e);
         u32x4 pa, pb;
         load_target<kVecOk, kLogits>(a, size_t(row), e, ve, pa, pb);
@@ -969,10 +997,10 @@ __device__ __forceinline__ void repair_row(const Args& a, int row, uint32_t tag,
   }
 }
 
-template <bool kVecOk, bool kLogits, bool kDbg, bool kXent, bool kAll>
+template <bool kVecOk, bool kLogits, bool kDbg, bool kXent, int kMode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void
 loss_halves(Args a) {
-  half_body<kVecOk, kLogits, kDbg, kXent, kAll>(a);
+  half_body<kVecOk, kLogits, kDbg, kXent, kMode>(a);
 }
 
 __device__ __forceinline__ int block_min(int v, Shared& sh) {
@@ -1058,13 +1086,14 @@ __global__ __launch_bounds__(256) void clear_words(u32x4* w, size_t n16) {
     w[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
-template <bool kDbg, bool kXent, bool kAll>
+template <bool kDbg, bool kXent, int kMode>
 void launch_halves(const Args& a, bool vec_ok, bool logits, unsigned rows, hipStream_t stream) {
-  auto halves = vec_ok ? (logits ? loss_halves<true, true, kDbg, false, kAll>
-                                 : loss_halves<true, false, kDbg, kXent, kAll>)
-                       : (logits ? loss_halves<false, true, kDbg, false, kAll>
-                                 : loss_halves<false, false, kDbg, kXent, kAll>);
-  hipLaunchKernelGGL(halves, dim3(2 * rows), dim3(kThreads), 0, stream, a);
+  const unsigned blocks = kMode == kWhole ? rows : 2 * rows;
+  auto halves = vec_ok ? (logits ? loss_halves<true, true, kDbg, false, kMode>
+                                 : loss_halves<true, false, kDbg, kXent, kMode>)
+                       : (logits ? loss_halves<false, true, kDbg, false, kMode>
+                                 : loss_halves<false, false, kDbg, kXent, kMode>);
+  hipLaunchKernelGGL(halves, dim3(blocks), dim3(kThreads), 0, stream, a);
 }
 
 template <bool kDbg, bool kXent>
@@ -1074,10 +1103,13 @@ hipError_t launch_kernels(const Args& a, bool vec_ok, bool logits, unsigned rows
                                  : loss_finish<true, false, kDbg, kXent>)
                        : (logits ? loss_finish<false, true, kDbg, false>
                                  : loss_finish<false, false, kDbg, kXent>);
-  if (half_groups(a.V, 0) == kZG && half_groups(a.V, 1) == kZG)
-    launch_halves<kDbg, kXent, true>(a, vec_ok, logits, rows, stream);
+  const int hv = half_len(a.V, a.whole);
+  if (a.whole)
+    launch_halves<kDbg, kXent, kWhole>(a, vec_ok, logits, rows, stream);
+  else if (half_groups(a.V, hv, 0) == kZG && half_groups(a.V, hv, 1) == kZG)
+    launch_halves<kDbg, kXent, kSplitAll>(a, vec_ok, logits, rows, stream);
   else
-    launch_halves<kDbg, kXent, false>(a, vec_ok, logits, rows, stream);
+    launch_halves<kDbg, kXent, kSplit>(a, vec_ok, logits, rows, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(finish, dim3(1), dim3(kThreads), 0, stream, a);
@@ -1131,6 +1163,9 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   a.V = c.V;
   a.objective = c.objective;
   a.spin_limit = c.spin_limit;
+  // rows that fit one workgroup's held copy go to one workgroup each: half
+  // as many workgroups, each with twice the tokens and no partner to wait for
+  a.whole = c.V <= kWholeMaxV ? 1 : 0;
   a.alpha = c.alpha;
   a.dz = c.dz;
   a.dz32 = c.dz32;

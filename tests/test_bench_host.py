@@ -56,7 +56,7 @@ def test_traffic_from_counters_scales_by_the_copy_calibration(tmp_path):
     gib_kib = float(1 << 20)
     rows = "void lvtv::vr::(anonymous namespace)::verify_rows_bf16<true, false>(Args)"
     fin = "void lvtv::vr::(anonymous namespace)::verify_finalize<1>(Args)"
-    loss = "void lvtv::lf::(anonymous namespace)::loss_halves<true, false, false, false, true>(Args)"
+    loss = "void lvtv::lf::(anonymous namespace)::loss_halves<true, false, false, false, 1>(Args)"
     finish = "void lvtv::lf::(anonymous namespace)::loss_finish<true, false, false, false>(Args)"
     clear = "lvtv::lf::(anonymous namespace)::clear_words(u32x4*, unsigned long)"
     # the counter reads half of the true fetch bytes (scale 2) and all written bytes
