@@ -324,6 +324,41 @@ def test_topkp_workspace_contents_do_not_matter():
             assert np.array_equal(x, y)
 
 
+def _offset_copy(t, offset):
+    """The values of `t` stored `offset` elements past a fresh allocation's
+    start: rows whose base is not 16-byte aligned."""
+    flat = torch.empty(t.numel() + offset, dtype=t.dtype, device=t.device)
+    view = flat[offset:].view(t.shape)
+    view.copy_(t)
+    return view
+
+
+@pytest.mark.parametrize("temperature", [0.7, 1.0])
+def test_topkp_unaligned_rows_match_aligned(temperature):
+    """Rows that are not 16-byte aligned (offset copies of the inputs) take
+    the unaligned loads in the selection and the row kernel; outputs must be
+    bit-identical to those of the aligned inputs."""
+    dev = device()
+    case = synth.verify_case(3, temperature=temperature, batch=17, vocab=40000)
+    B, _, V = case.shape
+    top_k, top_p = _settings(B, V, rotate=4)
+    inp = verify_inputs(case, dev)
+    tk = torch.from_numpy(top_k).to(dev)
+    tp = torch.from_numpy(top_p).to(dev)
+    shifted = dict(inp)
+    shifted["target_logits"] = _offset_copy(inp["target_logits"], 1)
+    shifted["draft_logits"] = _offset_copy(inp["draft_logits"], 3)
+    announce(f"topkp unaligned rows T={temperature} shape={case.shape}")
+    outs = []
+    for x in (inp, shifted):
+        acc, toks, alpha, status = lv.spec_verify_topkp(**x, top_k=tk, top_p=tp)
+        torch.cuda.synchronize(dev)
+        outs.append((acc.cpu().numpy(), toks.cpu().numpy(), alpha.cpu().numpy().view(np.uint32),
+                     status.cpu().numpy()))
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+
+
 @pytest.mark.parametrize("vocab", [None, 30000])
 def test_truncation_off_equals_plain_verify(vocab):
     """top_k <= 0 or >= V and top_p >= 1 keep every token: the outputs are
