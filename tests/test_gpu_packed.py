@@ -70,11 +70,16 @@ def test_packed_against_oracle():
         check_excused_bound(rep, tag)
 
 
-@pytest.mark.parametrize("which", ["workload5_full", "workload3_T0.6"])
+@pytest.mark.parametrize("which", ["workload5_full", "workload3_T0.6", "ragged_V9001"])
 def test_packed_equals_padded(which):
+    """Packed rows give the same outputs as padded ones; at V = 9001 the
+    packed rows (and all padded rows after the first) are not 16-byte
+    aligned."""
     dev = device()
     if which == "workload5_full":
         case = synth.verify_case(5)
+    elif which == "ragged_V9001":
+        case = synth.verify_case(5, batch=40, vocab=9001)
     else:
         case = synth.verify_case(3, temperature=0.6, batch=16)
     announce(f"packed vs padded: {which} shape={case.shape}")
