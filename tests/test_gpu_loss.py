@@ -91,6 +91,20 @@ def test_unaligned_bases_match_aligned(objective):
     assert torch.equal(ref[2].view(torch.int16), got[2].view(torch.int16))
 
 
+def test_loss_most_branches():
+    """The largest branch count (N = 65535, W = 1, V = 8; one workgroup a
+    row): the loss and every alpha against the oracle, the gradient element
+    by element on 256 branches spread over the batch."""
+    c = synth.loss_case(n_branches=65535, width=1, vocab=8)
+    z, p = c.draft_logits, c.target_probs
+    announce(f"loss most branches shape={z.shape}")
+    gpu = run_loss(z, p)
+    orc = ol.e2e_tv_loss(z, p)
+    assert rel_close(gpu["loss"], orc["loss"], LOSS_RTOL), (gpu["loss"], orc["loss"])
+    assert np.all(rel_close(gpu["alpha"], orc["alpha"], ALPHA_RTOL))
+    _check_branches(gpu, z, p, range(0, 65535, 257), "N=65535")
+
+
 def test_loss_single_position_and_branch():
     c = synth.loss_case(n_branches=1, width=1, vocab=5000)
     gpu, orc = _check_small(c.draft_logits, c.target_probs, "N=1 W=1")

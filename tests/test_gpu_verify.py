@@ -15,6 +15,8 @@ from scipy.stats import chisquare
 import lossless_verify_tv_amd as lv
 from lossless_verify_tv_amd import synth
 
+from oracle import verify as ov
+
 from .gpu_util import announce, device, logits_to_device, run_oracle_verify, run_verify, verify_inputs
 from .parity import check_excused_bound, compare_verify
 
@@ -67,6 +69,32 @@ def test_workload5_shrunk_ragged_fp32():
     case.target = synth.from_bf16(case.target)
     case.draft = synth.from_bf16(case.draft)
     _check(case, "w5-shrunk fp32 V=3001")
+
+
+def test_most_requests():
+    """The largest request count (B = 65535, Kmax = 1, V = 8, bf16; a third
+    of the requests greedy): 256 requests spread over the batch against the
+    oracle (Philox keyed on each request's own index), and no request
+    faulted."""
+    dev = device()
+    case = synth.verify_case(2, batch=65535, vocab=8, kmax=1)
+    case.temperature = np.where(np.arange(65535) % 3 == 0, 0.0, 1.0).astype(np.float32)
+    announce(f"most requests shape={case.shape}")
+    gpu = run_verify(case, dev)
+    sample = list(range(0, 65535, 257))
+    keys = ("accepted_len", "tokens", "alpha", "accept_margin", "draw_margin", "status",
+            "greedy")
+    res = [ov.verify_request(ov.decode_rows(case.target[b], case.dtype),
+                             ov.decode_rows(case.draft[b], case.dtype), case.tokens[b],
+                             case.k[b], case.temperature[b], int(case.seed[b]), b,
+                             case.shape[1]) for b in sample]
+    orc = {k: np.array([r[k] for r in res]) for k in keys}
+    g = {k: v[sample] for k, v in gpu.items()}
+    rep = compare_verify(g, orc, case.k[sample], case.shape[1])
+    assert not rep["failures"], rep["failures"][:5]
+    check_excused_bound(rep, "most requests")
+    assert np.all(gpu["status"] == 0)
+    assert np.all((gpu["accepted_len"] >= 0) & (gpu["accepted_len"] <= case.k))
 
 
 def test_k_zero_and_kmax_zero():
