@@ -105,6 +105,13 @@ def test_loss_most_branches():
     _check_branches(gpu, z, p, range(0, 65535, 257), "N=65535")
 
 
+@pytest.mark.parametrize("vocab", [1 << 20, 1000003])
+def test_loss_large_vocabulary(vocab):
+    """V far above the single-read limit (155648): the multi-pass kernels."""
+    c = synth.loss_case(n_branches=2, width=3, vocab=vocab)
+    _check_small(c.draft_logits, c.target_probs, f"N=2 W=3 V={vocab}")
+
+
 def test_loss_single_position_and_branch():
     c = synth.loss_case(n_branches=1, width=1, vocab=5000)
     gpu, orc = _check_small(c.draft_logits, c.target_probs, "N=1 W=1")

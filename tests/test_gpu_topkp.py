@@ -324,6 +324,19 @@ def test_topkp_workspace_contents_do_not_matter():
             assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("vocab", [600000, 600001])
+def test_topkp_large_vocabulary(vocab):
+    """Rows of more than 1024 chunks (V > 524288): the row kernel keeps no
+    list of kept tokens and applies the keep rule to the whole row."""
+    dev = device()
+    case = synth.verify_case(3, temperature=1.0, batch=6, vocab=vocab, kmax=2)
+    B, _, V = case.shape
+    top_k = np.array([50, 0, 1000, 5, 0, 200000], np.int32)
+    top_p = np.array([0.9, 0.8, 1.0, 1.0, 0.95, 0.5], np.float32)
+    announce(f"topkp large vocabulary shape={case.shape}")
+    _compare(case, _run_gpu(case, top_k, top_p, dev), top_k, top_p, f"V={vocab}")
+
+
 def _offset_copy(t, offset):
     """The values of `t` stored `offset` elements past a fresh allocation's
     start: rows whose base is not 16-byte aligned."""

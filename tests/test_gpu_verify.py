@@ -97,6 +97,16 @@ def test_most_requests():
     assert np.all((gpu["accepted_len"] >= 0) & (gpu["accepted_len"] <= case.k))
 
 
+@pytest.mark.parametrize("vocab", [300000, 1 << 20, 1000003])
+@pytest.mark.parametrize("temperature", [0.0, 0.8])
+def test_large_vocabulary(vocab, temperature):
+    """Rows of more than 512 chunks of 512 tokens (V > 262144): the residual
+    chunk is picked over several block scans instead of one; V = 1000003 is
+    also not a multiple of 8."""
+    case = synth.verify_case(3, temperature=temperature, batch=3, vocab=vocab, kmax=2)
+    _check(case, f"V={vocab} T={temperature}")
+
+
 def test_k_zero_and_kmax_zero():
     case = synth.verify_case(2, batch=8, vocab=4000, k_values=[0, 1, 0, 4, 2, 0, 3, 4])
     _check(case, "K_b=0 mix")
