@@ -390,6 +390,12 @@ int draft_loss_logits_fwd_bwd(const uint16_t* draft_logits, const uint16_t* targ
 /* Paths of lvtv_debug_draft_loss. */
 #define LVTV_PATH_AUTO 0       /* what the product entry points take        */
 #define LVTV_PATH_MULTI_PASS 2 /* force the multi-pass pipeline             */
+#define LVTV_PATH_REREAD 3     /* CE / KL on the single-read kernel with
+                                  every row's gradient rewritten from a
+                                  second read of the target (the product
+                                  calls do that only for rows whose
+                                  coefficient (sum p)/N rounds to another
+                                  binary32 than 1/N); same outputs        */
 
 /*
  * lvtv_debug_draft_loss -- test and debugging hook, not a product path.
@@ -397,7 +403,8 @@ int draft_loss_logits_fwd_bwd(const uint16_t* draft_logits, const uint16_t* targ
  * Runs draft_loss_fwd_bwd (target_probs given, target_logits NULL) or
  * draft_loss_logits_fwd_bwd (target_logits given with `temperature`,
  * target_probs NULL) with settings the product calls fix:
- *   path         LVTV_PATH_AUTO or LVTV_PATH_MULTI_PASS (else LVTV_ERR_OPTION);
+ *   path         LVTV_PATH_AUTO, LVTV_PATH_MULTI_PASS or LVTV_PATH_REREAD
+ *                (else LVTV_ERR_OPTION);
  *   spin_limit   polling rounds a half-row workgroup of the single-read
  *                kernel waits for the rest of its branch before leaving its
  *                row to the finishing launch, which recomputes it

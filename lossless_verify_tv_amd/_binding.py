@@ -56,7 +56,7 @@ SCHED_MAX_ITEMS = 8192  # LVTV_SCHED_MAX_ITEMS
 OBJECTIVES = {"e2e_tv": 0, "step_tv": 1, "ce": 2, "kl": 3}
 
 # Paths of lvtv_debug_draft_loss (LVTV_PATH_*).
-PATHS = {"auto": 0, "multi-pass": 2}
+PATHS = {"auto": 0, "multi-pass": 2, "reread": 3}
 SPIN_LIMIT = 1 << 16  # what the product calls use
 
 _lib = None

@@ -530,7 +530,9 @@ int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t 
   const float c = unit ? kLog2e : kLog2e * inv_t;
   // the single-read kernel serves the TV objectives (their gradients need
   // only the held z, the mask and per-row scalars) and, for a probability
-  // target, CE and KL (their gradient streams p a second time)
+  // target, CE and KL (their gradient written in the pass over p, and
+  // rewritten from a second pass where a row's target does not sum to one
+  // closely enough)
   const bool tv = objective == LVTV_OBJ_E2E_TV || objective == LVTV_OBJ_STEP_TV;
   const bool fused_ok = tv ? (!logits || lf::logits_supported()) : lf::xent_supported(logits);
   if (fused_ok && use_fused(opt, N, W, V)) {
@@ -546,6 +548,7 @@ int run_loss(const uint16_t* draft_logits, const Target& tg, int32_t N, int32_t 
     lc.objective = objective;
     lc.vec_ok = vec_ok;
     lc.spin_limit = opt.spin_limit;
+    lc.reread = opt.path == LVTV_PATH_REREAD;
     lc.loss = loss;
     lc.alpha = alpha;
     lc.dz = dlogits;
@@ -635,7 +638,8 @@ extern "C" int lvtv_debug_draft_loss(const uint16_t* draft_logits, const float* 
                                      int32_t spin_limit, float* loss, float* alpha,
                                      uint16_t* dlogits, float* dlogits_f32, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  if (path != LVTV_PATH_AUTO && path != LVTV_PATH_MULTI_PASS) return LVTV_ERR_OPTION;
+  if (path != LVTV_PATH_AUTO && path != LVTV_PATH_MULTI_PASS && path != LVTV_PATH_REREAD)
+    return LVTV_ERR_OPTION;
   if ((target_probs == nullptr) == (target_logits == nullptr)) return LVTV_ERR_NULL;
   lvtv::Options opt;
   opt.path = path;

@@ -89,6 +89,7 @@ struct Args {
   int objective;  // LVTV_OBJ_E2E_TV or LVTV_OBJ_STEP_TV
   int spin_limit;
   int whole;      // 1: one workgroup takes a whole row (its second half is empty)
+  int reread;     // CE / KL: 1 rewrites every row's dz from a second read of p
   float* alpha;
   uint16_t* dz;
   float* dz32;           // debug output: the fp32 gradient before rounding (kDbg only)
@@ -309,36 +310,82 @@ __device__ __forceinline__ uint32_t grp_overlap(const u32x4& g, const u32x4& pa,
   return bits;
 }
 
+// Stores a group's dz (8 bf16 in out; kDbg: their fp32 values g32 in dz32
+// as well): one 16-byte store inside the row, token by token in a ragged
+// last group.
+template <bool kVecOk, bool kDbg>
+__device__ __forceinline__ void store_dz(const u32x4& out, const float (&g32)[kVec], int e, int V,
+                                         uint16_t* dz, float* dz32) {
+  if (kVecOk) {
+    if (e < V) st_nt16(dz + e, out);
+  } else if (e + kVec <= V) {
+    st_nt16_u(dz + e, out);
+  } else {
+#pragma unroll
+    for (int t = 0; t < kVec; ++t)
+      if (e + t < V) dz[e + t] = uint16_t(out[t >> 1] >> (16 * (t & 1)));
+  }
+  if constexpr (kDbg) {
+#pragma unroll
+    for (int t = 0; t < kVec; ++t)
+      if (e + t < V) dz32[e + t] = g32[t];
+  }
+}
+
 // Cross-entropy and KL parts of a group (probability target): alpha's part
 // sum min(q, p), sum p, and the loss part sum p (M + ln L - z) = -sum p ln q
 // (KL adds p ln p per token), each in fp32 over the group and fp64 across
 // groups; mlnl = fl32(M + ln L) of the row. Tokens at or past V (z = -inf,
 // p = 0) add nothing (with kVecOk a group lies wholly inside or past the
-// row).
+// row). kDz: the group's dz as well, fma(q, c_p, -(p c_p)) from the same q,
+// in fp32 (g32) and as bf16 pairs (out): the gradient q (sum p)/N - p/N
+// whenever the row's coefficient (sum p)/N rounds to the same binary32 as
+// c_p = 1/N (times fl32(1/T) in both).
 constexpr float kLn2f = 0.693147180559945309f;
 
-template <bool kVecOk>
+template <bool kVecOk, bool kDz = false>
 __device__ __forceinline__ void grp_xent(const u32x4& g, const u32x4& pa, const u32x4& pb, int e,
                                          int V, float cz, const RowStats& rs, float mlnl, bool kl,
-                                         double& al, double& sp, double& sl) {
+                                         double& al, double& sp, double& sl, float c_p = 0.f,
+                                         float* g32 = nullptr, u32x4* out = nullptr) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   float a = 0.f, b = 0.f, c = 0.f;
 #pragma unroll
   for (int j = 0; j < kVec; ++j) {
     const bool in = kVecOk ? (e < V) : (e + j < V);
     const float x = zelem(g, j);
     const float p = pelem(pa, pb, j);
-    a += fminf(qval(x, cz, rs.nm, rs.inv_l), p);
+    const float q = qval(x, cz, rs.nm, rs.inv_l);
+    a += fminf(q, p);
     b += p;
     // -ln q, plus ln p for KL (from the hardware base-2 logarithm; p below
     // the smallest normal float takes ln p as 0: its term is below 1e-36)
     float t = mlnl - x;
     if (kl) t += (p >= 1.17549435e-38f) ? __builtin_amdgcn_logf(p) * kLn2f : 0.f;
     c += in ? p * t : 0.f;
+    if constexpr (kDz) {
+      g32[j] = __builtin_fmaf(q, c_p, -(p * c_p));
+      if (j & 1) {
+        const bf16x2 v = __builtin_convertvector(f32x2{g32[j - 1], g32[j]}, bf16x2);
+        (*out)[j >> 1] = __builtin_bit_cast(uint32_t, v);
+      }
+    }
   }
   al += (double)a;
   sp += (double)b;
   sl += (double)c;
 }
+
+// A buffer resource over the n bytes at p (raw, 32-bit data: the resource
+// word 0x00020000 of gfx9 parts). The hardware drops a store through it at
+// an offset at or past n, so a group that lies wholly past the end of a
+// half needs no branch around its store; a branch there per group makes the
+// compiler spill the unrolled pass over p.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, int(n), 0x00020000);
+}
+constexpr int kBufNt = 2;  // the nontemporal bit of a buffer store
 
 // Half statistics from per-thread partials: every thread's m is already the
 // block maximum; l is summed over the block.
@@ -507,20 +554,7 @@ __device__ __forceinline__ void dz_group(const u32x4& zv, uint32_t bits8, int e,
     const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
     out[h] = __builtin_bit_cast(uint32_t, b);
   }
-  if (kVecOk) {
-    if (e < V) st_nt16(dz + e, out);
-  } else if (e + kVec <= V) {
-    st_nt16_u(dz + e, out);
-  } else {
-#pragma unroll
-    for (int t = 0; t < kVec; ++t)
-      if (e + t < V) dz[e + t] = uint16_t(out[t >> 1] >> (16 * (t & 1)));
-  }
-  if constexpr (kDbg) {
-#pragma unroll
-    for (int t = 0; t < kVec; ++t)
-      if (e + t < V) dz32[e + t] = g32[t];
-  }
+  store_dz<kVecOk, kDbg>(out, g32, e, V, dz, dz32);
 }
 
 // CE / KL dz of one group, bf16 (nearest even): fma(q, c_q, -(p c_p)) with
@@ -546,20 +580,7 @@ __device__ __forceinline__ void dz_xent_group(const u32x4& zv, const u32x4& pa, 
     const bf16x2 b = __builtin_convertvector(f32x2{v2[0], v2[1]}, bf16x2);
     out[h] = __builtin_bit_cast(uint32_t, b);
   }
-  if (kVecOk) {
-    if (e < V) st_nt16(dz + e, out);
-  } else if (e + kVec <= V) {
-    st_nt16_u(dz + e, out);
-  } else {
-#pragma unroll
-    for (int t = 0; t < kVec; ++t)
-      if (e + t < V) dz[e + t] = uint16_t(out[t >> 1] >> (16 * (t & 1)));
-  }
-  if constexpr (kDbg) {
-#pragma unroll
-    for (int t = 0; t < kVec; ++t)
-      if (e + t < V) dz32[e + t] = g32[t];
-  }
+  store_dz<kVecOk, kDbg>(out, g32, e, V, dz, dz32);
 }
 
 __device__ __forceinline__ uint32_t mask_bits(const uint32_t (&mask)[kMaskWords], int g) {
@@ -710,6 +731,16 @@ __device__ __forceinline__ void half_body(const Args& a) {
   const int tbp = opaque(group_elem(hv, h, 0));
   const bool kl = a.objective == LVTV_OBJ_KL;
   const float mlnl = kXent ? float(row_mlnl_from(sh.words, 0, c)) : 0.f;
+  // CE / KL on 16-byte aligned rows: dz is written in this pass with the
+  // coefficient of a target row that sums to one (step 5 rewrites it where
+  // that is not so)
+  constexpr bool kDz = kXent && kVecOk;
+  const float c_one = kXent ? float(1.0 / double(a.N) * a.inv_t) : 0.f;
+  // (resources that end where this half's tokens end: a group past them
+  // holds zeros, which must not land on the other half's tokens)
+  const __amdgpu_buffer_rsrc_t dzr = row_rsrc(a.dz + row * V, uint32_t(ve) * 2u);
+  const __amdgpu_buffer_rsrc_t dz32r =
+      kDbg ? row_rsrc(a.dz32 + row * V, uint32_t(ve) * 4u) : row_rsrc(a.dz, 0u);
   constexpr int kB = kPBatch;
 #pragma unroll
   for (int g0 = 0; g0 < kZG; g0 += kB) {
@@ -727,9 +758,25 @@ __device__ __forceinline__ void half_body(const Args& a) {
       if (g0 + i < kZG && g0 + i < ng) {
         const int g = g0 + i;
         if constexpr (kXent) {
-          // al, sum p (in sb), the loss part (in sa)
-          grp_xent<kVecOk>(zg.get(g), pa[i], pb[i], opaque(tbp) + g * kTile, ve, c, rs, mlnl, kl,
-                           al, sb, sa);
+          // al, sum p (in sb), the loss part (in sa); dz
+          float g32[kVec];
+          u32x4 out;
+          grp_xent<kVecOk, kDz>(zg.get(g), pa[i], pb[i], opaque(tbp) + g * kTile, ve, c, rs,
+                                mlnl, kl, al, sb, sa, c_one, g32, &out);
+          if constexpr (kDz) {
+            const int e = opaque(tbp) + g * kTile;
+            __builtin_amdgcn_raw_buffer_store_b128(out, dzr, e * 2, 0, kBufNt);
+            if constexpr (kDbg) {
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  u32x4{__float_as_uint(g32[0]), __float_as_uint(g32[1]), __float_as_uint(g32[2]),
+                        __float_as_uint(g32[3])},
+                  dz32r, e * 4, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  u32x4{__float_as_uint(g32[4]), __float_as_uint(g32[5]), __float_as_uint(g32[6]),
+                        __float_as_uint(g32[7])},
+                  dz32r, e * 4 + 16, 0, 0);
+            }
+          }
         } else {
           const uint32_t bits =
               grp_overlap<kLogits>(zg.get(g), pa[i], pb[i], c, rs, ts, al, sb, sa);
@@ -766,11 +813,14 @@ __device__ __forceinline__ void half_body(const Args& a) {
   const float c_below = float(sh.coef[0]);
   const float c_above = float(sh.coef[1]);
 
-  // 5. dz of this half from the held copy and the mask (CE / KL: and p,
-  //    streamed again)
+  // 5. dz of this half from the held copy and the mask (CE / KL: written in
+  //    step 3 unless the row is not 16-byte aligned or its coefficient
+  //    (sum p)/N is not c_one's binary32; then from p, streamed again)
   uint16_t* dz = a.dz + row * V;
+  float* dz32 = kDbg ? a.dz32 + row * V : nullptr;
   const int tbd = opaque(group_elem(hv, h, 0));
   if constexpr (kXent) {
+    if (kDz && c_below == c_above && !a.reread) return;  // c_above is c_one
 #pragma unroll
     for (int g0 = 0; g0 < kZG; g0 += kB) {
       u32x4 pa[kB], pb[kB];
@@ -782,8 +832,7 @@ __device__ __forceinline__ void half_body(const Args& a) {
       for (int i = 0; i < kB; ++i)
         if (g0 + i < kZG && g0 + i < ng)
           dz_xent_group<kVecOk, kDbg>(zg.get(g0 + i), pa[i], pb[i], opaque(tbd) + (g0 + i) * kTile,
-                                      ve, c, rs, c_below, c_above, dz,
-                                      kDbg ? a.dz32 + row * V : nullptr);
+                                      ve, c, rs, c_below, c_above, dz, dz32);
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
@@ -791,7 +840,7 @@ __device__ __forceinline__ void half_body(const Args& a) {
     for (int g = 0; g < kZG; ++g) {
       if (g < ng)
         dz_group<kVecOk, kDbg>(zg.get(g), mask_bits(mask, g), opaque(tbd) + g * kTile, ve, c, rs,
-                               c_below, c_above, dz, kDbg ? a.dz32 + row * V : nullptr);
+                               c_below, c_above, dz, dz32);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -1166,6 +1215,7 @@ hipError_t run(const LossCall& c, void* workspace, hipStream_t stream) {
   // rows that fit one workgroup's held copy go to one workgroup each: half
   // as many workgroups, each with twice the tokens and no partner to wait for
   a.whole = c.V <= kWholeMaxV ? 1 : 0;
+  a.reread = c.reread ? 1 : 0;
   a.alpha = c.alpha;
   a.dz = c.dz;
   a.dz32 = c.dz32;

@@ -23,6 +23,7 @@ struct LossCall {
   int N, W, V;
   int objective;  // LVTV_OBJ_E2E_TV or LVTV_OBJ_STEP_TV
   bool vec_ok;
+  bool reread;            // CE / KL: every row's dz from a second read of p (debug)
   int spin_limit;
   float* loss;
   float* alpha;

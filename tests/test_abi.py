@@ -31,6 +31,17 @@ def lib():
     return lv.load_library()
 
 
+def test_binding_constants_match_the_header():
+    """The binding's objective and debug-path codes are the header's."""
+    text = open(HEADER).read()
+    defs = {k: int(v) for k, v in re.findall(r"#define\s+(LVTV_\w+)\s+\(?(-?\d+)\)?", text)}
+    paths = {k[len("LVTV_PATH_"):].lower().replace("_", "-"): v
+             for k, v in defs.items() if k.startswith("LVTV_PATH_")}
+    assert paths == _binding.PATHS
+    objs = {k[len("LVTV_OBJ_"):].lower(): v for k, v in defs.items() if k.startswith("LVTV_OBJ_")}
+    assert objs == _binding.OBJECTIVES
+
+
 def test_exports_every_declared_function(lib):
     declared = _declared_functions()
     assert set(declared) == set(lv.EXPORTS)
@@ -139,6 +150,7 @@ def test_debug_loss_host_errors(lib):
         z=FAKE, p=FAKE, t=NULL, T=1.0, N=4, W=3, V=100, obj=0, path=0, spin=0, loss=FAKE,
         alpha=FAKE, dz=FAKE, dz32=NULL, ws=FAKE, wsb=need, stream=NULL), **kw}.values())
     assert call(path=1) == -8
+    assert call(path=4) == -8
     assert call(path=7) == -8
     assert call(p=NULL) == -1              # neither target
     assert call(t=FAKE) == -1              # both targets

@@ -4,10 +4,12 @@ comparators: per-step TV, CE, KL) against the oracle, through the C ABI.
 Small and ragged shapes are compared element by element. At the full
 workload (N=512, W=7, V=151936) the loss and every alpha are compared with
 the oracle run over all 512 branches, the gradient on 32 branches. Every
-comparator runs on the single-read kernel (CE and KL streaming p a second
-time for the gradient) and, forced through the debug entry point, on the
-multi-pass pipeline; the single-read kernel's repair launch gives the same
-bits. Gradient rules: tests/parity.py."""
+comparator runs on the single-read kernel and, forced through the debug
+entry point, on the multi-pass pipeline; the single-read kernel's repair
+launch gives the same bits. CE and KL write the gradient in the kernel's
+pass over p where a row's coefficient (sum p)/N rounds to 1/N's binary32,
+and from a second read of p elsewhere; forcing the second read on every
+row gives the same bits. Gradient rules: tests/parity.py."""
 
 import numpy as np
 import pytest
@@ -132,3 +134,49 @@ def test_comparators_full_workload_against_the_oracle(objective):
     sample = list(range(0, N, 16))
     _check_branches(gpu, c.draft_logits, c.target_probs, objective, sample,
                     f"{objective} full, 32 branches")
+
+
+def _targets_on_both_routes(c):
+    """The case's targets with rows that certainly take each CE / KL route:
+    row (0, 0) one-hot and row (0, 1) uniform over a power-of-two count of
+    tokens (their sums are exactly one in any order: the gradient is written
+    in the pass over p), row (1, 0) scaled by 1.001 and row (1, 1) by 0.5
+    (their coefficients round elsewhere: the second read rewrites them)."""
+    p = c.target_probs.copy()
+    V = p.shape[2]
+    p[0, 0] = 0.0
+    p[0, 0, V // 3] = 1.0
+    k = 1 << (V.bit_length() - 2)
+    p[0, 1] = 0.0
+    p[0, 1, :k] = np.float32(1.0 / k)
+    p[1, 0] *= np.float32(1.001)
+    p[1, 1] *= np.float32(0.5)
+    return p
+
+
+@pytest.mark.parametrize("objective", ["ce", "kl"])
+@pytest.mark.parametrize("shape", [(4, 7, 24000), (3, 5, 100000), (2, 3, 151936),
+                                   (5, 2, 155648), (3, 4, 20001)])
+def test_xent_gradient_in_one_pass_equals_the_second_read(objective, shape):
+    """One workgroup a row (V=24000), halves that skip groups (V=100000),
+    halves with every group (V=151936, V=155648), an unaligned row length
+    (V=20001: always the second read); N not a power of two, so 1/N is not
+    exact. Every output bit-identical, the fp32 gradient too."""
+    N, W, V = shape
+    c = synth.loss_case(n_branches=N, width=W, vocab=V)
+    p = _targets_on_both_routes(c)
+    announce(f"{objective} one pass vs second read shape={shape}")
+    one = run_debug_loss(c.draft_logits, p, objective, path="auto", want_f32=True)
+    two = run_debug_loss(c.draft_logits, p, objective, path="reread", want_f32=True)
+    assert one["loss"] == two["loss"]
+    assert np.array_equal(one["alpha"], two["alpha"])
+    assert np.array_equal(one["dlogits"], two["dlogits"])
+    assert np.array_equal(one["dlogits_f32"].view(np.uint32), two["dlogits_f32"].view(np.uint32))
+
+
+@pytest.mark.parametrize("objective", ["ce", "kl"])
+@pytest.mark.parametrize("vocab", [24000, 151936])
+def test_xent_targets_on_both_routes_against_the_oracle(objective, vocab):
+    c = synth.loss_case(n_branches=3, width=4, vocab=vocab)
+    _check_small(c.draft_logits, _targets_on_both_routes(c), objective,
+                 f"{objective} one-hot, dyadic and scaled targets V={vocab}")
