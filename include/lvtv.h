@@ -339,10 +339,11 @@ size_t draft_loss_workspace_bytes(int32_t N, int32_t W, int32_t V);
  *   Other arguments, layouts, workspace rules and errors as for
  *   e2e_tv_loss_fwd_bwd; an unknown objective returns LVTV_ERR_OBJECTIVE
  *   before enqueueing anything.
- * Every objective runs the single-read kernel when V <= 155648: the TV
- * objectives read z and p once and write dz once; CE and KL read p a second
- * time for the gradient. Larger V take the multi-pass pipeline (z read three
- * times, p twice).
+ * Every objective runs the single-read kernel when V <= 155648: z and p
+ * are read once and dz written once (CE and KL read p a second time for a
+ * row whose coefficient (sum p)/N rounds to another binary32 than 1/N, or
+ * whose data is not 16-byte aligned). Larger V take the multi-pass pipeline
+ * (z read three times, p twice).
  */
 int draft_loss_fwd_bwd(const uint16_t* draft_logits, const float* target_probs,
                        int32_t N, int32_t W, int32_t V, int objective,
